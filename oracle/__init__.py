@@ -1,0 +1,132 @@
+"""fp64 CPU oracle for the selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library (``selective_state_space_51_amd``)
+never does: it shares no code with the oracle and fails loudly if its own HIP
+extension is missing.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, the
+recurrence in the order the method writes it).  This module compiles it with
+gcc and marshals numpy float64 arrays.  Every function here follows the
+passages cited at the top of ``oracle.c``.
+
+Pins (the tests under ``tests/test_oracle_*.py``) check these functions against
+closed forms, library routines, brute force and invariants; no function here
+is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-O2", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-pthread"]
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (no GPU needed)."""
+    cmd = ["gcc", *CFLAGS, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: Optional[str] = None):
+    """Load liboracle.so, building it first only if it is not there."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        build(out=p)
+    lib = ctypes.CDLL(p)
+    dp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    lib.oracle_selscan.argtypes = [dp] * 8 + [ci, ci, dp, dp, dp, i64, i64, i64, i64, ci]
+    lib.oracle_selscan.restype = ci
+    lib.oracle_selscan_bidir.argtypes = [dp] * 8 + [ci, ci, dp, i64, i64, i64, i64, ci]
+    lib.oracle_selscan_bidir.restype = ci
+    lib.oracle_ss2d.argtypes = [dp] * 8 + [ci, ci, dp, i64, i64, i64, i64, i64, ci]
+    lib.oracle_ss2d.restype = ci
+    lib.oracle_default_threads.argtypes = []
+    lib.oracle_default_threads.restype = ci
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def default_threads() -> int:
+    return int(load().oracle_default_threads())
+
+
+def selscan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, zoh=False,
+            h0=None, return_h_last=False, nthreads=0, lib=None):
+    """Single-direction selective scan.
+
+    x, delta, z: [batch][L][dim]; B, C: [batch][L][N]; A: [dim][N]; D, delta_bias: [dim];
+    h0: [batch][dim][N].  Returns y (and h_last [batch][dim][N] if asked).
+    """
+    lib = lib or load()
+    x, delta, A, B, C, D, z, delta_bias, h0 = map(_f64, (x, delta, A, B, C, D, z, delta_bias, h0))
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    assert delta.shape == x.shape and B.shape == (bt, L, N) and C.shape == (bt, L, N) and A.shape == (dim, N)
+    y = np.empty_like(x)
+    hl = np.empty((bt, dim, N)) if return_h_last else None
+    rc = lib.oracle_selscan(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                            int(bool(delta_softplus)), int(bool(zoh)), _ptr(h0), _ptr(hl), _ptr(y),
+                            bt, L, dim, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_selscan failed")
+    return (y, hl) if return_h_last else y
+
+
+def selscan_bidir(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, zoh=False,
+                  nthreads=0, lib=None):
+    """Bidirectional scan: per-direction arrays stacked on a leading axis of 2, token order."""
+    lib = lib or load()
+    x, delta, A, B, C, D, z, delta_bias = map(_f64, (x, delta, A, B, C, D, z, delta_bias))
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    assert delta.shape == (2, bt, L, dim) and B.shape == (2, bt, L, N) and A.shape == (2, dim, N)
+    y = np.empty_like(x)
+    rc = lib.oracle_selscan_bidir(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh)), _ptr(y),
+                                  bt, L, dim, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_selscan_bidir failed")
+    return y
+
+
+def ss2d(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_softplus=False, zoh=False,
+         nthreads=0, lib=None):
+    """SS2D four-direction scan with merge; per-direction arrays [4][...] in pixel order."""
+    lib = lib or load()
+    x, delta, A, B, C, D, z, delta_bias = map(_f64, (x, delta, A, B, C, D, z, delta_bias))
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    assert L == H * W and delta.shape == (4, bt, L, dim) and B.shape == (4, bt, L, N) and A.shape == (4, dim, N)
+    y = np.empty_like(x)
+    rc = lib.oracle_ss2d(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                         int(bool(delta_softplus)), int(bool(zoh)), _ptr(y), bt, H, W, dim, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_ss2d failed")
+    return y

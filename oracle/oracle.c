@@ -1,0 +1,295 @@
+/*
+ * oracle.c - plain, slow, double-precision CPU oracle for the selective
+ * state-space scan (the S6 core of Mamba) and its two vision variants.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Tests, the smoke check and the CPU-baseline leg
+ * of the benchmark may load this; the library's product path never does, and
+ * this file shares no code, header or table with the HIP kernels.
+ *
+ * Passages followed (page title, then section):
+ *  [MS] "Mamba Series from Selective State Spaces to Visual State Space Models"
+ *       - section "选择性 SSM 的数学形式" (mathematical form of the selective SSM):
+ *         continuous system h' = A h + B x, y = C h; zero-order-hold discretisation
+ *         Abar = exp(dA), Bbar = (dA)^-1 (exp(dA) - I) dB; selection
+ *         delta = softplus(W x + b), B = W_B x, C = W_C x, A a fixed diagonal.
+ *       - section "关键代码" (key code), cross_scan_fwd and SS2Dv0.forwardv0: the four
+ *         scan orders (row-major, column-major and the reversal of each), the scan
+ *         call with per-direction A, Ds, delta_bias and delta_softplus, the merge of the
+ *         four outputs back to pixel order by flip / transpose and sum, the SiLU gate.
+ *       - section "核心洞察", insight 1: the time-varying recurrence is evaluated as a
+ *         scan (here: the plain sequential recurrence, which the parallel scan
+ *         reassociates).
+ *  [LM] "从LSTM到Mamba：双向状态空间模型如何重塑视觉序列建模"
+ *       - §2.1: h' = A h + B x, y = C h + D x (the D skip term).
+ *       - §3.1: bidirectional SSM, a forward scan and a scan over reverse(x).
+ *
+ * Readings where the pages are silent or disagree (each listed in the design notes):
+ *  - Bbar: the default is Bbar = delta * B (Euler; what the workload statement uses);
+ *    zoh != 0 selects the [MS] zero-order-hold Bbar = expm1(delta*A)/A * B (delta*B at A = 0).
+ *  - initial state is zero unless h0 is given; D, z, delta_bias may be absent.
+ *  - bidirectional fusion is the SUM of the forward output and the backward output
+ *    re-reversed to token order (the page concatenates); one gate on the sum.
+ *  - SS2D per-direction delta, B, C are stored in pixel order; direction k visits pixel
+ *    pi_k(l) at scan step l (see ss2d_pixel below); outputs are added at the same pixel.
+ *
+ * Every function returns 0 on success, -1 on a bad argument.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---- scalar helpers ---------------------------------------------------- */
+
+/* softplus(w) = log(1 + e^w), written so that neither branch overflows. */
+static double softplus(double w) { return w > 0.0 ? w + log1p(exp(-w)) : log1p(exp(w)); }
+
+/* silu(z) = z * sigmoid(z); sigmoid evaluated on the side where exp cannot overflow. */
+static double silu(double z) {
+    if (z >= 0.0) return z / (1.0 + exp(-z));
+    double e = exp(z);
+    return z * e / (1.0 + e);
+}
+
+/* ---- one direction of the scan over [batch][L][dim] --------------------- */
+
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *D, *delta_bias, *h0;
+    double *y_pre; /* sum_n C h + D x, before any gate */
+    double *h_last;
+    int64_t batch, L, dim, N;
+    int softplus, zoh;
+} scan_t;
+
+/* The recurrence for stream (b, d), in the order the method writes it:
+ *   delta_t = softplus(delta[b,t,d] + bias[d])           (when enabled)
+ *   h_t[n]  = exp(delta_t A[d,n]) h_{t-1}[n] + Bbar_t[n] x[b,t,d]
+ *   y_t     = sum_n C[b,t,n] h_t[n] + D[d] x[b,t,d]                              */
+static void scan_stream(const scan_t *s, int64_t b, int64_t d, double *h) {
+    const int64_t N = s->N, dim = s->dim, L = s->L;
+    for (int64_t n = 0; n < N; ++n) h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;
+    const double Dd = s->D ? s->D[d] : 0.0;
+    const double *Arow = s->A + d * N;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * dim + d;
+        double dt = s->delta[i];
+        if (s->delta_bias) dt += s->delta_bias[d];
+        if (s->softplus) dt = softplus(dt);
+        const double xv = s->x[i];
+        const double *Bt = s->B + (b * L + t) * N;
+        const double *Ct = s->C + (b * L + t) * N;
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double a = Arow[n];
+            const double Abar = exp(dt * a);
+            double Bbar;
+            if (s->zoh)
+                Bbar = (a != 0.0 ? expm1(dt * a) / a : dt) * Bt[n];
+            else
+                Bbar = dt * Bt[n];
+            h[n] = Abar * h[n] + Bbar * xv;
+            acc += Ct[n] * h[n];
+        }
+        s->y_pre[i] = acc + Dd * xv;
+    }
+    if (s->h_last)
+        for (int64_t n = 0; n < N; ++n) s->h_last[(b * dim + d) * N + n] = h[n];
+}
+
+typedef struct {
+    const scan_t *s;
+    int64_t first, last; /* stream range [first, last) over batch*dim */
+} job_t;
+
+static void *scan_worker(void *p) {
+    const job_t *j = (const job_t *)p;
+    double *h = (double *)malloc(sizeof(double) * (size_t)j->s->N);
+    if (!h) return (void *)1;
+    for (int64_t q = j->first; q < j->last; ++q) scan_stream(j->s, q / j->s->dim, q % j->s->dim, h);
+    free(h);
+    return NULL;
+}
+
+static int resolve_threads(int nthreads, int64_t streams) {
+    if (nthreads <= 0) {
+        long c = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = c > 0 ? (int)c : 1;
+    }
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > streams) nthreads = (int)(streams > 0 ? streams : 1);
+    return nthreads;
+}
+
+static int run_scan(const scan_t *s, int nthreads) {
+    const int64_t streams = s->batch * s->dim;
+    if (streams == 0 || s->L == 0) {
+        if (s->h_last && s->L == 0)
+            for (int64_t q = 0; q < streams * s->N; ++q) s->h_last[q] = s->h0 ? s->h0[q] : 0.0;
+        return 0;
+    }
+    nthreads = resolve_threads(nthreads, streams);
+    pthread_t tid[256];
+    int live[256];
+    job_t jobs[256];
+    int rc = 0;
+    for (int k = 0; k < nthreads; ++k) {
+        jobs[k].s = s;
+        jobs[k].first = streams * k / nthreads;
+        jobs[k].last = streams * (k + 1) / nthreads;
+        live[k] = 0;
+    }
+    /* threads 1..n-1 run in the background, share 0 runs here; a thread that cannot be
+     * started has its share run here too */
+    for (int k = 1; k < nthreads; ++k) live[k] = pthread_create(&tid[k], NULL, scan_worker, &jobs[k]) == 0;
+    if (scan_worker(&jobs[0])) rc = -1;
+    for (int k = 1; k < nthreads; ++k) {
+        void *ret = NULL;
+        if (live[k]) {
+            if (pthread_join(tid[k], &ret) != 0 || ret) rc = -1;
+        } else if (scan_worker(&jobs[k])) {
+            rc = -1;
+        }
+    }
+    return rc;
+}
+
+static int bad_common(const void *x, const void *delta, const void *A, const void *B, const void *C,
+                      const void *y, int64_t batch, int64_t L, int64_t dim, int64_t N) {
+    return !x || !delta || !A || !B || !C || !y || batch < 0 || L < 0 || dim < 0 || N <= 0;
+}
+
+/* ---- public entry points ------------------------------------------------ */
+
+/* Single-direction scan.  x, delta, z, y: [batch][L][dim]; B, C: [batch][L][N];
+ * A: [dim][N]; D, delta_bias: [dim]; h0, h_last: [batch][dim][N].  D, z, delta_bias,
+ * h0, h_last may be NULL.  y = (sum_n C h + D x) * silu(z), the gate only if z is given. */
+int oracle_selscan(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                   const double *D, const double *z, const double *delta_bias, int delta_softplus, int zoh,
+                   const double *h0, double *h_last, double *y, int64_t batch, int64_t L, int64_t dim,
+                   int64_t N, int nthreads) {
+    if (bad_common(x, delta, A, B, C, y, batch, L, dim, N)) return -1;
+    scan_t s = {x, delta, A, B, C, D, delta_bias, h0, y, h_last, batch, L, dim, N, delta_softplus, zoh};
+    if (run_scan(&s, nthreads)) return -1;
+    if (z) {
+        const int64_t tot = batch * L * dim;
+        for (int64_t i = 0; i < tot; ++i) y[i] *= silu(z[i]);
+    }
+    return 0;
+}
+
+/* reverse the time axis of a [batch][L][w] array into out */
+static void reverse_time(const double *in, double *out, int64_t batch, int64_t L, int64_t w) {
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t t = 0; t < L; ++t)
+            memcpy(out + (b * L + t) * w, in + (b * L + (L - 1 - t)) * w, sizeof(double) * (size_t)w);
+}
+
+/* Bidirectional scan ([LM] §3.1).  delta, B, C, A, D, delta_bias carry a leading
+ * direction axis of 2: [0] forward, [1] backward; all per-token arrays are in token
+ * order.  Direction 1 is the same scan run over the time-reversed sequence with its own
+ * parameters; its output is reversed back to token order and added to direction 0's.
+ * y = (y_fwd + y_bwd) * silu(z).                                                        */
+int oracle_selscan_bidir(const double *x, const double *delta, const double *A, const double *B,
+                         const double *C, const double *D, const double *z, const double *delta_bias,
+                         int delta_softplus, int zoh, double *y, int64_t batch, int64_t L, int64_t dim,
+                         int64_t N, int nthreads) {
+    if (bad_common(x, delta, A, B, C, y, batch, L, dim, N)) return -1;
+    const int64_t tok = batch * L * dim, bc = batch * L * N;
+    int rc = 0;
+    double *yf = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *xr = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *dr = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *yr = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *Br = (double *)malloc(sizeof(double) * (size_t)(bc ? bc : 1));
+    double *Cr = (double *)malloc(sizeof(double) * (size_t)(bc ? bc : 1));
+    if (!yf || !xr || !dr || !yr || !Br || !Cr) { rc = -1; goto done; }
+    {
+        /* forward direction, in token order */
+        scan_t f = {x, delta, A, B, C, D, delta_bias, NULL, yf, NULL, batch, L, dim, N, delta_softplus, zoh};
+        if (run_scan(&f, nthreads)) { rc = -1; goto done; }
+        /* backward direction: reverse(x) and direction-1 parameters reversed */
+        reverse_time(x, xr, batch, L, dim);
+        reverse_time(delta + tok, dr, batch, L, dim);
+        reverse_time(B + bc, Br, batch, L, N);
+        reverse_time(C + bc, Cr, batch, L, N);
+        scan_t r = {xr, dr, A + dim * N, Br, Cr, D ? D + dim : NULL, delta_bias ? delta_bias + dim : NULL,
+                    NULL, yr, NULL, batch, L, dim, N, delta_softplus, zoh};
+        if (run_scan(&r, nthreads)) { rc = -1; goto done; }
+        reverse_time(yr, y, batch, L, dim); /* back to token order */
+        for (int64_t i = 0; i < tok; ++i) y[i] += yf[i];
+        if (z)
+            for (int64_t i = 0; i < tok; ++i) y[i] *= silu(z[i]);
+    }
+done:
+    free(yf); free(xr); free(dr); free(yr); free(Br); free(Cr);
+    return rc;
+}
+
+/* Pixel visited at scan step l by direction k on an H x W map stored row-major
+ * (pixel p = h*W + w, L = H*W), as the [MS] cross-scan builds the sequences:
+ *   k = 0: row-major flatten                      -> p = l
+ *   k = 1: transpose(H, W) then flatten           -> l = w*H + h, so p = (l % H)*W + l / H
+ *   k = 2: k = 0 flipped along the sequence       -> step L-1-l of k = 0
+ *   k = 3: k = 1 flipped along the sequence       -> step L-1-l of k = 1                    */
+static int64_t ss2d_pixel(int k, int64_t l, int64_t H, int64_t W) {
+    const int64_t L = H * W;
+    if (k >= 2) l = L - 1 - l;
+    if (k == 0 || k == 2) return l;
+    return (l % H) * W + l / H;
+}
+
+/* SS2D four-direction scan with merge ([MS] cross_scan_fwd, SS2Dv0.forwardv0).
+ * x, z, y: [batch][H*W][dim] (pixels row-major); delta: [4][batch][H*W][dim];
+ * B, C: [4][batch][H*W][N]; A: [4][dim][N]; D, delta_bias: [4][dim].  Per-direction
+ * arrays are in pixel order.  For each direction k the sequence of pixels pi_k(0..L-1)
+ * is gathered, scanned with direction k's parameters, and each output is added at the
+ * pixel it came from.  The page gates after a normalisation outside the scan, so z is
+ * normally absent; if given, it gates the merged sum.                                    */
+int oracle_ss2d(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                const double *D, const double *z, const double *delta_bias, int delta_softplus, int zoh,
+                double *y, int64_t batch, int64_t H, int64_t W, int64_t dim, int64_t N, int nthreads) {
+    if (H < 0 || W < 0) return -1;
+    const int64_t L = H * W;
+    if (bad_common(x, delta, A, B, C, y, batch, L, dim, N)) return -1;
+    const int64_t tok = batch * L * dim, bc = batch * L * N;
+    int rc = 0;
+    double *xs = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *ds = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *os = (double *)malloc(sizeof(double) * (size_t)(tok ? tok : 1));
+    double *Bs = (double *)malloc(sizeof(double) * (size_t)(bc ? bc : 1));
+    double *Cs = (double *)malloc(sizeof(double) * (size_t)(bc ? bc : 1));
+    if (!xs || !ds || !os || !Bs || !Cs) { rc = -1; goto done; }
+    for (int64_t i = 0; i < tok; ++i) y[i] = 0.0;
+    for (int k = 0; k < 4; ++k) {
+        for (int64_t b = 0; b < batch; ++b)
+            for (int64_t l = 0; l < L; ++l) {
+                const int64_t p = ss2d_pixel(k, l, H, W);
+                memcpy(xs + (b * L + l) * dim, x + (b * L + p) * dim, sizeof(double) * (size_t)dim);
+                memcpy(ds + (b * L + l) * dim, delta + k * tok + (b * L + p) * dim, sizeof(double) * (size_t)dim);
+                memcpy(Bs + (b * L + l) * N, B + k * bc + (b * L + p) * N, sizeof(double) * (size_t)N);
+                memcpy(Cs + (b * L + l) * N, C + k * bc + (b * L + p) * N, sizeof(double) * (size_t)N);
+            }
+        scan_t s = {xs, ds, A + k * dim * N, Bs, Cs, D ? D + k * dim : NULL,
+                    delta_bias ? delta_bias + k * dim : NULL, NULL, os, NULL, batch, L, dim, N,
+                    delta_softplus, zoh};
+        if (run_scan(&s, nthreads)) { rc = -1; goto done; }
+        for (int64_t b = 0; b < batch; ++b)
+            for (int64_t l = 0; l < L; ++l) {
+                const int64_t p = ss2d_pixel(k, l, H, W);
+                for (int64_t d = 0; d < dim; ++d) y[(b * L + p) * dim + d] += os[(b * L + l) * dim + d];
+            }
+    }
+    if (z)
+        for (int64_t i = 0; i < tok; ++i) y[i] *= silu(z[i]);
+done:
+    free(xs); free(ds); free(os); free(Bs); free(Cs);
+    return rc;
+}
+
+/* number of hardware threads the oracle would use for nthreads <= 0 */
+int oracle_default_threads(void) {
+    long c = sysconf(_SC_NPROCESSORS_ONLN);
+    return c > 0 ? (int)c : 1;
+}

@@ -1,0 +1,352 @@
+"""Pins for the fp64 oracle: each checks it against something other than itself.
+
+Every ``pin_*`` function takes a loaded oracle library (so the mutation test can
+run the same pins against copies of the oracle with planted mistakes) and
+raises AssertionError when the oracle disagrees with the closed form, library
+routine, brute-force evaluation or invariant it is pinned to.
+
+Passages behind each identity are named in each docstring:
+  [MS] "Mamba Series from Selective State Spaces to Visual State Space Models"
+  [LM] "从LSTM到Mamba：双向状态空间模型如何重塑视觉序列建模"
+"""
+from __future__ import annotations
+
+import decimal
+import math
+
+import numpy as np
+import scipy.signal
+
+import oracle
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if not (np.isfinite(a).all() and np.isfinite(b).all()):
+        return float("inf")
+    scale = max(np.abs(b).max(), 1e-300)
+    return float(np.abs(a - b).max() / scale)
+
+
+def _silu_np(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _case(seed, bt=2, L=33, dim=5, N=4, const=False):
+    r = _rng(seed)
+    x = r.standard_normal((bt, L, dim))
+    z = r.standard_normal((bt, L, dim))
+    if const:
+        dt = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), (bt, 1, dim))) * np.ones((1, L, 1))
+        B = r.standard_normal((bt, 1, N)) * np.ones((1, L, 1))
+        C = r.standard_normal((bt, 1, N)) * np.ones((1, L, 1))
+    else:
+        dt = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), (bt, L, dim)))
+        B = r.standard_normal((bt, L, N))
+        C = r.standard_normal((bt, L, N))
+    A = -np.exp(r.uniform(-1.0, 1.5, (dim, N)))
+    D = r.standard_normal(dim)
+    return x, z, dt, A, B, C, D
+
+
+# --------------------------------------------------------------------------- P-a
+def pin_lti_convolution(lib):
+    """P-a.  With delta, B, C constant in time the SSM is linear time-invariant and equals a
+    causal convolution of x with K_k = sum_n C_n exp(k delta A_n) Bbar_n ([MS] "选择性 SSM 的数学形式"
+    and insight 1: the LTI SSM is a global convolution; [LM] §2.1 convolution view).
+    Checked for both discretisations of Bbar, with D and the gate."""
+    for zoh in (False, True):
+        x, z, dt, A, B, C, D = _case(11 + zoh, bt=2, L=64, dim=3, N=5, const=True)
+        y = oracle.selscan(x, dt, A, B, C, D=D, z=z, zoh=zoh, lib=lib)
+        ref = np.empty_like(x)
+        L = x.shape[1]
+        k = np.arange(L)
+        for b in range(x.shape[0]):
+            for d in range(x.shape[2]):
+                delta = dt[b, 0, d]
+                a = A[d]
+                bbar = (np.expm1(delta * a) / a) * B[b, 0] if zoh else delta * B[b, 0]
+                K = (C[b, 0][None, :] * np.exp(np.outer(k, delta * a)) * bbar[None, :]).sum(axis=1)
+                conv = np.convolve(x[b, :, d], K)[:L]
+                ref[b, :, d] = (conv + D[d] * x[b, :, d]) * _silu_np(z[b, :, d])
+        assert _rel(y, ref) < 1e-12, ("lti", zoh, _rel(y, ref))
+
+
+# --------------------------------------------------------------------------- P-b
+def pin_delta_to_zero(lib):
+    """P-b.  Abar = exp(delta A) -> 1 and Bbar -> 0 as delta -> 0 ([MS] discretisation), so
+    y -> D x silu(z) and the gap shrinks linearly in delta (ratio 100 for delta 1e-6 vs 1e-8)."""
+    x, z, dt, A, B, C, D = _case(21, bt=1, L=40, dim=4, N=6)
+    base = D[None, None, :] * x * _silu_np(z)
+    gaps = []
+    for delta in (1e-6, 1e-8):
+        y = oracle.selscan(x, np.full_like(x, delta), A, B, C, D=D, z=z, lib=lib)
+        gaps.append(np.abs(y - base).max())
+    assert gaps[1] < 1e-6, gaps
+    assert abs(gaps[0] / gaps[1] / 100.0 - 1.0) < 0.02, gaps
+    y0 = oracle.selscan(x, np.zeros_like(x), A, B, C, D=D, z=z, lib=lib)
+    assert np.array_equal(y0, D[None, None, :] * x * (z / (1.0 + np.exp(-z)))) or _rel(y0, base) < 1e-15
+
+
+# --------------------------------------------------------------------------- P-c
+def pin_a_zero_prefix_sum(lib):
+    """P-c.  A = 0 makes Abar = 1, so h_t = sum_{s<=t} delta_s B_s x_s (a prefix sum).  With
+    dyadic delta and small-integer B, C, x, D every value is exact in binary floating
+    point, so the oracle must match numpy.cumsum bit for bit."""
+    r = _rng(31)
+    bt, L, dim, N = 2, 50, 3, 4
+    x = r.integers(-3, 4, (bt, L, dim)).astype(np.float64)
+    dt = r.choice([0.25, 0.5, 0.125], (bt, L, dim))
+    B = r.integers(-2, 3, (bt, L, N)).astype(np.float64)
+    C = r.integers(-2, 3, (bt, L, N)).astype(np.float64)
+    D = r.integers(-2, 3, dim).astype(np.float64)
+    A = np.zeros((dim, N))
+    y = oracle.selscan(x, dt, A, B, C, D=D, lib=lib)
+    h = np.cumsum((dt * x)[:, :, :, None] * B[:, :, None, :], axis=1)  # [bt, L, dim, N]
+    ref = np.einsum("btn,btdn->btd", C, h) + D[None, None, :] * x
+    assert np.array_equal(y, ref), np.abs(y - ref).max()
+
+
+# --------------------------------------------------------------------------- P-d
+def pin_first_order_iir(lib):
+    """P-d.  N = 1 and constant delta: h_t = e^{delta A} h_{t-1} + delta B_t x_t is a first-order
+    IIR filter; scipy.signal.lfilter evaluates it independently."""
+    r = _rng(41)
+    L = 300
+    x = r.standard_normal((1, L, 1))
+    B = r.standard_normal((1, L, 1))
+    C = r.standard_normal((1, L, 1))
+    delta, a, Dd = 0.07, -0.8, 0.3
+    y = oracle.selscan(x, np.full_like(x, delta), np.array([[a]]), B, C, D=np.array([Dd]), lib=lib)
+    h = scipy.signal.lfilter([1.0], [1.0, -math.exp(delta * a)], delta * B[0, :, 0] * x[0, :, 0])
+    ref = C[0, :, 0] * h + Dd * x[0, :, 0]
+    assert _rel(y[0, :, 0], ref) < 1e-12
+
+
+# --------------------------------------------------------------------------- P-e
+def pin_brute_force(lib):
+    """P-e.  Unrolled closed form for L <= 8, evaluated in 50-digit decimal arithmetic:
+    y_t = sum_n C_t[n] sum_{s<=t} exp(A_n sum_{r=s+1..t} delta_r) delta_s B_s[n] x_s + D x_t,
+    then the gate.  A different algorithm (exp of sums) from the oracle's product of exps."""
+    decimal.getcontext().prec = 50
+    Dec = decimal.Decimal
+    for seed, L in ((51, 8), (52, 5), (53, 1)):
+        x, z, dt, A, B, C, D = _case(seed, bt=1, L=L, dim=3, N=4)
+        y = oracle.selscan(x, dt, A, B, C, D=D, z=z, lib=lib)
+        for d in range(3):
+            for t in range(L):
+                acc = Dec(0)
+                for n in range(4):
+                    inner = Dec(0)
+                    for s in range(t + 1):
+                        ssum = sum((Dec(float(dt[0, q, d])) for q in range(s + 1, t + 1)), Dec(0))
+                        inner += (Dec(float(A[d, n])) * ssum).exp() * Dec(float(dt[0, s, d])) * \
+                            Dec(float(B[0, s, n])) * Dec(float(x[0, s, d]))
+                    acc += Dec(float(C[0, t, n])) * inner
+                acc += Dec(float(D[d])) * Dec(float(x[0, t, d]))
+                zz = Dec(float(z[0, t, d]))
+                ref = acc * zz / (1 + (-zz).exp())
+                got = Dec(float(y[0, t, d]))
+                assert abs(got - ref) <= Dec("1e-13") * max(abs(ref), Dec(1)), (seed, t, d, got, ref)
+
+
+# --------------------------------------------------------------------------- P-f
+def pin_chunk_associativity(lib):
+    """P-f.  The recurrence over [0, L) equals the recurrence over [0, m) followed by
+    [m, L) started from the carried state (the property the chunked parallel scan of
+    [MS] insight 1 relies on), and each chunk is the affine map h -> a*h + b with
+    a = exp(A * sum(delta)) and b its zero-start end state."""
+    x, z, dt, A, B, C, D = _case(61, bt=2, L=90, dim=3, N=5)
+    y, hl = oracle.selscan(x, dt, A, B, C, D=D, return_h_last=True, lib=lib)
+    m = 37
+    y1, h1 = oracle.selscan(x[:, :m], dt[:, :m], A, B[:, :m], C[:, :m], D=D, return_h_last=True, lib=lib)
+    y2, h2 = oracle.selscan(x[:, m:], dt[:, m:], A, B[:, m:], C[:, m:], D=D, h0=h1, return_h_last=True, lib=lib)
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y)
+    assert np.array_equal(h2, hl)
+    # affine composition (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2)
+    _, b2 = oracle.selscan(x[:, m:], dt[:, m:], A, B[:, m:], C[:, m:], D=D, return_h_last=True, lib=lib)
+    a2 = np.exp(A[None, :, :] * dt[:, m:].sum(axis=1)[:, :, None])
+    assert _rel(a2 * h1 + b2, hl) < 1e-12
+    r = _rng(62)
+    h0 = r.standard_normal(hl.shape)
+    _, hh = oracle.selscan(x[:, m:], dt[:, m:], A, B[:, m:], C[:, m:], D=D, h0=h0, return_h_last=True, lib=lib)
+    assert _rel(hh, a2 * h0 + b2) < 1e-12
+
+
+# --------------------------------------------------------------------------- P-g
+def pin_causality(lib):
+    """P-g.  A scan is causal: changing x at t0 leaves every y_t, t < t0, bit-identical."""
+    x, z, dt, A, B, C, D = _case(71, bt=1, L=60, dim=4, N=4)
+    y = oracle.selscan(x, dt, A, B, C, D=D, z=z, lib=lib)
+    x2 = x.copy()
+    x2[0, 25, :] += 1.0
+    y2 = oracle.selscan(x2, dt, A, B, C, D=D, z=z, lib=lib)
+    assert np.array_equal(y[:, :25], y2[:, :25])
+    assert not np.array_equal(y[:, 25], y2[:, 25])
+
+
+# --------------------------------------------------------------------------- P-h
+def pin_linearity(lib):
+    """P-h.  With delta, B, C fixed and no gate the output is linear in x ([LM] §2.1: linear
+    state-space system)."""
+    x, z, dt, A, B, C, D = _case(81, bt=2, L=45, dim=3, N=4)
+    x2 = _rng(82).standard_normal(x.shape)
+    y1 = oracle.selscan(x, dt, A, B, C, D=D, lib=lib)
+    y2 = oracle.selscan(x2, dt, A, B, C, D=D, lib=lib)
+    y12 = oracle.selscan(1.5 * x - 0.25 * x2, dt, A, B, C, D=D, lib=lib)
+    assert _rel(y12, 1.5 * y1 - 0.25 * y2) < 1e-12
+
+
+# --------------------------------------------------------------------------- softplus / bias
+def pin_softplus_bias(lib):
+    """delta = softplus(w + bias) ([MS] selection: delta = softplus(W x + b)); numpy.logaddexp
+    evaluates softplus independently.  Also checks the large-|w| branches."""
+    x, z, dt, A, B, C, D = _case(91, bt=1, L=30, dim=4, N=3)
+    r = _rng(92)
+    w = r.standard_normal(x.shape) * 3.0
+    w[0, 3, :] = [45.0, -45.0, 700.0, -700.0]
+    bias = r.standard_normal(4)
+    y = oracle.selscan(x, w, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=True, lib=lib)
+    ref = oracle.selscan(x, np.logaddexp(0.0, w + bias), A, B, C, D=D, z=z, lib=lib)
+    assert _rel(y, ref) < 1e-12
+
+
+# --------------------------------------------------------------------------- gate
+def pin_gate(lib):
+    """SiLU gate: y = y_pre * z * sigmoid(z) ([MS] SS2Dv0.forwardv0: z = act(z), y * z; Mamba block
+    diagram: the SiLU branch multiplies the SSM output).  Large |z| exercises both sides."""
+    x, z, dt, A, B, C, D = _case(101, bt=1, L=20, dim=3, N=3)
+    z[0, :5, :] = np.array([60.0, -60.0, 0.0])
+    ypre = oracle.selscan(x, dt, A, B, C, D=D, lib=lib)
+    y = oracle.selscan(x, dt, A, B, C, D=D, z=z, lib=lib)
+    sig = 0.5 * (1.0 + np.tanh(0.5 * z))  # sigmoid via tanh, an independent formula
+    assert _rel(y, ypre * z * sig) < 1e-12
+
+
+# --------------------------------------------------------------------------- P-i
+def _bidir_case(seed, bt=2, L=23, dim=4, N=3):
+    r = _rng(seed)
+    x = r.standard_normal((bt, L, dim))
+    z = r.standard_normal((bt, L, dim))
+    dt = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), (2, bt, L, dim)))
+    A = -np.exp(r.uniform(-1.0, 1.5, (2, dim, N)))
+    B = r.standard_normal((2, bt, L, N))
+    C = r.standard_normal((2, bt, L, N))
+    D = r.standard_normal((2, dim))
+    return x, z, dt, A, B, C, D
+
+
+def pin_bidir(lib):
+    """P-i.  [LM] §3.1: the backward branch is the forward scan applied to reverse(x) with its
+    own parameters.  (1) It equals two independent 1-D oracle scans composed by hand with
+    numpy flips, summed and gated.  (2) Reversing every per-token array and swapping the two
+    parameter sets reverses the output.  (3) delta_bwd = 0 leaves the backward branch = D_bwd x."""
+    x, z, dt, A, B, C, D = _bidir_case(111)
+    y = oracle.selscan_bidir(x, dt, A, B, C, D=D, z=z, lib=lib)
+    f = oracle.selscan(x, dt[0], A[0], B[0], C[0], D=D[0], lib=lib)
+    rb = oracle.selscan(x[:, ::-1], dt[1][:, ::-1], A[1], B[1][:, ::-1], C[1][:, ::-1], D=D[1], lib=lib)
+    assert _rel(y, (f + rb[:, ::-1]) * _silu_np(z)) < 1e-13
+    ys = oracle.selscan_bidir(x[:, ::-1], dt[::-1, :, ::-1], A[::-1], B[::-1, :, ::-1], C[::-1, :, ::-1],
+                              D=D[::-1], z=z[:, ::-1], lib=lib)
+    assert _rel(ys[:, ::-1], y) < 1e-13
+    dt0 = dt.copy()
+    dt0[1] = 0.0
+    y0 = oracle.selscan_bidir(x, dt0, A, B, C, D=D, z=z, lib=lib)
+    assert _rel(y0, (f + D[1][None, None, :] * x) * _silu_np(z)) < 1e-13
+
+
+# --------------------------------------------------------------------------- P-j
+def _ss2d_case(seed, bt=2, H=5, W=7, dim=3, N=3):
+    r = _rng(seed)
+    L = H * W
+    x = r.standard_normal((bt, L, dim))
+    dt = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), (4, bt, L, dim)))
+    A = -np.exp(r.uniform(-1.0, 1.5, (4, dim, N)))
+    B = r.standard_normal((4, bt, L, N))
+    C = r.standard_normal((4, bt, L, N))
+    D = r.standard_normal((4, dim))
+    return x, dt, A, B, C, D
+
+
+def _cross_scan_materialised(lib, x, dt, A, B, C, D, H, W):
+    """The four-direction procedure exactly as [MS] "关键代码" spells it in tensor operations,
+    driving the 1-D oracle: channel-first maps, flatten (row-major) and transpose-then-flatten
+    (column-major), flips of both, one scan per direction on its own sequence, then flip the
+    last two back, transpose the column-major ones back, and sum the four."""
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+
+    def seqs(t, ch):  # t: [bt, L(pixel, row-major), ch] -> [bt, 4, ch, L] in scan order
+        m = t.transpose(0, 2, 1).reshape(bt, ch, H, W)
+        hw = np.stack([m.reshape(bt, ch, L), m.transpose(0, 1, 3, 2).reshape(bt, ch, L)], axis=1)
+        return np.concatenate([hw, hw[..., ::-1]], axis=1)
+
+    xs = seqs(x, dim)
+    outs = []
+    for k in range(4):
+        dk = seqs(dt[k], dim)[:, k]
+        bk = seqs(B[k], N)[:, k]
+        ck = seqs(C[k], N)[:, k]
+        o = oracle.selscan(xs[:, k].transpose(0, 2, 1), dk.transpose(0, 2, 1), A[k], bk.transpose(0, 2, 1),
+                           ck.transpose(0, 2, 1), D=D[k], lib=lib)
+        outs.append(o.transpose(0, 2, 1))  # [bt, dim, L] scan order
+    out_y = np.stack(outs, axis=1)
+    inv_y = out_y[:, 2:4, :, ::-1]
+    wh_y = out_y[:, 1].reshape(bt, dim, W, H).transpose(0, 1, 3, 2).reshape(bt, dim, L)
+    invwh_y = inv_y[:, 1].reshape(bt, dim, W, H).transpose(0, 1, 3, 2).reshape(bt, dim, L)
+    y = out_y[:, 0] + inv_y[:, 0] + wh_y + invwh_y
+    return y.transpose(0, 2, 1)
+
+
+def pin_ss2d(lib):
+    """P-j.  SS2D = four independent 1-D scans over permuted sequences, summed at the pixel
+    they came from ([MS] cross_scan_fwd / SS2Dv0.forwardv0).  (1) The index-map oracle equals
+    the materialised flip/transpose procedure.  (2) H = 1: column-major equals row-major, so
+    with tied parameter pairs SS2D = 2 x bidirectional.  (3) Transposing the map (H <-> W) and
+    swapping directions 0<->1, 2<->3 transposes the output."""
+    for (H, W) in ((5, 7), (4, 4), (1, 6), (6, 1)):
+        x, dt, A, B, C, D = _ss2d_case(121 + H * 10 + W, H=H, W=W)
+        y = oracle.ss2d(x, dt, A, B, C, H, W, D=D, lib=lib)
+        ref = _cross_scan_materialised(lib, x, dt, A, B, C, D, H, W)
+        assert _rel(y, ref) < 1e-13, (H, W, _rel(y, ref))
+    # (2)
+    H, W = 1, 9
+    x, dt, A, B, C, D = _ss2d_case(131, H=H, W=W)
+    for k in (1, 3):
+        dt[k], A[k], B[k], C[k], D[k] = dt[k - 1], A[k - 1], B[k - 1], C[k - 1], D[k - 1]
+    y = oracle.ss2d(x, dt, A, B, C, H, W, D=D, lib=lib)
+    yb = oracle.selscan_bidir(x, dt[[0, 2]], A[[0, 2]], B[[0, 2]], C[[0, 2]], D=D[[0, 2]], lib=lib)
+    assert _rel(y, 2.0 * yb) < 1e-13
+    # (3)
+    H, W = 4, 6
+    x, dt, A, B, C, D = _ss2d_case(141, H=H, W=W)
+    y = oracle.ss2d(x, dt, A, B, C, H, W, D=D, lib=lib)
+
+    def tr(t):  # transpose the pixel axis (axis -2) of a [..., H*W, c] array: row-major H x W -> W x H
+        s = t.shape
+        return t.reshape(s[:-2] + (H, W, s[-1])).swapaxes(-3, -2).reshape(s)
+
+    perm = [1, 0, 3, 2]
+    yt = oracle.ss2d(tr(x), tr(dt)[perm], A[perm], tr(B)[perm], tr(C)[perm], W, H, D=D[perm], lib=lib)
+    assert _rel(yt, tr(y)) < 1e-13
+
+
+ALL_PINS = [
+    pin_lti_convolution,
+    pin_delta_to_zero,
+    pin_a_zero_prefix_sum,
+    pin_first_order_iir,
+    pin_brute_force,
+    pin_chunk_associativity,
+    pin_causality,
+    pin_linearity,
+    pin_softplus_bias,
+    pin_gate,
+    pin_bidir,
+    pin_ss2d,
+]

@@ -1,0 +1,69 @@
+"""CPU tests: the oracle against its pins, and the pins against planted mistakes.
+
+The mutation test copies ``oracle/oracle.c``, plants one plausible mistake (a
+dropped term, a wrong sign, a transposed index, a missing reversal ...),
+compiles the copy and requires that at least one pin fails on it.  Nothing is
+planted in the repository's oracle itself.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins as P
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin, lib):
+    pin(lib)
+
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text in oracle.c, replacement)
+MUTATIONS = [
+    ("drop_D_skip", "s->y_pre[i] = acc + Dd * xv;", "s->y_pre[i] = acc;"),
+    ("exp_sign", "const double Abar = exp(dt * a);", "const double Abar = exp(-dt * a);"),
+    ("drop_delta_in_Bbar", "Bbar = dt * Bt[n];", "Bbar = Bt[n];"),
+    ("C_reads_B", "const double *Ct = s->C + (b * L + t) * N;", "const double *Ct = s->B + (b * L + t) * N;"),
+    ("output_before_update", "h[n] = Abar * h[n] + Bbar * xv;\n            acc += Ct[n] * h[n];",
+     "acc += Ct[n] * h[n];\n            h[n] = Abar * h[n] + Bbar * xv;"),
+    ("A_transposed", "const double a = Arow[n];", "const double a = s->A[n * dim + d];"),
+    ("ss2d_colmajor_transposed", "return (l % H) * W + l / H;", "return (l % W) * H + l / W;"),
+    ("bidir_not_rereversed", "reverse_time(yr, y, batch, L, dim); /* back to token order */",
+     "memcpy(y, yr, sizeof(double) * (size_t)tok);"),
+    ("bidir_bwd_uses_fwd_params", "scan_t r = {xr, dr, A + dim * N,", "scan_t r = {xr, dr, A,"),
+    ("softplus_wrong_branch", "return w > 0.0 ? w + log1p(exp(-w)) : log1p(exp(w));",
+     "return w > 0.0 ? w + log1p(exp(w)) : log1p(exp(w));"),
+    ("silu_sign", "if (z >= 0.0) return z / (1.0 + exp(-z));", "if (z >= 0.0) return z / (1.0 + exp(z));"),
+    ("zoh_missing_divide", "Bbar = (a != 0.0 ? expm1(dt * a) / a : dt) * Bt[n];",
+     "Bbar = (a != 0.0 ? expm1(dt * a) : dt) * Bt[n];"),
+    ("bias_ignored", "if (s->delta_bias) dt += s->delta_bias[d];", ""),
+    ("h0_ignored", "h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, old, new, tmp_path):
+    text = open(SRC).read()
+    assert old in text, f"mutation site for {name} not found in oracle.c"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new, 1))
+    so = str(tmp_path / "libmutant.so")
+    oracle.build(str(src), so)
+    mutant = oracle.load(so)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except (RuntimeError, FloatingPointError, ValueError, OverflowError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module holds no arithmetic of the method: it only draws random
+numbers, rounds them to the I/O dtype and names the workload shapes.  It is
+the one piece shared by the CPU oracle side (tests, CPU baseline) and the
+HIP side (tests, bench), so both always see bit-identical inputs.
+
+Value distributions (plainest reading of the workload statements; the
+pages print no activation statistics):
+  x, z, B, C ~ N(0, 1)             activations, drawn in float32
+  D[d]       ~ N(0, 1)             per-channel skip weight (float32)
+  A[d, n]    = -(n + 1)            real, negative, diagonal (S4D-real style)
+  delta      = exp(U(ln 1e-3, ln 1e-1))   log-uniform step size
+  w          = log(expm1(delta))   pre-softplus value (softplus(w) == delta)
+Every direction of the bidirectional / SS2D workloads draws its own delta,
+B and C.  The 16-bit ``bf16`` arrays are raw IEEE bfloat16 bit patterns
+(round-to-nearest-even from float32), held as numpy uint16.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+SEED_BASE = 51000
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One workload shape.  ``kind`` is 'selscan', 'bidir' or 'ss2d'."""
+
+    name: str
+    kind: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    dtype: str  # 'f32' or 'bf16' (I/O dtype of x, delta, B, C, z, y)
+    gate: bool  # whether z is passed
+    H: int = 0
+    W: int = 0
+    index: int = 0  # position in WORKLOADS; the seed is SEED_BASE + index
+
+    @property
+    def ndir(self) -> int:
+        return {"selscan": 1, "bidir": 2, "ss2d": 4}[self.kind]
+
+    @property
+    def elements(self) -> int:
+        """batch * L * D * N * directions: the unit the throughput metric counts."""
+        return self.batch * self.seqlen * self.dim * self.dstate * self.ndir
+
+    @property
+    def io_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes a fused forward must move at least once: every input read once, y written once.
+
+        x once, delta once per direction, z once (if gated), y once, B and C once per
+        direction, A (D*N fp32) and D (fp32) once per direction.
+        """
+        s = self.io_bytes
+        tok = self.batch * self.seqlen * self.dim
+        k = self.ndir
+        big = tok * s * (1 + k + (1 if self.gate else 0) + 1)
+        bc = k * 2 * self.batch * self.seqlen * self.dstate * s
+        params = k * (self.dim * self.dstate + self.dim) * 4
+        return big + bc + params
+
+
+WORKLOADS: List[Workload] = [
+    Workload("s6_fp32_b1_L256_D16", "selscan", 1, 256, 16, 16, "f32", True, index=0),
+    Workload("mamba130m_layer_b8_L2048_D1536", "selscan", 8, 2048, 1536, 16, "bf16", True, index=1),
+    Workload("mamba1p4b_layer_b2_L65536_D4096", "selscan", 2, 65536, 4096, 16, "bf16", True, index=2),
+    Workload("vim_bidir_b64_L197_D768", "bidir", 64, 197, 768, 16, "bf16", True, index=3),
+    Workload("vmamba_ss2d_b32_56x56_D192", "ss2d", 32, 56 * 56, 192, 16, "bf16", False, H=56, W=56, index=4),
+]
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit pattern, round to nearest even (NaN kept quiet)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of an I/O array (bf16 bits or float32) to float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def _round_io(a32: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, dtype=np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    for s in range(0, out.size, chunk):
+        e = min(out.size, s + chunk)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def _log_uniform(rng: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
+    u = rng.random(int(np.prod(shape)), dtype=np.float32)
+    return np.exp(np.float32(math.log(lo)) + u * np.float32(math.log(hi) - math.log(lo))).reshape(shape)
+
+
+def generate(
+    w: Workload,
+    seed: Optional[int] = None,
+    with_w: bool = False,
+    with_bias: bool = False,
+    batch: Optional[int] = None,
+    seqlen: Optional[int] = None,
+    dim: Optional[int] = None,
+) -> Dict[str, np.ndarray]:
+    """Draw one seeded input set for workload ``w`` (shape overrides allowed for small cases).
+
+    Returns a dict with keys x, z (or None), delta, A, B, C, D and optionally
+    w (pre-softplus delta, for delta_softplus=1 runs) and delta_bias.  Per-
+    direction arrays carry a leading direction axis when ``w.ndir > 1``;
+    per-token/per-pixel arrays are in token (pixel, row-major) order.
+    """
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + w.index if seed is None else seed))
+    bt = w.batch if batch is None else batch
+    L = w.seqlen if seqlen is None else seqlen
+    d = w.dim if dim is None else dim
+    n = w.dstate
+    k = w.ndir
+    lead = (k,) if k > 1 else ()
+    out: Dict[str, np.ndarray] = {}
+    out["x"] = _round_io(_normal(rng, (bt, L, d)), w.dtype)
+    out["z"] = _round_io(_normal(rng, (bt, L, d)), w.dtype) if w.gate else None
+    delta = _log_uniform(rng, lead + (bt, L, d), 1e-3, 1e-1)
+    out["delta"] = _round_io(delta, w.dtype)
+    out["B"] = _round_io(_normal(rng, lead + (bt, L, n)), w.dtype)
+    out["C"] = _round_io(_normal(rng, lead + (bt, L, n)), w.dtype)
+    out["D"] = _normal(rng, lead + (d,))
+    A = -np.arange(1, n + 1, dtype=np.float32)
+    out["A"] = np.ascontiguousarray(np.broadcast_to(A, lead + (d, n)))
+    if with_bias:
+        out["delta_bias"] = (0.5 * _normal(rng, lead + (d,))).astype(np.float32)
+    if with_w:
+        # pre-softplus value such that softplus(w + bias) ~= delta; computed in fp64 from the
+        # delta actually stored, then rounded to the I/O dtype.
+        dl = to_f64(out["delta"], w.dtype)
+        wv = np.log(np.expm1(dl))
+        if with_bias:
+            wv = wv - out["delta_bias"].astype(np.float64).reshape(lead + (1, 1, d))
+        out["w"] = _round_io(wv.astype(np.float32), w.dtype)
+    return out
