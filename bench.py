@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan forward on one MI355X.
+
+A step is one pass of the whole hot path (one selscan_fwd / selscan_bidir_fwd /
+ss2d_fwd call) over one batch of synthetic input already resident in HBM.
+Prints ONE JSON line (rank 0).  Default workload: the Mamba-1.4B-layer
+long-context shape, batch 2 x L 65536 x D 4096, N 16, bf16 I/O, fp32 state.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
+METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc", "selscan.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_channels: int):
+    """The fp64 oracle as it stands, on all host cores, on a bounded sample of the workload:
+    every batch row and the whole sequence for the first `budget_channels` channels."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    inp = W.generate(w)
+    ch = min(budget_channels, w.dim)
+    f = lambda k: None if inp.get(k) is None else np.ascontiguousarray(W.to_f64(inp[k], w.dtype)[..., :ch])
+    x, dl, z = f("x"), f("delta"), f("z")
+    A = inp["A"].astype(np.float64)[..., :ch, :]
+    D = inp["D"].astype(np.float64)[..., :ch]
+    B, C = W.to_f64(inp["B"], w.dtype), W.to_f64(inp["C"], w.dtype)
+    del inp
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    if w.kind == "selscan":
+        oracle.selscan(x, dl, A, B, C, D=D, z=z, nthreads=threads)
+    elif w.kind == "bidir":
+        oracle.selscan_bidir(x, dl, A, B, C, D=D, z=z, nthreads=threads)
+    else:
+        oracle.ss2d(x, dl, A, B, C, w.H, w.W, D=D, z=z, nthreads=threads)
+    sec = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * ch * w.dstate * w.ndir
+    return {
+        "value": elems / sec,
+        "unit": "elem/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{w.name}: all {w.batch} batch rows x {w.seqlen} steps x first {ch} of {w.dim} channels"
+                  f" x {w.ndir} direction(s) ({elems:.3e} elements, {sec:.1f} s wall, fp64)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-channels", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the scan shards over batch x channel with no "
+              f"communication); --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_51_amd as S
+    import workloads as W
+
+    w = W.by_name(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.generate(w)
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    t = {k: up(v) for k, v in inp.items()}
+    del inp
+    y = torch.empty_like(t["x"])
+    ws = None
+    op = {"selscan": S.SELSCAN_OP_FWD, "bidir": S.SELSCAN_OP_BIDIR, "ss2d": S.SELSCAN_OP_SS2D}[w.kind]
+    need = S.selscan_workspace_bytes(op, w.batch, w.seqlen, w.dim, w.dstate,
+                                     S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32)
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if w.kind == "selscan":
+            S.selscan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, workspace=ws,
+                          stream=stream)
+        elif w.kind == "bidir":
+            S.selscan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
+                                workspace=ws, stream=stream)
+        else:
+            S.ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, D=t["D"], z=t["z"], y=y,
+                       workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch events on the stream the kernel runs on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = float(np.mean(launch_ms))
+    value = w.elements / (ms_step * 1e-3)
+    alg = w.algorithmic_bytes()
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: x, z, B, C ~ N(0,1); delta log-uniform [1e-3, 1e-1]; A[d,n] = -(n+1); D ~ N(0,1))",
+        "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),
+                     "algorithmic_bytes_per_launch": alg, "elements_per_launch": w.elements},
+    }
+    if not args.no_cpu_baseline:
+        del t, y, ws
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,141 @@
+/*
+ * selscan.h - C ABI of libselscan: the selective state-space scan (the S6 core of
+ * Mamba) and its two vision variants, as hand-written HIP kernels for MI355X (gfx950).
+ *
+ * What is computed (per batch b, channel d, state n, step t):
+ *     delta_t = softplus(delta[b,t,d] + delta_bias[d])   if SELSCAN_FLAG_DELTA_SOFTPLUS,
+ *               delta[b,t,d] (+ delta_bias[d])            otherwise
+ *     h_t[n]  = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B[b,t,n] * x[b,t,d],  h_{-1} = 0
+ *     y[b,t,d] = (sum_n C[b,t,n] * h_t[n] + D[d] * x[b,t,d]) * silu(z[b,t,d])
+ * Sources: "Mamba Series from Selective State Spaces to Visual State Space Models",
+ * section 选择性 SSM 的数学形式 (continuous system, Abar = exp(delta A), selection
+ * delta = softplus(W x + b), B and C functions of the input, A a fixed diagonal) and
+ * section 关键代码 (the selective_scan call with Ds, delta_bias, delta_softplus; the SiLU
+ * gate); "从LSTM到Mamba" §2.1 (the D x skip term).  Bbar is taken as delta * B (the
+ * first-order form of the page's zero-order-hold Bbar; equal to it as delta*A -> 0).
+ *
+ * Conventions shared by every entry point
+ *  - Layout: row-major, channels fastest.  Per-token tensors x, delta, z, y are
+ *    [batch][seqlen][dim]; B and C are [batch][seqlen][dstate]; A is [dim][dstate] fp32;
+ *    D and delta_bias are [dim] fp32.  Variants stack per-direction arrays on a leading
+ *    direction axis.
+ *  - io_dtype (SELSCAN_F32 or SELSCAN_BF16) is the element type of x, delta, B, C, z
+ *    and y.  A, D and delta_bias are always fp32.  The state and all arithmetic are fp32.
+ *  - Pointers are device pointers (HIP device memory) owned by the caller.  The library
+ *    allocates and frees nothing; it keeps no global mutable state and is re-entrant.
+ *    `workspace` is caller-owned scratch of at least selscan_workspace_bytes(...) bytes
+ *    (may be NULL when that is 0).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is only
+ *    enqueued: the call returns before the kernels run, and a fault during execution
+ *    surfaces on the stream, not in the return value.
+ *  - Optional pointers (D, z, delta_bias) may be NULL: no skip term, no gate, no bias.
+ *  - Every call validates its arguments on the host before any HIP call and returns a
+ *    selscan_status; nothing is enqueued unless it returns SELSCAN_OK:
+ *      SELSCAN_E_NULL         a required pointer is NULL (non-empty problem)
+ *      SELSCAN_E_SHAPE        a size is negative (any zero size is an OK no-op)
+ *      SELSCAN_E_ALIGN        a pointer is not aligned to its element size (4 B for fp32
+ *                             arrays, 2 B for bf16 arrays)
+ *      SELSCAN_E_ALIAS        y overlaps an input array
+ *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits
+ *      SELSCAN_E_WORKSPACE    workspace smaller than selscan_workspace_bytes(...)
+ *      SELSCAN_E_HIP          the kernel launch was rejected by the HIP runtime
+ *    Non-finite inputs are not checked; they propagate.
+ */
+#ifndef SELSCAN_H
+#define SELSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SELSCAN_ABI_VERSION 1
+
+typedef enum { SELSCAN_F32 = 0, SELSCAN_BF16 = 1 } selscan_dtype;
+
+typedef enum {
+    SELSCAN_OK = 0,
+    SELSCAN_E_NULL = 1,
+    SELSCAN_E_SHAPE = 2,
+    SELSCAN_E_ALIGN = 3,
+    SELSCAN_E_ALIAS = 4,
+    SELSCAN_E_UNSUPPORTED = 5,
+    SELSCAN_E_WORKSPACE = 6,
+    SELSCAN_E_HIP = 7
+} selscan_status;
+
+/* flag bits */
+#define SELSCAN_FLAG_DELTA_SOFTPLUS 1u /* delta_t = softplus(delta + delta_bias) */
+
+/* operation codes for selscan_workspace_bytes */
+typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2 } selscan_op;
+
+/*
+ * selscan_fwd - one selective scan over the sequence axis (Mamba's S6 layer core).
+ *   x, delta, z, y : [batch][seqlen][dim]     io_dtype
+ *   B, C           : [batch][seqlen][dstate]  io_dtype
+ *   A              : [dim][dstate]            fp32 (real, normally negative)
+ *   D, delta_bias  : [dim]                    fp32, nullable
+ *   z              : nullable (no gate)
+ *   flags          : SELSCAN_FLAG_DELTA_SOFTPLUS or 0
+ * Writes y only.
+ */
+int selscan_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+                const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t seqlen,
+                int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * selscan_bidir_fwd - bidirectional scan (Vim): "从LSTM到Mamba" §3.1, a forward scan plus
+ * the same scan over the time-reversed sequence with its own parameters.  The two
+ * outputs are summed in token order (the page concatenates; summing is the fusion this
+ * library implements) and gated once:
+ *   y = (scan(x; P0) + reverse(scan(reverse(x); reverse(P1)))) * silu(z)
+ *   delta, B, C : [2][batch][seqlen][...]  direction 0 forward, 1 backward, TOKEN order
+ *   A           : [2][dim][dstate];  D, delta_bias : [2][dim] (nullable)
+ *   x, z, y     : [batch][seqlen][dim]
+ */
+int selscan_bidir_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                      int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * ss2d_fwd - VMamba SS2D four-direction scan with merge: "Mamba Series from Selective
+ * State Spaces to Visual State Space Models", section 关键代码 (cross_scan_fwd and
+ * SS2Dv0.forwardv0).  On an H x W map with pixels p = h*W + w (row-major), L = H*W,
+ * direction k visits pixel pi_k(l) at scan step l:
+ *   k = 0 row-major (pi = l); k = 1 column-major (pi = (l % H)*W + l / H);
+ *   k = 2 reversed row-major; k = 3 reversed column-major.
+ * Each direction runs the scan with its own parameters; its output at step l is added
+ * at pixel pi_k(l); the sum of the four is written once:
+ *   y[b,p,d] = (sum_k o_k[b, pi_k^-1(p), d]) * silu(z[b,p,d])   (z nullable: no gate)
+ *   x, z, y     : [batch][H*W][dim]           pixel order
+ *   delta       : [4][batch][H*W][dim]        pixel order (value used when pixel p is visited)
+ *   B, C        : [4][batch][H*W][dstate]     pixel order
+ *   A           : [4][dim][dstate];  D, delta_bias : [4][dim] (nullable)
+ */
+int ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+             const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H, int64_t W,
+             int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes the caller must pass as `workspace` for this problem (0 = none). */
+size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,
+                               int io_dtype);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *selscan_status_str(int status);
+
+/* SELSCAN_ABI_VERSION of the loaded library. */
+int selscan_abi_version(void);
+
+/* Text of the HIP error behind the calling thread's most recent SELSCAN_E_HIP ("no error"
+ * if there was none).  Static storage per thread; never NULL. */
+const char *selscan_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELSCAN_H */

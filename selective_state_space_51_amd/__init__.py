@@ -1,0 +1,212 @@
+"""Python binding of libselscan (argument marshalling only).
+
+Every function here has the name of the C-ABI entry point it calls (see
+include/selscan.h).  torch supplies device memory and the current stream; all
+arithmetic of the scan runs in the library's HIP kernels.  If libselscan.so is
+missing the import fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libselscan.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "selscan.h")
+
+SELSCAN_F32 = 0
+SELSCAN_BF16 = 1
+SELSCAN_FLAG_DELTA_SOFTPLUS = 1
+SELSCAN_OP_FWD, SELSCAN_OP_BIDIR, SELSCAN_OP_SS2D = 0, 1, 2
+STATUS = {
+    0: "SELSCAN_OK", 1: "SELSCAN_E_NULL", 2: "SELSCAN_E_SHAPE", 3: "SELSCAN_E_ALIGN", 4: "SELSCAN_E_ALIAS",
+    5: "SELSCAN_E_UNSUPPORTED", 6: "SELSCAN_E_WORKSPACE", 7: "SELSCAN_E_HIP",
+}
+
+
+class SelscanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        extra = f"; HIP: {lib.selscan_last_hip_error().decode()}" if status == 7 else ""
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_str(status)}){extra}")
+
+
+def _load():
+    # torch carries its own HIP runtime; load it first so that the library binds to the same
+    # runtime (same soname) and torch's streams and device pointers are valid in it
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libselscan.so not found at {LIB_PATH}; build it with "
+            "`python selective_state_space_51_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, cu, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    common = [vp] * 8 + [cu, vp]
+    lib.selscan_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.selscan_bidir_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, ci, vp, sz, vp]
+    for f in (lib.selscan_fwd, lib.selscan_bidir_fwd, lib.ss2d_fwd):
+        f.restype = ci
+    lib.selscan_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci]
+    lib.selscan_workspace_bytes.restype = sz
+    lib.selscan_status_str.argtypes = [ci]
+    lib.selscan_status_str.restype = ctypes.c_char_p
+    lib.selscan_abi_version.argtypes = []
+    lib.selscan_abi_version.restype = ci
+    lib.selscan_last_hip_error.argtypes = []
+    lib.selscan_last_hip_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.selscan_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib.selscan_abi_version())
+
+
+def header_functions():
+    """Names of the functions include/selscan.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*\**\s*(\w+)\s*\(", text, re.M)))
+
+
+def selscan_workspace_bytes(op: int, batch: int, seqlen_or_hw: int, dim: int, dstate: int = 16,
+                            io_dtype: int = SELSCAN_BF16) -> int:
+    return int(lib.selscan_workspace_bytes(op, batch, seqlen_or_hw, dim, dstate, io_dtype))
+
+
+# ------------------------------------------------------------------------------ torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SELSCAN_BF16
+    if t.dtype == torch.float32:
+        return SELSCAN_F32
+    raise TypeError(f"unsupported io dtype {t.dtype}")
+
+
+def _ptr(t, name, io=None, f32=False):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if f32 and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if io is not None and t.dtype != io:
+        raise TypeError(f"{name} must have the io dtype {io}")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(op, x, bt, L, dim, workspace):
+    torch = _torch()
+    need = selscan_workspace_bytes(op, bt, L, dim, 16, _dtype_code(x))
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise SelscanError(rc, what)
+
+
+def _shape_check(name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def selscan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
+                workspace=None, stream=None):
+    """y = (sum_n C h + D x) * silu(z) for x, delta, z: [batch, L, dim]; B, C: [batch, L, N]; A: [dim, N]."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, (bt, L, dim)), ("B", B, (bt, L, N)), ("C", C, (bt, L, N)),
+                       ("A", A, (dim, N)), ("D", D, (dim,)), ("z", z, (bt, L, dim)),
+                       ("delta_bias", delta_bias, (dim,))):
+        _shape_check(n_, t_, s_)
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(SELSCAN_OP_FWD, x, bt, L, dim, workspace)
+    rc = lib.selscan_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
+                         _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                         _ptr(delta_bias, "delta_bias", f32=True),
+                         SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                         bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
+    _check(rc, "selscan_fwd")
+    return y
+
+
+def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
+                      workspace=None, stream=None):
+    """Bidirectional scan; per-direction arrays stacked on a leading axis of 2 (token order)."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, (2, bt, L, dim)), ("B", B, (2, bt, L, N)), ("C", C, (2, bt, L, N)),
+                       ("A", A, (2, dim, N)), ("D", D, (2, dim)), ("z", z, (bt, L, dim)),
+                       ("delta_bias", delta_bias, (2, dim))):
+        _shape_check(n_, t_, s_)
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(SELSCAN_OP_BIDIR, x, bt, L, dim, workspace)
+    rc = lib.selscan_bidir_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
+                               _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                               _ptr(delta_bias, "delta_bias", f32=True),
+                               SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                               bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
+    _check(rc, "selscan_bidir_fwd")
+    return y
+
+
+def ss2d_fwd(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
+             workspace=None, stream=None):
+    """SS2D four-direction scan with merge; per-direction arrays [4, ...] in pixel (row-major) order."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    io = x.dtype
+    if L != H * W:
+        raise ValueError(f"x has {L} pixels, expected H*W = {H * W}")
+    for n_, t_, s_ in (("delta", delta, (4, bt, L, dim)), ("B", B, (4, bt, L, N)), ("C", C, (4, bt, L, N)),
+                       ("A", A, (4, dim, N)), ("D", D, (4, dim)), ("z", z, (bt, L, dim)),
+                       ("delta_bias", delta_bias, (4, dim))):
+        _shape_check(n_, t_, s_)
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(SELSCAN_OP_SS2D, x, bt, L, dim, workspace)
+    rc = lib.ss2d_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
+                      _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                      _ptr(delta_bias, "delta_bias", f32=True),
+                      SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                      bt, H, W, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
+    _check(rc, "ss2d_fwd")
+    return y

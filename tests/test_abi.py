@@ -1,0 +1,93 @@
+"""CPU tests of the C ABI: the library loads, exports what include/selscan.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed: every call
+here returns from validation; none reaches a launch)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import selective_state_space_51_amd as S
+
+L = S.lib
+P = 0x10000  # a fake, aligned "device" address: validation never dereferences pointers
+MB = 1 << 20
+
+
+def test_exports_every_declared_symbol():
+    declared = S.header_functions()
+    assert set(declared) == {"selscan_fwd", "selscan_bidir_fwd", "ss2d_fwd", "selscan_workspace_bytes",
+                             "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings():
+    assert S.abi_version() == 1
+    for code in range(8):
+        assert S.status_str(code) and S.status_str(code) != "unknown status"
+    assert S.status_str(99) == "unknown status"
+
+
+def fwd(x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, D=None, z=None, bias=None, flags=0,
+        y=P + 8 * MB, batch=1, L_=16, dim=8, N=16, dtype=S.SELSCAN_BF16, ws=None, wsb=0):
+    return L.selscan_fwd(x, delta, A, B, C, D, z, bias, flags, y, batch, L_, dim, N, dtype, ws, wsb, None)
+
+
+def test_null_pointers():
+    for kw in ("x", "delta", "A", "B", "C", "y"):
+        assert fwd(**{kw: None}) == 1, kw
+
+
+def test_negative_sizes_and_empty_noop():
+    assert fwd(batch=-1) == 2
+    assert fwd(L_=-3) == 2
+    assert fwd(dim=-1) == 2
+    # any zero size is an OK no-op, even with NULL pointers
+    assert fwd(L_=0, x=None, y=None) == 0
+    assert fwd(batch=0) == 0
+    assert fwd(dim=0) == 0
+    assert L.ss2d_fwd(P, P, P, P, P, None, None, None, 0, P, 1, -1, 4, 8, 16, 1, None, 0, None) == 2
+
+
+def test_unsupported():
+    assert fwd(N=8) == 5
+    assert fwd(dtype=7) == 5
+    assert fwd(flags=4) == 5
+
+
+def test_alignment():
+    assert fwd(x=P + 1) == 3
+    assert fwd(A=P + 2 * MB + 2) == 3
+    assert fwd(dtype=S.SELSCAN_F32, delta=P + MB + 2) == 3
+    assert fwd(D=P + 5 * MB + 1) == 3
+
+
+def test_alias():
+    assert fwd(y=P) == 4  # y == x
+    assert fwd(y=P + MB + 2) == 4  # y inside delta
+    assert fwd(z=P + 6 * MB, y=P + 6 * MB) == 4
+    assert fwd(D=P + 8 * MB + 16, y=P + 8 * MB) == 4
+
+
+def test_workspace_query_and_check():
+    # bidirectional and SS2D currently stage fp32 partial sums in the workspace
+    need = S.selscan_workspace_bytes(S.SELSCAN_OP_BIDIR, 2, 10, 8)
+    assert S.selscan_workspace_bytes(S.SELSCAN_OP_FWD, 2, 10, 8) == 0
+    if need:
+        rc = L.selscan_bidir_fwd(P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0, P + 8 * MB,
+                                 2, 10, 8, 16, 1, None, 0, None)
+        assert rc == 6
+        rc = L.selscan_bidir_fwd(P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0, P + 8 * MB,
+                                 2, 10, 8, 16, 1, P + 8 * MB, need, None)
+        assert rc == 4  # workspace overlapping y
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.selscan_fwd(x, x, torch.zeros(8, 16), x.new_zeros(1, 4, 16), x.new_zeros(1, 4, 16), y=x.clone())

@@ -1,0 +1,178 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on the same
+seeded inputs.  Bar: max relative error (see tests/parity.py) <= 1e-5 for fp32 I/O and
+<= 2e-2 for bf16 I/O; bit-exact where the arithmetic is exact."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_51_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def _check(kind, w, inp, H=0, Wd=0, channels=None, **kw):
+    import torch
+    y = PT.run_gpu(kind, inp, w.dtype, H=H, Wd=Wd, **kw)
+    torch.cuda.synchronize()
+    yg = PT.from_dev(y)
+    r = PT.run_oracle(kind, inp, w.dtype, H=H, Wd=Wd, channels=channels, **kw)
+    if channels is not None:
+        yg = yg[..., np.asarray(channels)]
+    err = PT.rel_err(yg, r)
+    _say(kind, w.name, "max rel err", err)
+    assert err <= PT.TOL[w.dtype], err
+    return y
+
+
+# ----------------------------------------------------------------------------- workload shapes
+SMALL = [
+    # (workload index, overrides) -- sizes the oracle finishes in about a second, spanning
+    # several channel tiles and ragged sequence tails
+    (0, {}),
+    (1, dict(batch=2, seqlen=300, dim=1536)),
+    (2, dict(batch=1, seqlen=4100, dim=128)),
+    (3, dict(batch=4, seqlen=197, dim=768)),
+    (4, dict(batch=2, dim=64)),
+]
+
+
+@pytest.mark.parametrize("idx,ov", SMALL, ids=[W.WORKLOADS[i].name for i, _ in SMALL])
+def test_workload_small(idx, ov):
+    w = W.WORKLOADS[idx]
+    _say("small", w.name, ov)
+    inp = W.generate(w, **ov)
+    _check(w.kind, w, inp, H=w.H, Wd=w.W)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4], ids=[W.WORKLOADS[i].name for i in (1, 2, 3, 4)])
+def test_workload_full_size_sampled(idx):
+    """Full BASELINE sizes in the launch configuration the benchmark times; the oracle
+    checks a sample of channels (every batch row, whole sequence)."""
+    import torch
+    w = W.WORKLOADS[idx]
+    _say("full", w.name)
+    inp = W.generate(w)
+    chans = sorted({0, 1, 63, 64, w.dim // 2 + 5, w.dim - 1})
+    _check(w.kind, w, inp, H=w.H, Wd=w.W, channels=chans)
+    del inp
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- options and edges
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softplus_bias_and_optional_args(dtype):
+    base = W.Workload("opt", "selscan", 2, 333, 200, 16, dtype, True, index=7)
+    inp = W.generate(base, with_w=True, with_bias=True)
+    _say("softplus", dtype)
+    _check("selscan", base, inp, softplus=True, use_bias=True)
+    _check("selscan", base, inp, use_D=False, use_z=False)
+    # a bias without softplus must keep delta positive, or exp(delta A) grows without bound
+    inp = dict(inp, delta_bias=np.abs(inp["delta_bias"]) * np.float32(0.05))
+    _check("selscan", base, inp, use_bias=True)
+
+
+@pytest.mark.parametrize("L,dim,batch", [(1, 8, 1), (2, 24, 3), (17, 72, 2), (257, 8, 1), (64, 1, 2), (5, 3, 1)])
+def test_edge_shapes(L, dim, batch):
+    w = W.Workload("edge", "selscan", batch, L, dim, 16, "f32", True, index=8)
+    inp = W.generate(w)
+    _say("edge", L, dim, batch)
+    _check("selscan", w, inp)
+
+
+@pytest.mark.parametrize("L,dim", [(1, 8), (2, 16), (33, 40)])
+def test_bidir_edges(L, dim):
+    w = W.Workload("bidir_edge", "bidir", 2, L, dim, 16, "f32", True, index=9)
+    inp = W.generate(w, with_w=True, with_bias=True)
+    _say("bidir edge", L, dim)
+    _check("bidir", w, inp)
+    _check("bidir", w, inp, softplus=True, use_bias=True, use_z=False)
+
+
+@pytest.mark.parametrize("H,Wd,dim", [(1, 1, 8), (1, 9, 16), (7, 5, 24), (4, 4, 8), (9, 3, 64)])
+def test_ss2d_shapes(H, Wd, dim):
+    w = W.Workload("ss2d_edge", "ss2d", 2, H * Wd, dim, 16, "f32", False, H=H, W=Wd, index=10)
+    inp = W.generate(w, with_w=True, with_bias=True)
+    _say("ss2d", H, Wd, dim)
+    _check("ss2d", w, inp, H=H, Wd=Wd)
+    _check("ss2d", w, inp, H=H, Wd=Wd, softplus=True, use_bias=True)
+
+
+def test_ss2d_with_gate():
+    w = W.Workload("ss2d_gate", "ss2d", 2, 6 * 5, 16, 16, "bf16", True, H=6, W=5, index=11)
+    inp = W.generate(w)
+    _check("ss2d", w, inp, H=6, Wd=5)
+
+
+def test_empty_sequence_is_noop():
+    import torch
+    import selective_state_space_51_amd as S
+    x = torch.zeros(2, 0, 8, device="cuda", dtype=torch.bfloat16)
+    y = torch.full_like(x, 3.0)
+    S.selscan_fwd(x, x, torch.zeros(8, 16, device="cuda"), torch.zeros(2, 0, 16, device="cuda", dtype=x.dtype),
+                  torch.zeros(2, 0, 16, device="cuda", dtype=x.dtype), y=y)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+
+
+# ----------------------------------------------------------------------------- exactness
+def test_exact_prefix_sum_at_A_zero():
+    """A = 0 with dyadic delta and small-integer x, B, C, D: every operation is exact in fp32,
+    so the GPU result must equal the oracle bit for bit (fp32 I/O, no gate)."""
+    import torch
+    r = np.random.default_rng(3)
+    bt, L, dim = 2, 700, 72
+    inp = dict(x=r.integers(-3, 4, (bt, L, dim)).astype(np.float32),
+               delta=r.choice([0.25, 0.5, 0.125], (bt, L, dim)).astype(np.float32),
+               B=r.integers(-2, 3, (bt, L, 16)).astype(np.float32),
+               C=r.integers(-2, 3, (bt, L, 16)).astype(np.float32),
+               D=r.integers(-2, 3, dim).astype(np.float32), A=np.zeros((dim, 16), np.float32), z=None)
+    y = PT.run_gpu("selscan", inp, "f32", use_z=False)
+    torch.cuda.synchronize()
+    ref = PT.run_oracle("selscan", inp, "f32", use_z=False)
+    assert np.array_equal(PT.from_dev(y), ref)
+
+
+def test_causality_and_determinism():
+    import torch
+    w = W.Workload("causal", "selscan", 2, 1500, 96, 16, "bf16", True, index=12)
+    inp = W.generate(w)
+    y1 = PT.from_dev(PT.run_gpu("selscan", inp, "bf16"))
+    y2 = PT.from_dev(PT.run_gpu("selscan", inp, "bf16"))
+    assert np.array_equal(y1, y2), "run-to-run results differ"
+    t0 = 777
+    inp2 = dict(inp)
+    x = inp["x"].copy()
+    x[:, t0, :] ^= np.uint16(0x0100)  # change x at one step
+    inp2["x"] = x
+    y3 = PT.from_dev(PT.run_gpu("selscan", inp2, "bf16"))
+    torch.cuda.synchronize()
+    assert np.array_equal(y1[:, :t0], y3[:, :t0])
+    assert not np.array_equal(y1[:, t0], y3[:, t0])
+
+
+def test_side_stream():
+    import torch
+    w = W.WORKLOADS[1]
+    inp = W.generate(w, batch=1, seqlen=100, dim=256)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = PT.run_gpu("selscan", inp, w.dtype, stream=s)
+    s.synchronize()
+    r = PT.run_oracle("selscan", inp, w.dtype)
+    assert PT.rel_err(PT.from_dev(y), r) <= PT.TOL[w.dtype]

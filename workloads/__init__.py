@@ -110,21 +110,79 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
+_BLOCK = 1 << 22  # elements per independently seeded block
+
+
 def _round_io(a32: np.ndarray, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, dtype=np.float32)
 
 
-def _normal(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
-    out = np.empty(int(np.prod(shape)), dtype=np.float32)
-    for s in range(0, out.size, chunk):
-        e = min(out.size, s + chunk)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+def _rne_bits(a: np.ndarray, out: np.ndarray) -> None:
+    """float32 block (finite by construction) -> bf16 bits, round to nearest even, into out."""
+    u = a.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    out[:] = r
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        import os
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+_POOL = None
+
+
+def _draw_io(seed: int, tensor_id: int, shape, dtype: str, draw) -> np.ndarray:
+    """Fill a tensor block by block.  Block j of tensor ``tensor_id`` draws from its own PCG64
+    stream seeded by SeedSequence([seed, tensor_id, j]), so the values do not depend on how
+    many threads fill the blocks."""
+    size = int(np.prod(shape))
+    out = np.empty(size, dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(j):
+        s = j * _BLOCK
+        e = min(size, s + _BLOCK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id, j])))
+        a = draw(rng, e - s)
+        if dtype == "bf16":
+            _rne_bits(a, out[s:e])
+        else:
+            out[s:e] = a
+
+    nblk = (size + _BLOCK - 1) // _BLOCK
+    if nblk <= 1:
+        for j in range(nblk):
+            fill(j)
+    else:
+        list(_pool().map(fill, range(nblk)))
     return out.reshape(shape)
 
 
-def _log_uniform(rng: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
-    u = rng.random(int(np.prod(shape)), dtype=np.float32)
-    return np.exp(np.float32(math.log(lo)) + u * np.float32(math.log(hi) - math.log(lo))).reshape(shape)
+def _std_normal(rng, n):
+    return rng.standard_normal(n, dtype=np.float32)
+
+
+def _normal(seed, tensor_id, shape, dtype: str = "f32") -> np.ndarray:
+    return _draw_io(seed, tensor_id, shape, dtype, _std_normal)
+
+
+def _log_uniform(seed, tensor_id, shape, lo: float, hi: float, dtype: str = "f32") -> np.ndarray:
+    a, b = np.float32(math.log(lo)), np.float32(math.log(hi) - math.log(lo))
+
+    def draw(rng, n):
+        u = rng.random(n, dtype=np.float32)
+        u *= b
+        u += a
+        return np.exp(u, out=u)
+
+    return _draw_io(seed, tensor_id, shape, dtype, draw)
 
 
 def generate(
@@ -143,7 +201,7 @@ def generate(
     direction arrays carry a leading direction axis when ``w.ndir > 1``;
     per-token/per-pixel arrays are in token (pixel, row-major) order.
     """
-    rng = np.random.Generator(np.random.PCG64(SEED_BASE + w.index if seed is None else seed))
+    seed = SEED_BASE + w.index if seed is None else seed
     bt = w.batch if batch is None else batch
     L = w.seqlen if seqlen is None else seqlen
     d = w.dim if dim is None else dim
@@ -151,17 +209,16 @@ def generate(
     k = w.ndir
     lead = (k,) if k > 1 else ()
     out: Dict[str, np.ndarray] = {}
-    out["x"] = _round_io(_normal(rng, (bt, L, d)), w.dtype)
-    out["z"] = _round_io(_normal(rng, (bt, L, d)), w.dtype) if w.gate else None
-    delta = _log_uniform(rng, lead + (bt, L, d), 1e-3, 1e-1)
-    out["delta"] = _round_io(delta, w.dtype)
-    out["B"] = _round_io(_normal(rng, lead + (bt, L, n)), w.dtype)
-    out["C"] = _round_io(_normal(rng, lead + (bt, L, n)), w.dtype)
-    out["D"] = _normal(rng, lead + (d,))
+    out["x"] = _normal(seed, 0, (bt, L, d), w.dtype)
+    out["z"] = _normal(seed, 1, (bt, L, d), w.dtype) if w.gate else None
+    out["delta"] = _log_uniform(seed, 2, lead + (bt, L, d), 1e-3, 1e-1, w.dtype)
+    out["B"] = _normal(seed, 3, lead + (bt, L, n), w.dtype)
+    out["C"] = _normal(seed, 4, lead + (bt, L, n), w.dtype)
+    out["D"] = _normal(seed, 5, lead + (d,))
     A = -np.arange(1, n + 1, dtype=np.float32)
     out["A"] = np.ascontiguousarray(np.broadcast_to(A, lead + (d, n)))
     if with_bias:
-        out["delta_bias"] = (0.5 * _normal(rng, lead + (d,))).astype(np.float32)
+        out["delta_bias"] = (np.float32(0.5) * _normal(seed, 6, lead + (d,))).astype(np.float32)
     if with_w:
         # pre-softplus value such that softplus(w + bias) ~= delta; computed in fp64 from the
         # delta actually stored, then rounded to the I/O dtype.
