@@ -32,19 +32,12 @@
 
 namespace {
 
-constexpr int kN = 16;                   // d_state supported by this version
-constexpr int kK = 16;                   // consecutive scan steps per lane
-constexpr int kLanesPerRow = 16;         // lanes sharing one channel (one DPP row)
-constexpr int kRows = 4;                 // channels per wave
-constexpr int kWaves = 4;                // waves per workgroup
-constexpr int kThreads = 64 * kWaves;    // 256
-constexpr int kCT = kRows * kWaves;      // channels per workgroup tile (16)
-constexpr int kCH = kLanesPerRow * kK;   // scan steps per chunk (256)
-constexpr int kSegF = kK + 4;            // fp32 LDS stride of one lane segment (floats)
-constexpr int kColF = kLanesPerRow * kSegF + 4;  // fp32 LDS column pitch (floats)
+constexpr int kN = 16;                 // d_state supported by this version
+constexpr int kK = 16;                 // consecutive scan steps per lane
+constexpr int kLPR = 16;               // lanes per channel: one 16-lane DPP row, 4 channels per wave
+constexpr int kCH = kLPR * kK;         // scan steps per chunk (256)
+constexpr int kFP = kCH + 4;           // fp32 LDS pitch (floats) of the B, C and y tiles
 constexpr float kLog2e = 1.4426950408889634f;
-static_assert(kCH == kThreads, "B/C staging maps one chunk row to one thread");
-static_assert(kCT % 4 == 0, "channel groups of 4");
 
 thread_local char g_last_hip_error[160] = "no error";
 
@@ -148,28 +141,39 @@ template <>
 struct Io<uint16_t> {
     static constexpr int kPadE = 8;
     __device__ static float f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-    // round to nearest even; a NaN stays a (quiet) NaN
-    __device__ static uint16_t to(float v) {
-        const uint32_t u = __float_as_uint(v);
-        const uint32_t r =
-            (u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) | 0x40u) : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-        return (uint16_t)r;
+    // round to nearest even (v_cvt_pk_bf16_f32); a NaN stays a NaN
+    __device__ static uint16_t to(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+    __device__ static uint32_t to2(float lo, float hi) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const b2 r = __builtin_convertvector((f2){lo, hi}, b2);
+        return __builtin_bit_cast(uint32_t, r);
     }
 };
 
-// io-dtype column tile geometry: [channel][segment-padded steps]
-template <typename T>
-struct Tile {
-    static constexpr int kSegE = kK + Io<T>::kPadE;
-    static constexpr int kColE = kLanesPerRow * kSegE + Io<T>::kPadE;
-    static constexpr int kBytes = kCT * kColE * (int)sizeof(T);
-    static constexpr int kYBytes = kCT * kColF * 4;
-    static constexpr int kXDBytes = 2 * kBytes > kYBytes ? 2 * kBytes : kYBytes;  // x, delta or y
-    static constexpr int kBCBytes = 2 * kN * kColF * 4;
-    static constexpr int kSmem = kXDBytes + kBCBytes;
-    __device__ static int seg(int i) { return (i / kK) * kSegE + (i % kK); }
+// Shared-memory layout of a workgroup of W waves (4W channels), per chunk of kCH steps.  In
+// every tile row the 16 steps of a lane are stored as 16-byte pieces: piece q of lane l sits
+// at q * (16 lanes * piece) + l * piece, so that one 16-byte read by each of the 16 lanes of a
+// row covers 256 contiguous bytes (no bank conflicts).
+template <typename T, int W>
+struct Lds {
+    static constexpr int kCT = 4 * W;                                 // channels per tile
+    static constexpr int kV = 16 / (int)sizeof(T);                    // io elements per piece
+    static constexpr int kXP = kCH + kV;                              // io tile pitch (elements)
+    static constexpr int kIoBytes = kCT * kXP * (int)sizeof(T);       // x or delta tile
+    static constexpr int kYBytes = kCT * kFP * 4;                     // y tile fp32
+    static constexpr int kXD = 2 * kIoBytes > kYBytes ? 2 * kIoBytes : kYBytes;
+    static constexpr int kB = kXD;                                    // B tile [state][step] fp32
+    static constexpr int kC = kB + kN * kFP * 4;                      // C tile
+    static constexpr int kA = kC + kN * kFP * 4;                      // A*log2e [ch][state]
+    static constexpr int kCarry = kA + kCT * kN * 4;                  // chunk carry [ch][state]
+    static constexpr int kDb = kCarry + kCT * kN * 4;                 // D, bias [ch][2]
+    static constexpr int kBytes = kDb + kCT * 8;
+    // position of chunk step s in an io tile row
+    __device__ static int xpos(int s) { return ((s & 15) / kV) * (kLPR * kV) + (s >> 4) * kV + (s % kV); }
 };
-__device__ __forceinline__ int segf(int i) { return (i / kK) * kSegF + (i % kK); }
+// position of chunk step s in an fp32 tile row (pieces of 4 floats)
+__host__ __device__ constexpr int fpos(int s) { return ((s & 15) >> 2) * (kLPR * 4) + ((s >> 4) << 2) + (s & 3); }
 
 // row (token or pixel) visited at scan step l by direction k
 __device__ __forceinline__ int64_t visit(int kind, int k, int64_t l, int64_t L, int64_t H) {
@@ -188,258 +192,402 @@ __device__ __forceinline__ float silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// DPP move within 16-lane rows; lanes whose source is outside the row get `old`
-template <int CTRL>
-__device__ __forceinline__ float dpp(float old, float src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
-                                                                  __builtin_bit_cast(int, src), CTRL, 0xF, 0xF,
-                                                                  false));
-}
-constexpr int kRowShr = 0x110;  // row_shr:n = kRowShr + n
-constexpr int kRowRor1 = 0x121;  // row_ror:1
-
-// 4 consecutive io elements of one row -> float[4]; elements past `n` read as 0
+// 8 consecutive io elements of one row as raw bits (bf16: 4 dwords; fp32: 8); elements past
+// `n` read as 0
 template <typename T>
-__device__ __forceinline__ void load4(const T *p, int n, bool vec, float v[4]) {
-    if (vec && n >= 4) {
+struct Raw8 {
+    uint32_t w[sizeof(T) * 2];
+};
+
+template <typename T>
+__device__ __forceinline__ Raw8<T> load_raw8(const T *p, int n, bool vec) {
+    Raw8<T> r;
+    if (vec && n >= 8) {
+        const uint4 q = *(const uint4 *)p;
+        r.w[0] = q.x, r.w[1] = q.y, r.w[2] = q.z, r.w[3] = q.w;
         if constexpr (sizeof(T) == 4) {
-            const float4 q = *(const float4 *)p;
-            v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
-        } else {
-            const uint2 q = *(const uint2 *)p;
-            v[0] = __uint_as_float(q.x << 16), v[1] = __uint_as_float(q.x & 0xFFFF0000u);
-            v[2] = __uint_as_float(q.y << 16), v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+            const uint4 q2 = *(const uint4 *)(p + 4);
+            r.w[4] = q2.x, r.w[5] = q2.y, r.w[6] = q2.z, r.w[7] = q2.w;
         }
-        return;
+        return r;
     }
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = e < n ? Io<T>::f32(p[e]) : 0.f;
+        for (int e = 0; e < 8; ++e) r.w[e] = e < n ? __float_as_uint(p[e]) : 0u;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = 2 * e < n ? (uint32_t)p[2 * e] : 0u;
+            const uint32_t hi = 2 * e + 1 < n ? (uint32_t)p[2 * e + 1] : 0u;
+            r.w[e] = lo | (hi << 16);
+        }
+    }
+    return r;
+}
+
+// element e of a Raw8 as fp32 / as its raw io bits
+template <typename T>
+__device__ __forceinline__ float raw_f32(const Raw8<T> &r, int e) {
+    if constexpr (sizeof(T) == 4) return __uint_as_float(r.w[e]);
+    else return __uint_as_float((e & 1) ? (r.w[e >> 1] & 0xFFFF0000u) : (r.w[e >> 1] << 16));
 }
 
 template <typename T>
-__device__ __forceinline__ void store4(T *p, int n, bool vec, const float v[4]) {
-    if (vec && n >= 4) {
+__device__ __forceinline__ void store8(T *p, int n, bool vec, const float v[8]) {
+    if (vec && n >= 8) {
         if constexpr (sizeof(T) == 4) {
             *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4 *)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
         } else {
-            uint2 q;
-            q.x = (uint32_t)Io<T>::to(v[0]) | ((uint32_t)Io<T>::to(v[1]) << 16);
-            q.y = (uint32_t)Io<T>::to(v[2]) | ((uint32_t)Io<T>::to(v[3]) << 16);
-            *(uint2 *)p = q;
+            *(uint4 *)p = make_uint4(Io<T>::to2(v[0], v[1]), Io<T>::to2(v[2], v[3]), Io<T>::to2(v[4], v[5]),
+                                     Io<T>::to2(v[6], v[7]));
         }
         return;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 8; ++e)
         if (e < n) p[e] = Io<T>::to(v[e]);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void selscan_chunked(Params p) {
-    using TL = Tile<T>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[TL::kSmem];
-    T *xt = (T *)smem;                       // x column tile [kCT][kColE]
-    T *dtile = (T *)(smem + TL::kBytes);     // delta column tile
-    float *yt = (float *)smem;               // y partial [kCT][kColF] (reuses x/delta space)
-    float *Bs = (float *)(smem + TL::kXDBytes);  // [kN][kColF]
-    float *Cs = Bs + kN * kColF;
+__device__ __forceinline__ void load_f8(const float *p, int n, bool vec, float v[8]) {
+    if (vec && n >= 8) {
+        const float4 q = *(const float4 *)p, q2 = *(const float4 *)(p + 4);
+        v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w, v[4] = q2.x, v[5] = q2.y, v[6] = q2.z, v[7] = q2.w;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < n ? p[e] : 0.f;
+}
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, row = lane >> 4, l = lane & 15;
+// Inclusive scan of two states' lane maps (a, b) along each 16-lane row (one channel):
+// (a_l, b_l) <- (a_l a_{l-s}, a_l b_{l-s} + b_l) for s = 1, 2, 4, 8 with DPP row_shr; a lane
+// whose source is outside its row is not written, i.e. composed with the identity (1, 0).
+// Then every lane's start state: h enters holding the channel's carry and row_shr:1 overwrites
+// it with the left neighbour's end state everywhere except in lane 0 of the row, whose source
+// is out of range.  The two states alternate so that every DPP read comes at least two wait
+// states after the write of its source (the gfx9 VALU->DPP hazard); s_nop covers the ends.
+__device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float &a1, float &h0, float &h1) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_mov_b32_dpp %4, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %5, %1 row_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(b0), "+v"(b1), "+v"(a0), "+v"(a1), "+v"(h0), "+v"(h1));
+}
+
+// One workgroup: W waves, a tile of 4W channels of one batch row, every direction.
+template <typename T, int W>
+__global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
+    using S = Lds<T, W>;
+    constexpr int NT = 64 * W, CT = 4 * W, NG = CT / 8;  // threads, channels, 8-channel groups
+    static_assert((kCH / 2) * NG == NT, "one (step pair, channel group) item per thread");
+    constexpr int BPT = kCH * kN / NT;                   // B (and C) values staged per thread
+    static_assert(BPT == 8 || BPT == 16, "B/C staging granularity");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
+    T *xt = (T *)smem;
+    T *dtl = (T *)(smem + S::kIoBytes);
+    float *yt = (float *)smem;
+    float *Bs = (float *)(smem + S::kB);
+    float *Cs = (float *)(smem + S::kC);
+    float *As = (float *)(smem + S::kA);
+    float *Cy = (float *)(smem + S::kCarry);
+    float *Db = (float *)(smem + S::kDb);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l = lane & 15;
+    const int cl = wave * 4 + (lane >> 4);     // this lane's channel within the tile
+    const float firstf = l == 0 ? 1.f : 0.f;  // 1 on the first lane of each channel
     // consecutive channel tiles on one XCD: workgroups are dealt round-robin over 8 XCDs
     const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
     const int tile = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
     const int b = tile / p.ntc;
-    const int64_t c0 = (int64_t)(tile % p.ntc) * kCT;
-    const int cl = wave * kRows + row;
-    const int64_t c = c0 + cl;
-    const bool cvalid = c < p.dim;
+    const int64_t c0 = (int64_t)(tile % p.ntc) * CT;
     const int64_t L = p.L, dim = p.dim;
     const int64_t tok = (int64_t)p.batch * L * dim, bcn = (int64_t)p.batch * L * kN;
-    const int ncols = (int)(dim - c0 < kCT ? dim - c0 : kCT);  // valid channels in this tile
+    const int ncols = (int)(dim - c0 < CT ? dim - c0 : CT);
+    const bool cvalid = cl < ncols;
     const int nchunks = (int)((L + kCH - 1) / kCH);
     const bool vec = p.vec != 0;
     const T *x = (const T *)p.x;
     const T *z = (const T *)p.z;
     T *y = (T *)p.y;
 
+    // staging / output item of this thread: steps (2*ip, 2*ip+1) of the chunk, channels
+    // 8*g .. 8*g+7 of the tile
+    const int ip = tid / NG, g = tid % NG, nv = ncols - 8 * g;
+    // B/C staging item: step sb of the chunk, states hb .. hb+BPT-1
+    const int sb = BPT == 16 ? tid : tid >> 1, hb = BPT == 16 ? 0 : (tid & 1) * BPT;
+
     for (int k = 0; k < p.ndir; ++k) {
         const T *dl = (const T *)p.delta + k * tok;
         const T *Bk = (const T *)p.B + k * bcn;
         const T *Ck = (const T *)p.C + k * bcn;
-        const int64_t cc = cvalid ? c : 0;
-        float A2[kN], carry[kN];
-#pragma unroll
-        for (int n = 0; n < kN; ++n) {
-            A2[n] = p.A[(k * dim + cc) * kN + n] * kLog2e;
-            carry[n] = 0.f;
+        __syncthreads();  // the previous direction is done with the parameter tiles
+        for (int i = tid; i < CT * kN; i += NT) {
+            const int ch = i / kN, n = i % kN;
+            const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
+            As[i] = p.A[(k * dim + cc) * kN + n] * kLog2e;
+            Cy[i] = 0.f;
         }
-        const float Dd = p.D ? p.D[k * dim + cc] : 0.f;
-        const float bias = p.bias ? p.bias[k * dim + cc] : 0.f;
+        for (int i = tid; i < CT; i += NT) {
+            const int64_t cc = c0 + i < dim ? c0 + i : 0;
+            Db[2 * i] = p.D ? p.D[k * dim + cc] : 0.f;
+            Db[2 * i + 1] = p.bias ? p.bias[k * dim + cc] : 0.f;
+        }
 
+        // global -> registers for chunk q (prefetched one chunk ahead)
+        Raw8<T> px0, px1, pd0, pd1;
+        uint32_t pbc[2][BPT * sizeof(T) / 4];  // raw B and C values of one chunk step
+        auto fetch = [&](int q) {
+            const int64_t s0 = (int64_t)q * kCH;
+            const int64_t sa = s0 + 2 * ip, sbb = sa + 1;
+            px0 = px1 = pd0 = pd1 = Raw8<T>{};
+            if (nv > 0 && sa < L) {
+                const int64_t off = ((int64_t)b * L + visit(p.kind, k, sa, L, p.H)) * dim + c0 + 8 * g;
+                px0 = load_raw8(x + off, nv, vec);
+                pd0 = load_raw8(dl + off, nv, vec);
+            }
+            if (nv > 0 && sbb < L) {
+                const int64_t off = ((int64_t)b * L + visit(p.kind, k, sbb, L, p.H)) * dim + c0 + 8 * g;
+                px1 = load_raw8(x + off, nv, vec);
+                pd1 = load_raw8(dl + off, nv, vec);
+            }
+            const int64_t s = s0 + sb;
+            constexpr int NW = BPT * sizeof(T) / 4;
+#pragma unroll
+            for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
+            if (s < L) {
+                const int64_t roff = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * kN + hb;
+                if (p.vecbc) {
+#pragma unroll
+                    for (int h = 0; h < NW; h += 4) {
+                        const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + roff) + h);
+                        const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + roff) + h);
+                        pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                        pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                    }
+                } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                    for (int h = 0; h < NW; ++h) {
+                        pbc[0][h] = (uint32_t)Bk[roff + 2 * h] | ((uint32_t)Bk[roff + 2 * h + 1] << 16);
+                        pbc[1][h] = (uint32_t)Ck[roff + 2 * h] | ((uint32_t)Ck[roff + 2 * h + 1] << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < NW; ++h) {
+                        pbc[0][h] = __float_as_uint(Bk[roff + h]);
+                        pbc[1][h] = __float_as_uint(Ck[roff + h]);
+                    }
+                }
+            }
+        };
+        // registers -> LDS
+        auto commit = [&]() {
+            const int si = S::xpos(2 * ip);  // steps 2*ip and 2*ip+1 are adjacent in a piece
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ch = 8 * g + e;
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t xa = e & 1 ? px0.w[e >> 1] >> 16 : px0.w[e >> 1] & 0xFFFFu;
+                    const uint32_t xb = e & 1 ? px1.w[e >> 1] & 0xFFFF0000u : px1.w[e >> 1] << 16;
+                    const uint32_t da = e & 1 ? pd0.w[e >> 1] >> 16 : pd0.w[e >> 1] & 0xFFFFu;
+                    const uint32_t db = e & 1 ? pd1.w[e >> 1] & 0xFFFF0000u : pd1.w[e >> 1] << 16;
+                    *(uint32_t *)&xt[ch * S::kXP + si] = xa | xb;
+                    *(uint32_t *)&dtl[ch * S::kXP + si] = da | db;
+                } else {
+                    *(uint2 *)&xt[ch * S::kXP + si] = make_uint2(px0.w[e], px1.w[e]);
+                    *(uint2 *)&dtl[ch * S::kXP + si] = make_uint2(pd0.w[e], pd1.w[e]);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < BPT; ++h) {
+                float bv, cv;
+                if constexpr (sizeof(T) == 2) {
+                    bv = __uint_as_float(h & 1 ? pbc[0][h >> 1] & 0xFFFF0000u : pbc[0][h >> 1] << 16);
+                    cv = __uint_as_float(h & 1 ? pbc[1][h >> 1] & 0xFFFF0000u : pbc[1][h >> 1] << 16);
+                } else {
+                    bv = __uint_as_float(pbc[0][h]);
+                    cv = __uint_as_float(pbc[1][h]);
+                }
+                Bs[(hb + h) * kFP + fpos(sb)] = bv;
+                Cs[(hb + h) * kFP + fpos(sb)] = cv;
+            }
+        };
+
+        fetch(0);
         for (int q = 0; q < nchunks; ++q) {
             const int64_t s0 = (int64_t)q * kCH;
             __syncthreads();  // the previous chunk is done with every tile
-            // ---- stage x and delta: rows of 4 channels, written column-major
-#pragma unroll
-            for (int m = 0; m < kCH * (kCT / 4) / kThreads; ++m) {
-                const int item = tid + m * kThreads, i = item >> 2, g = item & 3;
-                const int64_t s = s0 + i;
-                float xv[4] = {0.f, 0.f, 0.f, 0.f}, dv[4] = {0.f, 0.f, 0.f, 0.f};
-                const int nv = ncols - 4 * g;
-                if (s < L && nv > 0) {
-                    const int64_t off = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * dim + c0 + 4 * g;
-                    load4(x + off, nv, vec, xv);
-                    load4(dl + off, nv, vec, dv);
-                }
-                const int si = TL::seg(i);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (sizeof(T) == 4) {
-                        xt[(4 * g + e) * TL::kColE + si] = xv[e];
-                        dtile[(4 * g + e) * TL::kColE + si] = dv[e];
-                    } else {
-                        xt[(4 * g + e) * TL::kColE + si] = (T)(__float_as_uint(xv[e]) >> 16);
-                        dtile[(4 * g + e) * TL::kColE + si] = (T)(__float_as_uint(dv[e]) >> 16);
-                    }
-                }
-            }
-            // ---- stage B and C for this chunk as fp32 [state][step]
-            {
-                const int i = tid;
-                const int64_t s = s0 + i;
-                float bv[kN], cv[kN];
-                if (s < L) {
-                    const int64_t roff = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * kN;
-                    if (p.vecbc) {
-#pragma unroll
-                        for (int h = 0; h < kN; h += 4) {
-                            load4(Bk + roff + h, 4, true, bv + h);
-                            load4(Ck + roff + h, 4, true, cv + h);
-                        }
-                    } else {
-#pragma unroll
-                        for (int n = 0; n < kN; ++n) {
-                            bv[n] = Io<T>::f32(Bk[roff + n]);
-                            cv[n] = Io<T>::f32(Ck[roff + n]);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int n = 0; n < kN; ++n) bv[n] = cv[n] = 0.f;
-                }
-                const int sf = segf(i);
-#pragma unroll
-                for (int n = 0; n < kN; ++n) {
-                    Bs[n * kColF + sf] = bv[n];
-                    Cs[n * kColF + sf] = cv[n];
-                }
-            }
+            commit();
             __syncthreads();
+            // gate input for this chunk's output item, then the next chunk's inputs: in flight
+            // while this chunk computes
+            const bool last = k == p.ndir - 1;
+            Raw8<T> zr[2] = {};
+            int64_t ooff[2] = {0, 0};
+            bool ovalid[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int64_t s = s0 + 2 * ip + r;
+                ovalid[r] = nv > 0 && s < L;
+                if (ovalid[r]) {
+                    ooff[r] = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * dim + c0 + 8 * g;
+                    if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                }
+            }
+            if (q + 1 < nchunks) fetch(q + 1);
 
             // ---- this lane's 16 steps of its channel
+            const bool full = s0 + kCH <= L && ncols == CT;  // no step or channel past the end
+            const int64_t rem = L - (s0 + l * kK);
+            const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= kK ? kK : (int)rem));
             float dt[kK], dx[kK], yv[kK];
             float sdt = 0.f;
             {
-                const T *xc = xt + cl * TL::kColE + l * TL::kSegE;
-                const T *dc = dtile + cl * TL::kColE + l * TL::kSegE;
-                T xr[kK], dr[kK];
+                const float Dd = Db[2 * cl], bias = Db[2 * cl + 1];
+                float xf[kK], df[kK];
+                constexpr int V = S::kV;
 #pragma unroll
-                for (int j = 0; j < kK; ++j) {
-                    xr[j] = xc[j];
-                    dr[j] = dc[j];
+                for (int pc = 0; pc < kK / V; ++pc) {
+                    const uint4 xq = *(const uint4 *)&xt[cl * S::kXP + pc * (kLPR * V) + l * V];
+                    const uint4 dq = *(const uint4 *)&dtl[cl * S::kXP + pc * (kLPR * V) + l * V];
+                    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w}, dw[4] = {dq.x, dq.y, dq.z, dq.w};
+#pragma unroll
+                    for (int i = 0; i < V; ++i) {
+                        if constexpr (sizeof(T) == 2) {
+                            xf[pc * V + i] = __uint_as_float(i & 1 ? xw[i >> 1] & 0xFFFF0000u : xw[i >> 1] << 16);
+                            df[pc * V + i] = __uint_as_float(i & 1 ? dw[i >> 1] & 0xFFFF0000u : dw[i >> 1] << 16);
+                        } else {
+                            xf[pc * V + i] = __uint_as_float(xw[i]);
+                            df[pc * V + i] = __uint_as_float(dw[i]);
+                        }
+                    }
+                }
+                if (p.softplus) {
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) dt[j] = softplus(df[j] + bias);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
+                }
+                if (!full) {
+                    // steps past the sequence end and channels past dim get delta = 0, the
+                    // identity step (staged x there is 0 too)
+                    const float limf = (float)lim;
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) dt[j] *= __saturatef(limf - (float)j);
                 }
 #pragma unroll
                 for (int j = 0; j < kK; ++j) {
-                    const bool v = cvalid && (s0 + l * kK + j < L);
-                    float d = Io<T>::f32(dr[j]) + bias;
-                    if (p.softplus) d = softplus(d);
-                    d = v ? d : 0.f;
-                    const float xv = Io<T>::f32(xr[j]);
-                    dt[j] = d;
-                    dx[j] = d * xv;
-                    yv[j] = Dd * xv;
-                    sdt += d;
+                    dx[j] = dt[j] * xf[j];
+                    yv[j] = Dd * xf[j];
+                    sdt += dt[j];
                 }
             }
-            const float *Bc = Bs + l * kSegF;
-            const float *Cc = Cs + l * kSegF;
-#pragma unroll
-            for (int n = 0; n < kN; ++n) {
-                const float a2 = A2[n];
-                float e[kK], u[kK];
-                float bb = 0.f;
-#pragma unroll
-                for (int j = 0; j < kK; ++j) {
-                    e[j] = __builtin_amdgcn_exp2f(dt[j] * a2);
-                    u[j] = dx[j] * Bc[n * kColF + j];
-                    bb = fmaf(e[j], bb, u[j]);
-                }
-                float a = __builtin_amdgcn_exp2f(a2 * sdt);
-                bb = fmaf(a, l == 0 ? carry[n] : 0.f, bb);
-                // inclusive scan of the lanes' affine maps along the row
+            const float *Bc = Bs + 4 * l;
+            const float *Cc = Cs + 4 * l;
+#pragma unroll 1
+            for (int n = 0; n < kN; n += 2) {
+                const float2 a2 = *(const float2 *)&As[cl * kN + n];
+                float e0[kK], u0[kK], e1[kK], u1[kK];
+                float b0, b1;
                 {
-                    float ap = dpp<kRowShr + 1>(1.f, a), bp = dpp<kRowShr + 1>(0.f, bb);
-                    bb = fmaf(a, bp, bb);
-                    a *= ap;
-                    ap = dpp<kRowShr + 2>(1.f, a), bp = dpp<kRowShr + 2>(0.f, bb);
-                    bb = fmaf(a, bp, bb);
-                    a *= ap;
-                    ap = dpp<kRowShr + 4>(1.f, a), bp = dpp<kRowShr + 4>(0.f, bb);
-                    bb = fmaf(a, bp, bb);
-                    a *= ap;
-                    bp = dpp<kRowShr + 8>(0.f, bb);
-                    bb = fmaf(a, bp, bb);
+                    float B0[kK], B1[kK];
+#pragma unroll
+                    for (int pc = 0; pc < 4; ++pc) {
+                        *(float4 *)&B0[4 * pc] = *(const float4 *)&Bc[n * kFP + pc * (kLPR * 4)];
+                        *(float4 *)&B1[4 * pc] = *(const float4 *)&Bc[(n + 1) * kFP + pc * (kLPR * 4)];
+                    }
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) {
+                        e0[j] = __builtin_amdgcn_exp2f(dt[j] * a2.x);
+                        e1[j] = __builtin_amdgcn_exp2f(dt[j] * a2.y);
+                        u0[j] = dx[j] * B0[j];
+                        u1[j] = dx[j] * B1[j];
+                        b0 = j == 0 ? u0[0] : fmaf(e0[j], b0, u0[j]);  // from a zero state
+                        b1 = j == 0 ? u1[0] : fmaf(e1[j], b1, u1[j]);
+                    }
                 }
-                // lane l >= 1 starts from lane l-1's end state; lane 0 from the chunk carry;
-                // lane 0 receives lane 15's end state, the carry of the next chunk
-                const float rot = dpp<kRowRor1>(0.f, bb);
-                float h = l == 0 ? carry[n] : rot;
-                carry[n] = rot;
+                float a0 = __builtin_amdgcn_exp2f(a2.x * sdt);
+                float a1 = __builtin_amdgcn_exp2f(a2.y * sdt);
+                // the previous chunk's end state of this channel enters through its first lane
+                const float2 cy = *(const float2 *)&Cy[cl * kN + n];
+                float h0 = cy.x, h1 = cy.y;
+                b0 = fmaf(a0, h0 * firstf, b0);
+                b1 = fmaf(a1, h1 * firstf, b1);
+                scan16x2(b0, b1, a0, a1, h0, h1);
+                // the last lane of a channel holds the chunk's end state: the next chunk's carry
+                if (l == kLPR - 1) *(float2 *)&Cy[cl * kN + n] = make_float2(b0, b1);
+                float C0[kK], C1[kK];
+#pragma unroll
+                for (int pc = 0; pc < 4; ++pc) {
+                    *(float4 *)&C0[4 * pc] = *(const float4 *)&Cc[n * kFP + pc * (kLPR * 4)];
+                    *(float4 *)&C1[4 * pc] = *(const float4 *)&Cc[(n + 1) * kFP + pc * (kLPR * 4)];
+                }
 #pragma unroll
                 for (int j = 0; j < kK; ++j) {
-                    h = fmaf(e[j], h, u[j]);
-                    yv[j] = fmaf(Cc[n * kColF + j], h, yv[j]);
+                    h0 = fmaf(e0[j], h0, u0[j]);
+                    h1 = fmaf(e1[j], h1, u1[j]);
+                    yv[j] = fmaf(C0[j], h0, yv[j]);
+                    yv[j] = fmaf(C1[j], h1, yv[j]);
                 }
             }
             __syncthreads();  // x/delta tiles fully read before y reuses their space
-            {
-                float *yc = yt + cl * kColF + l * kSegF;
 #pragma unroll
-                for (int j = 0; j < kK; ++j) yc[j] = yv[j];
-            }
+            for (int pc = 0; pc < 4; ++pc)
+                *(float4 *)&yt[cl * kFP + pc * (kLPR * 4) + 4 * l] =
+                    make_float4(yv[4 * pc], yv[4 * pc + 1], yv[4 * pc + 2], yv[4 * pc + 3]);
             __syncthreads();
             // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
 #pragma unroll
-            for (int m = 0; m < kCH * (kCT / 4) / kThreads; ++m) {
-                const int item = tid + m * kThreads, i = item >> 2, g = item & 3;
-                const int64_t s = s0 + i;
-                const int nv = ncols - 4 * g;
-                if (s >= L || nv <= 0) continue;
-                const int64_t off = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * dim + c0 + 4 * g;
-                float v[4];
-                const int sf = segf(i);
+            for (int r = 0; r < 2; ++r) {
+                if (!ovalid[r]) continue;
+                float v[8], wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (k > 0) load_f8(p.ws + ooff[r], nv, vec, wv);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = yt[(4 * g + e) * kColF + sf];
-                if (k > 0) {
-                    float w4[4];
-                    load4(p.ws + off, nv, vec, w4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] += w4[e];
-                }
-                if (k == p.ndir - 1) {
+                for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(2 * ip + r)] + wv[e];
+                if (last) {
                     if (z) {
-                        float zv[4];
-                        load4(z + off, nv, vec, zv);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] *= silu(zv[e]);
+                        for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
                     }
-                    store4(y + off, nv, vec, v);
+                    store8(y + ooff[r], nv, vec, v);
                 } else {
-                    store4(p.ws + off, nv, vec, v);
+                    store8(p.ws + ooff[r], nv, vec, v);
                 }
             }
         }
     }
+}
+
+template <typename T, int W>
+int launch_tiles(const Params &a, int64_t batch, void *stream) {
+    constexpr int CT = 4 * W;
+    Params c = a;
+    c.ntc = (int)((a.dim + CT - 1) / CT);
+    const int64_t blocks = batch * (int64_t)c.ntc;
+    if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    void *args[] = {&c};
+    hipError_t e = hipLaunchKernel((const void *)&selscan_chunked<T, W>, dim3((unsigned)blocks), dim3(64 * W),
+                                   args, 0, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
+        return SELSCAN_E_HIP;
+    }
+    return SELSCAN_OK;
 }
 
 int launch(const Problem &p, void *stream) {
@@ -451,24 +599,16 @@ int launch(const Problem &p, void *stream) {
     a.L = p.L, a.dim = p.dim, a.H = p.H;
     a.batch = (int)p.batch, a.ndir = p.ndir, a.kind = p.kind;
     a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+    // rows of 8 channels move as 16-byte vectors when every row start is 16-byte aligned
     const void *rows[] = {p.x, p.delta, p.z, p.y};
-    bool vec = p.dim % 4 == 0 && (!a.ws || aligned(a.ws, 16));
+    bool vec = p.dim % 8 == 0 && (!a.ws || aligned(a.ws, 16));
     for (const void *q : rows)
-        if (q && !aligned(q, 4 * s)) vec = false;
+        if (q && !aligned(q, 16)) vec = false;
     a.vec = vec;
     a.vecbc = aligned(p.B, 16) && aligned(p.C, 16);
-    a.ntc = (int)((p.dim + kCT - 1) / kCT);
-    const int64_t blocks = p.batch * (int64_t)a.ntc;
-    if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
-    void *args[] = {&a};
-    const void *fn = p.dtype == SELSCAN_BF16 ? (const void *)&selscan_chunked<uint16_t>
-                                             : (const void *)&selscan_chunked<float>;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), args, 0, (hipStream_t)stream);
-    if (e != hipSuccess) {
-        strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
-        return SELSCAN_E_HIP;
-    }
-    return SELSCAN_OK;
+    a.ntc = 0;
+    if (p.dtype == SELSCAN_BF16) return launch_tiles<uint16_t, 4>(a, p.batch, stream);
+    return launch_tiles<float, 4>(a, p.batch, stream);
 }
 
 int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {
