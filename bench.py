@@ -21,6 +21,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# ALU roofline.  Per element (b, t, d, n, direction) the method needs one exp2 and four fp32
+# lane operations (delta*A, (delta*x)*B, the state FMA, the output FMA).  MI355X issues
+# transcendentals at a quarter of the fp32 FMA lane rate, so one exp2 occupies the VALU like
+# four FMAs: 8 FMA slots = 16 fp32 flop-equivalents per element, against the published fp32
+# vector peak of 157.3 TFLOP/s (256 CUs x 2.4 GHz x 128 FMA lanes x 2).
+ALU_PEAK_TFLOPS = 157.3
+FLOP_EQ_PER_ELEMENT = 16
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc", "selscan.hip")
@@ -87,7 +94,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-channels", type=int, default=512)
+    ap.add_argument("--cpu-channels", type=int, default=4096)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one device copy of 1 GiB (a plain copy of known size, for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the scan shards over batch x channel with no "
@@ -134,6 +144,13 @@ def main() -> int:
             S.ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, D=t["D"], z=t["z"], y=y,
                        workspace=ws, stream=stream)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -152,7 +169,8 @@ def main() -> int:
     kern_ms = float(np.mean(launch_ms))
     value = w.elements / (ms_step * 1e-3)
     alg = w.algorithmic_bytes()
-    achieved = alg / (kern_ms * 1e-3) / 1e9
+    hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
+    alu_tflops = w.elements * FLOP_EQ_PER_ELEMENT / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,
@@ -169,10 +187,13 @@ def main() -> int:
         "data": "synthetic (seeded: x, z, B, C ~ N(0,1); delta log-uniform [1e-3, 1e-1]; A[d,n] = -(n+1); D ~ N(0,1))",
         "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),
-                     "algorithmic_bytes_per_launch": alg, "elements_per_launch": w.elements},
+        "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
+                     "work_per_element": "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents",
+                     "kernel": "selscan_chunked", "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),
+                     "elements_per_launch": w.elements, "algorithmic_bytes_per_launch": alg,
+                     "hbm_achieved_GBps": hbm_gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
+                     "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
         del t, y, ws
