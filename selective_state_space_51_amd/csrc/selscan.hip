@@ -37,6 +37,7 @@ constexpr int kK = 16;                 // consecutive scan steps per lane
 constexpr int kLPR = 16;               // lanes per channel: one 16-lane DPP row, 4 channels per wave
 constexpr int kCH = kLPR * kK;         // scan steps per chunk (256)
 constexpr int kFP = kCH + 4;           // fp32 LDS pitch (floats) of the B, C and y tiles
+constexpr int kTC = 16;                // channels per workgroup tile: 4 waves x 4 channels
 constexpr float kLog2e = 1.4426950408889634f;
 
 thread_local char g_last_hip_error[160] = "no error";
@@ -80,6 +81,8 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
     if (p.dtype != SELSCAN_F32 && p.dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
     if (p.flags & ~SELSCAN_FLAG_DELTA_SOFTPLUS) return SELSCAN_E_UNSUPPORTED;
     if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
+    if (p.kind == SELSCAN_OP_SS2D && (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
+        return SELSCAN_E_UNSUPPORTED;
     if (p.batch == 0 || p.L == 0 || p.dim == 0) return SELSCAN_OK;
     if (!p.x || !p.delta || !p.A || !p.B || !p.C || !p.y) return SELSCAN_E_NULL;
     const size_t s = p.dtype == SELSCAN_BF16 ? 2 : 4;
@@ -122,9 +125,10 @@ struct Params {
     const float *A, *D, *bias;
     void *y;
     float *ws;        // fp32 [batch][L][dim] partial sums when ndir > 1
-    int64_t L, dim, H;
-    int batch, ndir, kind, softplus;
-    int vec;          // rows of 4 channels may be moved as one vector
+    int64_t L, dim;
+    int H, Wd;        // SS2D image height and width (H * Wd == L)
+    int batch, ndir, softplus;
+    int vec;          // rows of 8 channels may be moved as 16-byte vectors
     int vecbc;        // a 16-value B/C row may be moved as 16-byte vectors
     int ntc;          // channel tiles per batch row
 };
@@ -151,19 +155,24 @@ struct Io<uint16_t> {
     }
 };
 
-// Shared-memory layout of a workgroup of W waves (4W channels), per chunk of kCH steps.  In
-// every tile row the 16 steps of a lane are stored as 16-byte pieces: piece q of lane l sits
-// at q * (16 lanes * piece) + l * piece, so that one 16-byte read by each of the 16 lanes of a
+// Shared-memory layout of a workgroup (16 channels), per chunk of kCH steps.  In every tile
+// row the 16 steps of a lane are stored as 16-byte pieces: piece q of lane l sits at
+// q * (16 lanes * piece) + l * piece, so that one 16-byte read by each of the 16 lanes of a
 // row covers 256 contiguous bytes (no bank conflicts).
-template <typename T, int W>
+template <typename T>
 struct Lds {
-    static constexpr int kCT = 4 * W;                                 // channels per tile
+    static constexpr int kCT = kTC;                                  // channels per tile
     static constexpr int kV = 16 / (int)sizeof(T);                    // io elements per piece
     static constexpr int kXP = kCH + kV;                              // io tile pitch (elements)
     static constexpr int kIoBytes = kCT * kXP * (int)sizeof(T);       // x or delta tile
     static constexpr int kYBytes = kCT * kFP * 4;                     // y tile fp32
-    static constexpr int kXD = 2 * kIoBytes > kYBytes ? 2 * kIoBytes : kYBytes;
-    static constexpr int kB = kXD;                                    // B tile [state][step] fp32
+    // bf16 io: the y tile has space of its own, so a wave writes its outputs without waiting
+    // for the other waves to finish reading x and delta.  fp32 io: y reuses the x/delta space
+    // (space of its own would leave room for only one workgroup per compute unit).
+    static constexpr bool kYOwn = sizeof(T) == 2;
+    static constexpr int kXD = 2 * kIoBytes;
+    static constexpr int kY = kYOwn ? kXD : 0;
+    static constexpr int kB = kYOwn ? kXD + kYBytes : (kXD > kYBytes ? kXD : kYBytes);  // B [state][step]
     static constexpr int kC = kB + kN * kFP * 4;                      // C tile
     static constexpr int kA = kC + kN * kFP * 4;                      // A*log2e [ch][state]
     static constexpr int kCarry = kA + kCT * kN * 4;                  // chunk carry [ch][state]
@@ -175,13 +184,20 @@ struct Lds {
 // position of chunk step s in an fp32 tile row (pieces of 4 floats)
 __host__ __device__ constexpr int fpos(int s) { return ((s & 15) >> 2) * (kLPR * 4) + ((s >> 4) << 2) + (s & 3); }
 
-// row (token or pixel) visited at scan step l by direction k
-__device__ __forceinline__ int64_t visit(int kind, int k, int64_t l, int64_t L, int64_t H) {
-    if (kind == SELSCAN_OP_FWD) return l;
-    if (kind == SELSCAN_OP_BIDIR) return k == 0 ? l : L - 1 - l;
-    if (k >= 2) l = L - 1 - l;
-    if (k == 0 || k == 2) return l;
-    return (l % H) * (L / H) + l / H;
+// row (token or pixel) visited at scan step l, 0 <= l < L, by direction k
+template <int KIND>
+__device__ __forceinline__ int64_t visit(int k, int64_t l, int64_t L, int H, int Wd) {
+    if constexpr (KIND == SELSCAN_OP_FWD) {
+        return l;
+    } else if constexpr (KIND == SELSCAN_OP_BIDIR) {
+        return k == 0 ? l : L - 1 - l;
+    } else {
+        // SS2D: k = 0 row-major, 1 column-major, 2 and 3 the same orders reversed (L < 2^31)
+        if (k >= 2) l = L - 1 - l;
+        if ((k & 1) == 0) return l;
+        const uint32_t u = (uint32_t)l, q = u / (uint32_t)H, r = u - q * (uint32_t)H;
+        return (int64_t)r * Wd + q;
+    }
 }
 
 // softplus(w) = log(1 + e^w) without overflow
@@ -289,18 +305,26 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
         : "+v"(b0), "+v"(b1), "+v"(a0), "+v"(a1), "+v"(h0), "+v"(h1));
 }
 
-// One workgroup: W waves, a tile of 4W channels of one batch row, every direction.
-template <typename T, int W>
-__global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
-    using S = Lds<T, W>;
-    constexpr int NT = 64 * W, CT = 4 * W, NG = CT / 8;  // threads, channels, 8-channel groups
-    static_assert((kCH / 2) * NG == NT, "one (step pair, channel group) item per thread");
-    constexpr int BPT = kCH * kN / NT;                   // B (and C) values staged per thread
-    static_assert(BPT == 8 || BPT == 16, "B/C staging granularity");
+// One workgroup: 4 waves, a tile of 16 channels of one batch row, every direction.
+//
+// Lane maps of the staging and output items (wave w, lane i of the wave) are chosen so that
+// each LDS write or read instruction of a wave touches 64 distinct banks:
+//  - x/delta staging: chunk steps 2p, 2p+1 of the 8-channel group g = i / 32, with
+//    p = 8 (((i / 4) % 8) + 8 (w / 2)) + 4 (w % 2) + i % 4;
+//  - B/C staging: chunk step 16 (i / 4) + 4 w + i % 4, all 16 states;
+//  - output: chunk steps 16 ((i / 4) % 8 + 8 r) + 4 w + i % 4, r = 0, 1, group g = i / 32.
+// Priority: the waves of the two workgroups that share a SIMD run their state loops at
+// priorities that alternate with the chunk count, so neither workgroup starves the other,
+// and every phase outside the state loop runs above both.
+template <typename T, int KIND>
+__global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
+    using S = Lds<T>;
+    constexpr int CT = kTC;
+    constexpr int NW = kN * (int)sizeof(T) / 4;  // dwords of one 16-value B or C row
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
     T *xt = (T *)smem;
     T *dtl = (T *)(smem + S::kIoBytes);
-    float *yt = (float *)smem;
+    float *yt = (float *)(smem + S::kY);
     float *Bs = (float *)(smem + S::kB);
     float *Cs = (float *)(smem + S::kC);
     float *As = (float *)(smem + S::kA);
@@ -320,29 +344,32 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
     const int ncols = (int)(dim - c0 < CT ? dim - c0 : CT);
     const bool cvalid = cl < ncols;
     const int nchunks = (int)((L + kCH - 1) / kCH);
+    const bool tile_fast = ncols == CT && p.vec && p.vecbc;  // full tile, vector rows
     const bool vec = p.vec != 0;
     const T *x = (const T *)p.x;
     const T *z = (const T *)p.z;
     T *y = (T *)p.y;
+    const int64_t rowb = (int64_t)b * L;
 
-    // staging / output item of this thread: steps (2*ip, 2*ip+1) of the chunk, channels
-    // 8*g .. 8*g+7 of the tile
-    const int ip = tid / NG, g = tid % NG, nv = ncols - 8 * g;
-    // B/C staging item: step sb of the chunk, states hb .. hb+BPT-1
-    const int sb = BPT == 16 ? tid : tid >> 1, hb = BPT == 16 ? 0 : (tid & 1) * BPT;
+    const int g = lane >> 5, nv = ncols - 8 * g;  // 8-channel group of the row items
+    const int64_t cg = c0 + 8 * g;
+    const int pp = 8 * (((lane >> 2) & 7) + 8 * (wave >> 1)) + 4 * (wave & 1) + (lane & 3);
+    const int sb = 16 * (lane >> 2) + 4 * wave + (lane & 3);
+    const int so = 16 * ((lane >> 2) & 7) + 4 * wave + (lane & 3);
 
+    int qq = 0;  // chunks done over all directions (priority parity)
     for (int k = 0; k < p.ndir; ++k) {
         const T *dl = (const T *)p.delta + k * tok;
         const T *Bk = (const T *)p.B + k * bcn;
         const T *Ck = (const T *)p.C + k * bcn;
         __syncthreads();  // the previous direction is done with the parameter tiles
-        for (int i = tid; i < CT * kN; i += NT) {
+        for (int i = tid; i < CT * kN; i += 256) {
             const int ch = i / kN, n = i % kN;
             const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
             As[i] = p.A[(k * dim + cc) * kN + n] * kLog2e;
             Cy[i] = 0.f;
         }
-        for (int i = tid; i < CT; i += NT) {
+        for (int i = tid; i < CT; i += 256) {
             const int64_t cc = c0 + i < dim ? c0 + i : 0;
             Db[2 * i] = p.D ? p.D[k * dim + cc] : 0.f;
             Db[2 * i + 1] = p.bias ? p.bias[k * dim + cc] : 0.f;
@@ -350,53 +377,68 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
 
         // global -> registers for chunk q (prefetched one chunk ahead)
         Raw8<T> px0, px1, pd0, pd1;
-        uint32_t pbc[2][BPT * sizeof(T) / 4];  // raw B and C values of one chunk step
+        uint32_t pbc[2][NW];  // raw B and C values of one chunk step
         auto fetch = [&](int q) {
             const int64_t s0 = (int64_t)q * kCH;
-            const int64_t sa = s0 + 2 * ip, sbb = sa + 1;
+            const int64_t sa = s0 + 2 * pp, sbb = sa + 1, s = s0 + sb;
+            if (tile_fast && s0 + kCH <= L) {
+                const int64_t oa = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
+                const int64_t ob = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
+                px0 = load_raw8(x + oa, 8, true);
+                pd0 = load_raw8(dl + oa, 8, true);
+                px1 = load_raw8(x + ob, 8, true);
+                pd1 = load_raw8(dl + ob, 8, true);
+                const int64_t ro = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * kN;
+#pragma unroll
+                for (int h = 0; h < NW; h += 4) {
+                    const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                    const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
+                    pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                    pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                }
+                return;
+            }
             px0 = px1 = pd0 = pd1 = Raw8<T>{};
             if (nv > 0 && sa < L) {
-                const int64_t off = ((int64_t)b * L + visit(p.kind, k, sa, L, p.H)) * dim + c0 + 8 * g;
+                const int64_t off = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
                 px0 = load_raw8(x + off, nv, vec);
                 pd0 = load_raw8(dl + off, nv, vec);
             }
             if (nv > 0 && sbb < L) {
-                const int64_t off = ((int64_t)b * L + visit(p.kind, k, sbb, L, p.H)) * dim + c0 + 8 * g;
+                const int64_t off = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
                 px1 = load_raw8(x + off, nv, vec);
                 pd1 = load_raw8(dl + off, nv, vec);
             }
-            const int64_t s = s0 + sb;
-            constexpr int NW = BPT * sizeof(T) / 4;
 #pragma unroll
             for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
             if (s < L) {
-                const int64_t roff = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * kN + hb;
+                const int64_t ro = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * kN;
                 if (p.vecbc) {
 #pragma unroll
                     for (int h = 0; h < NW; h += 4) {
-                        const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + roff) + h);
-                        const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + roff) + h);
+                        const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                        const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
                         pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
                         pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
                     }
                 } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
                     for (int h = 0; h < NW; ++h) {
-                        pbc[0][h] = (uint32_t)Bk[roff + 2 * h] | ((uint32_t)Bk[roff + 2 * h + 1] << 16);
-                        pbc[1][h] = (uint32_t)Ck[roff + 2 * h] | ((uint32_t)Ck[roff + 2 * h + 1] << 16);
+                        pbc[0][h] = (uint32_t)Bk[ro + 2 * h] | ((uint32_t)Bk[ro + 2 * h + 1] << 16);
+                        pbc[1][h] = (uint32_t)Ck[ro + 2 * h] | ((uint32_t)Ck[ro + 2 * h + 1] << 16);
                     }
                 } else {
 #pragma unroll
                     for (int h = 0; h < NW; ++h) {
-                        pbc[0][h] = __float_as_uint(Bk[roff + h]);
-                        pbc[1][h] = __float_as_uint(Ck[roff + h]);
+                        pbc[0][h] = __float_as_uint(Bk[ro + h]);
+                        pbc[1][h] = __float_as_uint(Ck[ro + h]);
                     }
                 }
             }
         };
         // registers -> LDS
         auto commit = [&]() {
-            const int si = S::xpos(2 * ip);  // steps 2*ip and 2*ip+1 are adjacent in a piece
+            const int si = S::xpos(2 * pp);  // steps 2p and 2p+1 are adjacent in a piece
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int ch = 8 * g + e;
@@ -412,8 +454,9 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
                     *(uint2 *)&dtl[ch * S::kXP + si] = make_uint2(pd0.w[e], pd1.w[e]);
                 }
             }
+            const int sp = fpos(sb);
 #pragma unroll
-            for (int h = 0; h < BPT; ++h) {
+            for (int h = 0; h < kN; ++h) {
                 float bv, cv;
                 if constexpr (sizeof(T) == 2) {
                     bv = __uint_as_float(h & 1 ? pbc[0][h >> 1] & 0xFFFF0000u : pbc[0][h >> 1] << 16);
@@ -422,36 +465,38 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
                     bv = __uint_as_float(pbc[0][h]);
                     cv = __uint_as_float(pbc[1][h]);
                 }
-                Bs[(hb + h) * kFP + fpos(sb)] = bv;
-                Cs[(hb + h) * kFP + fpos(sb)] = cv;
+                Bs[h * kFP + sp] = bv;
+                Cs[h * kFP + sp] = cv;
             }
         };
 
         fetch(0);
-        for (int q = 0; q < nchunks; ++q) {
+        for (int q = 0; q < nchunks; ++q, ++qq) {
             const int64_t s0 = (int64_t)q * kCH;
+            const bool fast = tile_fast && s0 + kCH <= L;  // no step or channel past the end
+            __builtin_amdgcn_s_setprio(2);
             __syncthreads();  // the previous chunk is done with every tile
             commit();
             __syncthreads();
-            // gate input for this chunk's output item, then the next chunk's inputs: in flight
+            // gate input for this chunk's output items, then the next chunk's inputs: in flight
             // while this chunk computes
             const bool last = k == p.ndir - 1;
             Raw8<T> zr[2] = {};
             int64_t ooff[2] = {0, 0};
-            bool ovalid[2];
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int64_t s = s0 + 2 * ip + r;
-                ovalid[r] = nv > 0 && s < L;
-                if (ovalid[r]) {
-                    ooff[r] = ((int64_t)b * L + visit(p.kind, k, s, L, p.H)) * dim + c0 + 8 * g;
+                const int64_t s = s0 + so + 128 * r;
+                if (fast) {
+                    ooff[r] = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * dim + cg;
+                    if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
+                } else if (nv > 0 && s < L) {
+                    ooff[r] = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * dim + cg;
                     if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                 }
             }
             if (q + 1 < nchunks) fetch(q + 1);
 
             // ---- this lane's 16 steps of its channel
-            const bool full = s0 + kCH <= L && ncols == CT;  // no step or channel past the end
             const int64_t rem = L - (s0 + l * kK);
             const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= kK ? kK : (int)rem));
             float dt[kK], dx[kK], yv[kK];
@@ -483,7 +528,7 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
 #pragma unroll
                     for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
                 }
-                if (!full) {
+                if (!(s0 + kCH <= L && ncols == CT)) {
                     // steps past the sequence end and channels past dim get delta = 0, the
                     // identity step (staged x there is 0 too)
                     const float limf = (float)lim;
@@ -497,6 +542,8 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
                     sdt += dt[j];
                 }
             }
+            if (qq & 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
             const float *Bc = Bs + 4 * l;
             const float *Cc = Cs + 4 * l;
 #pragma unroll 1
@@ -545,7 +592,8 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
                     yv[j] = fmaf(C1[j], h1, yv[j]);
                 }
             }
-            __syncthreads();  // x/delta tiles fully read before y reuses their space
+            __builtin_amdgcn_s_setprio(2);
+            if constexpr (!S::kYOwn) __syncthreads();  // x/delta tiles fully read before y reuses their space
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc)
                 *(float4 *)&yt[cl * kFP + pc * (kLPR * 4) + 4 * l] =
@@ -554,34 +602,52 @@ __global__ __launch_bounds__(64 * W, 2) void selscan_chunked(Params p) {
             // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                if (!ovalid[r]) continue;
+                const int sl = so + 128 * r;
                 float v[8], wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (k > 0) load_f8(p.ws + ooff[r], nv, vec, wv);
+                if (fast) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(2 * ip + r)] + wv[e];
-                if (last) {
-                    if (z) {
+                    for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
+                    if (k > 0) load_f8(p.ws + ooff[r], 8, true, wv);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                    for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                    if (last) {
+                        if (z) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                        }
+                        store8(y + ooff[r], 8, true, v);
+                    } else {
+                        store8(p.ws + ooff[r], 8, true, v);
                     }
-                    store8(y + ooff[r], nv, vec, v);
-                } else {
-                    store8(p.ws + ooff[r], nv, vec, v);
+                } else if (nv > 0 && s0 + sl < L) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
+                    if (k > 0) load_f8(p.ws + ooff[r], nv, vec, wv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                    if (last) {
+                        if (z) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                        }
+                        store8(y + ooff[r], nv, vec, v);
+                    } else {
+                        store8(p.ws + ooff[r], nv, vec, v);
+                    }
                 }
             }
         }
     }
 }
 
-template <typename T, int W>
+template <typename T, int KIND>
 int launch_tiles(const Params &a, int64_t batch, void *stream) {
-    constexpr int CT = 4 * W;
     Params c = a;
-    c.ntc = (int)((a.dim + CT - 1) / CT);
+    c.ntc = (int)((a.dim + kTC - 1) / kTC);
     const int64_t blocks = batch * (int64_t)c.ntc;
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&c};
-    hipError_t e = hipLaunchKernel((const void *)&selscan_chunked<T, W>, dim3((unsigned)blocks), dim3(64 * W),
+    hipError_t e = hipLaunchKernel((const void *)&selscan_chunked<T, KIND>, dim3((unsigned)blocks), dim3(256),
                                    args, 0, (hipStream_t)stream);
     if (e != hipSuccess) {
         strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
@@ -590,14 +656,20 @@ int launch_tiles(const Params &a, int64_t batch, void *stream) {
     return SELSCAN_OK;
 }
 
+template <typename T>
+int launch_kind(const Params &a, int kind, int64_t batch, void *stream) {
+    if (kind == SELSCAN_OP_FWD) return launch_tiles<T, SELSCAN_OP_FWD>(a, batch, stream);
+    if (kind == SELSCAN_OP_BIDIR) return launch_tiles<T, SELSCAN_OP_BIDIR>(a, batch, stream);
+    return launch_tiles<T, SELSCAN_OP_SS2D>(a, batch, stream);
+}
+
 int launch(const Problem &p, void *stream) {
-    const size_t s = p.dtype == SELSCAN_BF16 ? 2 : 4;
     Params a;
     a.x = p.x, a.delta = p.delta, a.B = p.B, a.C = p.C, a.z = p.z;
     a.A = p.A, a.D = p.D, a.bias = p.bias, a.y = p.y;
     a.ws = p.ndir > 1 ? (float *)p.ws : nullptr;
-    a.L = p.L, a.dim = p.dim, a.H = p.H;
-    a.batch = (int)p.batch, a.ndir = p.ndir, a.kind = p.kind;
+    a.L = p.L, a.dim = p.dim, a.H = (int)p.H, a.Wd = (int)p.W;
+    a.batch = (int)p.batch, a.ndir = p.ndir;
     a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
     // rows of 8 channels move as 16-byte vectors when every row start is 16-byte aligned
     const void *rows[] = {p.x, p.delta, p.z, p.y};
@@ -607,8 +679,8 @@ int launch(const Problem &p, void *stream) {
     a.vec = vec;
     a.vecbc = aligned(p.B, 16) && aligned(p.C, 16);
     a.ntc = 0;
-    if (p.dtype == SELSCAN_BF16) return launch_tiles<uint16_t, 4>(a, p.batch, stream);
-    return launch_tiles<float, 4>(a, p.batch, stream);
+    if (p.dtype == SELSCAN_BF16) return launch_kind<uint16_t>(a, p.kind, p.batch, stream);
+    return launch_kind<float>(a, p.kind, p.batch, stream);
 }
 
 int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {
