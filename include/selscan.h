@@ -36,7 +36,8 @@
  *      SELSCAN_E_ALIGN        a pointer is not aligned to its element size (4 B for fp32
  *                             arrays, 2 B for bf16 arrays)
  *      SELSCAN_E_ALIAS        y overlaps an input array
- *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits
+ *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits, or an
+ *                             SS2D map with H*W >= 2^31 pixels
  *      SELSCAN_E_WORKSPACE    workspace smaller than selscan_workspace_bytes(...)
  *      SELSCAN_E_HIP          the kernel launch was rejected by the HIP runtime
  *    Non-finite inputs are not checked; they propagate.
@@ -115,6 +116,7 @@ int selscan_bidir_fwd(const void *x, const void *delta, const float *A, const vo
  *   delta       : [4][batch][H*W][dim]        pixel order (value used when pixel p is visited)
  *   B, C        : [4][batch][H*W][dstate]     pixel order
  *   A           : [4][dim][dstate];  D, delta_bias : [4][dim] (nullable)
+ * H*W must be below 2^31 (SELSCAN_E_UNSUPPORTED otherwise).
  */
 int ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
              const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H, int64_t W,

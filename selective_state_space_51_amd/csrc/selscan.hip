@@ -184,6 +184,11 @@ struct Lds {
 // position of chunk step s in an fp32 tile row (pieces of 4 floats)
 __host__ __device__ constexpr int fpos(int s) { return ((s & 15) >> 2) * (kLPR * 4) + ((s >> 4) << 2) + (s & 3); }
 
+template <bool V>
+struct BoolC {
+    static constexpr bool value = V;
+};
+
 // row (token or pixel) visited at scan step l, 0 <= l < L, by direction k
 template <int KIND>
 __device__ __forceinline__ int64_t visit(int k, int64_t l, int64_t L, int H, int Wd) {
@@ -378,10 +383,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         // global -> registers for chunk q (prefetched one chunk ahead)
         Raw8<T> px0, px1, pd0, pd1;
         uint32_t pbc[2][NW];  // raw B and C values of one chunk step
-        auto fetch = [&](int q) {
+        auto fetch = [&](int q, auto fast_c) {
             const int64_t s0 = (int64_t)q * kCH;
             const int64_t sa = s0 + 2 * pp, sbb = sa + 1, s = s0 + sb;
-            if (tile_fast && s0 + kCH <= L) {
+            if constexpr (decltype(fast_c)::value) {
                 const int64_t oa = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
                 const int64_t ob = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
                 px0 = load_raw8(x + oa, 8, true);
@@ -396,42 +401,42 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
                     pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
                 }
-                return;
-            }
-            px0 = px1 = pd0 = pd1 = Raw8<T>{};
-            if (nv > 0 && sa < L) {
-                const int64_t off = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
-                px0 = load_raw8(x + off, nv, vec);
-                pd0 = load_raw8(dl + off, nv, vec);
-            }
-            if (nv > 0 && sbb < L) {
-                const int64_t off = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
-                px1 = load_raw8(x + off, nv, vec);
-                pd1 = load_raw8(dl + off, nv, vec);
-            }
+            } else {
+                px0 = px1 = pd0 = pd1 = Raw8<T>{};
+                if (nv > 0 && sa < L) {
+                    const int64_t off = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
+                    px0 = load_raw8(x + off, nv, vec);
+                    pd0 = load_raw8(dl + off, nv, vec);
+                }
+                if (nv > 0 && sbb < L) {
+                    const int64_t off = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
+                    px1 = load_raw8(x + off, nv, vec);
+                    pd1 = load_raw8(dl + off, nv, vec);
+                }
 #pragma unroll
-            for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
-            if (s < L) {
-                const int64_t ro = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * kN;
-                if (p.vecbc) {
+                for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
+                if (s < L) {
+                    const int64_t ro = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * kN;
+                    if (p.vecbc) {
 #pragma unroll
-                    for (int h = 0; h < NW; h += 4) {
-                        const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
-                        const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
-                        pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
-                        pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
-                    }
-                } else if constexpr (sizeof(T) == 2) {
+                        for (int h = 0; h < NW; h += 4) {
+                            const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                            const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
+                            pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                            pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                        }
+                    } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                    for (int h = 0; h < NW; ++h) {
-                        pbc[0][h] = (uint32_t)Bk[ro + 2 * h] | ((uint32_t)Bk[ro + 2 * h + 1] << 16);
-                        pbc[1][h] = (uint32_t)Ck[ro + 2 * h] | ((uint32_t)Ck[ro + 2 * h + 1] << 16);
-                    }
-                } else {
+                        for (int h = 0; h < NW; ++h) {
+                            pbc[0][h] = (uint32_t)Bk[ro + 2 * h] | ((uint32_t)Bk[ro + 2 * h + 1] << 16);
+                            pbc[1][h] = (uint32_t)Ck[ro + 2 * h] | ((uint32_t)Ck[ro + 2 * h + 1] << 16);
+                        }
+                    } else {
 #pragma unroll
-                    for (int h = 0; h < NW; ++h) {
-                        pbc[0][h] = __float_as_uint(Bk[ro + h]);
-                        pbc[1][h] = __float_as_uint(Ck[ro + h]);
+                        for (int h = 0; h < NW; ++h) {
+                            pbc[0][h] = __float_as_uint(Bk[ro + h]);
+                            pbc[1][h] = __float_as_uint(Ck[ro + h]);
+                        }
                     }
                 }
             }
@@ -443,12 +448,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             for (int e = 0; e < 8; ++e) {
                 const int ch = 8 * g + e;
                 if constexpr (sizeof(T) == 2) {
-                    const uint32_t xa = e & 1 ? px0.w[e >> 1] >> 16 : px0.w[e >> 1] & 0xFFFFu;
-                    const uint32_t xb = e & 1 ? px1.w[e >> 1] & 0xFFFF0000u : px1.w[e >> 1] << 16;
-                    const uint32_t da = e & 1 ? pd0.w[e >> 1] >> 16 : pd0.w[e >> 1] & 0xFFFFu;
-                    const uint32_t db = e & 1 ? pd1.w[e >> 1] & 0xFFFF0000u : pd1.w[e >> 1] << 16;
-                    *(uint32_t *)&xt[ch * S::kXP + si] = xa | xb;
-                    *(uint32_t *)&dtl[ch * S::kXP + si] = da | db;
+                    // low half: step 2p, high half: step 2p+1, of channel e (v_perm_b32)
+                    const uint32_t sel = e & 1 ? 0x07060302u : 0x05040100u;
+                    *(uint32_t *)&xt[ch * S::kXP + si] = __builtin_amdgcn_perm(px1.w[e >> 1], px0.w[e >> 1], sel);
+                    *(uint32_t *)&dtl[ch * S::kXP + si] = __builtin_amdgcn_perm(pd1.w[e >> 1], pd0.w[e >> 1], sel);
                 } else {
                     *(uint2 *)&xt[ch * S::kXP + si] = make_uint2(px0.w[e], px1.w[e]);
                     *(uint2 *)&dtl[ch * S::kXP + si] = make_uint2(pd0.w[e], pd1.w[e]);
@@ -470,10 +473,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             }
         };
 
-        fetch(0);
-        for (int q = 0; q < nchunks; ++q, ++qq) {
+        // one chunk; FAST: a full chunk of a full tile whose successor is full too
+        auto chunk = [&](int q, auto fast_c) {
+            constexpr bool fast = decltype(fast_c)::value;
             const int64_t s0 = (int64_t)q * kCH;
-            const bool fast = tile_fast && s0 + kCH <= L;  // no step or channel past the end
             __builtin_amdgcn_s_setprio(2);
             __syncthreads();  // the previous chunk is done with every tile
             commit();
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int64_t s = s0 + so + 128 * r;
-                if (fast) {
+                if constexpr (fast) {
                     ooff[r] = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * dim + cg;
                     if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
                 } else if (nv > 0 && s < L) {
@@ -494,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                 }
             }
-            if (q + 1 < nchunks) fetch(q + 1);
+            if (q + 1 < nchunks) fetch(q + 1, fast_c);
 
             // ---- this lane's 16 steps of its channel
             const int64_t rem = L - (s0 + l * kK);
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 #pragma unroll
                     for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
                 }
-                if (!(s0 + kCH <= L && ncols == CT)) {
+                if (!fast && !(s0 + kCH <= L && ncols == CT)) {
                     // steps past the sequence end and channels past dim get delta = 0, the
                     // identity step (staged x there is 0 too)
                     const float limf = (float)lim;
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             for (int r = 0; r < 2; ++r) {
                 const int sl = so + 128 * r;
                 float v[8], wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (fast) {
+                if constexpr (fast) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
                     if (k > 0) load_f8(p.ws + ooff[r], 8, true, wv);
@@ -636,7 +639,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     }
                 }
             }
-        }
+        };
+        fetch(0, BoolC<false>{});
+        const int nfast = tile_fast ? (int)(L / kCH) - 1 : 0;
+        int q = 0;
+        for (; q < nfast; ++q, ++qq) chunk(q, BoolC<true>{});
+        for (; q < nchunks; ++q, ++qq) chunk(q, BoolC<false>{});
     }
 }
 

@@ -57,6 +57,10 @@ def test_unsupported():
     assert fwd(N=8) == 5
     assert fwd(dtype=7) == 5
     assert fwd(flags=4) == 5
+    # SS2D pixel indices are 32-bit: a map of 2^31 pixels is refused before any other check
+    assert L.ss2d_fwd(P, P, P, P, P, None, None, None, 0, P, 1, 1 << 16, 1 << 15, 8, 16, 1, None, 0, None) == 5
+    # 2^31 - 1 pixels passes that check and fails the next one (every pointer here is the same)
+    assert L.ss2d_fwd(P, P, P, P, P, None, None, None, 0, P, 1, (1 << 31) - 1, 1, 8, 16, 1, None, 0, None) == 4
 
 
 def test_alignment():
