@@ -94,6 +94,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--state", action="store_true",
+                    help="single-direction workloads: run selscan_fwd_state with an initial state and the "
+                         "final state written (recurrent / chunked inference)")
     ap.add_argument("--cpu-channels", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (a plain copy of known size, for scaling "
@@ -132,9 +135,19 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.state and w.kind != "selscan":
+        print("--state applies to single-direction workloads only", file=sys.stderr)
+        return 2
+    h0 = hl = None
+    if args.state:
+        h0 = up(W.generate_state(w.batch, w.dim, w.dstate))
+        hl = torch.empty_like(h0)
 
     def step():
-        if w.kind == "selscan":
+        if args.state:
+            S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, h0=h0,
+                                h_last=hl, workspace=ws, stream=stream)
+        elif w.kind == "selscan":
             S.selscan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, workspace=ws,
                           stream=stream)
         elif w.kind == "bidir":
@@ -186,7 +199,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seeded: x, z, B, C ~ N(0,1); delta log-uniform [1e-3, 1e-1]; A[d,n] = -(n+1); D ~ N(0,1))",
         "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
-                   "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate},
+                   "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate,
+                   "state_io": bool(args.state)},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
                      "work_per_element": "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents",
@@ -196,7 +210,7 @@ def main() -> int:
                      "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
-        del t, y, ws
+        del t, y, ws, h0, hl
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels)
     print(json.dumps(out))

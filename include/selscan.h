@@ -88,6 +88,24 @@ int selscan_fwd(const void *x, const void *delta, const float *A, const void *B,
                 int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * selscan_fwd_state - selscan_fwd with the recurrent state carried in and out, for recurrent
+ * (step-by-step or chunk-by-chunk) inference: "Mamba论文", section "Computation计算" (the
+ * parallel mode for training, the recurrent mode for inference).  Calling it on [0, m) and
+ * then on [m, L) with h0 = the first call's h_last gives the same y as one call on [0, L).
+ *   h0     : [batch][dim][dstate] fp32, the state before step 0; NULL = zero state
+ *   h_last : [batch][dim][dstate] fp32, written with the state after step seqlen-1 (h0, or
+ *            zero, when seqlen == 0); NULL = not written
+ * Every other argument is as for selscan_fwd.  h_last may be the same pointer as h0 (in-place
+ * update); any other overlap of h_last or h0 with y, or of h_last with an input, is
+ * SELSCAN_E_ALIAS.  Both must be 4-byte aligned (SELSCAN_E_ALIGN).  With seqlen == 0 and a
+ * non-NULL h_last, only h0 and h_last are read or written (the other pointers may be NULL).
+ */
+int selscan_fwd_state(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                      const float *h0, float *h_last, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * selscan_bidir_fwd - bidirectional scan (Vim): "从LSTM到Mamba" §3.1, a forward scan plus
  * the same scan over the time-reversed sequence with its own parameters.  The two
  * outputs are summed in token order (the page concatenates; summing is the fusion this

@@ -45,9 +45,10 @@ def _load():
     vp, i64, ci, cu, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
     common = [vp] * 8 + [cu, vp]
     lib.selscan_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.selscan_fwd_state.argtypes = common + [vp, vp, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.selscan_bidir_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
     lib.ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, ci, vp, sz, vp]
-    for f in (lib.selscan_fwd, lib.selscan_bidir_fwd, lib.ss2d_fwd):
+    for f in (lib.selscan_fwd, lib.selscan_fwd_state, lib.selscan_bidir_fwd, lib.ss2d_fwd):
         f.restype = ci
     lib.selscan_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci]
     lib.selscan_workspace_bytes.restype = sz
@@ -162,6 +163,36 @@ def selscan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softpl
                          bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_fwd")
     return y
+
+
+def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
+                      h0=None, h_last=None, workspace=None, stream=None):
+    """selscan_fwd with the state carried in (h0) and out (h_last), both fp32 [batch, dim, N].
+
+    h_last=True allocates the output state; a tensor is written in place (it may be h0 itself).
+    Returns y, or (y, h_last) when h_last is given."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, (bt, L, dim)), ("B", B, (bt, L, N)), ("C", C, (bt, L, N)),
+                       ("A", A, (dim, N)), ("D", D, (dim,)), ("z", z, (bt, L, dim)),
+                       ("delta_bias", delta_bias, (dim,)), ("h0", h0, (bt, dim, N))):
+        _shape_check(n_, t_, s_)
+    if h_last is True:
+        h_last = torch.empty(bt, dim, N, dtype=torch.float32, device=x.device)
+    _shape_check("h_last", h_last, (bt, dim, N))
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(SELSCAN_OP_FWD, x, bt, L, dim, workspace)
+    rc = lib.selscan_fwd_state(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
+                               _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                               _ptr(delta_bias, "delta_bias", f32=True),
+                               SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                               _ptr(h0, "h0", f32=True), _ptr(h_last, "h_last", f32=True),
+                               bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
+    _check(rc, "selscan_fwd_state")
+    return (y, h_last) if h_last is not None else y
 
 
 def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,

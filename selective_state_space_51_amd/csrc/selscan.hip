@@ -69,6 +69,8 @@ struct Problem {
     int kind;   // SELSCAN_OP_*
     int dtype;  // SELSCAN_F32 / SELSCAN_BF16
     unsigned flags;
+    const float *h0 = nullptr;  // [batch][dim][N] initial state (forward scan only)
+    float *hlast = nullptr;     // [batch][dim][N] state after the last step
 };
 
 size_t workspace_bytes_for(int op, int64_t batch, int64_t L, int64_t dim) {
@@ -83,8 +85,9 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
     if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
     if (p.kind == SELSCAN_OP_SS2D && (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
         return SELSCAN_E_UNSUPPORTED;
-    if (p.batch == 0 || p.L == 0 || p.dim == 0) return SELSCAN_OK;
-    if (!p.x || !p.delta || !p.A || !p.B || !p.C || !p.y) return SELSCAN_E_NULL;
+    if (p.batch == 0 || p.dim == 0) return SELSCAN_OK;
+    if (p.L == 0 && !p.hlast) return SELSCAN_OK;  // nothing to scan and no state to write
+    if (p.L > 0 && (!p.x || !p.delta || !p.A || !p.B || !p.C || !p.y)) return SELSCAN_E_NULL;
     const size_t s = p.dtype == SELSCAN_BF16 ? 2 : 4;
     const void *io[] = {p.x, p.delta, p.B, p.C, p.z, p.y};
     for (const void *q : io)
@@ -113,6 +116,14 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
         for (int i = 0; i < 8; ++i)
             if (overlap({p.ws, need}, in[i])) return SELSCAN_E_ALIAS;
     }
+    // state in/out: h_last may be h0 itself (in-place update) but must not overlap anything else
+    const size_t st = (size_t)p.batch * (size_t)p.dim * kN * 4;
+    if ((p.h0 && !aligned(p.h0, 4)) || (p.hlast && !aligned(p.hlast, 4))) return SELSCAN_E_ALIGN;
+    const Span h0s{p.h0, st}, hls{p.hlast, st};
+    if (overlap(y, h0s) || overlap(y, hls)) return SELSCAN_E_ALIAS;
+    for (const Span &q : in)
+        if (overlap(hls, q)) return SELSCAN_E_ALIAS;
+    if (p.h0 != (const float *)p.hlast && overlap(hls, h0s)) return SELSCAN_E_ALIAS;
     return SELSCAN_OK;
 }
 
@@ -125,6 +136,8 @@ struct Params {
     const float *A, *D, *bias;
     void *y;
     float *ws;        // fp32 [batch][L][dim] partial sums when ndir > 1
+    const float *h0;  // fp32 [batch][dim][N] initial state, or NULL (zero)
+    float *hlast;     // fp32 [batch][dim][N] final state, or NULL (not written)
     int64_t L, dim;
     int H, Wd;        // SS2D image height and width (H * Wd == L)
     int batch, ndir, softplus;
@@ -371,10 +384,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         for (int i = tid; i < CT * kN; i += 256) {
             const int ch = i / kN, n = i % kN;
             const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
-            As[i] = p.A[(k * dim + cc) * kN + n] * kLog2e;
-            Cy[i] = 0.f;
+            if (nchunks > 0) As[i] = p.A[(k * dim + cc) * kN + n] * kLog2e;
+            // the carry into the first chunk: the caller's initial state, else zero
+            Cy[i] = p.h0 && c0 + ch < dim ? p.h0[((int64_t)b * dim + c0 + ch) * kN + n] : 0.f;
         }
-        for (int i = tid; i < CT; i += 256) {
+        for (int i = tid; i < CT && nchunks > 0; i += 256) {
             const int64_t cc = c0 + i < dim ? c0 + i : 0;
             Db[2 * i] = p.D ? p.D[k * dim + cc] : 0.f;
             Db[2 * i + 1] = p.bias ? p.bias[k * dim + cc] : 0.f;
@@ -646,6 +660,14 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         for (; q < nfast; ++q, ++qq) chunk(q, BoolC<true>{});
         for (; q < nchunks; ++q, ++qq) chunk(q, BoolC<false>{});
     }
+    if (p.hlast) {
+        // the last chunk's carry is the state after step L-1 (steps past L are identity steps)
+        __syncthreads();
+        for (int i = tid; i < CT * kN; i += 256) {
+            const int ch = i / kN, n = i % kN;
+            if (c0 + ch < dim) p.hlast[((int64_t)b * dim + c0 + ch) * kN + n] = Cy[i];
+        }
+    }
 }
 
 template <typename T, int KIND>
@@ -676,6 +698,7 @@ int launch(const Problem &p, void *stream) {
     a.x = p.x, a.delta = p.delta, a.B = p.B, a.C = p.C, a.z = p.z;
     a.A = p.A, a.D = p.D, a.bias = p.bias, a.y = p.y;
     a.ws = p.ndir > 1 ? (float *)p.ws : nullptr;
+    a.h0 = p.h0, a.hlast = p.hlast;
     a.L = p.L, a.dim = p.dim, a.H = (int)p.H, a.Wd = (int)p.W;
     a.batch = (int)p.batch, a.ndir = p.ndir;
     a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
@@ -694,7 +717,7 @@ int launch(const Problem &p, void *stream) {
 int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {
     int rc = validate(p, dstate, ws_bytes);
     if (rc != SELSCAN_OK) return rc;
-    if (p.batch == 0 || p.L == 0 || p.dim == 0) return SELSCAN_OK;
+    if (p.batch == 0 || p.dim == 0 || (p.L == 0 && !p.hlast)) return SELSCAN_OK;
     if (p.batch > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     return launch(p, stream);
 }
@@ -708,6 +731,15 @@ int selscan_fwd(const void *x, const void *delta, const float *A, const void *B,
                 int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
     Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, seqlen, dim, 0, 0, 1, SELSCAN_OP_FWD,
               io_dtype, flags};
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+int selscan_fwd_state(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                      const float *h0, float *h_last, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                      int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, seqlen, dim, 0, 0, 1, SELSCAN_OP_FWD,
+              io_dtype, flags, h0, h_last};
     return run(p, dstate, workspace_bytes, stream);
 }
 

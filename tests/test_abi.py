@@ -15,7 +15,8 @@ MB = 1 << 20
 
 def test_exports_every_declared_symbol():
     declared = S.header_functions()
-    assert set(declared) == {"selscan_fwd", "selscan_bidir_fwd", "ss2d_fwd", "selscan_workspace_bytes",
+    assert set(declared) == {"selscan_fwd", "selscan_fwd_state", "selscan_bidir_fwd", "ss2d_fwd",
+                             "selscan_workspace_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -75,6 +76,27 @@ def test_alias():
     assert fwd(y=P + MB + 2) == 4  # y inside delta
     assert fwd(z=P + 6 * MB, y=P + 6 * MB) == 4
     assert fwd(D=P + 8 * MB + 16, y=P + 8 * MB) == 4
+
+
+def state(h0=None, h_last=None, x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, y=P + 8 * MB,
+          batch=1, L_=16, dim=8):
+    return L.selscan_fwd_state(x, delta, A, B, C, None, None, None, 0, y, h0, h_last, batch, L_, dim, 16,
+                               S.SELSCAN_BF16, None, 0, None)
+
+
+def test_state_arguments():
+    H = P + 16 * MB  # states: 1 x 8 x 16 fp32 = 512 bytes
+    assert state(h0=H + 2) == 3
+    assert state(h_last=H + 1) == 3
+    assert state(h0=H, h_last=H + 256) == 4  # partial overlap (exact aliasing is allowed)
+    assert state(h_last=P + 16) == 4  # inside x
+    assert state(h_last=P + 2 * MB) == 4  # on A
+    assert state(h0=P + 8 * MB + 8) == 4  # h0 inside y
+    assert state(h_last=P + 8 * MB) == 4  # h_last on y
+    # empty sequence: a no-op without h_last, and only the states are checked with it
+    assert state(L_=0, x=None, delta=None, A=None, B=None, C=None, y=None) == 0
+    assert state(L_=0, x=None, delta=None, A=None, B=None, C=None, y=None, h_last=H + 2) == 3
+    assert state(L_=0, h0=H, h_last=H + 4) == 4
 
 
 def test_workspace_query_and_check():

@@ -228,3 +228,10 @@ def generate(
             wv = wv - out["delta_bias"].astype(np.float64).reshape(lead + (1, 1, d))
         out["w"] = _round_io(wv.astype(np.float32), w.dtype)
     return out
+
+
+def generate_state(batch: int, dim: int, dstate: int = 16, seed: int = SEED_BASE + 50) -> np.ndarray:
+    """A seeded initial state h0 ~ N(0, 1), fp32 [batch][dim][dstate] (for the state-in/out
+    entry point)."""
+    return _normal(seed, 7, (batch, dim, dstate))
+
