@@ -56,6 +56,8 @@ def load(path: Optional[str] = None):
     lib.oracle_selscan_bidir.restype = ci
     lib.oracle_ss2d.argtypes = [dp] * 8 + [ci, ci, dp, i64, i64, i64, i64, i64, ci]
     lib.oracle_ss2d.restype = ci
+    lib.oracle_selscan_bwd.argtypes = [dp] * 8 + [ci] + [dp] * 11 + [i64, i64, i64, i64, ci]
+    lib.oracle_selscan_bwd.restype = ci
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ci
     if path is None:
@@ -130,3 +132,36 @@ def ss2d(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_softplu
     if rc != 0:
         raise RuntimeError("oracle_ss2d failed")
     return y
+
+
+def selscan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                nthreads=0, lib=None):
+    """Gradients of sum(dy * selscan(...)) (Euler Bbar) with respect to every input.
+
+    Returns a dict with dx, ddelta (with respect to the delta argument, before bias and
+    softplus), dA, dB, dC, and dD / dz / ddelta_bias / dh0 for the inputs that are given.
+    """
+    lib = lib or load()
+    x, delta, A, B, C, dy, D, z, delta_bias, h0 = map(_f64, (x, delta, A, B, C, dy, D, z, delta_bias, h0))
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    assert delta.shape == x.shape and dy.shape == x.shape and B.shape == (bt, L, N) and A.shape == (dim, N)
+    out = {"dx": np.empty_like(x), "ddelta": np.empty_like(x), "dA": np.empty((dim, N)),
+           "dB": np.empty((bt, L, N)), "dC": np.empty((bt, L, N))}
+    if D is not None:
+        out["dD"] = np.empty(dim)
+    if z is not None:
+        out["dz"] = np.empty_like(x)
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.empty(dim)
+    if h0 is not None:
+        out["dh0"] = np.empty((bt, dim, N))
+    g = lambda k: _ptr(out.get(k))
+    rc = lib.oracle_selscan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy), g("dx"),
+                                g("ddelta"), g("dA"), g("dB"), g("dC"), g("dD"), g("dz"), g("ddelta_bias"),
+                                g("dh0"), bt, L, dim, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_selscan_bwd failed")
+    return out
+

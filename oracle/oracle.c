@@ -293,3 +293,167 @@ int oracle_default_threads(void) {
     long c = sysconf(_SC_NPROCESSORS_ONLN);
     return c > 0 ? (int)c : 1;
 }
+
+/* ---- backward of the single-direction scan ------------------------------ */
+
+/* sigmoid without overflow on either side */
+static double sigmoid(double z) {
+    if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
+    double e = exp(z);
+    return e / (1.0 + e);
+}
+
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *D, *z, *delta_bias, *h0, *dy;
+    double *dx, *ddelta, *dz, *dh0;           /* per stream: written by the stream's thread */
+    int64_t batch, L, dim, N;
+    int softplus;
+} bwd_t;
+
+typedef struct {
+    const bwd_t *s;
+    int64_t first, last;
+    double *dB, *dC;   /* [batch][L][N] private partial sums */
+    double *dA;        /* [dim][N] */
+    double *dD, *dbias;/* [dim] */
+    double *h;         /* (L + 1) x N states of one stream */
+    double *dt, *w;    /* L: delta_t after bias/softplus, and its pre-softplus argument */
+    int failed;
+} bwd_job_t;
+
+/* Reverse-mode derivative of the recurrence of scan_stream (Euler Bbar), for stream (b, d),
+ * given dL/dy.  The forward is rerun and every state kept; then, from t = L-1 down to 0, with
+ * g[n] the derivative of L with respect to h_t[n]:
+ *   y_t = yp_t * silu(z_t), yp_t = sum_n C_t[n] h_t[n] + D x_t
+ *   h_t[n] = e_t[n] h_{t-1}[n] + delta_t B_t[n] x_t,   e_t[n] = exp(delta_t A[n])
+ * so  g_t += C_t dyp_t;  then the parameters of step t take their share of g_t and
+ * g_{t-1} = e_t g_t.                                                                       */
+static void bwd_stream(bwd_job_t *j, int64_t b, int64_t d) {
+    const bwd_t *s = j->s;
+    const int64_t N = s->N, dim = s->dim, L = s->L;
+    double *h = j->h; /* h + (t + 1) * N holds h_t; h holds h_{-1} */
+    for (int64_t n = 0; n < N; ++n) h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;
+    const double Dd = s->D ? s->D[d] : 0.0;
+    const double *Arow = s->A + d * N;
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * dim + d;
+        double w = s->delta[i];
+        if (s->delta_bias) w += s->delta_bias[d];
+        const double dt = s->softplus ? softplus(w) : w;
+        j->w[t] = w;
+        j->dt[t] = dt;
+        const double xv = s->x[i];
+        const double *Bt = s->B + (b * L + t) * N;
+        for (int64_t n = 0; n < N; ++n)
+            h[(t + 1) * N + n] = exp(dt * Arow[n]) * h[t * N + n] + dt * Bt[n] * xv;
+    }
+    double *g = (double *)calloc((size_t)N, sizeof(double));
+    if (!g) { j->failed = 1; return; }
+    for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t i = (b * L + t) * dim + d;
+        const double xv = s->x[i], dt = j->dt[t];
+        const double *Bt = s->B + (b * L + t) * N;
+        const double *Ct = s->C + (b * L + t) * N;
+        const double *ht = h + (t + 1) * N, *hp = h + t * N;
+        double yp = Dd * xv;
+        for (int64_t n = 0; n < N; ++n) yp += Ct[n] * ht[n];
+        double dyp = s->dy[i];
+        if (s->z) {
+            const double zv = s->z[i], sg = sigmoid(zv);
+            if (s->dz) s->dz[i] = s->dy[i] * yp * sg * (1.0 + zv * (1.0 - sg));
+            dyp = s->dy[i] * zv * sg;
+        }
+        j->dD[d] += dyp * xv;
+        double dxv = Dd * dyp, ddt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            g[n] += Ct[n] * dyp;
+            j->dC[(b * L + t) * N + n] += dyp * ht[n];
+            const double e = exp(dt * Arow[n]);
+            ddt += g[n] * (Arow[n] * e * hp[n] + Bt[n] * xv);
+            j->dA[d * N + n] += g[n] * dt * e * hp[n];
+            j->dB[(b * L + t) * N + n] += g[n] * dt * xv;
+            dxv += g[n] * dt * Bt[n];
+            g[n] *= e;
+        }
+        s->dx[i] = dxv;
+        const double dw = s->softplus ? ddt * sigmoid(j->w[t]) : ddt;
+        s->ddelta[i] = dw;
+        j->dbias[d] += dw;
+    }
+    if (s->dh0)
+        for (int64_t n = 0; n < N; ++n) s->dh0[(b * dim + d) * N + n] = g[n];
+    free(g);
+}
+
+static void *bwd_worker(void *p) {
+    bwd_job_t *j = (bwd_job_t *)p;
+    for (int64_t q = j->first; q < j->last && !j->failed; ++q) bwd_stream(j, q / j->s->dim, q % j->s->dim);
+    return NULL;
+}
+
+/* Backward of oracle_selscan (Euler Bbar; zoh is not supported here).  Inputs as for
+ * oracle_selscan plus dy [batch][L][dim].  Outputs: dx, ddelta [batch][L][dim] (derivative
+ * with respect to the delta argument, before bias and softplus); dA [dim][N]; dB, dC
+ * [batch][L][N]; dD, ddelta_bias [dim]; dz [batch][L][dim]; dh0 [batch][dim][N].  dx,
+ * ddelta, dA, dB, dC are required; dD, dz, ddelta_bias, dh0 may be NULL (not written).    */
+int oracle_selscan_bwd(const double *x, const double *delta, const double *A, const double *B,
+                       const double *C, const double *D, const double *z, const double *delta_bias,
+                       int delta_softplus, const double *h0, const double *dy, double *dx, double *ddelta,
+                       double *dA, double *dB, double *dC, double *dD, double *dz, double *ddelta_bias,
+                       double *dh0, int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads) {
+    if (bad_common(x, delta, A, B, C, dy, batch, L, dim, N) || !dx || !ddelta || !dA || !dB || !dC) return -1;
+    const int64_t streams = batch * dim, bc = batch * L * N;
+    memset(dA, 0, sizeof(double) * (size_t)(dim * N));
+    memset(dB, 0, sizeof(double) * (size_t)bc);
+    memset(dC, 0, sizeof(double) * (size_t)bc);
+    if (dD) memset(dD, 0, sizeof(double) * (size_t)dim);
+    if (ddelta_bias) memset(ddelta_bias, 0, sizeof(double) * (size_t)dim);
+    if (dh0) {
+        for (int64_t q = 0; q < streams * N; ++q) dh0[q] = 0.0;
+    }
+    if (streams == 0 || L == 0) return 0;
+    bwd_t s = {x, delta, A, B, C, D, z, delta_bias, h0, dy, dx, ddelta, dz, dh0, batch, L, dim, N,
+               delta_softplus};
+    nthreads = resolve_threads(nthreads, streams);
+    bwd_job_t jobs[256];
+    pthread_t tid[256];
+    int live[256];
+    int rc = 0;
+    for (int k = 0; k < nthreads; ++k) {
+        bwd_job_t *j = &jobs[k];
+        memset(j, 0, sizeof(*j));
+        j->s = &s;
+        j->first = streams * k / nthreads;
+        j->last = streams * (k + 1) / nthreads;
+        j->dB = (double *)calloc((size_t)bc, sizeof(double));
+        j->dC = (double *)calloc((size_t)bc, sizeof(double));
+        j->dA = (double *)calloc((size_t)(dim * N), sizeof(double));
+        j->dD = (double *)calloc((size_t)dim, sizeof(double));
+        j->dbias = (double *)calloc((size_t)dim, sizeof(double));
+        j->h = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));
+        j->dt = (double *)malloc(sizeof(double) * (size_t)L);
+        j->w = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!j->dB || !j->dC || !j->dA || !j->dD || !j->dbias || !j->h || !j->dt || !j->w) j->failed = 1;
+    }
+    for (int k = 1; k < nthreads; ++k) live[k] = !jobs[k].failed && pthread_create(&tid[k], NULL, bwd_worker, &jobs[k]) == 0;
+    if (!jobs[0].failed) bwd_worker(&jobs[0]);
+    for (int k = 1; k < nthreads; ++k) {
+        if (live[k]) pthread_join(tid[k], NULL);
+        else if (!jobs[k].failed) bwd_worker(&jobs[k]);
+    }
+    /* shared sums, added in a fixed thread order */
+    for (int k = 0; k < nthreads; ++k) {
+        bwd_job_t *j = &jobs[k];
+        if (j->failed) rc = -1;
+        if (!rc) {
+            for (int64_t q = 0; q < bc; ++q) { dB[q] += j->dB[q]; dC[q] += j->dC[q]; }
+            for (int64_t q = 0; q < dim * N; ++q) dA[q] += j->dA[q];
+            for (int64_t q = 0; q < dim; ++q) {
+                if (dD) dD[q] += j->dD[q];
+                if (ddelta_bias) ddelta_bias[q] += j->dbias[q];
+            }
+        }
+        free(j->dB); free(j->dC); free(j->dA); free(j->dD); free(j->dbias); free(j->h); free(j->dt); free(j->w);
+    }
+    return rc;
+}

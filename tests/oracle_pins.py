@@ -336,6 +336,67 @@ def pin_ss2d(lib):
     assert _rel(yt, tr(y)) < 1e-13
 
 
+
+# --------------------------------------------------------------------------- backward
+def _bwd_case(seed, bt=2, L=9, dim=3, N=4, gate=True, softplus=False, bias=True, h0=True, D=True):
+    x, z, dt, A, B, C, Dv = _case(seed, bt, L, dim, N)
+    r = _rng(seed + 1000)
+    delta = np.log(np.expm1(dt)) if softplus else dt
+    args = dict(x=x, delta=delta, A=A, B=B, C=C, D=Dv if D else None, z=z if gate else None,
+                delta_bias=0.1 * r.standard_normal(dim) if bias else None, delta_softplus=softplus,
+                h0=r.standard_normal((bt, dim, N)) if h0 else None)
+    dy = r.standard_normal((bt, L, dim))
+    return args, dy
+
+
+def _loss(lib, args, dy):
+    a = dict(args)
+    h0 = a.pop("h0")
+    return float(np.sum(dy * oracle.selscan(**a, h0=h0, lib=lib)))
+
+
+_GRAD_OF = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+            "delta_bias": "ddelta_bias", "h0": "dh0"}
+
+
+def pin_bwd_directional_fd(lib):
+    """Reverse-mode gradients of L = sum(dy * y) against central finite differences of the
+    (separately pinned) forward oracle along random directions, for every input, with and
+    without gate, skip, bias, softplus and initial state.  fp64: the two agree to ~1e-9."""
+    for i, kw in enumerate([dict(), dict(softplus=True), dict(gate=False, bias=False, h0=False),
+                            dict(D=False, softplus=True, L=17, dim=2, N=3)]):
+        args, dy = _bwd_case(40 + i, **kw)
+        g = oracle.selscan_bwd(dy=dy, lib=lib, **args)
+        r = _rng(90 + i)
+        for name, gname in _GRAD_OF.items():
+            if args.get(name) is None:
+                continue
+            v = r.standard_normal(np.shape(args[name]))
+            eps = 1e-5
+            up, dn = dict(args), dict(args)
+            up[name] = args[name] + eps * v
+            dn[name] = args[name] - eps * v
+            fd = (_loss(lib, up, dy) - _loss(lib, dn, dy)) / (2 * eps)
+            an = float(np.sum(g[gname] * v))
+            assert abs(fd - an) <= 1e-6 * max(abs(fd), 1.0), (kw, name, fd, an)
+
+
+def pin_bwd_elementwise_fd(lib):
+    """Every entry of every gradient of a tiny problem against its own central difference."""
+    args, dy = _bwd_case(77, bt=2, L=4, dim=2, N=3, softplus=True)
+    g = oracle.selscan_bwd(dy=dy, lib=lib, **args)
+    eps = 1e-6
+    for name, gname in _GRAD_OF.items():
+        base = np.asarray(args[name], dtype=np.float64)
+        fd = np.empty_like(base)
+        for idx in np.ndindex(base.shape):
+            up, dn = dict(args), dict(args)
+            a = base.copy(); a[idx] += eps; up[name] = a
+            b = base.copy(); b[idx] -= eps; dn[name] = b
+            fd[idx] = (_loss(lib, up, dy) - _loss(lib, dn, dy)) / (2 * eps)
+        assert np.abs(fd - g[gname]).max() <= 1e-6 * max(np.abs(fd).max(), 1.0), (name, fd, g[gname])
+
+
 ALL_PINS = [
     pin_lti_convolution,
     pin_delta_to_zero,
@@ -349,4 +410,6 @@ ALL_PINS = [
     pin_gate,
     pin_bidir,
     pin_ss2d,
+    pin_bwd_directional_fd,
+    pin_bwd_elementwise_fd,
 ]

@@ -46,6 +46,20 @@ MUTATIONS = [
      "Bbar = (a != 0.0 ? expm1(dt * a) : dt) * Bt[n];"),
     ("bias_ignored", "if (s->delta_bias) dt += s->delta_bias[d];", ""),
     ("h0_ignored", "h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    # backward
+    ("bwd_adjoint_not_decayed", "            g[n] *= e;\n", ""),
+    ("bwd_dA_missing_decay", "j->dA[d * N + n] += g[n] * dt * e * hp[n];", "j->dA[d * N + n] += g[n] * dt * hp[n];"),
+    ("bwd_dB_missing_delta", "j->dB[(b * L + t) * N + n] += g[n] * dt * xv;", "j->dB[(b * L + t) * N + n] += g[n] * xv;"),
+    ("bwd_dC_previous_state", "j->dC[(b * L + t) * N + n] += dyp * ht[n];", "j->dC[(b * L + t) * N + n] += dyp * hp[n];"),
+    ("bwd_dx_missing_skip", "double dxv = Dd * dyp, ddt = 0.0;", "double dxv = 0.0, ddt = 0.0;"),
+    ("bwd_ddelta_missing_input_term", "ddt += g[n] * (Arow[n] * e * hp[n] + Bt[n] * xv);",
+     "ddt += g[n] * (Arow[n] * e * hp[n]);"),
+    ("bwd_softplus_derivative_sign", "ddt * sigmoid(j->w[t])", "ddt * sigmoid(-j->w[t])"),
+    ("bwd_silu_derivative_sign", "(1.0 + zv * (1.0 - sg))", "(1.0 - zv * (1.0 - sg))"),
+    ("bwd_gate_not_applied", "dyp = s->dy[i] * zv * sg;", "dyp = s->dy[i];"),
+    ("bwd_C_after_decay", "            g[n] += Ct[n] * dyp;\n", ""),
+    ("bwd_h0_read_transposed", "for (int64_t n = 0; n < N; ++n) h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;\n    const double Dd = s->D ? s->D[d] : 0.0;\n    const double *Arow = s->A + d * N;\n    for (int64_t t = 0; t < L; ++t) {\n        const int64_t i = (b * L + t) * dim + d;\n        double w",
+     "for (int64_t n = 0; n < N; ++n) h[n] = s->h0 ? s->h0[(n * dim + d) % (s->batch * dim * N)] : 0.0;\n    const double Dd = s->D ? s->D[d] : 0.0;\n    const double *Arow = s->A + d * N;\n    for (int64_t t = 0; t < L; ++t) {\n        const int64_t i = (b * L + t) * dim + d;\n        double w"),
 ]
 
 
