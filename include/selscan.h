@@ -90,20 +90,61 @@ int selscan_fwd(const void *x, const void *delta, const float *A, const void *B,
 /*
  * selscan_fwd_state - selscan_fwd with the recurrent state carried in and out, for recurrent
  * (step-by-step or chunk-by-chunk) inference: "Mamba论文", section "Computation计算" (the
- * parallel mode for training, the recurrent mode for inference).  Calling it on [0, m) and
- * then on [m, L) with h0 = the first call's h_last gives the same y as one call on [0, L).
- *   h0     : [batch][dim][dstate] fp32, the state before step 0; NULL = zero state
- *   h_last : [batch][dim][dstate] fp32, written with the state after step seqlen-1 (h0, or
- *            zero, when seqlen == 0); NULL = not written
+ * parallel mode for training, the recurrent mode for inference), and with the states a
+ * later selscan_bwd needs.  Calling it on [0, m) and then on [m, L) with h0 = the first
+ * call's h_last gives the same y as one call on [0, L).
+ *   h0           : [batch][dim][dstate] fp32, the state before step 0; NULL = zero state
+ *   h_last       : [batch][dim][dstate] fp32, written with the state after step seqlen-1 (h0,
+ *                  or zero, when seqlen == 0); NULL = not written
+ *   chunk_states : selscan_chunk_states_bytes(...) bytes, 4-byte aligned: the states the
+ *                  backward restarts from (the library's own layout; pass it unchanged to
+ *                  selscan_bwd with the same inputs); NULL = not written
  * Every other argument is as for selscan_fwd.  h_last may be the same pointer as h0 (in-place
- * update); any other overlap of h_last or h0 with y, or of h_last with an input, is
- * SELSCAN_E_ALIAS.  Both must be 4-byte aligned (SELSCAN_E_ALIGN).  With seqlen == 0 and a
- * non-NULL h_last, only h0 and h_last are read or written (the other pointers may be NULL).
+ * update); any other overlap of h_last, chunk_states or h0 with y, or of h_last or
+ * chunk_states with an input or with each other, is SELSCAN_E_ALIAS.  All three must be
+ * 4-byte aligned (SELSCAN_E_ALIGN).  With seqlen == 0 and a non-NULL h_last, only h0 and h_last
+ * are read or written (the other pointers may be NULL).
  */
 int selscan_fwd_state(const void *x, const void *delta, const float *A, const void *B, const void *C,
                       const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
-                      const float *h0, float *h_last, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                      int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+                      const float *h0, float *h_last, float *chunk_states, int64_t batch, int64_t seqlen,
+                      int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Bytes of the chunk_states buffer of selscan_fwd_state / selscan_bwd (0 if a size is not
+ * positive or dstate != 16). */
+size_t selscan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * selscan_bwd - gradients of L = sum(dy * y) for y = selscan_fwd(...) (Euler Bbar), with the
+ * states recomputed from the chunk states the forward saved instead of stored: "Mamba论文"
+ * (backward recomputes the intermediate states) and "Mamba Series from Selective State
+ * Spaces to Visual State Space Models", section 核心洞察.  Inputs are exactly those of the
+ * forward call (with its h0 folded into chunk_states) plus
+ *   dy           : [batch][seqlen][dim] io_dtype, dL/dy
+ * Outputs (caller-owned, written in full):
+ *   dx, ddelta   : [batch][seqlen][dim] io_dtype; ddelta is with respect to the delta
+ *                  argument (before delta_bias and softplus)
+ *   dB, dC       : [batch][seqlen][dstate] io_dtype (summed over channels in fp32)
+ *   dA           : [dim][dstate] fp32 (required even when seqlen == 0: written with zeros)
+ *   dD           : [dim] fp32, nullable; the derivative for the skip weight (also when D is NULL)
+ *   dz           : [batch][seqlen][dim] io_dtype, nullable; written only when z is given
+ *   ddelta_bias  : [dim] fp32, nullable; sum of ddelta over batch and time
+ *   dh0          : [batch][dim][dstate] fp32, nullable; dL/dh0 of the forward's initial state
+ * workspace: at least selscan_bwd_workspace_bytes(...) bytes, 4-byte aligned (per-tile fp32
+ * partial sums of dB and dC, per-batch-row partials of dA, dD, ddelta_bias).  No output may
+ * overlap an input, another output or the workspace (SELSCAN_E_ALIAS).  dB, dC, dA, dD and
+ * ddelta_bias are sums in a fixed order: the results are the same from run to run.
+ */
+int selscan_bwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+                const void *z, const float *delta_bias, unsigned flags, const float *chunk_states, const void *dy,
+                void *dx, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz, float *ddelta_bias,
+                float *dh0, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes selscan_bwd needs as `workspace` (0 if batch or dim is not positive or
+ * dstate != 16). */
+size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype);
 
 /*
  * selscan_bidir_fwd - bidirectional scan (Vim): "从LSTM到Mamba" §3.1, a forward scan plus

@@ -45,7 +45,13 @@ def _load():
     vp, i64, ci, cu, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
     common = [vp] * 8 + [cu, vp]
     lib.selscan_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
-    lib.selscan_fwd_state.argtypes = common + [vp, vp, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.selscan_fwd_state.argtypes = common + [vp, vp, vp, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.selscan_bwd.argtypes = [vp] * 8 + [cu] + [vp] * 11 + [i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.selscan_bwd.restype = ci
+    lib.selscan_chunk_states_bytes.argtypes = [i64, i64, i64, i64]
+    lib.selscan_chunk_states_bytes.restype = sz
+    lib.selscan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    lib.selscan_bwd_workspace_bytes.restype = sz
     lib.selscan_bidir_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
     lib.ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, ci, vp, sz, vp]
     for f in (lib.selscan_fwd, lib.selscan_fwd_state, lib.selscan_bidir_fwd, lib.ss2d_fwd):
@@ -165,12 +171,23 @@ def selscan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softpl
     return y
 
 
-def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
-                      h0=None, h_last=None, workspace=None, stream=None):
-    """selscan_fwd with the state carried in (h0) and out (h_last), both fp32 [batch, dim, N].
+def selscan_chunk_states_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16) -> int:
+    return int(lib.selscan_chunk_states_bytes(batch, seqlen, dim, dstate))
 
-    h_last=True allocates the output state; a tensor is written in place (it may be h0 itself).
-    Returns y, or (y, h_last) when h_last is given."""
+
+def selscan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int = 16,
+                                io_dtype: int = SELSCAN_BF16) -> int:
+    return int(lib.selscan_bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype))
+
+
+def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
+                      h0=None, h_last=None, chunk_states=None, workspace=None, stream=None):
+    """selscan_fwd with the state carried in (h0) and out (h_last), both fp32 [batch, dim, N],
+    and optionally the chunk states selscan_bwd restarts from.
+
+    h_last=True / chunk_states=True allocate those outputs; tensors are written in place
+    (h_last may be h0 itself).  Returns y, or a tuple (y, h_last, chunk_states) holding the
+    outputs that were asked for."""
     torch = _torch()
     bt, L, dim = x.shape
     N = A.shape[-1]
@@ -182,6 +199,12 @@ def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     if h_last is True:
         h_last = torch.empty(bt, dim, N, dtype=torch.float32, device=x.device)
     _shape_check("h_last", h_last, (bt, dim, N))
+    if chunk_states is True:
+        chunk_states = torch.empty(max(selscan_chunk_states_bytes(bt, L, dim, N) // 4, 1), dtype=torch.float32,
+                                   device=x.device)
+    if chunk_states is not None and chunk_states.numel() * chunk_states.element_size() < \
+            selscan_chunk_states_bytes(bt, L, dim, N):
+        raise ValueError("chunk_states is smaller than selscan_chunk_states_bytes(...)")
     if y is None:
         y = torch.empty_like(x)
     ws, wsb = _workspace(SELSCAN_OP_FWD, x, bt, L, dim, workspace)
@@ -190,9 +213,52 @@ def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
                                _ptr(delta_bias, "delta_bias", f32=True),
                                SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
                                _ptr(h0, "h0", f32=True), _ptr(h_last, "h_last", f32=True),
+                               _ptr(chunk_states, "chunk_states", f32=True),
                                bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_fwd_state")
-    return (y, h_last) if h_last is not None else y
+    extra = tuple(t for t in (h_last, chunk_states) if t is not None)
+    return (y, *extra) if extra else y
+
+
+def selscan_bwd(x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None, delta_softplus=False,
+                dh0=False, workspace=None, stream=None):
+    """Gradients of sum(dy * y) for y = selscan_fwd(...); chunk_states from selscan_fwd_state on the
+    same inputs.  Returns a dict: dx, ddelta, dA, dB, dC, and dD / dz / ddelta_bias / dh0 for the
+    inputs that were given (dh0 when asked for)."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, (bt, L, dim)), ("B", B, (bt, L, N)), ("C", C, (bt, L, N)),
+                       ("A", A, (dim, N)), ("D", D, (dim,)), ("z", z, (bt, L, dim)),
+                       ("delta_bias", delta_bias, (dim,)), ("dy", dy, (bt, L, dim))):
+        _shape_check(n_, t_, s_)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dA": torch.empty(dim, N, **f32),
+         "dB": torch.empty(bt, L, N, dtype=io, device=x.device), "dC": torch.empty(bt, L, N, dtype=io, device=x.device)}
+    if D is not None:
+        g["dD"] = torch.empty(dim, **f32)
+    if z is not None:
+        g["dz"] = torch.empty_like(x)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(dim, **f32)
+    if dh0:
+        g["dh0"] = torch.empty(bt, dim, N, **f32)
+    need = selscan_bwd_workspace_bytes(bt, L, dim, N, _dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    p = lambda k, **kw: _ptr(g.get(k), k, **kw)
+    rc = lib.selscan_bwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
+                         _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                         _ptr(delta_bias, "delta_bias", f32=True),
+                         SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0,
+                         _ptr(chunk_states, "chunk_states", f32=True), _ptr(dy, "dy", io),
+                         p("dx", io=io), p("ddelta", io=io), p("dA", f32=True), p("dB", io=io), p("dC", io=io),
+                         p("dD", f32=True), p("dz", io=io), p("ddelta_bias", f32=True), p("dh0", f32=True),
+                         bt, L, dim, N, _dtype_code(x), workspace.data_ptr(), wsb, _stream(stream))
+    _check(rc, "selscan_bwd")
+    return g
 
 
 def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,

@@ -16,6 +16,7 @@ MB = 1 << 20
 def test_exports_every_declared_symbol():
     declared = S.header_functions()
     assert set(declared) == {"selscan_fwd", "selscan_fwd_state", "selscan_bidir_fwd", "ss2d_fwd",
+                             "selscan_bwd", "selscan_chunk_states_bytes", "selscan_bwd_workspace_bytes",
                              "selscan_workspace_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
@@ -78,9 +79,9 @@ def test_alias():
     assert fwd(D=P + 8 * MB + 16, y=P + 8 * MB) == 4
 
 
-def state(h0=None, h_last=None, x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, y=P + 8 * MB,
+def state(h0=None, h_last=None, ckpt=None, x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, y=P + 8 * MB,
           batch=1, L_=16, dim=8):
-    return L.selscan_fwd_state(x, delta, A, B, C, None, None, None, 0, y, h0, h_last, batch, L_, dim, 16,
+    return L.selscan_fwd_state(x, delta, A, B, C, None, None, None, 0, y, h0, h_last, ckpt, batch, L_, dim, 16,
                                S.SELSCAN_BF16, None, 0, None)
 
 
@@ -97,6 +98,43 @@ def test_state_arguments():
     assert state(L_=0, x=None, delta=None, A=None, B=None, C=None, y=None) == 0
     assert state(L_=0, x=None, delta=None, A=None, B=None, C=None, y=None, h_last=H + 2) == 3
     assert state(L_=0, h0=H, h_last=H + 4) == 4
+    # chunk states: 1 chunk x 8 x 16 fp32 = 512 bytes
+    assert state(ckpt=H + 2) == 3
+    assert state(ckpt=H, h_last=H + 256) == 4
+    assert state(ckpt=P + 3 * MB + 8) == 4  # inside B
+    assert S.selscan_chunk_states_bytes(2, 257, 8) == 2 * 2 * 8 * 16 * 4
+    assert S.selscan_chunk_states_bytes(2, 0, 8) == 0
+
+
+def bwd(**kw):
+    a = dict(x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, D=None, z=None, bias=None, flags=0,
+             ck=P + 5 * MB, dy=P + 6 * MB, dx=P + 10 * MB, ddelta=P + 11 * MB, dA=P + 12 * MB, dB=P + 13 * MB,
+             dC=P + 14 * MB, dD=None, dz=None, dbias=None, dh0=None, batch=1, L_=16, dim=8, N=16,
+             dtype=S.SELSCAN_BF16, ws=P + 20 * MB, wsb=1 << 20)
+    a.update(kw)
+    return L.selscan_bwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["flags"], a["ck"],
+                         a["dy"], a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"],
+                         a["dh0"], a["batch"], a["L_"], a["dim"], a["N"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_bwd_arguments():
+    need = S.selscan_bwd_workspace_bytes(1, 16, 8)
+    assert 0 < need <= 1 << 20
+    assert S.selscan_bwd_workspace_bytes(0, 16, 8) == 0
+    for k in ("x", "delta", "A", "B", "C", "ck", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        assert bwd(**{k: None}) == 1, k
+    assert bwd(batch=-1) == 2
+    assert bwd(N=8) == 5 and bwd(flags=2) == 5 and bwd(dtype=3) == 5
+    assert bwd(dx=P + 10 * MB + 1) == 3
+    assert bwd(dA=P + 12 * MB + 2) == 3
+    assert bwd(ws=None) == 6 and bwd(wsb=need - 4) == 6
+    assert bwd(dx=P + 16) == 4  # output on an input
+    assert bwd(dB=P + 10 * MB + 64) == 4  # two outputs overlap
+    assert bwd(ws=P + 11 * MB) == 4  # workspace on an output
+    assert bwd(dh0=P + 6 * MB + 4) == 4  # on dy
+    # empty problems: nothing to do, or only dA (zeros) with seqlen 0
+    assert bwd(batch=0, x=None, dA=None) == 0
+    assert bwd(L_=0, dA=None) == 1
 
 
 def test_workspace_query_and_check():

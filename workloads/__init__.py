@@ -235,3 +235,9 @@ def generate_state(batch: int, dim: int, dstate: int = 16, seed: int = SEED_BASE
     entry point)."""
     return _normal(seed, 7, (batch, dim, dstate))
 
+
+def generate_cotangent(batch: int, seqlen: int, dim: int, dtype: str, seed: int = SEED_BASE + 60) -> np.ndarray:
+    """A seeded upstream gradient dL/dy ~ N(0, 1) of the output's shape and I/O dtype (for the
+    backward pass)."""
+    return _normal(seed, 8, (batch, seqlen, dim), dtype)
+
