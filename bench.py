@@ -28,10 +28,27 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # vector peak of 157.3 TFLOP/s (256 CUs x 2.4 GHz x 128 FMA lanes x 2).
 ALU_PEAK_TFLOPS = 157.3
 FLOP_EQ_PER_ELEMENT = 16
+# Backward: per element the recomputed forward (1 exp2, delta*A, u = (delta*x)*B, the state FMA,
+# the output FMA for the gate's derivative) plus the adjoint (C*dyp, g = c + carry, the carry
+# e*g) and the step's derivatives (e*h_prev, its product with g, dA, ddelta, sum g*u, sum g*B,
+# g*(delta*x) for dB, dyp*h for dC): 1 exp2 + 15 fp32 ops = 19 FMA slots = 38 flop-equivalents.
+FLOP_EQ_PER_ELEMENT_BWD = 38
+METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc", "selscan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def bwd_algorithmic_bytes(w) -> int:
+    """Bytes a fused backward must move at least once: x, delta, z, dy and the chunk states read,
+    dx, ddelta, dz written (io dtype); B, C read and dB, dC written; A, D read, dA, dD written."""
+    s = w.io_bytes
+    tok = w.batch * w.seqlen * w.dim
+    bc = w.batch * w.seqlen * w.dstate * s
+    ck = w.batch * ((w.seqlen + 255) // 256) * w.dim * w.dstate * 4
+    params = 2 * (w.dim * w.dstate + w.dim) * 4
+    return tok * s * ((4 if w.gate else 3) + (3 if w.gate else 2)) + 4 * bc + ck + params
 
 
 def kernel_source_hash() -> str:
@@ -94,6 +111,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
+                    help="fwd: the forward scan (default); bwd: selscan_bwd (gradients of every input, chunk "
+                         "states recomputed) on single-direction workloads, the chunk states saved beforehand")
     ap.add_argument("--state", action="store_true",
                     help="single-direction workloads: run selscan_fwd_state with an initial state and the "
                          "final state written (recurrent / chunked inference)")
@@ -135,16 +155,28 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    if args.state and w.kind != "selscan":
-        print("--state applies to single-direction workloads only", file=sys.stderr)
+    if (args.state or args.pass_ == "bwd") and w.kind != "selscan":
+        print("--state and --pass bwd apply to single-direction workloads only", file=sys.stderr)
         return 2
     h0 = hl = None
     if args.state:
         h0 = up(W.generate_state(w.batch, w.dim, w.dstate))
         hl = torch.empty_like(h0)
 
+    ck = dy = bws = None
+    if args.pass_ == "bwd":
+        _, ck = S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
+                                    chunk_states=True, stream=stream)
+        dy = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
+        bws = torch.empty(S.selscan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate,
+                                                        S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32),
+                          dtype=torch.uint8, device=dev)
+
     def step():
-        if args.state:
+        if args.pass_ == "bwd":
+            S.selscan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dy, ck, D=t["D"], z=t["z"], workspace=bws,
+                          stream=stream)
+        elif args.state:
             S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, h0=h0,
                                 h_last=hl, workspace=ws, stream=stream)
         elif w.kind == "selscan":
@@ -181,12 +213,14 @@ def main() -> int:
     ms_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(launch_ms))
     value = w.elements / (ms_step * 1e-3)
-    alg = w.algorithmic_bytes()
+    bwd = args.pass_ == "bwd"
+    alg = bwd_algorithmic_bytes(w) if bwd else w.algorithmic_bytes()
     hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
-    alu_tflops = w.elements * FLOP_EQ_PER_ELEMENT / (kern_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else FLOP_EQ_PER_ELEMENT
+    alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name + ("/bwd" if bwd else ""))
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
         "unit": "elem/s",
         "n_gpus": 1,
@@ -200,16 +234,20 @@ def main() -> int:
         "data": "synthetic (seeded: x, z, B, C ~ N(0,1); delta log-uniform [1e-3, 1e-1]; A[d,n] = -(n+1); D ~ N(0,1))",
         "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate,
-                   "state_io": bool(args.state)},
+                   "state_io": bool(args.state), "pass": args.pass_},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
-                     "work_per_element": "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents",
-                     "kernel": "selscan_chunked", "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),
+                     "work_per_element": ("1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
+                                          "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents"),
+                     "kernel": "selscan_bwd_chunked + selscan_bwd_reduce" if bwd else "selscan_chunked",
+                     "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),
                      "elements_per_launch": w.elements, "algorithmic_bytes_per_launch": alg,
                      "hbm_achieved_GBps": hbm_gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
                      "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and bwd:
+        out["cpu_baseline"] = None  # the timed oracle baseline is the forward's
+    elif not args.no_cpu_baseline:
         del t, y, ws, h0, hl
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels)

@@ -233,6 +233,14 @@ __device__ __forceinline__ int64_t visit(int k, int64_t l, int64_t L, int H, int
     }
 }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations only.  A
+// __syncthreads would also wait for every global load and store the wave has in flight (its
+// release fence drains vmcnt), which stalls on stores issued just before the barrier and on
+// loads issued for the next chunk.  Within one scan direction no wave reads back global memory
+// another wave of the workgroup wrote, so LDS ordering is all these barriers have to give; the
+// barrier between directions (where the partial sums change hands) stays a full one.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // softplus(w) = log(1 + e^w) without overflow
 __device__ __forceinline__ float softplus(float w) { return w > 0.f ? w + log1pf(__expf(-w)) : log1pf(__expf(w)); }
 
@@ -396,7 +404,9 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         const T *dl = (const T *)p.delta + k * tok;
         const T *Bk = (const T *)p.B + k * bcn;
         const T *Ck = (const T *)p.C + k * bcn;
-        __syncthreads();  // the previous direction is done with the parameter tiles
+        // the previous direction is done with the parameter tiles, and its stores of the partial
+        // sums (which other waves read back in this direction) are complete: a full barrier
+        __syncthreads();
         for (int i = tid; i < CT * kN; i += 256) {
             const int ch = i / kN, n = i % kN;
             const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
@@ -508,9 +518,9 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             constexpr bool fast = decltype(fast_c)::value;
             const int64_t s0 = (int64_t)q * kCH;
             __builtin_amdgcn_s_setprio(2);
-            __syncthreads();  // the previous chunk is done with every tile
+            lds_barrier();  // the previous chunk is done with every tile
             commit();
-            __syncthreads();
+            lds_barrier();
             if (p.ckpt) {
                 // the carry entering this chunk, kept for the backward pass
                 const int ch = tid / kN, n = tid % kN;
@@ -631,12 +641,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 }
             }
             __builtin_amdgcn_s_setprio(2);
-            if constexpr (!S::kYOwn) __syncthreads();  // x/delta tiles fully read before y reuses their space
+            if constexpr (!S::kYOwn) lds_barrier();  // x/delta tiles fully read before y reuses their space
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc)
                 *(float4 *)&yt[cl * kFP + pc * (kLPR * 4) + 4 * l] =
                     make_float4(yv[4 * pc], yv[4 * pc + 1], yv[4 * pc + 2], yv[4 * pc + 3]);
-            __syncthreads();
+            lds_barrier();
             // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -683,7 +693,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     }
     if (p.hlast) {
         // the last chunk's carry is the state after step L-1 (steps past L are identity steps)
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < CT * kN; i += 256) {
             const int ch = i / kN, n = i % kN;
             if (c0 + ch < dim) p.hlast[((int64_t)b * dim + c0 + ch) * kN + n] = Cy[i];
@@ -936,7 +946,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
 
     for (int q = nchunks - 1; q >= 0; --q) {
         const int64_t s0 = (int64_t)q * kCH;
-        __syncthreads();  // the previous (later) chunk is done with every tile
+        lds_barrier();  // the previous (later) chunk is done with every tile
         // ---- stage x, delta, dy, z (io) and B, C (fp32); the chunk's entry state
         {
             Raw8<T> r0[4], r1[4];
@@ -1009,7 +1019,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
             const int ch = tid / kN, n = tid % kN;
             Hc[tid] = c0 + ch < dim ? p.ckpt[(((int64_t)b * nchunks + q) * dim + c0 + ch) * kN + n] : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- this lane's 16 steps of its channel
         const int64_t rem = L - (s0 + l * kK);
@@ -1135,7 +1145,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
             }
             dAl = rowsum16(dAl);
             if (l == kLPR - 1) dAs[cl * kN + n] += dAl;
-            __syncthreads();
+            lds_barrier();
             {
                 // channel sums of this state's dB, dC for step tid of the chunk
                 float sB = 0.f, sC = 0.f;
@@ -1150,7 +1160,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                     dst[(int64_t)kN * L] = sC;
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- per (step, channel) derivatives: dx, ddelta, dz
@@ -1211,7 +1221,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                     *(float4 *)&Cs[cl * kFP + pc * (kLPR * 4) + 4 * l] =
                         make_float4(o1[4 * pc], o1[4 * pc + 1], o1[4 * pc + 2], o1[4 * pc + 3]);
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int sl = so + 128 * r;
@@ -1228,10 +1238,10 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                     store8((T *)p.ddelta + off, nv, vec, v);
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
-    __syncthreads();
+    lds_barrier();
     {
         const int ch = tid / kN, n = tid % kN;
         if (c0 + ch < dim) {

@@ -308,3 +308,14 @@ def test_bwd_against_oracle(dtype, batch, L, dim, kw):
     errs = _bwd_run(dtype, batch, L, dim, **kw)
     for k, e in errs.items():
         assert e <= _BWD_TOL[dtype], (k, e)
+
+
+def test_bwd_full_size_130m():
+    """The backward at the Mamba-130M layer shape (batch 8 x L 2048 x D 1536, bf16), every
+    gradient against the oracle on every element."""
+    import torch
+    w = W.WORKLOADS[1]
+    errs = _bwd_run(w.dtype, w.batch, w.seqlen, w.dim)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL[w.dtype], (k, e)
+    torch.cuda.empty_cache()
