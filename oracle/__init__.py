@@ -56,6 +56,8 @@ def load(path: Optional[str] = None):
     lib.oracle_selscan_bidir.restype = ci
     lib.oracle_ss2d.argtypes = [dp] * 8 + [ci, ci, dp, i64, i64, i64, i64, i64, ci]
     lib.oracle_ss2d.restype = ci
+    lib.oracle_local_ss2d.argtypes = [dp] * 8 + [ci, ci, dp, i64, i64, i64, i64, i64, i64, ci]
+    lib.oracle_local_ss2d.restype = ci
     lib.oracle_selscan_bwd.argtypes = [dp] * 8 + [ci] + [dp] * 11 + [i64, i64, i64, i64, ci]
     lib.oracle_selscan_bwd.restype = ci
     lib.oracle_default_threads.argtypes = []
@@ -131,6 +133,23 @@ def ss2d(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_softplu
                          int(bool(delta_softplus)), int(bool(zoh)), _ptr(y), bt, H, W, dim, N, int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_ss2d failed")
+    return y
+
+
+def local_ss2d(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=None, delta_softplus=False,
+               zoh=False, nthreads=0, lib=None):
+    """Windowed four-direction scan with merge (square windows of side ``window``); arrays as for ss2d."""
+    lib = lib or load()
+    x, delta, A, B, C, D, z, delta_bias = map(_f64, (x, delta, A, B, C, D, z, delta_bias))
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    assert L == H * W and delta.shape == (4, bt, L, dim) and B.shape == (4, bt, L, N) and A.shape == (4, dim, N)
+    y = np.empty_like(x)
+    rc = lib.oracle_local_ss2d(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh)), _ptr(y), bt, H, W,
+                               window, dim, N, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_local_ss2d failed")
     return y
 
 

@@ -240,6 +240,33 @@ static int64_t ss2d_pixel(int k, int64_t l, int64_t H, int64_t W) {
     return (l % H) * W + l / H;
 }
 
+/* Pixel visited at scan step l by direction k of the windowed cross-scan on an H x W map cut
+ * into square windows of side w (w divides H and W): [DP] LocalMamba, the image is divided
+ * into windows and the selective scan runs inside each window.  The pages give no more, so
+ * the reading is the SS2D cross-scan with windows:
+ *   k = 0: windows in row-major order, the pixels of each window in row-major order;
+ *   k = 1: the same on the transposed map (windows and pixels column-major);
+ *   k = 2, 3: k = 0, 1 reversed.
+ * With w = 1, or one window (w = H = W), this is the SS2D cross-scan.                        */
+static void win_rowmajor(int64_t l, int64_t Ww, int64_t w, int64_t *row, int64_t *col) {
+    const int64_t per = w * w, nwx = Ww / w;
+    const int64_t wi = l / per, r = l % per;
+    *row = (wi / nwx) * w + r / w;
+    *col = (wi % nwx) * w + r % w;
+}
+
+static int64_t local_pixel(int k, int64_t l, int64_t H, int64_t W, int64_t w) {
+    const int64_t L = H * W;
+    int64_t r, c;
+    if (k >= 2) l = L - 1 - l;
+    if (k == 0 || k == 2) {
+        win_rowmajor(l, W, w, &r, &c);
+        return r * W + c;
+    }
+    win_rowmajor(l, H, w, &r, &c); /* on the transposed (W x H) map: its row r is column r here */
+    return c * W + r;
+}
+
 /* SS2D four-direction scan with merge ([MS] cross_scan_fwd, SS2Dv0.forwardv0).
  * x, z, y: [batch][H*W][dim] (pixels row-major); delta: [4][batch][H*W][dim];
  * B, C: [4][batch][H*W][N]; A: [4][dim][N]; D, delta_bias: [4][dim].  Per-direction
@@ -247,9 +274,10 @@ static int64_t ss2d_pixel(int k, int64_t l, int64_t H, int64_t W) {
  * is gathered, scanned with direction k's parameters, and each output is added at the
  * pixel it came from.  The page gates after a normalisation outside the scan, so z is
  * normally absent; if given, it gates the merged sum.                                    */
-int oracle_ss2d(const double *x, const double *delta, const double *A, const double *B, const double *C,
-                const double *D, const double *z, const double *delta_bias, int delta_softplus, int zoh,
-                double *y, int64_t batch, int64_t H, int64_t W, int64_t dim, int64_t N, int nthreads) {
+static int cross_scan(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                      const double *D, const double *z, const double *delta_bias, int delta_softplus, int zoh,
+                      double *y, int64_t batch, int64_t H, int64_t W, int64_t win, int64_t dim, int64_t N,
+                      int nthreads) {
     if (H < 0 || W < 0) return -1;
     const int64_t L = H * W;
     if (bad_common(x, delta, A, B, C, y, batch, L, dim, N)) return -1;
@@ -265,7 +293,7 @@ int oracle_ss2d(const double *x, const double *delta, const double *A, const dou
     for (int k = 0; k < 4; ++k) {
         for (int64_t b = 0; b < batch; ++b)
             for (int64_t l = 0; l < L; ++l) {
-                const int64_t p = ss2d_pixel(k, l, H, W);
+                const int64_t p = win ? local_pixel(k, l, H, W, win) : ss2d_pixel(k, l, H, W);
                 memcpy(xs + (b * L + l) * dim, x + (b * L + p) * dim, sizeof(double) * (size_t)dim);
                 memcpy(ds + (b * L + l) * dim, delta + k * tok + (b * L + p) * dim, sizeof(double) * (size_t)dim);
                 memcpy(Bs + (b * L + l) * N, B + k * bc + (b * L + p) * N, sizeof(double) * (size_t)N);
@@ -277,7 +305,7 @@ int oracle_ss2d(const double *x, const double *delta, const double *A, const dou
         if (run_scan(&s, nthreads)) { rc = -1; goto done; }
         for (int64_t b = 0; b < batch; ++b)
             for (int64_t l = 0; l < L; ++l) {
-                const int64_t p = ss2d_pixel(k, l, H, W);
+                const int64_t p = win ? local_pixel(k, l, H, W, win) : ss2d_pixel(k, l, H, W);
                 for (int64_t d = 0; d < dim; ++d) y[(b * L + p) * dim + d] += os[(b * L + l) * dim + d];
             }
     }
@@ -286,6 +314,24 @@ int oracle_ss2d(const double *x, const double *delta, const double *A, const dou
 done:
     free(xs); free(ds); free(os); free(Bs); free(Cs);
     return rc;
+}
+
+int oracle_ss2d(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                const double *D, const double *z, const double *delta_bias, int delta_softplus, int zoh,
+                double *y, int64_t batch, int64_t H, int64_t W, int64_t dim, int64_t N, int nthreads) {
+    return cross_scan(x, delta, A, B, C, D, z, delta_bias, delta_softplus, zoh, y, batch, H, W, 0, dim, N,
+                      nthreads);
+}
+
+/* Windowed (local) four-direction scan with merge: as oracle_ss2d, with local_pixel's orders
+ * for window side win (win >= 1 dividing H and W).                                        */
+int oracle_local_ss2d(const double *x, const double *delta, const double *A, const double *B, const double *C,
+                      const double *D, const double *z, const double *delta_bias, int delta_softplus, int zoh,
+                      double *y, int64_t batch, int64_t H, int64_t W, int64_t win, int64_t dim, int64_t N,
+                      int nthreads) {
+    if (win < 1 || H % win || W % win) return -1;
+    return cross_scan(x, delta, A, B, C, D, z, delta_bias, delta_softplus, zoh, y, batch, H, W, win, dim, N,
+                      nthreads);
 }
 
 /* number of hardware threads the oracle would use for nthreads <= 0 */

@@ -337,6 +337,48 @@ def pin_ss2d(lib):
 
 
 
+
+# --------------------------------------------------------------------------- windowed (local) scans
+def _window_orders(H, W, w):
+    """Scan orders of the windowed cross-scan built with array reshapes, independently of the
+    oracle's index arithmetic: cut the (H, W) pixel grid into (H/w, w, W/w, w) blocks, bring
+    the two window axes in front of the two in-window axes and flatten; the transposed grid
+    gives direction 1; reversals give 2 and 3.  Returns [4][L] pixel indices."""
+    def blocks(grid, hh, ww):
+        return grid.reshape(hh // w, w, ww // w, w).transpose(0, 2, 1, 3).reshape(-1)
+    pix = np.arange(H * W).reshape(H, W)
+    o0 = blocks(pix, H, W)
+    o1 = blocks(pix.T.copy(), W, H)
+    return np.stack([o0, o1, o0[::-1], o1[::-1]])
+
+
+def pin_local_ss2d_windows(lib):
+    """Windowed cross-scan ([DP] LocalMamba: scan inside windows of the image) against a
+    reference that gathers each direction's sequence with the reshape-built orders, runs the
+    1-D oracle on it and adds the outputs back at the pixels they came from; square and
+    rectangular maps, several window sides."""
+    for seed, (H, W, w) in enumerate([(6, 4, 2), (6, 6, 3), (4, 8, 4), (6, 9, 3)]):
+        x, dt, A, B, C, D = _ss2d_case(500 + seed, H=H, W=W)
+        y = oracle.local_ss2d(x, dt, A, B, C, H, W, w, D=D, lib=lib)
+        orders = _window_orders(H, W, w)
+        ref = np.zeros_like(x)
+        for k in range(4):
+            o = orders[k]
+            yk = oracle.selscan(x[:, o], dt[k][:, o], A[k], B[k][:, o], C[k][:, o], D=D[k], lib=lib)
+            ref[:, o] += yk
+        assert _rel(y, ref) < 1e-13, (H, W, w)
+
+
+def pin_local_ss2d_limits(lib):
+    """With windows of side 1, or a single window covering a square map, the windowed cross-scan
+    is the SS2D cross-scan (pinned on its own by pin_ss2d): the results must be identical."""
+    for H, W, w in [(5, 7, 1), (6, 6, 6), (4, 4, 1)]:
+        x, dt, A, B, C, D = _ss2d_case(600 + H + w, H=H, W=W)
+        a = oracle.local_ss2d(x, dt, A, B, C, H, W, w, D=D, lib=lib)
+        b = oracle.ss2d(x, dt, A, B, C, H, W, D=D, lib=lib)
+        assert np.array_equal(a, b), (H, W, w)
+
+
 # --------------------------------------------------------------------------- backward
 def _bwd_case(seed, bt=2, L=9, dim=3, N=4, gate=True, softplus=False, bias=True, h0=True, D=True):
     x, z, dt, A, B, C, Dv = _case(seed, bt, L, dim, N)
@@ -410,6 +452,8 @@ ALL_PINS = [
     pin_gate,
     pin_bidir,
     pin_ss2d,
+    pin_local_ss2d_windows,
+    pin_local_ss2d_limits,
     pin_bwd_directional_fd,
     pin_bwd_elementwise_fd,
 ]

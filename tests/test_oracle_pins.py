@@ -46,6 +46,11 @@ MUTATIONS = [
      "Bbar = (a != 0.0 ? expm1(dt * a) : dt) * Bt[n];"),
     ("bias_ignored", "if (s->delta_bias) dt += s->delta_bias[d];", ""),
     ("h0_ignored", "h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    # windowed cross-scan
+    ("local_window_axes_swapped", "*row = (wi / nwx) * w + r / w;\n    *col = (wi % nwx) * w + r % w;",
+     "*row = (wi / nwx) * w + r % w;\n    *col = (wi % nwx) * w + r / w;"),
+    ("local_reversal_missing", "    int64_t r, c;\n    if (k >= 2) l = L - 1 - l;\n", "    int64_t r, c;\n"),
+    ("local_window_rows_from_width", "*row = (wi / nwx) * w + r / w;", "*row = (wi / nwx) * w + (r / w + 1) % w;"),
     # backward
     ("bwd_adjoint_not_decayed", "            g[n] *= e;\n", ""),
     ("bwd_dA_missing_decay", "j->dA[d * N + n] += g[n] * dt * e * hp[n];", "j->dA[d * N + n] += g[n] * dt * hp[n];"),
