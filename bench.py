@@ -90,6 +90,8 @@ def cpu_baseline(w, budget_channels: int):
         oracle.selscan(x, dl, A, B, C, D=D, z=z, nthreads=threads)
     elif w.kind == "bidir":
         oracle.selscan_bidir(x, dl, A, B, C, D=D, z=z, nthreads=threads)
+    elif w.kind == "local_ss2d":
+        oracle.local_ss2d(x, dl, A, B, C, w.H, w.W, w.window, D=D, z=z, nthreads=threads)
     else:
         oracle.ss2d(x, dl, A, B, C, w.H, w.W, D=D, z=z, nthreads=threads)
     sec = time.perf_counter() - t0
@@ -149,7 +151,8 @@ def main() -> int:
     del inp
     y = torch.empty_like(t["x"])
     ws = None
-    op = {"selscan": S.SELSCAN_OP_FWD, "bidir": S.SELSCAN_OP_BIDIR, "ss2d": S.SELSCAN_OP_SS2D}[w.kind]
+    op = {"selscan": S.SELSCAN_OP_FWD, "bidir": S.SELSCAN_OP_BIDIR, "ss2d": S.SELSCAN_OP_SS2D,
+          "local_ss2d": S.SELSCAN_OP_LOCAL_SS2D}[w.kind]
     need = S.selscan_workspace_bytes(op, w.batch, w.seqlen, w.dim, w.dstate,
                                      S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32)
     if need:
@@ -185,6 +188,9 @@ def main() -> int:
         elif w.kind == "bidir":
             S.selscan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
                                 workspace=ws, stream=stream)
+        elif w.kind == "local_ss2d":
+            S.local_ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, w.window, D=t["D"], z=t["z"], y=y,
+                             workspace=ws, stream=stream)
         else:
             S.ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, D=t["D"], z=t["z"], y=y,
                        workspace=ws, stream=stream)
@@ -234,6 +240,7 @@ def main() -> int:
         "data": "synthetic (seeded: x, z, B, C ~ N(0,1); delta log-uniform [1e-3, 1e-1]; A[d,n] = -(n+1); D ~ N(0,1))",
         "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate,
+                   "window": w.window or None,
                    "state_io": bool(args.state), "pass": args.pass_},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,

@@ -32,7 +32,8 @@
  *  - Every call validates its arguments on the host before any HIP call and returns a
  *    selscan_status; nothing is enqueued unless it returns SELSCAN_OK:
  *      SELSCAN_E_NULL         a required pointer is NULL (non-empty problem)
- *      SELSCAN_E_SHAPE        a size is negative (any zero size is an OK no-op)
+ *      SELSCAN_E_SHAPE        a size is negative (any zero size is an OK no-op), or a window
+ *                             side that does not divide the map
  *      SELSCAN_E_ALIGN        a pointer is not aligned to its element size (4 B for fp32
  *                             arrays, 2 B for bf16 arrays)
  *      SELSCAN_E_ALIAS        y overlaps an input array
@@ -71,7 +72,7 @@ typedef enum {
 #define SELSCAN_FLAG_DELTA_SOFTPLUS 1u /* delta_t = softplus(delta + delta_bias) */
 
 /* operation codes for selscan_workspace_bytes */
-typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2 } selscan_op;
+typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2, SELSCAN_OP_LOCAL_SS2D = 3 } selscan_op;
 
 /*
  * selscan_fwd - one selective scan over the sequence axis (Mamba's S6 layer core).
@@ -180,6 +181,24 @@ int selscan_bidir_fwd(const void *x, const void *delta, const float *A, const vo
 int ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
              const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H, int64_t W,
              int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * local_ss2d_fwd - the four-direction cross-scan of ss2d_fwd with windowed orders: the map is
+ * cut into square windows of side `window` and each window is scanned as a whole before the
+ * next ("LocalMamba: Visual State Space Model with Windowed Selective Scan", as the deep-paper
+ * listing and the CSDN notes on it describe it: divide the image into windows, scan within the
+ * windows).  The pages give no more, so the orders are the SS2D ones with windows:
+ *   k = 0: windows in row-major order, the pixels of each window in row-major order;
+ *   k = 1: the same on the transposed map (windows and pixels column-major);
+ *   k = 2, 3: k = 0, 1 reversed.
+ * window >= 1 must divide H and W (SELSCAN_E_SHAPE otherwise); window 1, or one window over a
+ * square map, is ss2d_fwd.  Every array, the merge and the workspace are as for ss2d_fwd
+ * (selscan_workspace_bytes with SELSCAN_OP_LOCAL_SS2D).
+ */
+int local_ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+                   const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H,
+                   int64_t W, int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /* Scratch bytes the caller must pass as `workspace` for this problem (0 = none). */
 size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,

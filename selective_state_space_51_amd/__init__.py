@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "selscan.h")
 SELSCAN_F32 = 0
 SELSCAN_BF16 = 1
 SELSCAN_FLAG_DELTA_SOFTPLUS = 1
-SELSCAN_OP_FWD, SELSCAN_OP_BIDIR, SELSCAN_OP_SS2D = 0, 1, 2
+SELSCAN_OP_FWD, SELSCAN_OP_BIDIR, SELSCAN_OP_SS2D, SELSCAN_OP_LOCAL_SS2D = 0, 1, 2, 3
 STATUS = {
     0: "SELSCAN_OK", 1: "SELSCAN_E_NULL", 2: "SELSCAN_E_SHAPE", 3: "SELSCAN_E_ALIGN", 4: "SELSCAN_E_ALIAS",
     5: "SELSCAN_E_UNSUPPORTED", 6: "SELSCAN_E_WORKSPACE", 7: "SELSCAN_E_HIP",
@@ -54,6 +54,8 @@ def _load():
     lib.selscan_bwd_workspace_bytes.restype = sz
     lib.selscan_bidir_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
     lib.ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.local_ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.local_ss2d_fwd.restype = ci
     for f in (lib.selscan_fwd, lib.selscan_fwd_state, lib.selscan_bidir_fwd, lib.ss2d_fwd):
         f.restype = ci
     lib.selscan_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci]
@@ -307,3 +309,29 @@ def ss2d_fwd(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_sof
                       bt, H, W, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "ss2d_fwd")
     return y
+
+
+def local_ss2d_fwd(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
+                   workspace=None, stream=None):
+    """Windowed four-direction cross-scan (square windows of side ``window``); arrays as for ss2d_fwd."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    io = x.dtype
+    if L != H * W:
+        raise ValueError(f"x has {L} pixels, expected H*W = {H * W}")
+    for n_, t_, s_ in (("delta", delta, (4, bt, L, dim)), ("B", B, (4, bt, L, N)), ("C", C, (4, bt, L, N)),
+                       ("A", A, (4, dim, N)), ("D", D, (4, dim)), ("z", z, (bt, L, dim)),
+                       ("delta_bias", delta_bias, (4, dim))):
+        _shape_check(n_, t_, s_)
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(SELSCAN_OP_LOCAL_SS2D, x, bt, L, dim, workspace)
+    rc = lib.local_ss2d_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
+                            _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                            _ptr(delta_bias, "delta_bias", f32=True),
+                            SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                            bt, H, W, window, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
+    _check(rc, "local_ss2d_fwd")
+    return y
+

@@ -73,6 +73,7 @@ struct Problem {
     const float *h0 = nullptr;  // [batch][dim][N] initial state (forward scan only)
     float *hlast = nullptr;     // [batch][dim][N] state after the last step
     float *ckpt = nullptr;      // [batch][nchunks][dim][N] state entering each chunk
+    int64_t win = 0;            // window side of the windowed cross-scan
 };
 
 __host__ __device__ inline int64_t chunks_of(int64_t L) { return (L + kCH - 1) / kCH; }
@@ -90,8 +91,10 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
     if (p.dtype != SELSCAN_F32 && p.dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
     if (p.flags & ~SELSCAN_FLAG_DELTA_SOFTPLUS) return SELSCAN_E_UNSUPPORTED;
     if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
-    if (p.kind == SELSCAN_OP_SS2D && (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
+    if ((p.kind == SELSCAN_OP_SS2D || p.kind == SELSCAN_OP_LOCAL_SS2D) &&
+        (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
         return SELSCAN_E_UNSUPPORTED;
+    if (p.kind == SELSCAN_OP_LOCAL_SS2D && (p.win < 1 || p.H % p.win || p.W % p.win)) return SELSCAN_E_SHAPE;
     if (p.batch == 0 || p.dim == 0) return SELSCAN_OK;
     if (p.L == 0 && !p.hlast) return SELSCAN_OK;  // nothing to scan and no state to write
     if (p.L > 0 && (!p.x || !p.delta || !p.A || !p.B || !p.C || !p.y)) return SELSCAN_E_NULL;
@@ -145,6 +148,24 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
 // device side
 // ------------------------------------------------------------------------------------
 
+// n / d for 0 <= n < 2^31 as a multiply-high and a shift (Granlund-Montgomery): with
+// 2^(s-1) < d <= 2^s, m = ceil(2^(31+s) / d) < 2^32 and floor(n m / 2^(31+s)) = floor(n / d).
+struct FastDiv {
+    uint32_t d, m, sh;
+};
+FastDiv make_div(uint32_t d) {
+    FastDiv f{d, 0u, 0u};
+    if (d <= 1) return f;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.m = (uint32_t)(((1ull << (31 + s)) + d - 1) / d);
+    f.sh = s - 1;
+    return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+    return f.d <= 1 ? n : __umulhi(n, f.m) >> f.sh;
+}
+
 struct Params {
     const void *x, *delta, *B, *C, *z;
     const float *A, *D, *bias;
@@ -155,6 +176,9 @@ struct Params {
     float *ckpt;      // fp32 [batch][nchunks][dim][N] state entering each chunk, or NULL
     int64_t L, dim;
     int H, Wd;        // SS2D image height and width (H * Wd == L)
+    int win;          // window side of the windowed cross-scan
+    FastDiv dH;       // division by H (SS2D column-major order)
+    FastDiv dWin, dWin2, dNx, dNy;  // by w, w*w, W/w, H/w (windowed orders)
     int batch, ndir, softplus;
     int vec;          // rows of 8 channels may be moved as 16-byte vectors
     int vecbc;        // a 16-value B/C row may be moved as 16-byte vectors
@@ -219,17 +243,32 @@ struct BoolC {
 
 // row (token or pixel) visited at scan step l, 0 <= l < L, by direction k
 template <int KIND>
-__device__ __forceinline__ int64_t visit(int k, int64_t l, int64_t L, int H, int Wd) {
+__device__ __forceinline__ int64_t visit(const Params &p, int k, int64_t l) {
+    const int64_t L = p.L;
     if constexpr (KIND == SELSCAN_OP_FWD) {
         return l;
     } else if constexpr (KIND == SELSCAN_OP_BIDIR) {
         return k == 0 ? l : L - 1 - l;
-    } else {
-        // SS2D: k = 0 row-major, 1 column-major, 2 and 3 the same orders reversed (L < 2^31)
+    } else if constexpr (KIND == SELSCAN_OP_SS2D) {
+        // k = 0 row-major, 1 column-major, 2 and 3 the same orders reversed (L < 2^31)
         if (k >= 2) l = L - 1 - l;
         if ((k & 1) == 0) return l;
-        const uint32_t u = (uint32_t)l, q = u / (uint32_t)H, r = u - q * (uint32_t)H;
-        return (int64_t)r * Wd + q;
+        const uint32_t u = (uint32_t)l, q = fdiv(u, p.dH), r = u - q * (uint32_t)p.H;
+        return (int64_t)r * p.Wd + q;
+    } else {
+        // windowed: square windows of side w; k = 0 windows and their pixels row-major, 1 the
+        // same on the transposed map, 2 and 3 reversed
+        if (k >= 2) l = L - 1 - l;
+        const uint32_t w = (uint32_t)p.win, u = (uint32_t)l;
+        const uint32_t wi = fdiv(u, p.dWin2), r = u - wi * (w * w);
+        const uint32_t ry = fdiv(r, p.dWin), rx = r - ry * w;
+        if ((k & 1) == 0) {
+            const uint32_t nx = (uint32_t)p.Wd / w, wy = fdiv(wi, p.dNx), wx = wi - wy * nx;
+            return (int64_t)(wy * w + ry) * p.Wd + (wx * w + rx);
+        }
+        const uint32_t ny = (uint32_t)p.H / w, wy = fdiv(wi, p.dNy), wx = wi - wy * ny;
+        // on the transposed map, row wy*w+ry is column wy*w+ry of this map and column wx*w+rx is a row
+        return (int64_t)(wx * w + rx) * p.Wd + (wy * w + ry);
     }
 }
 
@@ -427,13 +466,13 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             const int64_t s0 = (int64_t)q * kCH;
             const int64_t sa = s0 + 2 * pp, sbb = sa + 1, s = s0 + sb;
             if constexpr (decltype(fast_c)::value) {
-                const int64_t oa = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
-                const int64_t ob = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
+                const int64_t oa = (rowb + visit<KIND>(p, k, sa)) * dim + cg;
+                const int64_t ob = (rowb + visit<KIND>(p, k, sbb)) * dim + cg;
                 px0 = load_raw8(x + oa, 8, true);
                 pd0 = load_raw8(dl + oa, 8, true);
                 px1 = load_raw8(x + ob, 8, true);
                 pd1 = load_raw8(dl + ob, 8, true);
-                const int64_t ro = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * kN;
+                const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
 #pragma unroll
                 for (int h = 0; h < NW; h += 4) {
                     const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
@@ -444,19 +483,19 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             } else {
                 px0 = px1 = pd0 = pd1 = Raw8<T>{};
                 if (nv > 0 && sa < L) {
-                    const int64_t off = (rowb + visit<KIND>(k, sa, L, p.H, p.Wd)) * dim + cg;
+                    const int64_t off = (rowb + visit<KIND>(p, k, sa)) * dim + cg;
                     px0 = load_raw8(x + off, nv, vec);
                     pd0 = load_raw8(dl + off, nv, vec);
                 }
                 if (nv > 0 && sbb < L) {
-                    const int64_t off = (rowb + visit<KIND>(k, sbb, L, p.H, p.Wd)) * dim + cg;
+                    const int64_t off = (rowb + visit<KIND>(p, k, sbb)) * dim + cg;
                     px1 = load_raw8(x + off, nv, vec);
                     pd1 = load_raw8(dl + off, nv, vec);
                 }
 #pragma unroll
                 for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
                 if (s < L) {
-                    const int64_t ro = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * kN;
+                    const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
                     if (p.vecbc) {
 #pragma unroll
                         for (int h = 0; h < NW; h += 4) {
@@ -535,10 +574,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             for (int r = 0; r < 2; ++r) {
                 const int64_t s = s0 + so + 128 * r;
                 if constexpr (fast) {
-                    ooff[r] = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * dim + cg;
+                    ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
                     if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
                 } else if (nv > 0 && s < L) {
-                    ooff[r] = (rowb + visit<KIND>(k, s, L, p.H, p.Wd)) * dim + cg;
+                    ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
                     if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                 }
             }
@@ -721,7 +760,8 @@ template <typename T>
 int launch_kind(const Params &a, int kind, int64_t batch, void *stream) {
     if (kind == SELSCAN_OP_FWD) return launch_tiles<T, SELSCAN_OP_FWD>(a, batch, stream);
     if (kind == SELSCAN_OP_BIDIR) return launch_tiles<T, SELSCAN_OP_BIDIR>(a, batch, stream);
-    return launch_tiles<T, SELSCAN_OP_SS2D>(a, batch, stream);
+    if (kind == SELSCAN_OP_SS2D) return launch_tiles<T, SELSCAN_OP_SS2D>(a, batch, stream);
+    return launch_tiles<T, SELSCAN_OP_LOCAL_SS2D>(a, batch, stream);
 }
 
 int launch(const Problem &p, void *stream) {
@@ -730,7 +770,16 @@ int launch(const Problem &p, void *stream) {
     a.A = p.A, a.D = p.D, a.bias = p.bias, a.y = p.y;
     a.ws = p.ndir > 1 ? (float *)p.ws : nullptr;
     a.h0 = p.h0, a.hlast = p.hlast, a.ckpt = p.ckpt;
-    a.L = p.L, a.dim = p.dim, a.H = (int)p.H, a.Wd = (int)p.W;
+    a.L = p.L, a.dim = p.dim, a.H = (int)p.H, a.Wd = (int)p.W, a.win = (int)p.win;
+    a.dH = make_div((uint32_t)p.H);
+    if (p.kind == SELSCAN_OP_LOCAL_SS2D) {
+        a.dWin = make_div((uint32_t)p.win);
+        a.dWin2 = make_div((uint32_t)(p.win * p.win));
+        a.dNx = make_div((uint32_t)(p.W / p.win));
+        a.dNy = make_div((uint32_t)(p.H / p.win));
+    } else {
+        a.dWin = a.dWin2 = a.dNx = a.dNy = make_div(1);
+    }
     a.batch = (int)p.batch, a.ndir = p.ndir;
     a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
     // rows of 8 channels move as 16-byte vectors when every row start is 16-byte aligned
@@ -1443,12 +1492,24 @@ int ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, co
     return run(p, dstate, workspace_bytes, stream);
 }
 
+int local_ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+                   const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H,
+                   int64_t W, int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (H < 0 || W < 0) return SELSCAN_E_SHAPE;
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, H * W, dim, H, W, 4, SELSCAN_OP_LOCAL_SS2D,
+              io_dtype, flags};
+    p.win = window;
+    return run(p, dstate, workspace_bytes, stream);
+}
+
 size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,
                                int io_dtype) {
     (void)dstate;
     (void)io_dtype;
     if (batch <= 0 || seqlen_or_hw <= 0 || dim <= 0) return 0;
-    if (op != SELSCAN_OP_FWD && op != SELSCAN_OP_BIDIR && op != SELSCAN_OP_SS2D) return 0;
+    if (op != SELSCAN_OP_FWD && op != SELSCAN_OP_BIDIR && op != SELSCAN_OP_SS2D && op != SELSCAN_OP_LOCAL_SS2D)
+        return 0;
     return workspace_bytes_for(op, batch, seqlen_or_hw, dim);
 }
 

@@ -17,6 +17,7 @@ def test_exports_every_declared_symbol():
     declared = S.header_functions()
     assert set(declared) == {"selscan_fwd", "selscan_fwd_state", "selscan_bidir_fwd", "ss2d_fwd",
                              "selscan_bwd", "selscan_chunk_states_bytes", "selscan_bwd_workspace_bytes",
+                             "local_ss2d_fwd",
                              "selscan_workspace_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
@@ -155,3 +156,33 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         S.selscan_fwd(x, x, torch.zeros(8, 16), x.new_zeros(1, 4, 16), x.new_zeros(1, 4, 16), y=x.clone())
+
+
+def test_local_ss2d_window_checks():
+    loc = lambda H, W, w: L.local_ss2d_fwd(P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0,
+                                           P + 8 * MB, 1, H, W, w, 8, 16, 1, None, 0, None)
+    assert loc(6, 4, 0) == 2   # no window
+    assert loc(6, 4, 4) == 2   # does not divide H
+    assert loc(6, 4, 3) == 2   # does not divide W
+    assert loc(-1, 4, 1) == 2
+    assert loc(6, 4, 2) == 6   # valid window: stops at the missing workspace
+    assert S.selscan_workspace_bytes(S.SELSCAN_OP_LOCAL_SS2D, 1, 24, 8) == 24 * 8 * 4
+
+
+def test_fast_division_identity():
+    """The kernels divide pixel indices (< 2^31) by a runtime constant d with a multiply-high:
+    m = ceil(2^(31+s) / d), 2^(s-1) < d <= 2^s, q = (n * m) >> (31 + s).  Check the identity
+    on the host with the same integer recipe."""
+    import numpy as np
+    r = np.random.default_rng(3)
+    ds = list(range(1, 300)) + [2 ** k for k in range(1, 16)] + [2 ** k + 1 for k in range(1, 16)] + \
+        [int(v) for v in r.integers(2, 1 << 16, 200)] + [3136, 56, 49, 7, 65535, 65536]
+    ns = np.concatenate([r.integers(0, 1 << 31, 4000), np.arange(0, 5000), [(1 << 31) - 1, (1 << 31) - 2]])
+    for d in ds:
+        if d == 1:
+            continue
+        s = (d - 1).bit_length()
+        m = ((1 << (31 + s)) + d - 1) // d
+        assert m < (1 << 32)
+        q = [(int(n) * m) >> 32 >> (s - 1) for n in ns]
+        assert q == [int(n) // d for n in ns], d

@@ -49,6 +49,7 @@ SMALL = [
     (2, dict(batch=1, seqlen=4100, dim=128)),
     (3, dict(batch=4, seqlen=197, dim=768)),
     (4, dict(batch=2, dim=64)),
+    (5, dict(batch=2, dim=40)),
 ]
 
 
@@ -57,10 +58,10 @@ def test_workload_small(idx, ov):
     w = W.WORKLOADS[idx]
     _say("small", w.name, ov)
     inp = W.generate(w, **ov)
-    _check(w.kind, w, inp, H=w.H, Wd=w.W)
+    _check(w.kind, w, inp, H=w.H, Wd=w.W, window=w.window)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4], ids=[W.WORKLOADS[i].name for i in (1, 2, 3, 4)])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5], ids=[W.WORKLOADS[i].name for i in (1, 2, 3, 4, 5)])
 def test_workload_full_size_sampled(idx):
     """Full BASELINE sizes in the launch configuration the benchmark times; the oracle
     checks a sample of channels (every batch row, whole sequence)."""
@@ -69,7 +70,7 @@ def test_workload_full_size_sampled(idx):
     _say("full", w.name)
     inp = W.generate(w)
     chans = sorted({0, 1, 63, 64, w.dim // 2 + 5, w.dim - 1})
-    _check(w.kind, w, inp, H=w.H, Wd=w.W, channels=chans)
+    _check(w.kind, w, inp, H=w.H, Wd=w.W, channels=chans, window=w.window)
     del inp
     torch.cuda.empty_cache()
 
@@ -319,3 +320,13 @@ def test_bwd_full_size_130m():
     for k, e in errs.items():
         assert e <= _BWD_TOL[w.dtype], (k, e)
     torch.cuda.empty_cache()
+
+
+
+@pytest.mark.parametrize("H,Wd,win,dim", [(6, 4, 2, 16), (8, 8, 4, 40), (9, 6, 3, 24), (4, 4, 1, 8), (6, 6, 6, 8),
+                                          (12, 20, 4, 17)])
+def test_local_ss2d_shapes(H, Wd, win, dim):
+    w = W.Workload("local", "local_ss2d", 2, H * Wd, dim, 16, "f32", True, H=H, W=Wd, index=9, window=win)
+    _say("local", H, Wd, win, dim)
+    inp = W.generate(w)
+    _check("local_ss2d", w, inp, H=H, Wd=Wd, window=win)

@@ -42,10 +42,11 @@ class Workload:
     H: int = 0
     W: int = 0
     index: int = 0  # position in WORKLOADS; the seed is SEED_BASE + index
+    window: int = 0  # window side of the windowed cross-scan
 
     @property
     def ndir(self) -> int:
-        return {"selscan": 1, "bidir": 2, "ss2d": 4}[self.kind]
+        return {"selscan": 1, "bidir": 2, "ss2d": 4, "local_ss2d": 4}[self.kind]
 
     @property
     def elements(self) -> int:
@@ -77,6 +78,9 @@ WORKLOADS: List[Workload] = [
     Workload("mamba1p4b_layer_b2_L65536_D4096", "selscan", 2, 65536, 4096, 16, "bf16", True, index=2),
     Workload("vim_bidir_b64_L197_D768", "bidir", 64, 197, 768, 16, "bf16", True, index=3),
     Workload("vmamba_ss2d_b32_56x56_D192", "ss2d", 32, 56 * 56, 192, 16, "bf16", False, H=56, W=56, index=4),
+    # the windowed cross-scan on the VMamba stage-1 map, windows of 7 x 7 pixels
+    Workload("localmamba_local_ss2d_b32_56x56_w7_D192", "local_ss2d", 32, 56 * 56, 192, 16, "bf16", False, H=56, W=56,
+             index=5, window=7),
 ]
 
 
