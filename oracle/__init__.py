@@ -60,6 +60,8 @@ def load(path: Optional[str] = None):
     lib.oracle_local_ss2d.restype = ci
     lib.oracle_selscan_bwd.argtypes = [dp] * 8 + [ci] + [dp] * 11 + [i64, i64, i64, i64, ci]
     lib.oracle_selscan_bwd.restype = ci
+    lib.oracle_scan_order.argtypes = [ci, ci, i64, i64, i64, i64, dp]
+    lib.oracle_scan_order.restype = ci
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ci
     if path is None:
@@ -182,5 +184,72 @@ def selscan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_so
                                 g("dh0"), bt, L, dim, N, int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_selscan_bwd failed")
+    return out
+
+
+_KIND = {"bidir": 1, "ss2d": 2, "local_ss2d": 3}
+
+
+def scan_orders(kind, L, H=0, W=0, window=0, lib=None):
+    """[K][L] int64: the pixel (token) direction k visits at scan step l, from the oracle's own maps."""
+    lib = lib or load()
+    K = 2 if kind == "bidir" else 4
+    out = np.empty((K, L), dtype=np.int64)
+    for k in range(K):
+        if lib.oracle_scan_order(_KIND[kind], k, H, W, window, L, out[k].ctypes.data) != 0:
+            raise ValueError("bad scan order arguments")
+    return out
+
+
+def multi_bwd(kind, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, H=0, W=0,
+              window=0, nthreads=0, lib=None):
+    """Gradients of sum(dy * y) for the multi-direction scans (bidirectional, SS2D, windowed):
+    y = (sum_k scatter_k(scan_k(gather_k(x), gather_k(params_k)))) * silu(z).
+
+    Each direction is the single-direction scan on its gathered sequence, so its gradients are
+    oracle_selscan_bwd's with dL/d(its output) = gather_k(dy * silu(z)); per-token gradients are
+    scattered back (dx summed over the directions).  dz = dy * yp * silu'(z) with yp the merged
+    output before the gate.  Per-direction arrays carry the leading direction axis."""
+    lib = lib or load()
+    x, delta, A, B, C, dy, D, z, delta_bias = map(_f64, (x, delta, A, B, C, dy, D, z, delta_bias))
+    bt, L, dim = x.shape
+    orders = scan_orders(kind, L, H, W, window, lib=lib)
+    K = orders.shape[0]
+    if z is not None:
+        sg = 1.0 / (1.0 + np.exp(-z))
+        dyp = dy * z * sg
+        if kind == "bidir":
+            yp = selscan_bidir(x, delta, A, B, C, D=D, delta_bias=delta_bias, delta_softplus=delta_softplus,
+                               nthreads=nthreads, lib=lib)
+        elif kind == "ss2d":
+            yp = ss2d(x, delta, A, B, C, H, W, D=D, delta_bias=delta_bias, delta_softplus=delta_softplus,
+                      nthreads=nthreads, lib=lib)
+        else:
+            yp = local_ss2d(x, delta, A, B, C, H, W, window, D=D, delta_bias=delta_bias,
+                            delta_softplus=delta_softplus, nthreads=nthreads, lib=lib)
+    else:
+        dyp = dy
+    out = {"dx": np.zeros_like(x), "ddelta": np.zeros_like(delta), "dA": np.zeros_like(A), "dB": np.zeros_like(B),
+           "dC": np.zeros_like(C)}
+    if D is not None:
+        out["dD"] = np.zeros_like(D)
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.zeros_like(delta_bias)
+    for k in range(K):
+        o = orders[k]
+        g = selscan_bwd(x[:, o], delta[k][:, o], A[k], B[k][:, o], C[k][:, o], dyp[:, o],
+                        D=None if D is None else D[k], delta_bias=None if delta_bias is None else delta_bias[k],
+                        delta_softplus=delta_softplus, nthreads=nthreads, lib=lib)
+        out["dx"][:, o] += g["dx"]
+        out["ddelta"][k][:, o] = g["ddelta"]
+        out["dB"][k][:, o] = g["dB"]
+        out["dC"][k][:, o] = g["dC"]
+        out["dA"][k] = g["dA"]
+        if D is not None:
+            out["dD"][k] = g["dD"]
+        if delta_bias is not None:
+            out["ddelta_bias"][k] = g["ddelta_bias"]
+    if z is not None:
+        out["dz"] = dy * yp * sg * (1.0 + z * (1.0 - sg))
     return out
 

@@ -334,6 +334,28 @@ int oracle_local_ss2d(const double *x, const double *delta, const double *A, con
                       nthreads);
 }
 
+/* The pixel (token) each direction visits at each scan step, as the scans above use it:
+ * kind 1 bidirectional (k = 0, 1), 2 SS2D (k = 0..3), 3 windowed cross-scan (k = 0..3,
+ * window win).  Fills order[l], l = 0..L-1, for direction k; returns -1 on a bad argument. */
+int oracle_scan_order(int kind, int k, int64_t H, int64_t W, int64_t win, int64_t L, int64_t *order) {
+    if (!order || L < 0) return -1;
+    for (int64_t l = 0; l < L; ++l) {
+        if (kind == 1) {
+            if (k < 0 || k > 1) return -1;
+            order[l] = k == 0 ? l : L - 1 - l;
+        } else if (kind == 2) {
+            if (k < 0 || k > 3 || H * W != L) return -1;
+            order[l] = ss2d_pixel(k, l, H, W);
+        } else if (kind == 3) {
+            if (k < 0 || k > 3 || H * W != L || win < 1 || H % win || W % win) return -1;
+            order[l] = local_pixel(k, l, H, W, win);
+        } else {
+            return -1;
+        }
+    }
+    return 0;
+}
+
 /* number of hardware threads the oracle would use for nthreads <= 0 */
 int oracle_default_threads(void) {
     long c = sysconf(_SC_NPROCESSORS_ONLN);

@@ -439,6 +439,41 @@ def pin_bwd_elementwise_fd(lib):
         assert np.abs(fd - g[gname]).max() <= 1e-6 * max(np.abs(fd).max(), 1.0), (name, fd, g[gname])
 
 
+
+def pin_multi_bwd_fd(lib):
+    """Gradients of the bidirectional, SS2D and windowed scans against central finite
+    differences of their (separately pinned) forward oracles along random directions."""
+    r = _rng(321)
+    for kind, H, W, w in [("bidir", 0, 0, 0), ("ss2d", 3, 4, 0), ("local_ss2d", 4, 6, 2)]:
+        K = 2 if kind == "bidir" else 4
+        bt, L, dim, N = 2, (7 if kind == "bidir" else H * W), 3, 3
+        args = dict(x=r.standard_normal((bt, L, dim)), delta=np.exp(r.uniform(-5, -1.5, (K, bt, L, dim))),
+                    A=-np.exp(r.uniform(-1.0, 1.5, (K, dim, N))), B=r.standard_normal((K, bt, L, N)),
+                    C=r.standard_normal((K, bt, L, N)), D=r.standard_normal((K, dim)), z=r.standard_normal((bt, L, dim)),
+                    delta_bias=0.1 * r.standard_normal((K, dim)))
+        dy = r.standard_normal((bt, L, dim))
+
+        def loss(a):
+            if kind == "bidir":
+                y = oracle.selscan_bidir(**a, lib=lib)
+            elif kind == "ss2d":
+                y = oracle.ss2d(**a, H=H, W=W, lib=lib)
+            else:
+                y = oracle.local_ss2d(**a, H=H, W=W, window=w, lib=lib)
+            return float(np.sum(dy * y))
+
+        g = oracle.multi_bwd(kind, dy=dy, H=H, W=W, window=w, lib=lib, **args)
+        for name, gname in [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"),
+                            ("z", "dz"), ("delta_bias", "ddelta_bias")]:
+            v = r.standard_normal(np.shape(args[name]))
+            up, dn = dict(args), dict(args)
+            up[name] = args[name] + 1e-5 * v
+            dn[name] = args[name] - 1e-5 * v
+            fd = (loss(up) - loss(dn)) / 2e-5
+            an = float(np.sum(g[gname] * v))
+            assert abs(fd - an) <= 1e-6 * max(abs(fd), 1.0), (kind, name, fd, an)
+
+
 ALL_PINS = [
     pin_lti_convolution,
     pin_delta_to_zero,
@@ -456,4 +491,5 @@ ALL_PINS = [
     pin_local_ss2d_limits,
     pin_bwd_directional_fd,
     pin_bwd_elementwise_fd,
+    pin_multi_bwd_fd,
 ]

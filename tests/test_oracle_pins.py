@@ -86,3 +86,32 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
         except (RuntimeError, FloatingPointError, ValueError, OverflowError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+
+# (name, text in oracle/__init__.py, replacement): mistakes in the composition of the
+# multi-direction gradients out of the single-direction ones.
+PY_MUTATIONS = [
+    ("multi_dx_not_summed", 'out["dx"][:, o] += g["dx"]', 'out["dx"][:, o] = g["dx"]'),
+    ("multi_dyp_not_gated", "dyp = dy * z * sg", "dyp = dy"),
+    ("multi_dz_missing_silu_derivative", 'out["dz"] = dy * yp * sg * (1.0 + z * (1.0 - sg))', 'out["dz"] = dy * yp * sg'),
+    ("multi_first_direction_params", "A[k], B[k][:, o], C[k][:, o]", "A[0], B[k][:, o], C[k][:, o]"),
+    ("multi_dC_not_scattered", 'out["dC"][k][:, o] = g["dC"]', 'out["dC"][k] = g["dC"]'),
+    ("multi_ddelta_token_order", 'out["ddelta"][k][:, o] = g["ddelta"]', 'out["ddelta"][k] = g["ddelta"]'),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_pins_catch_planted_python_mistake(name, old, new, lib, monkeypatch):
+    text = open(PY_SRC).read()
+    assert old in text, f"mutation site for {name} not found in oracle/__init__.py"
+    ns = {"__name__": "oracle_mutant", "__file__": PY_SRC}
+    exec(compile(text.replace(old, new, 1), PY_SRC, "exec"), ns)
+    monkeypatch.setattr(oracle, "multi_bwd", ns["multi_bwd"])
+    try:
+        P.pin_multi_bwd_fd(lib)
+    except AssertionError:
+        return
+    pytest.fail(f"no pin caught the planted mistake {name}")
+
