@@ -2,7 +2,8 @@
 """Throughput of the selective-scan forward on one MI355X.
 
 A step is one pass of the whole hot path (one selscan_fwd / selscan_bidir_fwd /
-ss2d_fwd call) over one batch of synthetic input already resident in HBM.
+ss2d_fwd / local_ss2d_fwd call; with --pass bwd one selscan_scan_bwd call) over one batch
+of synthetic input already resident in HBM.
 Prints ONE JSON line (rank 0).  Default workload: the Mamba-1.4B-layer
 long-context shape, batch 2 x L 65536 x D 4096, N 16, bf16 I/O, fp32 state.
 
@@ -41,14 +42,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def bwd_algorithmic_bytes(w) -> int:
-    """Bytes a fused backward must move at least once: x, delta, z, dy and the chunk states read,
-    dx, ddelta, dz written (io dtype); B, C read and dB, dC written; A, D read, dA, dD written."""
-    s = w.io_bytes
+    """Bytes a fused backward must move at least once: x, dy, z and each direction's delta and
+    chunk states read, dx, dz and each direction's ddelta written (io dtype); each direction's
+    B, C read and dB, dC written; A, D read and dA, dD written per direction."""
+    s, k = w.io_bytes, w.ndir
     tok = w.batch * w.seqlen * w.dim
     bc = w.batch * w.seqlen * w.dstate * s
-    ck = w.batch * ((w.seqlen + 255) // 256) * w.dim * w.dstate * 4
-    params = 2 * (w.dim * w.dstate + w.dim) * 4
-    return tok * s * ((4 if w.gate else 3) + (3 if w.gate else 2)) + 4 * bc + ck + params
+    ck = k * w.batch * ((w.seqlen + 255) // 256) * w.dim * w.dstate * 4
+    params = 2 * k * (w.dim * w.dstate + w.dim) * 4
+    g = 1 if w.gate else 0
+    return tok * s * ((2 + k + g) + (1 + k + g)) + 4 * k * bc + ck + params
 
 
 def kernel_source_hash() -> str:
@@ -114,8 +117,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
-                    help="fwd: the forward scan (default); bwd: selscan_bwd (gradients of every input, chunk "
-                         "states recomputed) on single-direction workloads, the chunk states saved beforehand")
+                    help="fwd: the forward scan (default); bwd: selscan_scan_bwd (gradients of every input, "
+                         "states recomputed from the chunk states a forward saved beforehand)")
     ap.add_argument("--state", action="store_true",
                     help="single-direction workloads: run selscan_fwd_state with an initial state and the "
                          "final state written (recurrent / chunked inference)")
@@ -158,8 +161,8 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    if (args.state or args.pass_ == "bwd") and w.kind != "selscan":
-        print("--state and --pass bwd apply to single-direction workloads only", file=sys.stderr)
+    if args.state and w.kind != "selscan":
+        print("--state applies to single-direction workloads only", file=sys.stderr)
         return 2
     h0 = hl = None
     if args.state:
@@ -167,18 +170,19 @@ def main() -> int:
         hl = torch.empty_like(h0)
 
     ck = dy = bws = None
+    geo = dict(H=w.H, W=w.W, window=w.window)
     if args.pass_ == "bwd":
-        _, ck = S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
-                                    chunk_states=True, stream=stream)
+        _, ck = S.selscan_scan_fwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
+                                   chunk_states=True, workspace=ws, stream=stream, **geo)
         dy = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
-        bws = torch.empty(S.selscan_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate,
-                                                        S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32),
+        bws = torch.empty(S.selscan_scan_bwd_workspace_bytes(op, w.batch, w.seqlen, w.dim, w.dstate,
+                                                             S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32),
                           dtype=torch.uint8, device=dev)
 
     def step():
         if args.pass_ == "bwd":
-            S.selscan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dy, ck, D=t["D"], z=t["z"], workspace=bws,
-                          stream=stream)
+            S.selscan_scan_bwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], dy, ck, D=t["D"], z=t["z"],
+                               workspace=bws, stream=stream, **geo)
         elif args.state:
             S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, h0=h0,
                                 h_last=hl, workspace=ws, stream=stream)

@@ -71,7 +71,7 @@ typedef enum {
 /* flag bits */
 #define SELSCAN_FLAG_DELTA_SOFTPLUS 1u /* delta_t = softplus(delta + delta_bias) */
 
-/* operation codes for selscan_workspace_bytes */
+/* operation codes (scan orders) for selscan_workspace_bytes and the selscan_scan_* calls */
 typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2, SELSCAN_OP_LOCAL_SS2D = 3 } selscan_op;
 
 /*
@@ -199,6 +199,64 @@ int local_ss2d_fwd(const void *x, const void *delta, const float *A, const void 
                    const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H,
                    int64_t W, int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * selscan_scan_fwd - the forward of any of the scan orders above, selected by `op`
+ * (SELSCAN_OP_FWD: selscan_fwd; SELSCAN_OP_BIDIR: selscan_bidir_fwd; SELSCAN_OP_SS2D: ss2d_fwd;
+ * SELSCAN_OP_LOCAL_SS2D: local_ss2d_fwd), also keeping the chunk states that selscan_scan_bwd
+ * restarts from.  Arrays, layouts and workspace are those of the op's own entry point.
+ *   seqlen       : tokens (pixels) per batch row; for the two-dimensional orders it must equal
+ *                  H * W (SELSCAN_E_SHAPE otherwise), for the others H and W are ignored
+ *   window       : window side, read by SELSCAN_OP_LOCAL_SS2D only
+ *   chunk_states : selscan_scan_chunk_states_bytes(op, ...) bytes, 4-byte aligned, one block of
+ *                  states per direction (the library's own layout); NULL = not written.  It may
+ *                  overlap no input, y or the workspace (SELSCAN_E_ALIAS).
+ * An unknown op is SELSCAN_E_UNSUPPORTED.
+ */
+int selscan_scan_fwd(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                     float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W, int64_t window,
+                     int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Bytes of the chunk_states buffer of selscan_scan_fwd / selscan_scan_bwd for `op` (0 if op is
+ * unknown, a size is not positive or dstate != 16). */
+size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * selscan_scan_bwd - gradients of L = sum(dy * y) for y = selscan_scan_fwd(op, ...), the states
+ * recomputed from that call's chunk_states (as selscan_bwd does for one direction).  The merged
+ * output is y = (sum_k o_k) * silu(z) with o_k one single-direction scan on direction k's
+ * visiting order, so direction k's gradients are the single-direction ones for dL/do_k =
+ * dy * silu(z) at the pixels it visits ("从LSTM到Mamba" §3.1 for the two directions; "Mamba
+ * Series from Selective State Spaces to Visual State Space Models", section 关键代码, for the
+ * four-direction merge; "Mamba论文" for recomputing the states in the backward).
+ * Inputs: those of the forward call, chunk_states, and dy [batch][seqlen][dim] io_dtype.
+ * Outputs (caller-owned, written in full), in the forward's layouts:
+ *   dx           : [batch][seqlen][dim] io_dtype, summed over the directions
+ *   ddelta       : [ndir][batch][seqlen][dim] io_dtype (token / pixel order; before
+ *                  delta_bias and softplus)
+ *   dB, dC       : [ndir][batch][seqlen][dstate] io_dtype (summed over channels in fp32)
+ *   dA           : [ndir][dim][dstate] fp32 (required)
+ *   dD, ddelta_bias : [ndir][dim] fp32, nullable
+ *   dz           : [batch][seqlen][dim] io_dtype, nullable; written only when z is given
+ * (ndir = 1, 2, 4 for FWD, BIDIR, SS2D / LOCAL_SS2D; with ndir = 1 the leading axis is absent
+ * and the call equals selscan_bwd without dh0.)  workspace: at least
+ * selscan_scan_bwd_workspace_bytes(op, ...) bytes, 4-byte aligned.  No output may overlap an
+ * input, another output or the workspace (SELSCAN_E_ALIAS).  All sums are in a fixed order:
+ * the results are the same from run to run.
+ */
+int selscan_scan_bwd(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias, unsigned flags,
+                     const float *chunk_states, const void *dy, void *dx, void *ddelta, float *dA, void *dB,
+                     void *dC, float *dD, void *dz, float *ddelta_bias, int64_t batch, int64_t seqlen, int64_t H,
+                     int64_t W, int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Scratch bytes selscan_scan_bwd needs as `workspace` for `op` (0 if op is unknown, batch or dim
+ * is not positive or dstate != 16). */
+size_t selscan_scan_bwd_workspace_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                        int io_dtype);
 
 /* Scratch bytes the caller must pass as `workspace` for this problem (0 = none). */
 size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,

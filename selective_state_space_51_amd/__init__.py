@@ -56,6 +56,14 @@ def _load():
     lib.ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.local_ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.local_ss2d_fwd.restype = ci
+    lib.selscan_scan_fwd.argtypes = [ci] + common + [vp, i64, i64, i64, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.selscan_scan_fwd.restype = ci
+    lib.selscan_scan_bwd.argtypes = [ci] + [vp] * 8 + [cu] + [vp] * 10 + [i64] * 7 + [ci, vp, sz, vp]
+    lib.selscan_scan_bwd.restype = ci
+    lib.selscan_scan_chunk_states_bytes.argtypes = [ci, i64, i64, i64, i64]
+    lib.selscan_scan_chunk_states_bytes.restype = sz
+    lib.selscan_scan_bwd_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci]
+    lib.selscan_scan_bwd_workspace_bytes.restype = sz
     for f in (lib.selscan_fwd, lib.selscan_fwd_state, lib.selscan_bidir_fwd, lib.ss2d_fwd):
         f.restype = ci
     lib.selscan_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci]
@@ -334,4 +342,99 @@ def local_ss2d_fwd(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=N
                             bt, H, W, window, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "local_ss2d_fwd")
     return y
+
+
+_NDIR = {SELSCAN_OP_FWD: 1, SELSCAN_OP_BIDIR: 2, SELSCAN_OP_SS2D: 4, SELSCAN_OP_LOCAL_SS2D: 4}
+
+
+def selscan_scan_chunk_states_bytes(op: int, batch: int, seqlen: int, dim: int, dstate: int = 16) -> int:
+    return int(lib.selscan_scan_chunk_states_bytes(op, batch, seqlen, dim, dstate))
+
+
+def selscan_scan_bwd_workspace_bytes(op: int, batch: int, seqlen: int, dim: int, dstate: int = 16,
+                                     io_dtype: int = SELSCAN_BF16) -> int:
+    return int(lib.selscan_scan_bwd_workspace_bytes(op, batch, seqlen, dim, dstate, io_dtype))
+
+
+def _scan_shapes(op, x, A, H, W):
+    bt, L, dim = x.shape
+    N = A.shape[-1]
+    if op not in _NDIR:
+        raise ValueError(f"unknown op {op}")
+    K = _NDIR[op]
+    if op in (SELSCAN_OP_SS2D, SELSCAN_OP_LOCAL_SS2D) and L != H * W:
+        raise ValueError(f"x has {L} pixels, expected H*W = {H * W}")
+    lead = (K,) if K > 1 else ()
+    return bt, L, dim, N, K, lead
+
+
+def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, H=0, W=0,
+                     window=0, y=None, chunk_states=None, workspace=None, stream=None):
+    """Forward of any scan order (SELSCAN_OP_*), optionally keeping the chunk states the backward
+    restarts from (chunk_states=True allocates them).  Per-direction arrays carry a leading
+    direction axis for the multi-direction orders.  Returns y, or (y, chunk_states)."""
+    torch = _torch()
+    bt, L, dim, N, K, lead = _scan_shapes(op, x, A, H, W)
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, lead + (bt, L, dim)), ("B", B, lead + (bt, L, N)),
+                       ("C", C, lead + (bt, L, N)), ("A", A, lead + (dim, N)), ("D", D, lead + (dim,)),
+                       ("z", z, (bt, L, dim)), ("delta_bias", delta_bias, lead + (dim,))):
+        _shape_check(n_, t_, s_)
+    need_cs = selscan_scan_chunk_states_bytes(op, bt, L, dim, N)
+    if chunk_states is True:
+        chunk_states = torch.empty(max(need_cs // 4, 1), dtype=torch.float32, device=x.device)
+    if chunk_states is not None and chunk_states.numel() * chunk_states.element_size() < need_cs:
+        raise ValueError("chunk_states is smaller than selscan_scan_chunk_states_bytes(...)")
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(op, x, bt, L, dim, workspace)
+    rc = lib.selscan_scan_fwd(op, _ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
+                              _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                              _ptr(delta_bias, "delta_bias", f32=True),
+                              SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                              _ptr(chunk_states, "chunk_states", f32=True), bt, L, H, W, window, dim, N,
+                              _dtype_code(x), ws, wsb, _stream(stream))
+    _check(rc, "selscan_scan_fwd")
+    return (y, chunk_states) if chunk_states is not None else y
+
+
+def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None,
+                     delta_softplus=False, H=0, W=0, window=0, workspace=None, stream=None):
+    """Gradients of sum(dy * y) for y = selscan_scan_fwd(op, ...) with chunk_states from that call.
+    Returns a dict: dx, ddelta, dA, dB, dC, and dD / dz / ddelta_bias for the inputs that were given;
+    per-direction gradients carry the leading direction axis."""
+    torch = _torch()
+    bt, L, dim, N, K, lead = _scan_shapes(op, x, A, H, W)
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, lead + (bt, L, dim)), ("B", B, lead + (bt, L, N)),
+                       ("C", C, lead + (bt, L, N)), ("A", A, lead + (dim, N)), ("D", D, lead + (dim,)),
+                       ("z", z, (bt, L, dim)), ("delta_bias", delta_bias, lead + (dim,)),
+                       ("dy", dy, (bt, L, dim))):
+        _shape_check(n_, t_, s_)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty_like(x), "ddelta": torch.empty(lead + (bt, L, dim), dtype=io, device=x.device),
+         "dA": torch.empty(lead + (dim, N), **f32), "dB": torch.empty(lead + (bt, L, N), dtype=io, device=x.device),
+         "dC": torch.empty(lead + (bt, L, N), dtype=io, device=x.device)}
+    if D is not None:
+        g["dD"] = torch.empty(lead + (dim,), **f32)
+    if z is not None:
+        g["dz"] = torch.empty_like(x)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(lead + (dim,), **f32)
+    need = selscan_scan_bwd_workspace_bytes(op, bt, L, dim, N, _dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    p = lambda k, **kw: _ptr(g.get(k), k, **kw)
+    rc = lib.selscan_scan_bwd(op, _ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
+                              _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                              _ptr(delta_bias, "delta_bias", f32=True),
+                              SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0,
+                              _ptr(chunk_states, "chunk_states", f32=True), _ptr(dy, "dy", io),
+                              p("dx", io=io), p("ddelta", io=io), p("dA", f32=True), p("dB", io=io), p("dC", io=io),
+                              p("dD", f32=True), p("dz", io=io), p("ddelta_bias", f32=True),
+                              bt, L, H, W, window, dim, N, _dtype_code(x), workspace.data_ptr(), wsb,
+                              _stream(stream))
+    _check(rc, "selscan_scan_bwd")
+    return g
 

@@ -72,7 +72,7 @@ struct Problem {
     unsigned flags;
     const float *h0 = nullptr;  // [batch][dim][N] initial state (forward scan only)
     float *hlast = nullptr;     // [batch][dim][N] state after the last step
-    float *ckpt = nullptr;      // [batch][nchunks][dim][N] state entering each chunk
+    float *ckpt = nullptr;      // [ndir][batch][nchunks][dim][N] state entering each chunk
     int64_t win = 0;            // window side of the windowed cross-scan
 };
 
@@ -135,7 +135,7 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
         if (overlap(hls, q)) return SELSCAN_E_ALIAS;
     if (p.h0 != (const float *)p.hlast && overlap(hls, h0s)) return SELSCAN_E_ALIAS;
     if (p.ckpt) {
-        const Span cks{p.ckpt, ckpt_bytes_for(p.batch, p.L, p.dim)};
+        const Span cks{p.ckpt, K * ckpt_bytes_for(p.batch, p.L, p.dim)};
         if (!aligned(p.ckpt, 4)) return SELSCAN_E_ALIGN;
         if (overlap(cks, y) || overlap(cks, h0s) || overlap(cks, hls)) return SELSCAN_E_ALIAS;
         for (const Span &q : in)
@@ -173,7 +173,7 @@ struct Params {
     float *ws;        // fp32 [batch][L][dim] partial sums when ndir > 1
     const float *h0;  // fp32 [batch][dim][N] initial state, or NULL (zero)
     float *hlast;     // fp32 [batch][dim][N] final state, or NULL (not written)
-    float *ckpt;      // fp32 [batch][nchunks][dim][N] state entering each chunk, or NULL
+    float *ckpt;      // fp32 [ndir][batch][nchunks][dim][N] state entering each chunk, or NULL
     int64_t L, dim;
     int H, Wd;        // SS2D image height and width (H * Wd == L)
     int win;          // window side of the windowed cross-scan
@@ -241,9 +241,10 @@ struct BoolC {
     static constexpr bool value = V;
 };
 
-// row (token or pixel) visited at scan step l, 0 <= l < L, by direction k
-template <int KIND>
-__device__ __forceinline__ int64_t visit(const Params &p, int k, int64_t l) {
+// row (token or pixel) visited at scan step l, 0 <= l < L, by direction k; P carries L, H, Wd,
+// win and the divisions by H, w, w*w, W/w, H/w
+template <int KIND, typename P>
+__device__ __forceinline__ int64_t visit(const P &p, int k, int64_t l) {
     const int64_t L = p.L;
     if constexpr (KIND == SELSCAN_OP_FWD) {
         return l;
@@ -563,7 +564,8 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             if (p.ckpt) {
                 // the carry entering this chunk, kept for the backward pass
                 const int ch = tid / kN, n = tid % kN;
-                if (c0 + ch < dim) p.ckpt[(((int64_t)b * nchunks + q) * dim + c0 + ch) * kN + n] = Cy[tid];
+                if (c0 + ch < dim)
+                    p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] = Cy[tid];
             }
             // gate input for this chunk's output items, then the next chunk's inputs: in flight
             // while this chunk computes
@@ -740,6 +742,21 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     }
 }
 
+// the scan-order fields of a kernel's parameters (visit() reads them)
+template <class P>
+void set_order(P &a, int kind, int64_t L, int64_t H, int64_t W, int64_t win) {
+    a.L = L, a.H = (int)H, a.Wd = (int)W, a.win = (int)win;
+    a.dH = make_div((uint32_t)H);
+    if (kind == SELSCAN_OP_LOCAL_SS2D) {
+        a.dWin = make_div((uint32_t)win);
+        a.dWin2 = make_div((uint32_t)(win * win));
+        a.dNx = make_div((uint32_t)(W / win));
+        a.dNy = make_div((uint32_t)(H / win));
+    } else {
+        a.dWin = a.dWin2 = a.dNx = a.dNy = make_div(1);
+    }
+}
+
 template <typename T, int KIND>
 int launch_tiles(const Params &a, int64_t batch, void *stream) {
     Params c = a;
@@ -770,16 +787,8 @@ int launch(const Problem &p, void *stream) {
     a.A = p.A, a.D = p.D, a.bias = p.bias, a.y = p.y;
     a.ws = p.ndir > 1 ? (float *)p.ws : nullptr;
     a.h0 = p.h0, a.hlast = p.hlast, a.ckpt = p.ckpt;
-    a.L = p.L, a.dim = p.dim, a.H = (int)p.H, a.Wd = (int)p.W, a.win = (int)p.win;
-    a.dH = make_div((uint32_t)p.H);
-    if (p.kind == SELSCAN_OP_LOCAL_SS2D) {
-        a.dWin = make_div((uint32_t)p.win);
-        a.dWin2 = make_div((uint32_t)(p.win * p.win));
-        a.dNx = make_div((uint32_t)(p.W / p.win));
-        a.dNy = make_div((uint32_t)(p.H / p.win));
-    } else {
-        a.dWin = a.dWin2 = a.dNx = a.dNy = make_div(1);
-    }
+    a.dim = p.dim;
+    set_order(a, p.kind, p.L, p.H, p.W, p.win);
     a.batch = (int)p.batch, a.ndir = p.ndir;
     a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
     // rows of 8 channels move as 16-byte vectors when every row start is 16-byte aligned
@@ -822,17 +831,28 @@ int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {
 // tile's 16 channels (v_permlane32/16_swap across the 4 channel rows of a wave, then LDS
 // across the 4 waves) and leave as one fp32 partial per tile; selscan_bwd_reduce adds the
 // tiles and the batch rows.
+//
+// Several directions (bidirectional, SS2D, windowed): the merged output is
+// y = (sum_k o_k) silu(z), each o_k a single-direction scan on its own visiting order, so
+// direction k's backward is the one above with dL/do_k = dy silu(z) at the pixels it visits.
+// The workgroup walks the directions one after another, as the forward does; dx (summed over
+// the directions) and the pre-gate output sum_k o_k (which dz needs) build up in fp32 rows
+// of the workspace, and the last direction writes dx and dz.
 
 struct BwdParams {
     const void *x, *delta, *B, *C, *z, *dy;
     const float *A, *D, *bias, *ckpt;
     void *dx, *ddelta, *dz;
     float *dh0;
-    float *wsBC;  // [ntc][batch][2][N][L] per-tile partial sums of dB (0) and dC (1)
-    float *wsA;   // [batch][dim][N] per-batch-row partial sums of dA
-    float *wsD;   // [batch][dim][2] per-batch-row partial sums of dD and ddelta_bias
+    float *wsBC;  // [ndir][ntc][batch][2][N][L] per-tile partial sums of dB (0) and dC (1), by scan step
+    float *wsA;   // [ndir][batch][dim][N] per-batch-row partial sums of dA
+    float *wsD;   // [ndir][batch][dim][2] per-batch-row partial sums of dD and ddelta_bias
+    float *wsX;   // [batch][L][dim] dx summed over the directions done so far (ndir > 1)
+    float *wsY;   // [batch][L][dim] pre-gate output summed over the directions done so far (ndir > 1)
     int64_t L, dim;
-    int batch, softplus, ntc, vec, vecbc;
+    int H, Wd, win;  // scan order (as for the forward)
+    FastDiv dH, dWin, dWin2, dNx, dNy;
+    int batch, ndir, softplus, ntc, vec, vecbc;
 };
 
 // Shared memory of one backward workgroup (16 channels, one chunk).
@@ -933,8 +953,9 @@ __device__ __forceinline__ void rows4_sum(const float p[kK], float out[4]) {
 
 __device__ __forceinline__ float sigmoidf_(float w) { return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e)); }
 
-template <typename T>
+template <typename T, int KIND>
 __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
+    constexpr bool multi = KIND != SELSCAN_OP_FWD;
     using S = BwdLds<T>;
     constexpr int CT = kTC;
     static_assert(CT * kN == 256, "one (channel, state) entry per thread");
@@ -966,12 +987,10 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
     const int nchunks = (int)chunks_of(L);
     const bool vec = p.vec != 0;
     const T *x = (const T *)p.x;
-    const T *dl = (const T *)p.delta;
     const T *dy = (const T *)p.dy;
     const T *z = (const T *)p.z;
-    const T *Bg = (const T *)p.B;
-    const T *Cg = (const T *)p.C;
     const int64_t rowb = (int64_t)b * L;
+    const int64_t tok = (int64_t)p.batch * L * dim, bcn = (int64_t)p.batch * L * kN;
     const int g = lane >> 5, nv = ncols - 8 * g;
     const int64_t cg = c0 + 8 * g;
     const int pp = 8 * (((lane >> 2) & 7) + 8 * (wave >> 1)) + 4 * (wave & 1) + (lane & 3);
@@ -979,16 +998,25 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
     const int so = 16 * ((lane >> 2) & 7) + 4 * wave + (lane & 3);
     constexpr int NW = kN * (int)sizeof(T) / 4;
 
+  const int ndir = multi ? p.ndir : 1;
+  for (int k = 0; k < ndir; ++k) {
+    const T *dl = (const T *)p.delta + k * tok;
+    const T *Bg = (const T *)p.B + k * bcn;
+    const T *Cg = (const T *)p.C + k * bcn;
+    const bool last = k == ndir - 1;
+    // the previous direction is done with every tile, and its stores of the summed rows (read
+    // back here by other waves) are complete: a full barrier
+    __syncthreads();
     {
         const int ch = tid / kN, n = tid % kN;
         const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
-        As[tid] = nchunks > 0 ? p.A[cc * kN + n] * kLog2e : 0.f;
+        As[tid] = nchunks > 0 ? p.A[(k * dim + cc) * kN + n] * kLog2e : 0.f;
         Gc[tid] = 0.f;  // nothing flows back from after the last step
         dAs[tid] = 0.f;
         if (tid < CT) {
             const int64_t c1 = c0 + tid < dim ? c0 + tid : 0;
-            Db[2 * tid] = p.D ? p.D[c1] : 0.f;
-            Db[2 * tid + 1] = p.bias ? p.bias[c1] : 0.f;
+            Db[2 * tid] = p.D ? p.D[k * dim + c1] : 0.f;
+            Db[2 * tid + 1] = p.bias ? p.bias[k * dim + c1] : 0.f;
             dDs[2 * tid] = dDs[2 * tid + 1] = 0.f;
         }
     }
@@ -1005,15 +1033,15 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
             for (int m = 0; m < 4; ++m) {
                 r0[m] = r1[m] = Raw8<T>{};
                 if (!src[m]) continue;
-                if (nv > 0 && sa < L) r0[m] = load_raw8(src[m] + (rowb + sa) * dim + cg, nv, vec);
-                if (nv > 0 && sbb < L) r1[m] = load_raw8(src[m] + (rowb + sbb) * dim + cg, nv, vec);
+                if (nv > 0 && sa < L) r0[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sa)) * dim + cg, nv, vec);
+                if (nv > 0 && sbb < L) r1[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sbb)) * dim + cg, nv, vec);
             }
             uint32_t pbc[2][NW];
 #pragma unroll
             for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
             const int64_t s = s0 + sb;
             if (s < L) {
-                const int64_t ro = (rowb + s) * kN;
+                const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
                 if (p.vecbc) {
 #pragma unroll
                     for (int h = 0; h < NW; h += 4) {
@@ -1066,7 +1094,8 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                 Cs[h * kFP + sp] = cv;
             }
             const int ch = tid / kN, n = tid % kN;
-            Hc[tid] = c0 + ch < dim ? p.ckpt[(((int64_t)b * nchunks + q) * dim + c0 + ch) * kN + n] : 0.f;
+            Hc[tid] = c0 + ch < dim ? p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n]
+                                    : 0.f;
         }
         lds_barrier();
 
@@ -1204,7 +1233,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                     sC += red[4 * kCH + w * kCH + tid];
                 }
                 if (s0 + tid < L) {
-                    float *dst = p.wsBC + ((((int64_t)tc * p.batch + b) * 2) * kN + n) * L + s0 + tid;
+                    float *dst = p.wsBC + (((((int64_t)k * p.ntc + tc) * p.batch + b) * 2) * kN + n) * L + s0 + tid;
                     dst[0] = sB;
                     dst[(int64_t)kN * L] = sC;
                 }
@@ -1242,7 +1271,9 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                 ddt = j < lim ? ddt : 0.f;
                 o0[j] = dt[j] * accx[j] + Dd * dyp[j];  // dx
                 o1[j] = ddt;                            // d(delta)
-                if (z) {
+                if constexpr (multi) {
+                    o2[j] = yv[j];  // this direction's output; dz waits for the sum over directions
+                } else if (z) {
                     const float sg = sigmoidf_(zf[j]);
                     o2[j] = yf[j] * yv[j] * sg * (1.f + zf[j] * (1.f - sg));
                 } else {
@@ -1276,15 +1307,41 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                 const int sl = so + 128 * r;
                 const int64_t s = s0 + sl;
                 if (nv <= 0 || s >= L) continue;
-                const int64_t off = (rowb + s) * dim + cg;
+                const int64_t off = (rowb + visit<KIND>(p, k, s)) * dim + cg;
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = Bs[(8 * g + e) * kFP + fpos(sl)];
-                store8((T *)(round == 0 ? p.dx : p.dz) + off, nv, vec, v);
+                if constexpr (multi) {
+                    // add the earlier directions' sum; keep it, or finish dx / dz
+                    float* acc = round == 0 ? p.wsX : p.wsY;
+                    if (k > 0) {
+                        float w8[8];
+                        load_f8(acc + off, nv, vec, w8);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] += w8[e];
+                    }
+                    if (!last) {
+                        store8(acc + off, nv, vec, v);
+                    } else if (round == 0) {
+                        store8((T *)p.dx + off, nv, vec, v);
+                    } else {
+                        const int xs = S::xpos(sl);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float dyv = Io<T>::f32(dyt[(8 * g + e) * S::kXP + xs]);
+                            const float zv = Io<T>::f32(zt[(8 * g + e) * S::kXP + xs]);
+                            const float sg = sigmoidf_(zv);
+                            v[e] = dyv * v[e] * sg * (1.f + zv * (1.f - sg));
+                        }
+                        store8((T *)p.dz + off, nv, vec, v);
+                    }
+                } else {
+                    store8((T *)(round == 0 ? p.dx : p.dz) + off, nv, vec, v);
+                }
                 if (round == 0) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = Cs[(8 * g + e) * kFP + fpos(sl)];
-                    store8((T *)p.ddelta + off, nv, vec, v);
+                    store8((T *)p.ddelta + k * tok + off, nv, vec, v);
                 }
             }
             lds_barrier();
@@ -1295,13 +1352,14 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
         const int ch = tid / kN, n = tid % kN;
         if (c0 + ch < dim) {
             if (p.dh0) p.dh0[((int64_t)b * dim + c0 + ch) * kN + n] = Gc[tid];
-            p.wsA[((int64_t)b * dim + c0 + ch) * kN + n] = dAs[tid];
+            p.wsA[(((int64_t)k * p.batch + b) * dim + c0 + ch) * kN + n] = dAs[tid];
         }
         if (tid < CT && c0 + tid < dim) {
-            p.wsD[((int64_t)b * dim + c0 + tid) * 2] = dDs[2 * tid];
-            p.wsD[((int64_t)b * dim + c0 + tid) * 2 + 1] = dDs[2 * tid + 1];
+            p.wsD[(((int64_t)k * p.batch + b) * dim + c0 + tid) * 2] = dDs[2 * tid];
+            p.wsD[(((int64_t)k * p.batch + b) * dim + c0 + tid) * 2 + 1] = dDs[2 * tid + 1];
         }
     }
+  }
 }
 
 struct BwdReduceParams {
@@ -1309,56 +1367,66 @@ struct BwdReduceParams {
     void *dB, *dC;
     float *dA, *dD, *dbias;
     int64_t L, dim;
-    int batch, ntc;
+    int H, Wd, win;  // scan order (dB, dC partials are by scan step)
+    FastDiv dH, dWin, dWin2, dNx, dNy;
+    int batch, ntc, ndir;
 };
 
-// dB[b,t,:], dC[b,t,:] = sum over the channel tiles of their partials (one thread per (b, t));
-// dA, dD, ddelta_bias = sum over the batch rows (one thread per (channel, state)).
-template <typename T>
+// dB[k,b,pi_k(t),:], dC[k,b,pi_k(t),:] = sum over the channel tiles of their partials for scan
+// step t (one thread per (k, b, t)); dA, dD, ddelta_bias = sum over the batch rows (one thread
+// per (k, channel, state)).
+template <typename T, int KIND>
 __global__ __launch_bounds__(256) void selscan_bwd_reduce(BwdReduceParams f) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t nbt = (int64_t)f.batch * f.L;
+    const int64_t nbt = (int64_t)f.ndir * f.batch * f.L;
     if (i < nbt) {
-        const int64_t b = i / f.L, t = i % f.L;
+        const int64_t kb = i / f.L, t = i % f.L;  // kb = k * batch + b
+        const int k = (int)(kb / f.batch), b = (int)(kb % f.batch);
+        const int64_t row = kb * f.L + visit<KIND>(f, k, t);
 #pragma unroll 1
         for (int qt = 0; qt < 2; ++qt) {
             float acc[kN];
 #pragma unroll
             for (int n = 0; n < kN; ++n) acc[n] = 0.f;
 #pragma unroll 1
-            for (int k = 0; k < f.ntc; ++k) {
-                const float *src = f.wsBC + (((int64_t)k * f.batch + b) * 2 + qt) * kN * f.L + t;
+            for (int c = 0; c < f.ntc; ++c) {
+                const float *src = f.wsBC + ((((int64_t)k * f.ntc + c) * f.batch + b) * 2 + qt) * kN * f.L + t;
 #pragma unroll
                 for (int n = 0; n < kN; ++n) acc[n] += src[(int64_t)n * f.L];
             }
-            T *dst = (T *)(qt == 0 ? f.dB : f.dC) + i * kN;
+            T *dst = (T *)(qt == 0 ? f.dB : f.dC) + row * kN;
             store8(dst, 8, false, acc);
             store8(dst + 8, 8, false, acc + 8);
         }
         return;
     }
-    const int64_t j = i - nbt;
-    if (j < f.dim * kN) {
+    const int64_t j = i - nbt, dn = f.dim * kN;
+    if (j < f.ndir * dn) {
+        const int64_t k = j / dn, jj = j % dn;
         float s = 0.f;
-        for (int b = 0; b < f.batch; ++b) s += f.wsA[(int64_t)b * f.dim * kN + j];
+        for (int b = 0; b < f.batch; ++b) s += f.wsA[(k * f.batch + b) * dn + jj];
         f.dA[j] = s;
-        if (j % kN < 2) {
-            const int64_t d = j / kN;
+        if (jj % kN < 2) {
+            const int64_t d = jj / kN;
             float t = 0.f;
-            for (int b = 0; b < f.batch; ++b) t += f.wsD[((int64_t)b * f.dim + d) * 2 + j % kN];
-            float *o = j % kN == 0 ? f.dD : f.dbias;
-            if (o) o[d] = t;
+            for (int b = 0; b < f.batch; ++b) t += f.wsD[((k * f.batch + b) * f.dim + d) * 2 + jj % kN];
+            float *o = jj % kN == 0 ? f.dD : f.dbias;
+            if (o) o[k * f.dim + d] = t;
         }
     }
 }
 
-size_t bwd_ws_parts(int64_t batch, int64_t L, int64_t dim, size_t part[3]) {
+// workspace of the backward: dB/dC tile partials, dA and dD/dbias batch-row partials, and
+// with several directions the dx and pre-gate output sums
+size_t bwd_ws_parts(int ndir, int64_t batch, int64_t L, int64_t dim, size_t part[5]) {
     const int64_t ntc = (dim + kTC - 1) / kTC;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    part[0] = up((size_t)ntc * (size_t)batch * 2 * kN * (size_t)L * 4);
-    part[1] = up((size_t)batch * (size_t)dim * kN * 4);
-    part[2] = up((size_t)batch * (size_t)dim * 2 * 4);
-    return part[0] + part[1] + part[2];
+    const size_t K = (size_t)ndir;
+    part[0] = up(K * (size_t)ntc * (size_t)batch * 2 * kN * (size_t)L * 4);
+    part[1] = up(K * (size_t)batch * (size_t)dim * kN * 4);
+    part[2] = up(K * (size_t)batch * (size_t)dim * 2 * 4);
+    part[3] = part[4] = ndir > 1 ? up((size_t)batch * (size_t)L * (size_t)dim * 4) : 0;
+    return part[0] + part[1] + part[2] + part[3] + part[4];
 }
 
 struct BwdProblem {
@@ -1370,13 +1438,20 @@ struct BwdProblem {
     int64_t batch, L, dim;
     int dtype;
     unsigned flags;
+    int kind = SELSCAN_OP_FWD;
+    int ndir = 1;
+    int64_t H = 0, W = 0, win = 0;
 };
 
 int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
-    if (p.batch < 0 || p.L < 0 || p.dim < 0 || dstate < 0) return SELSCAN_E_SHAPE;
+    if (p.batch < 0 || p.L < 0 || p.dim < 0 || p.H < 0 || p.W < 0 || dstate < 0) return SELSCAN_E_SHAPE;
     if (p.dtype != SELSCAN_F32 && p.dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
     if (p.flags & ~SELSCAN_FLAG_DELTA_SOFTPLUS) return SELSCAN_E_UNSUPPORTED;
     if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
+    if ((p.kind == SELSCAN_OP_SS2D || p.kind == SELSCAN_OP_LOCAL_SS2D) &&
+        (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
+        return SELSCAN_E_UNSUPPORTED;
+    if (p.kind == SELSCAN_OP_LOCAL_SS2D && (p.win < 1 || p.H % p.win || p.W % p.win)) return SELSCAN_E_SHAPE;
     if (p.batch == 0 || p.dim == 0) return SELSCAN_OK;
     if (!p.dA) return SELSCAN_E_NULL;
     if (p.L > 0 && (!p.x || !p.delta || !p.A || !p.B || !p.C || !p.ckpt || !p.dy || !p.dx || !p.ddelta ||
@@ -1389,15 +1464,18 @@ int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
     const void *f32[] = {p.A, p.D, p.bias, p.ckpt, p.dA, p.dD, p.dbias, p.dh0, p.ws};
     for (const void *q : f32)
         if (q && !aligned(q, 4)) return SELSCAN_E_ALIGN;
-    size_t part[3];
-    const size_t need = bwd_ws_parts(p.batch, p.L, p.dim, part);
+    size_t part[5];
+    const size_t need = bwd_ws_parts(p.ndir, p.batch, p.L, p.dim, part);
     if (!p.ws || ws_bytes < need) return SELSCAN_E_WORKSPACE;
+    const size_t K = (size_t)p.ndir;
     const size_t tok = (size_t)p.batch * p.L * p.dim * s, bc = (size_t)p.batch * p.L * kN * s;
     const size_t dn = (size_t)p.dim * kN * 4, dv = (size_t)p.dim * 4, hs = (size_t)p.batch * p.dim * kN * 4;
-    const Span in[] = {{p.x, tok}, {p.delta, tok}, {p.B, bc}, {p.C, bc}, {p.z, tok}, {p.dy, tok}, {p.A, dn},
-                       {p.D, dv}, {p.bias, dv}, {p.ckpt, ckpt_bytes_for(p.batch, p.L, p.dim)}};
-    const Span out[] = {{p.dx, tok}, {p.ddelta, tok}, {p.dB, bc}, {p.dC, bc}, {p.z ? p.dz : nullptr, tok},
-                        {p.dA, dn}, {p.dD, dv}, {p.dbias, dv}, {p.dh0, hs}, {p.ws, need}};
+    const Span in[] = {{p.x, tok},        {p.delta, K * tok}, {p.B, K * bc},   {p.C, K * bc},
+                       {p.z, tok},        {p.dy, tok},        {p.A, K * dn},   {p.D, K * dv},
+                       {p.bias, K * dv},  {p.ckpt, K * ckpt_bytes_for(p.batch, p.L, p.dim)}};
+    const Span out[] = {{p.dx, tok},       {p.ddelta, K * tok}, {p.dB, K * bc},    {p.dC, K * bc},
+                        {p.z ? p.dz : nullptr, tok},            {p.dA, K * dn},    {p.dD, K * dv},
+                        {p.dbias, K * dv}, {p.dh0, hs},         {p.ws, need}};
     constexpr int NO = sizeof(out) / sizeof(out[0]);
     for (int i = 0; i < NO; ++i) {
         for (const Span &q : in)
@@ -1408,21 +1486,26 @@ int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
     return SELSCAN_OK;
 }
 
-template <typename T>
-int bwd_launch(const BwdProblem &q, void *stream) {
+template <typename T, int KIND>
+int bwd_launch_kind(const BwdProblem &q, void *stream) {
     BwdParams a;
     a.x = q.x, a.delta = q.delta, a.B = q.B, a.C = q.C, a.z = q.z, a.dy = q.dy;
     a.A = q.A, a.D = q.D, a.bias = q.bias, a.ckpt = q.ckpt;
     a.dx = q.dx, a.ddelta = q.ddelta, a.dz = q.z ? q.dz : nullptr, a.dh0 = q.dh0;
-    size_t part[3];
-    bwd_ws_parts(q.batch, q.L, q.dim, part);
-    a.wsBC = (float *)q.ws;
-    a.wsA = (float *)((char *)q.ws + part[0]);
-    a.wsD = (float *)((char *)q.ws + part[0] + part[1]);
-    a.L = q.L, a.dim = q.dim, a.batch = (int)q.batch;
+    size_t part[5];
+    bwd_ws_parts(q.ndir, q.batch, q.L, q.dim, part);
+    char *w = (char *)q.ws;
+    a.wsBC = (float *)w;
+    a.wsA = (float *)(w + part[0]);
+    a.wsD = (float *)(w + part[0] + part[1]);
+    a.wsX = q.ndir > 1 ? (float *)(w + part[0] + part[1] + part[2]) : nullptr;
+    a.wsY = q.ndir > 1 ? (float *)(w + part[0] + part[1] + part[2] + part[3]) : nullptr;
+    a.dim = q.dim;
+    set_order(a, q.kind, q.L, q.H, q.W, q.win);
+    a.batch = (int)q.batch, a.ndir = q.ndir;
     a.softplus = (q.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
     a.ntc = (int)((q.dim + kTC - 1) / kTC);
-    const void *rows[] = {q.x, q.delta, q.dy, q.z, q.dx, q.ddelta, q.dz};
+    const void *rows[] = {q.x, q.delta, q.dy, q.z, q.dx, q.ddelta, q.dz, a.wsX, a.wsY};
     bool vec = q.dim % 8 == 0;
     for (const void *r : rows)
         if (r && !aligned(r, 16)) vec = false;
@@ -1431,23 +1514,67 @@ int bwd_launch(const BwdProblem &q, void *stream) {
     const int64_t blocks = q.batch * (int64_t)a.ntc;
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&a};
-    hipError_t e = hipLaunchKernel((const void *)&selscan_bwd_chunked<T>, dim3((unsigned)blocks), dim3(256), args, 0,
-                                   (hipStream_t)stream);
+    hipError_t e = hipLaunchKernel((const void *)&selscan_bwd_chunked<T, KIND>, dim3((unsigned)blocks), dim3(256),
+                                   args, 0, (hipStream_t)stream);
     if (e == hipSuccess) {
         BwdReduceParams f;
         f.wsBC = a.wsBC, f.wsA = a.wsA, f.wsD = a.wsD;
         f.dB = q.dB, f.dC = q.dC, f.dA = q.dA, f.dD = q.dD, f.dbias = q.dbias;
-        f.L = q.L, f.dim = q.dim, f.batch = (int)q.batch, f.ntc = a.ntc;
-        const int64_t items = q.batch * q.L + q.dim * kN;
+        f.dim = q.dim;
+        set_order(f, q.kind, q.L, q.H, q.W, q.win);
+        f.batch = (int)q.batch, f.ntc = a.ntc, f.ndir = q.ndir;
+        const int64_t items = q.ndir * (q.batch * q.L + q.dim * kN);
         const int64_t rb = (items + 255) / 256;
         if (rb > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
         void *fargs[] = {&f};
-        e = hipLaunchKernel((const void *)&selscan_bwd_reduce<T>, dim3((unsigned)rb), dim3(256), fargs, 0,
+        e = hipLaunchKernel((const void *)&selscan_bwd_reduce<T, KIND>, dim3((unsigned)rb), dim3(256), fargs, 0,
                             (hipStream_t)stream);
     }
     if (e != hipSuccess) {
         strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
         return SELSCAN_E_HIP;
+    }
+    return SELSCAN_OK;
+}
+
+template <typename T>
+int bwd_launch(const BwdProblem &q, void *stream) {
+    if (q.kind == SELSCAN_OP_FWD) return bwd_launch_kind<T, SELSCAN_OP_FWD>(q, stream);
+    if (q.kind == SELSCAN_OP_BIDIR) return bwd_launch_kind<T, SELSCAN_OP_BIDIR>(q, stream);
+    if (q.kind == SELSCAN_OP_SS2D) return bwd_launch_kind<T, SELSCAN_OP_SS2D>(q, stream);
+    return bwd_launch_kind<T, SELSCAN_OP_LOCAL_SS2D>(q, stream);
+}
+
+int bwd_run(BwdProblem &p, int64_t dstate, size_t ws_bytes, void *stream) {
+    const int rc = bwd_validate(p, dstate, ws_bytes);
+    if (rc != SELSCAN_OK) return rc;
+    if (p.batch == 0 || p.dim == 0) return SELSCAN_OK;
+    if (p.batch > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    if (p.dtype == SELSCAN_BF16) return bwd_launch<uint16_t>(p, stream);
+    return bwd_launch<float>(p, stream);
+}
+
+// scan directions of an op (0: not an op)
+int ndir_of(int op) {
+    switch (op) {
+        case SELSCAN_OP_FWD: return 1;
+        case SELSCAN_OP_BIDIR: return 2;
+        case SELSCAN_OP_SS2D:
+        case SELSCAN_OP_LOCAL_SS2D: return 4;
+        default: return 0;
+    }
+}
+
+// sequence length and direction count of an op; H and W apply to the two-dimensional orders,
+// whose seqlen must be H * W
+int resolve_op(int op, int64_t seqlen, int64_t H, int64_t W, int64_t *L, int *ndir) {
+    *ndir = ndir_of(op);
+    if (*ndir == 0) return SELSCAN_E_UNSUPPORTED;
+    *L = seqlen;
+    if (op == SELSCAN_OP_SS2D || op == SELSCAN_OP_LOCAL_SS2D) {
+        if (seqlen < 0 || H < 0 || W < 0) return SELSCAN_E_SHAPE;
+        if (W > 0 && H > INT64_MAX / W) return SELSCAN_E_UNSUPPORTED;
+        if (seqlen != H * W) return SELSCAN_E_SHAPE;
     }
     return SELSCAN_OK;
 }
@@ -1521,8 +1648,8 @@ size_t selscan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, in
 size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype) {
     (void)io_dtype;
     if (batch <= 0 || seqlen < 0 || dim <= 0 || dstate != kN) return 0;
-    size_t part[3];
-    return bwd_ws_parts(batch, seqlen, dim, part);
+    size_t part[5];
+    return bwd_ws_parts(1, batch, seqlen, dim, part);
 }
 
 int selscan_bwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
@@ -1533,12 +1660,59 @@ int selscan_bwd(const void *x, const void *delta, const float *A, const void *B,
     BwdProblem p{x,  delta, B,  C,  z,     dy,    A,     D,     delta_bias, chunk_states, dx,    ddelta,
                  dB, dC,    dz, dA, dD,    ddelta_bias, dh0, workspace,  batch,        seqlen, dim,
                  io_dtype, flags};
-    const int rc = bwd_validate(p, dstate, workspace_bytes);
+    return bwd_run(p, dstate, workspace_bytes, stream);
+}
+
+int selscan_scan_fwd(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                     float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W, int64_t window,
+                     int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    int64_t L;
+    int ndir;
+    const int rc = resolve_op(op, seqlen, H, W, &L, &ndir);
     if (rc != SELSCAN_OK) return rc;
-    if (batch == 0 || dim == 0) return SELSCAN_OK;
-    if (batch > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
-    if (io_dtype == SELSCAN_BF16) return bwd_launch<uint16_t>(p, stream);
-    return bwd_launch<float>(p, stream);
+    const bool two_d = op == SELSCAN_OP_SS2D || op == SELSCAN_OP_LOCAL_SS2D;
+    Problem p{x,     delta, B, C, z, A, D, delta_bias, y, workspace, batch, L, dim, two_d ? H : 0, two_d ? W : 0,
+              ndir,  op,    io_dtype, flags};
+    p.ckpt = chunk_states;
+    p.win = op == SELSCAN_OP_LOCAL_SS2D ? window : 0;
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+int selscan_scan_bwd(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias, unsigned flags,
+                     const float *chunk_states, const void *dy, void *dx, void *ddelta, float *dA, void *dB,
+                     void *dC, float *dD, void *dz, float *ddelta_bias, int64_t batch, int64_t seqlen, int64_t H,
+                     int64_t W, int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    int64_t L;
+    int ndir;
+    const int rc = resolve_op(op, seqlen, H, W, &L, &ndir);
+    if (rc != SELSCAN_OK) return rc;
+    const bool two_d = op == SELSCAN_OP_SS2D || op == SELSCAN_OP_LOCAL_SS2D;
+    BwdProblem p{x,  delta, B,  C,  z,     dy,    A,     D,     delta_bias, chunk_states, dx,    ddelta,
+                 dB, dC,    dz, dA, dD,    ddelta_bias, nullptr, workspace, batch,      L,      dim,
+                 io_dtype, flags};
+    p.kind = op, p.ndir = ndir;
+    p.H = two_d ? H : 0, p.W = two_d ? W : 0;
+    p.win = op == SELSCAN_OP_LOCAL_SS2D ? window : 0;
+    return bwd_run(p, dstate, workspace_bytes, stream);
+}
+
+size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+    const int ndir = ndir_of(op);
+    if (ndir == 0 || batch <= 0 || seqlen <= 0 || dim <= 0 || dstate != kN) return 0;
+    return (size_t)ndir * ckpt_bytes_for(batch, seqlen, dim);
+}
+
+size_t selscan_scan_bwd_workspace_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                        int io_dtype) {
+    (void)io_dtype;
+    const int ndir = ndir_of(op);
+    if (ndir == 0 || batch <= 0 || seqlen < 0 || dim <= 0 || dstate != kN) return 0;
+    size_t part[5];
+    return bwd_ws_parts(ndir, batch, seqlen, dim, part);
 }
 
 const char *selscan_status_str(int status) {

@@ -17,7 +17,8 @@ def test_exports_every_declared_symbol():
     declared = S.header_functions()
     assert set(declared) == {"selscan_fwd", "selscan_fwd_state", "selscan_bidir_fwd", "ss2d_fwd",
                              "selscan_bwd", "selscan_chunk_states_bytes", "selscan_bwd_workspace_bytes",
-                             "local_ss2d_fwd",
+                             "local_ss2d_fwd", "selscan_scan_fwd", "selscan_scan_bwd",
+                             "selscan_scan_chunk_states_bytes", "selscan_scan_bwd_workspace_bytes",
                              "selscan_workspace_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
@@ -136,6 +137,66 @@ def test_bwd_arguments():
     # empty problems: nothing to do, or only dA (zeros) with seqlen 0
     assert bwd(batch=0, x=None, dA=None) == 0
     assert bwd(L_=0, dA=None) == 1
+
+
+def scan_fwd(**kw):
+    a = dict(op=S.SELSCAN_OP_BIDIR, x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, D=None, z=None,
+             bias=None, flags=0, y=P + 8 * MB, ck=None, batch=1, L_=16, H=0, W=0, win=0, dim=8, N=16,
+             dtype=S.SELSCAN_BF16, ws=P + 20 * MB, wsb=1 << 20)
+    a.update(kw)
+    return L.selscan_scan_fwd(a["op"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                              a["flags"], a["y"], a["ck"], a["batch"], a["L_"], a["H"], a["W"], a["win"], a["dim"],
+                              a["N"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_scan_fwd_arguments():
+    """Every call here fails a host-side check (none reaches a launch)."""
+    assert scan_fwd(op=7) == 5
+    assert scan_fwd(op=S.SELSCAN_OP_SS2D, H=3, W=4) == 2          # 16 tokens, not 3 x 4
+    assert scan_fwd(op=S.SELSCAN_OP_SS2D, H=-4, W=-4) == 2
+    assert scan_fwd(op=S.SELSCAN_OP_LOCAL_SS2D, H=4, W=4, win=3) == 2
+    assert scan_fwd(op=S.SELSCAN_OP_SS2D, H=4, W=4, ws=None) == 6  # shapes accepted: stops at the workspace
+    # chunk states hold one block per direction: two blocks of 512 bytes for the bidirectional scan
+    assert scan_fwd(ck=P + MB - 600) == 4          # the second block reaches into delta
+    assert scan_fwd(ck=P + 8 * MB + 100) == 4      # on y
+    assert scan_fwd(ck=P + 20 * MB + 2) == 3
+    for op, K in ((S.SELSCAN_OP_FWD, 1), (S.SELSCAN_OP_BIDIR, 2), (S.SELSCAN_OP_SS2D, 4), (S.SELSCAN_OP_LOCAL_SS2D, 4)):
+        assert S.selscan_scan_chunk_states_bytes(op, 2, 257, 8) == K * 2 * 2 * 8 * 16 * 4
+    assert S.selscan_scan_chunk_states_bytes(9, 2, 257, 8) == 0
+    assert S.selscan_scan_chunk_states_bytes(S.SELSCAN_OP_FWD, 2, 257, 8) == S.selscan_chunk_states_bytes(2, 257, 8)
+
+
+def scan_bwd(**kw):
+    a = dict(op=S.SELSCAN_OP_SS2D, x=P, delta=P + MB, A=P + 2 * MB, B=P + 3 * MB, C=P + 4 * MB, D=None, z=None,
+             bias=None, flags=0, ck=P + 5 * MB, dy=P + 6 * MB, dx=P + 10 * MB, ddelta=P + 11 * MB, dA=P + 12 * MB,
+             dB=P + 13 * MB, dC=P + 14 * MB, dD=None, dz=None, dbias=None, batch=1, L_=16, H=4, W=4, win=2, dim=8,
+             N=16, dtype=S.SELSCAN_BF16, ws=P + 20 * MB, wsb=1 << 20)
+    a.update(kw)
+    return L.selscan_scan_bwd(a["op"], a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                              a["flags"], a["ck"], a["dy"], a["dx"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"],
+                              a["dz"], a["dbias"], a["batch"], a["L_"], a["H"], a["W"], a["win"], a["dim"], a["N"],
+                              a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_scan_bwd_arguments():
+    """Every call here fails a host-side check (none reaches a launch)."""
+    ws = S.selscan_scan_bwd_workspace_bytes
+    # per-tile dB/dC partials, dA and dD/dbias partials, and the fp32 dx and output sums
+    assert ws(S.SELSCAN_OP_SS2D, 1, 16, 8) == 8192 + 2048 + 256 + 512 + 512
+    assert ws(S.SELSCAN_OP_FWD, 1, 16, 8) == S.selscan_bwd_workspace_bytes(1, 16, 8)
+    assert ws(S.SELSCAN_OP_BIDIR, 1, 16, 8) == 4096 + 1024 + 256 + 512 + 512
+    assert ws(5, 1, 16, 8) == 0 and ws(S.SELSCAN_OP_SS2D, 0, 16, 8) == 0
+    assert scan_bwd(op=5) == 5
+    assert scan_bwd(H=2) == 2
+    assert scan_bwd(op=S.SELSCAN_OP_LOCAL_SS2D, win=3) == 2
+    for k in ("x", "delta", "A", "B", "C", "ck", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        assert scan_bwd(**{k: None}) == 1, k
+    assert scan_bwd(ws=None) == 6
+    assert scan_bwd(wsb=ws(S.SELSCAN_OP_SS2D, 1, 16, 8) - 4) == 6
+    # four directions: dB is 4 x 512 bytes, so a dC 1 KiB after it overlaps
+    assert scan_bwd(dC=P + 13 * MB + 1024) == 4
+    assert scan_bwd(ddelta=P + 10 * MB - 512) == 4    # its third direction lands on dx (256 bytes)
+    assert scan_bwd(dA=P + 5 * MB + 1536) == 4        # on the fourth block of chunk states (512 bytes each)
 
 
 def test_workspace_query_and_check():

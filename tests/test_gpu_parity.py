@@ -323,6 +323,100 @@ def test_bwd_full_size_130m():
 
 
 
+
+_OP = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
+
+
+def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softplus=False, bias=False, D=True):
+    """selscan_scan_fwd (with chunk states) then selscan_scan_bwd for a multi-direction order,
+    every gradient against oracle.multi_bwd on every element; also checks that the forward's y
+    equals the plain entry point's bit for bit."""
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    w = W.Workload("bwd_" + kind, kind, batch, L, dim, 16, dtype, gate, H=H, W=Wd, index=13, window=win)
+    inp = W.generate(w, with_w=softplus, with_bias=bias)
+    dy = W.generate_cotangent(batch, L, dim, dtype)
+    dev = lambda a, dt=dtype: None if a is None else PT.to_dev(a, dt)
+    delta = inp["w"] if softplus else inp["delta"]
+    args = dict(D=dev(inp["D"], "f32") if D else None, z=dev(inp["z"]), delta_bias=dev(inp.get("delta_bias"), "f32"),
+                delta_softplus=softplus)
+    x, dl, A, B, C = dev(inp["x"]), dev(delta), dev(inp["A"], "f32"), dev(inp["B"]), dev(inp["C"])
+    op = _OP[kind]
+    y, ck = S.selscan_scan_fwd(op, x, dl, A, B, C, H=H, W=Wd, window=win, chunk_states=True, **args)
+    if kind == "bidir":
+        y0 = S.selscan_bidir_fwd(x, dl, A, B, C, **args)
+    elif kind == "ss2d":
+        y0 = S.ss2d_fwd(x, dl, A, B, C, H, Wd, **args)
+    else:
+        y0 = S.local_ss2d_fwd(x, dl, A, B, C, H, Wd, win, **args)
+    g = S.selscan_scan_bwd(op, x, dl, A, B, C, dev(dy), ck, H=H, W=Wd, window=win, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    f = lambda a: None if a is None else W.to_f64(a, dtype)
+    r = oracle.multi_bwd(kind, f(inp["x"]), f(delta), inp["A"].astype(np.float64), f(inp["B"]), f(inp["C"]), f(dy),
+                         D=inp["D"].astype(np.float64) if D else None, z=f(inp["z"]),
+                         delta_bias=None if inp.get("delta_bias") is None else inp["delta_bias"].astype(np.float64),
+                         delta_softplus=softplus, H=H, W=Wd, window=win)
+    errs = {k: PT.rel_err(PT.from_dev(g[k]), r[k]) for k in r}
+    _say("scan_bwd", kind, dtype, batch, L, dim, (H, Wd, win), dict(gate=gate, softplus=softplus, bias=bias, D=D),
+         {k: f"{v:.2e}" for k, v in errs.items()})
+    assert set(g) == set(r), (sorted(g), sorted(r))
+    return errs
+
+
+@pytest.mark.parametrize("kind,dtype,batch,L,dim,H,Wd,win,kw", [
+    ("bidir", "f32", 1, 16, 16, 0, 0, 0, {}),
+    ("bidir", "f32", 2, 300, 40, 0, 0, 0, dict(softplus=True, bias=True)),
+    ("bidir", "bf16", 3, 197, 24, 0, 0, 0, {}),
+    ("ss2d", "f32", 2, 30, 16, 5, 6, 0, {}),
+    ("ss2d", "f32", 1, 340, 24, 17, 20, 0, dict(softplus=True, bias=True, gate=False)),
+    ("ss2d", "bf16", 2, 784, 40, 28, 28, 0, dict(D=False)),
+    ("local_ss2d", "f32", 2, 48, 16, 6, 8, 2, {}),
+    ("local_ss2d", "f32", 1, 324, 24, 18, 18, 3, dict(softplus=True, bias=True)),
+    ("local_ss2d", "bf16", 2, 784, 17, 28, 28, 7, dict(gate=False)),
+], ids=lambda v: str(v))
+def test_scan_bwd_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw):
+    errs = _scan_bwd_run(kind, dtype, batch, L, dim, H=H, Wd=Wd, win=win, **kw)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL[dtype], (k, e)
+
+
+@pytest.mark.parametrize("idx,batch", [(3, 64), (4, 4), (5, 4)], ids=["vim_bidir_full", "ss2d_56x56_b4",
+                                                                      "local_56x56_w7_b4"])
+def test_scan_bwd_full_shape(idx, batch):
+    """The multi-direction backward at the workloads' full sequence, map and channel sizes
+    (the SS2D maps with 4 of their 32 batch rows), every gradient against the oracle."""
+    import torch
+    w = W.WORKLOADS[idx]
+    errs = _scan_bwd_run(w.kind, w.dtype, batch, w.seqlen, w.dim, H=w.H, Wd=w.W, win=w.window, gate=w.gate)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL[w.dtype], (k, e)
+    torch.cuda.empty_cache()
+
+
+def test_scan_entry_points_match_single_direction():
+    """selscan_scan_fwd / selscan_scan_bwd with SELSCAN_OP_FWD equal selscan_fwd_state /
+    selscan_bwd bit for bit (same kernels)."""
+    import torch
+    import selective_state_space_51_amd as S
+    w = W.Workload("scan_fwd", "selscan", 2, 700, 48, 16, "bf16", True, index=14)
+    inp = W.generate(w, with_bias=True)
+    dev = lambda a, dt="bf16": None if a is None else PT.to_dev(a, dt)
+    args = dict(D=dev(inp["D"], "f32"), z=dev(inp["z"]), delta_bias=dev(inp["delta_bias"], "f32"), delta_softplus=True)
+    x, dl, A, B, C = dev(inp["x"]), dev(inp["delta"]), dev(inp["A"], "f32"), dev(inp["B"]), dev(inp["C"])
+    dy = dev(W.generate_cotangent(2, 700, 48, "bf16"))
+    y1, ck1 = S.selscan_scan_fwd(0, x, dl, A, B, C, chunk_states=True, **args)
+    y2, ck2 = S.selscan_fwd_state(x, dl, A, B, C, chunk_states=True, **args)
+    g1 = S.selscan_scan_bwd(0, x, dl, A, B, C, dy, ck1, **args)
+    g2 = S.selscan_bwd(x, dl, A, B, C, dy, ck2, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(ck1, ck2)
+    assert set(g1) == set(g2)
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
 @pytest.mark.parametrize("H,Wd,win,dim", [(6, 4, 2, 16), (8, 8, 4, 40), (9, 6, 3, 24), (4, 4, 1, 8), (6, 6, 6, 8),
                                           (12, 20, 4, 17)])
 def test_local_ss2d_shapes(H, Wd, win, dim):
