@@ -37,7 +37,9 @@ FLOP_EQ_PER_ELEMENT_BWD = 38
 METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc", "selscan.hip")
+CSRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc")
+# the sources each pass's kernels are built from (the hash ties a traffic record to them)
+KERNEL_SRCS = {"fwd": ("selscan_common.h", "selscan_fwd.hip"), "bwd": ("selscan_common.h", "selscan_bwd.hip")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -54,19 +56,22 @@ def bwd_algorithmic_bytes(w) -> int:
     return tok * s * ((2 + k + g) + (1 + k + g)) + 4 * k * bc + ck + params
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(pass_: str = "fwd") -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS[pass_]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, pass_: str = "fwd"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
     current kernel source; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get(workload)
-    if not e or e.get("kernel_source_sha") != kernel_source_hash():
+    e = t.get(workload + ("/bwd" if pass_ == "bwd" else ""))
+    if not e or e.get("kernel_source_sha") != kernel_source_hash(pass_):
         return None
     return e.get("bytes_per_launch")
 
@@ -228,7 +233,7 @@ def main() -> int:
     hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
     flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else FLOP_EQ_PER_ELEMENT
     alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name + ("/bwd" if bwd else ""))
+    traffic = measured_traffic(w.name, args.pass_)
     out = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": value,

@@ -7,7 +7,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "selscan.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRCS = [os.path.join(CSRC, "selscan_fwd.hip"), os.path.join(CSRC, "selscan_bwd.hip")]
 OUT = os.path.join(PKG, "libselscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,8 +26,9 @@ HIP_FLAGS = [
 ]
 
 
-def build(extra=None, out=OUT, src=SRC, verbose=False) -> str:
-    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-o", out, src]
+def build(extra=None, out=OUT, srcs=None, verbose=False) -> str:
+    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out,
+           *(srcs or SRCS)]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,709 @@
+// libselscan - forward of the selective state-space scan for MI355X (gfx950) behind the C
+// ABI declared in include/selscan.h (the backward is in selscan_bwd.hip).
+//
+// Method: "Mamba Series from Selective State Spaces to Visual State Space Models",
+// section 选择性 SSM 的数学形式 (Abar = exp(delta A), selection of delta, B, C), insight 1
+// (scan evaluated on chip with a parallel prefix scan, Abar/Bbar never written to HBM) and
+// section 关键代码 (scan call with Ds, delta_bias, delta_softplus; the SS2D scan orders
+// and merge; the SiLU gate); "从LSTM到Mamba" §2.1 (D skip) and §3.1 (bidirectional scan).
+//
+// Work decomposition (one kernel for every forward entry point):
+//  - A workgroup owns one batch row and a tile of kCT = 16 channels, and walks every scan
+//    direction of that tile over the whole sequence in chunks of kCH = 256 scan steps.
+//  - A wave holds 4 channels, one per 16-lane DPP row.  Lane l of a row owns kK = 16
+//    consecutive scan steps of its channel.  All fp32 state stays in VGPRs.
+//  - Per chunk: x, delta (io dtype) are staged in LDS column-major per channel; B, C are
+//    staged once as fp32 [state][step] and shared by the 16 channels of the tile.
+//  - For each state n: pass 1 runs each lane's 16 steps from a zero state and keeps
+//    dA = exp2(delta * A * log2 e) and u = delta * B * x in registers; the lanes' affine
+//    maps (a, b) with a = exp2(A log2e * sum(delta)) are combined by a 4-step inclusive
+//    Hillis-Steele scan across the 16-lane row (DPP row_shr, identity (1, 0)), with the
+//    carry of the previous chunk folded into lane 0; pass 2 re-runs the 16 steps from the
+//    true start state and accumulates y += C h.
+//  - The chunk's outputs go through LDS and leave as coalesced row segments.  With several
+//    directions, partial sums are kept in an fp32 workspace row-aligned with y; the last
+//    direction adds, gates and writes y once.
+#include "selscan_common.h"
+
+namespace selscan_rt {
+thread_local char g_last_hip_error[160] = "no error";
+}  // namespace selscan_rt
+
+namespace {
+
+// ------------------------------------------------------------------------------------
+// host-side validation (pure host code: runs before any HIP call)
+// ------------------------------------------------------------------------------------
+
+struct Problem {
+    const void *x, *delta, *B, *C, *z;
+    const float *A, *D, *bias;
+    void *y;
+    void *ws;
+    int64_t batch, L, dim, H, W;
+    int ndir;   // 1, 2 or 4
+    int kind;   // SELSCAN_OP_*
+    int dtype;  // SELSCAN_F32 / SELSCAN_BF16
+    unsigned flags;
+    const float *h0 = nullptr;  // [batch][dim][N] initial state (forward scan only)
+    float *hlast = nullptr;     // [batch][dim][N] state after the last step
+    float *ckpt = nullptr;      // [ndir][batch][nchunks][dim][N] state entering each chunk
+    int64_t win = 0;            // window side of the windowed cross-scan
+};
+
+size_t workspace_bytes_for(int op, int64_t batch, int64_t L, int64_t dim) {
+    if (op == SELSCAN_OP_FWD) return 0;
+    return (size_t)batch * (size_t)L * (size_t)dim * sizeof(float);
+}
+
+int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
+    if (p.batch < 0 || p.L < 0 || p.dim < 0 || p.H < 0 || p.W < 0 || dstate < 0) return SELSCAN_E_SHAPE;
+    if (p.dtype != SELSCAN_F32 && p.dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
+    if (p.flags & ~SELSCAN_FLAG_DELTA_SOFTPLUS) return SELSCAN_E_UNSUPPORTED;
+    if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
+    if ((p.kind == SELSCAN_OP_SS2D || p.kind == SELSCAN_OP_LOCAL_SS2D) &&
+        (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
+        return SELSCAN_E_UNSUPPORTED;
+    if (p.kind == SELSCAN_OP_LOCAL_SS2D && (p.win < 1 || p.H % p.win || p.W % p.win)) return SELSCAN_E_SHAPE;
+    if (p.batch == 0 || p.dim == 0) return SELSCAN_OK;
+    if (p.L == 0 && !p.hlast) return SELSCAN_OK;  // nothing to scan and no state to write
+    if (p.L > 0 && (!p.x || !p.delta || !p.A || !p.B || !p.C || !p.y)) return SELSCAN_E_NULL;
+    const size_t s = p.dtype == SELSCAN_BF16 ? 2 : 4;
+    const void *io[] = {p.x, p.delta, p.B, p.C, p.z, p.y};
+    for (const void *q : io)
+        if (q && !aligned(q, s)) return SELSCAN_E_ALIGN;
+    const void *f32[] = {p.A, p.D, p.bias};
+    for (const void *q : f32)
+        if (q && !aligned(q, 4)) return SELSCAN_E_ALIGN;
+    const size_t need = workspace_bytes_for(p.kind, p.batch, p.L, p.dim);
+    if (need && p.ws && !aligned(p.ws, 4)) return SELSCAN_E_ALIGN;
+    const size_t tok = (size_t)p.batch * p.L * p.dim, bc = (size_t)p.batch * p.L * kN;
+    const size_t K = (size_t)p.ndir;
+    Span y{p.y, tok * s};
+    Span in[] = {{p.x, tok * s},
+                 {p.delta, K * tok * s},
+                 {p.B, K * bc * s},
+                 {p.C, K * bc * s},
+                 {p.z, tok * s},
+                 {p.A, K * (size_t)p.dim * kN * 4},
+                 {p.D, K * (size_t)p.dim * 4},
+                 {p.bias, K * (size_t)p.dim * 4},
+                 {need ? p.ws : nullptr, need}};
+    for (const Span &q : in)
+        if (overlap(y, q)) return SELSCAN_E_ALIAS;
+    if (need) {
+        if (!p.ws || ws_bytes < need) return SELSCAN_E_WORKSPACE;
+        for (int i = 0; i < 8; ++i)
+            if (overlap({p.ws, need}, in[i])) return SELSCAN_E_ALIAS;
+    }
+    // state in/out: h_last may be h0 itself (in-place update) but must not overlap anything else
+    const size_t st = (size_t)p.batch * (size_t)p.dim * kN * 4;
+    if ((p.h0 && !aligned(p.h0, 4)) || (p.hlast && !aligned(p.hlast, 4))) return SELSCAN_E_ALIGN;
+    const Span h0s{p.h0, st}, hls{p.hlast, st};
+    if (overlap(y, h0s) || overlap(y, hls)) return SELSCAN_E_ALIAS;
+    for (const Span &q : in)
+        if (overlap(hls, q)) return SELSCAN_E_ALIAS;
+    if (p.h0 != (const float *)p.hlast && overlap(hls, h0s)) return SELSCAN_E_ALIAS;
+    if (p.ckpt) {
+        const Span cks{p.ckpt, K * ckpt_bytes_for(p.batch, p.L, p.dim)};
+        if (!aligned(p.ckpt, 4)) return SELSCAN_E_ALIGN;
+        if (overlap(cks, y) || overlap(cks, h0s) || overlap(cks, hls)) return SELSCAN_E_ALIAS;
+        for (const Span &q : in)
+            if (overlap(cks, q)) return SELSCAN_E_ALIAS;
+    }
+    return SELSCAN_OK;
+}
+
+struct Params {
+    const void *x, *delta, *B, *C, *z;
+    const float *A, *D, *bias;
+    void *y;
+    float *ws;        // fp32 [batch][L][dim] partial sums when ndir > 1
+    const float *h0;  // fp32 [batch][dim][N] initial state, or NULL (zero)
+    float *hlast;     // fp32 [batch][dim][N] final state, or NULL (not written)
+    float *ckpt;      // fp32 [ndir][batch][nchunks][dim][N] state entering each chunk, or NULL
+    int64_t L, dim;
+    int H, Wd;        // SS2D image height and width (H * Wd == L)
+    int win;          // window side of the windowed cross-scan
+    FastDiv dH;       // division by H (SS2D column-major order)
+    FastDiv dWin, dWin2, dNx, dNy;  // by w, w*w, W/w, H/w (windowed orders)
+    int batch, ndir, softplus;
+    int vec;          // rows of 8 channels may be moved as 16-byte vectors
+    int vecbc;        // a 16-value B/C row may be moved as 16-byte vectors
+    int ntc;          // channel tiles per batch row
+};
+
+// Shared-memory layout of a workgroup (16 channels), per chunk of kCH steps.  In every tile
+// row the 16 steps of a lane are stored as 16-byte pieces: piece q of lane l sits at
+// q * (16 lanes * piece) + l * piece, so that one 16-byte read by each of the 16 lanes of a
+// row covers 256 contiguous bytes (no bank conflicts).
+template <typename T>
+struct Lds {
+    static constexpr int kCT = kTC;                                  // channels per tile
+    static constexpr int kV = 16 / (int)sizeof(T);                    // io elements per piece
+    static constexpr int kXP = kCH + kV;                              // io tile pitch (elements)
+    static constexpr int kIoBytes = kCT * kXP * (int)sizeof(T);       // x or delta tile
+    static constexpr int kYBytes = kCT * kFP * 4;                     // y tile fp32
+    // bf16 io: the y tile has space of its own, so a wave writes its outputs without waiting
+    // for the other waves to finish reading x and delta.  fp32 io: y reuses the x/delta space
+    // (space of its own would leave room for only one workgroup per compute unit).
+    static constexpr bool kYOwn = sizeof(T) == 2;
+    static constexpr int kXD = 2 * kIoBytes;
+    static constexpr int kY = kYOwn ? kXD : 0;
+    static constexpr int kB = kYOwn ? kXD + kYBytes : (kXD > kYBytes ? kXD : kYBytes);  // B [state][step]
+    static constexpr int kC = kB + kN * kFP * 4;                      // C tile
+    static constexpr int kA = kC + kN * kFP * 4;                      // A*log2e [ch][state]
+    static constexpr int kCarry = kA + kCT * kN * 4;                  // chunk carry [ch][state]
+    static constexpr int kDb = kCarry + kCT * kN * 4;                 // D, bias [ch][2]
+    static constexpr int kBytes = kDb + kCT * 8;
+    // position of chunk step s in an io tile row
+    __device__ static int xpos(int s) { return ((s & 15) / kV) * (kLPR * kV) + (s >> 4) * kV + (s % kV); }
+};
+// Inclusive scan of two states' lane maps (a, b) along each 16-lane row (one channel):
+// (a_l, b_l) <- (a_l a_{l-s}, a_l b_{l-s} + b_l) for s = 1, 2, 4, 8 with DPP row_shr; a lane
+// whose source is outside its row is not written, i.e. composed with the identity (1, 0).
+// Then every lane's start state: h enters holding the channel's carry and row_shr:1 overwrites
+// it with the left neighbour's end state everywhere except in lane 0 of the row, whose source
+// is out of range.  The two states alternate so that every DPP read comes at least two wait
+// states after the write of its source (the gfx9 VALU->DPP hazard); s_nop covers the ends.
+__device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float &a1, float &h0, float &h1) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %0, %2 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %3 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_mov_b32_dpp %4, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %5, %1 row_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(b0), "+v"(b1), "+v"(a0), "+v"(a1), "+v"(h0), "+v"(h1));
+}
+
+// One workgroup: 4 waves, a tile of 16 channels of one batch row, every direction.
+//
+// Lane maps of the staging and output items (wave w, lane i of the wave) are chosen so that
+// each LDS write or read instruction of a wave touches 64 distinct banks:
+//  - x/delta staging: chunk steps 2p, 2p+1 of the 8-channel group g = i / 32, with
+//    p = 8 (((i / 4) % 8) + 8 (w / 2)) + 4 (w % 2) + i % 4;
+//  - B/C staging: chunk step 16 (i / 4) + 4 w + i % 4, all 16 states;
+//  - output: chunk steps 16 ((i / 4) % 8 + 8 r) + 4 w + i % 4, r = 0, 1, group g = i / 32.
+// Priority: the waves of the two workgroups that share a SIMD run their state loops at
+// priorities that alternate with the chunk count, so neither workgroup starves the other,
+// and every phase outside the state loop runs above both.
+template <typename T, int KIND>
+__global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
+    using S = Lds<T>;
+    constexpr int CT = kTC;
+    constexpr int NW = kN * (int)sizeof(T) / 4;  // dwords of one 16-value B or C row
+    static_assert(CT * kN == 256, "one (channel, state) carry entry per thread");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
+    T *xt = (T *)smem;
+    T *dtl = (T *)(smem + S::kIoBytes);
+    float *yt = (float *)(smem + S::kY);
+    float *Bs = (float *)(smem + S::kB);
+    float *Cs = (float *)(smem + S::kC);
+    float *As = (float *)(smem + S::kA);
+    float *Cy = (float *)(smem + S::kCarry);
+    float *Db = (float *)(smem + S::kDb);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l = lane & 15;
+    const int cl = wave * 4 + (lane >> 4);     // this lane's channel within the tile
+    const float firstf = l == 0 ? 1.f : 0.f;  // 1 on the first lane of each channel
+    // consecutive channel tiles on one XCD: workgroups are dealt round-robin over 8 XCDs
+    const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
+    const int tile = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
+    const int b = tile / p.ntc;
+    const int64_t c0 = (int64_t)(tile % p.ntc) * CT;
+    const int64_t L = p.L, dim = p.dim;
+    const int64_t tok = (int64_t)p.batch * L * dim, bcn = (int64_t)p.batch * L * kN;
+    const int ncols = (int)(dim - c0 < CT ? dim - c0 : CT);
+    const bool cvalid = cl < ncols;
+    const int nchunks = (int)((L + kCH - 1) / kCH);
+    const bool tile_fast = ncols == CT && p.vec && p.vecbc;  // full tile, vector rows
+    const bool vec = p.vec != 0;
+    const T *x = (const T *)p.x;
+    const T *z = (const T *)p.z;
+    T *y = (T *)p.y;
+    const int64_t rowb = (int64_t)b * L;
+
+    const int g = lane >> 5, nv = ncols - 8 * g;  // 8-channel group of the row items
+    const int64_t cg = c0 + 8 * g;
+    const int pp = 8 * (((lane >> 2) & 7) + 8 * (wave >> 1)) + 4 * (wave & 1) + (lane & 3);
+    const int sb = 16 * (lane >> 2) + 4 * wave + (lane & 3);
+    const int so = 16 * ((lane >> 2) & 7) + 4 * wave + (lane & 3);
+
+    int qq = 0;  // chunks done over all directions (priority parity)
+    for (int k = 0; k < p.ndir; ++k) {
+        const T *dl = (const T *)p.delta + k * tok;
+        const T *Bk = (const T *)p.B + k * bcn;
+        const T *Ck = (const T *)p.C + k * bcn;
+        // the previous direction is done with the parameter tiles, and its stores of the partial
+        // sums (which other waves read back in this direction) are complete: a full barrier
+        __syncthreads();
+        for (int i = tid; i < CT * kN; i += 256) {
+            const int ch = i / kN, n = i % kN;
+            const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
+            if (nchunks > 0) As[i] = p.A[(k * dim + cc) * kN + n] * kLog2e;
+            // the carry into the first chunk: the caller's initial state, else zero
+            Cy[i] = p.h0 && c0 + ch < dim ? p.h0[((int64_t)b * dim + c0 + ch) * kN + n] : 0.f;
+        }
+        for (int i = tid; i < CT && nchunks > 0; i += 256) {
+            const int64_t cc = c0 + i < dim ? c0 + i : 0;
+            Db[2 * i] = p.D ? p.D[k * dim + cc] : 0.f;
+            Db[2 * i + 1] = p.bias ? p.bias[k * dim + cc] : 0.f;
+        }
+
+        // global -> registers for chunk q (prefetched one chunk ahead)
+        Raw8<T> px0, px1, pd0, pd1;
+        uint32_t pbc[2][NW];  // raw B and C values of one chunk step
+        auto fetch = [&](int q, auto fast_c) {
+            const int64_t s0 = (int64_t)q * kCH;
+            const int64_t sa = s0 + 2 * pp, sbb = sa + 1, s = s0 + sb;
+            if constexpr (decltype(fast_c)::value) {
+                const int64_t oa = (rowb + visit<KIND>(p, k, sa)) * dim + cg;
+                const int64_t ob = (rowb + visit<KIND>(p, k, sbb)) * dim + cg;
+                px0 = load_raw8(x + oa, 8, true);
+                pd0 = load_raw8(dl + oa, 8, true);
+                px1 = load_raw8(x + ob, 8, true);
+                pd1 = load_raw8(dl + ob, 8, true);
+                const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
+#pragma unroll
+                for (int h = 0; h < NW; h += 4) {
+                    const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                    const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
+                    pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                    pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                }
+            } else {
+                px0 = px1 = pd0 = pd1 = Raw8<T>{};
+                if (nv > 0 && sa < L) {
+                    const int64_t off = (rowb + visit<KIND>(p, k, sa)) * dim + cg;
+                    px0 = load_raw8(x + off, nv, vec);
+                    pd0 = load_raw8(dl + off, nv, vec);
+                }
+                if (nv > 0 && sbb < L) {
+                    const int64_t off = (rowb + visit<KIND>(p, k, sbb)) * dim + cg;
+                    px1 = load_raw8(x + off, nv, vec);
+                    pd1 = load_raw8(dl + off, nv, vec);
+                }
+#pragma unroll
+                for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
+                if (s < L) {
+                    const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
+                    if (p.vecbc) {
+#pragma unroll
+                        for (int h = 0; h < NW; h += 4) {
+                            const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                            const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
+                            pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                            pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                        }
+                    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                        for (int h = 0; h < NW; ++h) {
+                            pbc[0][h] = (uint32_t)Bk[ro + 2 * h] | ((uint32_t)Bk[ro + 2 * h + 1] << 16);
+                            pbc[1][h] = (uint32_t)Ck[ro + 2 * h] | ((uint32_t)Ck[ro + 2 * h + 1] << 16);
+                        }
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < NW; ++h) {
+                            pbc[0][h] = __float_as_uint(Bk[ro + h]);
+                            pbc[1][h] = __float_as_uint(Ck[ro + h]);
+                        }
+                    }
+                }
+            }
+        };
+        // registers -> LDS
+        auto commit = [&]() {
+            const int si = S::xpos(2 * pp);  // steps 2p and 2p+1 are adjacent in a piece
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ch = 8 * g + e;
+                if constexpr (sizeof(T) == 2) {
+                    // low half: step 2p, high half: step 2p+1, of channel e (v_perm_b32)
+                    const uint32_t sel = e & 1 ? 0x07060302u : 0x05040100u;
+                    *(uint32_t *)&xt[ch * S::kXP + si] = __builtin_amdgcn_perm(px1.w[e >> 1], px0.w[e >> 1], sel);
+                    *(uint32_t *)&dtl[ch * S::kXP + si] = __builtin_amdgcn_perm(pd1.w[e >> 1], pd0.w[e >> 1], sel);
+                } else {
+                    *(uint2 *)&xt[ch * S::kXP + si] = make_uint2(px0.w[e], px1.w[e]);
+                    *(uint2 *)&dtl[ch * S::kXP + si] = make_uint2(pd0.w[e], pd1.w[e]);
+                }
+            }
+            const int sp = fpos(sb);
+#pragma unroll
+            for (int h = 0; h < kN; ++h) {
+                float bv, cv;
+                if constexpr (sizeof(T) == 2) {
+                    bv = __uint_as_float(h & 1 ? pbc[0][h >> 1] & 0xFFFF0000u : pbc[0][h >> 1] << 16);
+                    cv = __uint_as_float(h & 1 ? pbc[1][h >> 1] & 0xFFFF0000u : pbc[1][h >> 1] << 16);
+                } else {
+                    bv = __uint_as_float(pbc[0][h]);
+                    cv = __uint_as_float(pbc[1][h]);
+                }
+                Bs[h * kFP + sp] = bv;
+                Cs[h * kFP + sp] = cv;
+            }
+        };
+
+        // one chunk; FAST: a full chunk of a full tile whose successor is full too
+        auto chunk = [&](int q, auto fast_c) {
+            constexpr bool fast = decltype(fast_c)::value;
+            const int64_t s0 = (int64_t)q * kCH;
+            __builtin_amdgcn_s_setprio(2);
+            lds_barrier();  // the previous chunk is done with every tile
+            commit();
+            lds_barrier();
+            if (p.ckpt) {
+                // the carry entering this chunk, kept for the backward pass
+                const int ch = tid / kN, n = tid % kN;
+                if (c0 + ch < dim)
+                    p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] = Cy[tid];
+            }
+            // gate input for this chunk's output items, then the next chunk's inputs: in flight
+            // while this chunk computes
+            const bool last = k == p.ndir - 1;
+            Raw8<T> zr[2] = {};
+            int64_t ooff[2] = {0, 0};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int64_t s = s0 + so + 128 * r;
+                if constexpr (fast) {
+                    ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+                    if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
+                } else if (nv > 0 && s < L) {
+                    ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+                    if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                }
+            }
+            if (q + 1 < nchunks) fetch(q + 1, fast_c);
+
+            // ---- this lane's 16 steps of its channel
+            const int64_t rem = L - (s0 + l * kK);
+            const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= kK ? kK : (int)rem));
+            float dt[kK], dx[kK], yv[kK];
+            float sdt = 0.f;
+            {
+                const float Dd = Db[2 * cl], bias = Db[2 * cl + 1];
+                float xf[kK], df[kK];
+                constexpr int V = S::kV;
+#pragma unroll
+                for (int pc = 0; pc < kK / V; ++pc) {
+                    const uint4 xq = *(const uint4 *)&xt[cl * S::kXP + pc * (kLPR * V) + l * V];
+                    const uint4 dq = *(const uint4 *)&dtl[cl * S::kXP + pc * (kLPR * V) + l * V];
+                    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w}, dw[4] = {dq.x, dq.y, dq.z, dq.w};
+#pragma unroll
+                    for (int i = 0; i < V; ++i) {
+                        if constexpr (sizeof(T) == 2) {
+                            xf[pc * V + i] = __uint_as_float(i & 1 ? xw[i >> 1] & 0xFFFF0000u : xw[i >> 1] << 16);
+                            df[pc * V + i] = __uint_as_float(i & 1 ? dw[i >> 1] & 0xFFFF0000u : dw[i >> 1] << 16);
+                        } else {
+                            xf[pc * V + i] = __uint_as_float(xw[i]);
+                            df[pc * V + i] = __uint_as_float(dw[i]);
+                        }
+                    }
+                }
+                if (p.softplus) {
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) dt[j] = softplus(df[j] + bias);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
+                }
+                if (!fast && !(s0 + kCH <= L && ncols == CT)) {
+                    // steps past the sequence end and channels past dim get delta = 0, the
+                    // identity step (staged x there is 0 too)
+                    const float limf = (float)lim;
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) dt[j] *= __saturatef(limf - (float)j);
+                }
+#pragma unroll
+                for (int j = 0; j < kK; ++j) {
+                    dx[j] = dt[j] * xf[j];
+                    yv[j] = Dd * xf[j];
+                    sdt += dt[j];
+                }
+            }
+            if (qq & 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            const float *Bc = Bs + 4 * l;
+            const float *Cc = Cs + 4 * l;
+#pragma unroll 1
+            for (int n = 0; n < kN; n += 2) {
+                const float2 a2 = *(const float2 *)&As[cl * kN + n];
+                float e0[kK], u0[kK], e1[kK], u1[kK];
+                float b0, b1;
+                {
+                    float B0[kK], B1[kK];
+#pragma unroll
+                    for (int pc = 0; pc < 4; ++pc) {
+                        *(float4 *)&B0[4 * pc] = *(const float4 *)&Bc[n * kFP + pc * (kLPR * 4)];
+                        *(float4 *)&B1[4 * pc] = *(const float4 *)&Bc[(n + 1) * kFP + pc * (kLPR * 4)];
+                    }
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) {
+                        e0[j] = __builtin_amdgcn_exp2f(dt[j] * a2.x);
+                        e1[j] = __builtin_amdgcn_exp2f(dt[j] * a2.y);
+                        u0[j] = dx[j] * B0[j];
+                        u1[j] = dx[j] * B1[j];
+                        b0 = j == 0 ? u0[0] : fmaf(e0[j], b0, u0[j]);  // from a zero state
+                        b1 = j == 0 ? u1[0] : fmaf(e1[j], b1, u1[j]);
+                    }
+                }
+                float a0 = __builtin_amdgcn_exp2f(a2.x * sdt);
+                float a1 = __builtin_amdgcn_exp2f(a2.y * sdt);
+                // the previous chunk's end state of this channel enters through its first lane
+                const float2 cy = *(const float2 *)&Cy[cl * kN + n];
+                float h0 = cy.x, h1 = cy.y;
+                b0 = fmaf(a0, h0 * firstf, b0);
+                b1 = fmaf(a1, h1 * firstf, b1);
+                scan16x2(b0, b1, a0, a1, h0, h1);
+                // the last lane of a channel holds the chunk's end state: the next chunk's carry
+                if (l == kLPR - 1) *(float2 *)&Cy[cl * kN + n] = make_float2(b0, b1);
+                float C0[kK], C1[kK];
+#pragma unroll
+                for (int pc = 0; pc < 4; ++pc) {
+                    *(float4 *)&C0[4 * pc] = *(const float4 *)&Cc[n * kFP + pc * (kLPR * 4)];
+                    *(float4 *)&C1[4 * pc] = *(const float4 *)&Cc[(n + 1) * kFP + pc * (kLPR * 4)];
+                }
+#pragma unroll
+                for (int j = 0; j < kK; ++j) {
+                    h0 = fmaf(e0[j], h0, u0[j]);
+                    h1 = fmaf(e1[j], h1, u1[j]);
+                    yv[j] = fmaf(C0[j], h0, yv[j]);
+                    yv[j] = fmaf(C1[j], h1, yv[j]);
+                }
+            }
+            __builtin_amdgcn_s_setprio(2);
+            if constexpr (!S::kYOwn) lds_barrier();  // x/delta tiles fully read before y reuses their space
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc)
+                *(float4 *)&yt[cl * kFP + pc * (kLPR * 4) + 4 * l] =
+                    make_float4(yv[4 * pc], yv[4 * pc + 1], yv[4 * pc + 2], yv[4 * pc + 3]);
+            lds_barrier();
+            // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int sl = so + 128 * r;
+                float v[8], wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if constexpr (fast) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
+                    if (k > 0) load_f8(p.ws + ooff[r], 8, true, wv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                    if (last) {
+                        if (z) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                        }
+                        store8(y + ooff[r], 8, true, v);
+                    } else {
+                        store8(p.ws + ooff[r], 8, true, v);
+                    }
+                } else if (nv > 0 && s0 + sl < L) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
+                    if (k > 0) load_f8(p.ws + ooff[r], nv, vec, wv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                    if (last) {
+                        if (z) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                        }
+                        store8(y + ooff[r], nv, vec, v);
+                    } else {
+                        store8(p.ws + ooff[r], nv, vec, v);
+                    }
+                }
+            }
+        };
+        fetch(0, BoolC<false>{});
+        const int nfast = tile_fast ? (int)(L / kCH) - 1 : 0;
+        int q = 0;
+        for (; q < nfast; ++q, ++qq) chunk(q, BoolC<true>{});
+        for (; q < nchunks; ++q, ++qq) chunk(q, BoolC<false>{});
+    }
+    if (p.hlast) {
+        // the last chunk's carry is the state after step L-1 (steps past L are identity steps)
+        lds_barrier();
+        for (int i = tid; i < CT * kN; i += 256) {
+            const int ch = i / kN, n = i % kN;
+            if (c0 + ch < dim) p.hlast[((int64_t)b * dim + c0 + ch) * kN + n] = Cy[i];
+        }
+    }
+}
+
+template <typename T, int KIND>
+int launch_tiles(const Params &a, int64_t batch, void *stream) {
+    Params c = a;
+    c.ntc = (int)((a.dim + kTC - 1) / kTC);
+    const int64_t blocks = batch * (int64_t)c.ntc;
+    if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    void *args[] = {&c};
+    hipError_t e = hipLaunchKernel((const void *)&selscan_chunked<T, KIND>, dim3((unsigned)blocks), dim3(256),
+                                   args, 0, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        record_hip_error(e);
+        return SELSCAN_E_HIP;
+    }
+    return SELSCAN_OK;
+}
+
+template <typename T>
+int launch_kind(const Params &a, int kind, int64_t batch, void *stream) {
+    if (kind == SELSCAN_OP_FWD) return launch_tiles<T, SELSCAN_OP_FWD>(a, batch, stream);
+    if (kind == SELSCAN_OP_BIDIR) return launch_tiles<T, SELSCAN_OP_BIDIR>(a, batch, stream);
+    if (kind == SELSCAN_OP_SS2D) return launch_tiles<T, SELSCAN_OP_SS2D>(a, batch, stream);
+    return launch_tiles<T, SELSCAN_OP_LOCAL_SS2D>(a, batch, stream);
+}
+
+int launch(const Problem &p, void *stream) {
+    Params a;
+    a.x = p.x, a.delta = p.delta, a.B = p.B, a.C = p.C, a.z = p.z;
+    a.A = p.A, a.D = p.D, a.bias = p.bias, a.y = p.y;
+    a.ws = p.ndir > 1 ? (float *)p.ws : nullptr;
+    a.h0 = p.h0, a.hlast = p.hlast, a.ckpt = p.ckpt;
+    a.dim = p.dim;
+    set_order(a, p.kind, p.L, p.H, p.W, p.win);
+    a.batch = (int)p.batch, a.ndir = p.ndir;
+    a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
+    // rows of 8 channels move as 16-byte vectors when every row start is 16-byte aligned
+    const void *rows[] = {p.x, p.delta, p.z, p.y};
+    bool vec = p.dim % 8 == 0 && (!a.ws || aligned(a.ws, 16));
+    for (const void *q : rows)
+        if (q && !aligned(q, 16)) vec = false;
+    a.vec = vec;
+    a.vecbc = aligned(p.B, 16) && aligned(p.C, 16);
+    a.ntc = 0;
+    if (p.dtype == SELSCAN_BF16) return launch_kind<uint16_t>(a, p.kind, p.batch, stream);
+    return launch_kind<float>(a, p.kind, p.batch, stream);
+}
+
+int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {
+    int rc = validate(p, dstate, ws_bytes);
+    if (rc != SELSCAN_OK) return rc;
+    if (p.batch == 0 || p.dim == 0 || (p.L == 0 && !p.hlast)) return SELSCAN_OK;
+    if (p.batch > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    return launch(p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int selscan_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+                const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t seqlen,
+                int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, seqlen, dim, 0, 0, 1, SELSCAN_OP_FWD,
+              io_dtype, flags};
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+int selscan_fwd_state(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                      const float *h0, float *h_last, float *chunk_states, int64_t batch, int64_t seqlen,
+                      int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, seqlen, dim, 0, 0, 1, SELSCAN_OP_FWD,
+              io_dtype, flags, h0, h_last, chunk_states};
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+int selscan_bidir_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                      int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, seqlen, dim, 0, 0, 2, SELSCAN_OP_BIDIR,
+              io_dtype, flags};
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+int ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+             const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H, int64_t W,
+             int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (H < 0 || W < 0) return SELSCAN_E_SHAPE;
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, H * W, dim, H, W, 4, SELSCAN_OP_SS2D,
+              io_dtype, flags};
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+int local_ss2d_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,
+                   const void *z, const float *delta_bias, unsigned flags, void *y, int64_t batch, int64_t H,
+                   int64_t W, int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (H < 0 || W < 0) return SELSCAN_E_SHAPE;
+    Problem p{x, delta, B, C, z, A, D, delta_bias, y, workspace, batch, H * W, dim, H, W, 4, SELSCAN_OP_LOCAL_SS2D,
+              io_dtype, flags};
+    p.win = window;
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,
+                               int io_dtype) {
+    (void)dstate;
+    (void)io_dtype;
+    if (batch <= 0 || seqlen_or_hw <= 0 || dim <= 0) return 0;
+    if (op != SELSCAN_OP_FWD && op != SELSCAN_OP_BIDIR && op != SELSCAN_OP_SS2D && op != SELSCAN_OP_LOCAL_SS2D)
+        return 0;
+    return workspace_bytes_for(op, batch, seqlen_or_hw, dim);
+}
+
+size_t selscan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || dstate != kN) return 0;
+    return ckpt_bytes_for(batch, seqlen, dim);
+}
+
+int selscan_scan_fwd(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                     float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W, int64_t window,
+                     int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    int64_t L;
+    int ndir;
+    const int rc = resolve_op(op, seqlen, H, W, &L, &ndir);
+    if (rc != SELSCAN_OK) return rc;
+    const bool two_d = op == SELSCAN_OP_SS2D || op == SELSCAN_OP_LOCAL_SS2D;
+    Problem p{x,     delta, B, C, z, A, D, delta_bias, y, workspace, batch, L, dim, two_d ? H : 0, two_d ? W : 0,
+              ndir,  op,    io_dtype, flags};
+    p.ckpt = chunk_states;
+    p.win = op == SELSCAN_OP_LOCAL_SS2D ? window : 0;
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+    const int ndir = ndir_of(op);
+    if (ndir == 0 || batch <= 0 || seqlen <= 0 || dim <= 0 || dstate != kN) return 0;
+    return (size_t)ndir * ckpt_bytes_for(batch, seqlen, dim);
+}
+
+const char *selscan_status_str(int status) {
+    switch (status) {
+        case SELSCAN_OK: return "ok";
+        case SELSCAN_E_NULL: return "a required pointer is NULL";
+        case SELSCAN_E_SHAPE: return "a size is negative";
+        case SELSCAN_E_ALIGN: return "a pointer is not aligned to its element size";
+        case SELSCAN_E_ALIAS: return "the output overlaps an input or the workspace";
+        case SELSCAN_E_UNSUPPORTED: return "unsupported dstate, dtype, flag or size";
+        case SELSCAN_E_WORKSPACE: return "workspace missing or too small";
+        case SELSCAN_E_HIP: return "the HIP runtime rejected the kernel launch";
+        default: return "unknown status";
+    }
+}
+
+int selscan_abi_version(void) { return SELSCAN_ABI_VERSION; }
+
+const char *selscan_last_hip_error(void) { return selscan_rt::g_last_hip_error; }
+
+}  // extern "C"
