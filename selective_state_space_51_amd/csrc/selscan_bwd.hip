@@ -66,6 +66,7 @@ struct BwdLds {
     static constexpr int kDD = kDb + kTC * 8;               // dD, dbias accumulated [ch][2]
     static constexpr int kRed = kDD + kTC * 8;              // channel sums of dB, dC: fp32 [2][4 waves][256]
     static constexpr int kBytes = kRed + 2 * 4 * kCH * 4;
+    static_assert(kTC * kFP * 4 <= 2 * kIo, "an fp32 output tile fits in the x and delta tiles");
     __device__ static int xpos(int s) { return ((s & 15) / kV) * (kLPR * kV) + (s >> 4) * kV + (s % kV); }
 };
 
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
     float *Db = (float *)(smem + S::kDb);
     float *dDs = (float *)(smem + S::kDD);
     float *red = (float *)(smem + S::kRed);
+    float *Os = (float *)(smem + S::kX);  // third output tile (x and delta space)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l = lane & 15, row = lane >> 4;
     const int cl = wave * 4 + row;
@@ -213,82 +215,91 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
         }
     }
 
+    // global -> registers for chunk q: x, delta, dy, z rows of steps 2p, 2p+1 (8 channels each),
+    // the B and C rows of one step, the chunk's entry state.  (Not issued a chunk ahead: the
+    // state loop holds every register, and a load kept in flight across it would be waited
+    // for by the first spill reload after it.)
+    Raw8<T> r0[4], r1[4];
+    uint32_t pbc[2][NW];
+    float hck;
+    auto fetch = [&](int q) {
+        const int64_t s0 = (int64_t)q * kCH;
+        const int64_t sa = s0 + 2 * pp, sbb = sa + 1;
+        const T *src[4] = {x, dl, dy, z};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            r0[m] = r1[m] = Raw8<T>{};
+            if (!src[m]) continue;
+            if (nv > 0 && sa < L) r0[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sa)) * dim + cg, nv, vec);
+            if (nv > 0 && sbb < L) r1[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sbb)) * dim + cg, nv, vec);
+        }
+#pragma unroll
+        for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
+        const int64_t s = s0 + sb;
+        if (s < L) {
+            const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
+            if (p.vecbc) {
+#pragma unroll
+                for (int h = 0; h < NW; h += 4) {
+                    const uint4 qb = *(const uint4 *)((const uint32_t *)(Bg + ro) + h);
+                    const uint4 qc = *(const uint4 *)((const uint32_t *)(Cg + ro) + h);
+                    pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                    pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                }
+            } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int h = 0; h < NW; ++h) {
+                    pbc[0][h] = (uint32_t)Bg[ro + 2 * h] | ((uint32_t)Bg[ro + 2 * h + 1] << 16);
+                    pbc[1][h] = (uint32_t)Cg[ro + 2 * h] | ((uint32_t)Cg[ro + 2 * h + 1] << 16);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < NW; ++h) {
+                    pbc[0][h] = __float_as_uint(Bg[ro + h]);
+                    pbc[1][h] = __float_as_uint(Cg[ro + h]);
+                }
+            }
+        }
+        const int ch = tid / kN, n = tid % kN;
+        hck = c0 + ch < dim ? p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] : 0.f;
+    };
+    auto commit = [&]() {
+        const int si = S::xpos(2 * pp);
+        T *dst[4] = {xt, dtl, dyt, zt};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ch = 8 * g + e;
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t sel = e & 1 ? 0x07060302u : 0x05040100u;
+                    *(uint32_t *)&dst[m][ch * S::kXP + si] = __builtin_amdgcn_perm(r1[m].w[e >> 1], r0[m].w[e >> 1], sel);
+                } else {
+                    *(uint2 *)&dst[m][ch * S::kXP + si] = make_uint2(r0[m].w[e], r1[m].w[e]);
+                }
+            }
+        }
+        const int sp = fpos(sb);
+#pragma unroll
+        for (int h = 0; h < kN; ++h) {
+            float bv, cv;
+            if constexpr (sizeof(T) == 2) {
+                bv = __uint_as_float(h & 1 ? pbc[0][h >> 1] & 0xFFFF0000u : pbc[0][h >> 1] << 16);
+                cv = __uint_as_float(h & 1 ? pbc[1][h >> 1] & 0xFFFF0000u : pbc[1][h >> 1] << 16);
+            } else {
+                bv = __uint_as_float(pbc[0][h]);
+                cv = __uint_as_float(pbc[1][h]);
+            }
+            Bs[h * kFP + sp] = bv;
+            Cs[h * kFP + sp] = cv;
+        }
+        Hc[tid] = hck;
+    };
     for (int q = nchunks - 1; q >= 0; --q) {
         const int64_t s0 = (int64_t)q * kCH;
+        fetch(q);
         lds_barrier();  // the previous (later) chunk is done with every tile
-        // ---- stage x, delta, dy, z (io) and B, C (fp32); the chunk's entry state
-        {
-            Raw8<T> r0[4], r1[4];
-            const int64_t sa = s0 + 2 * pp, sbb = sa + 1;
-            const T *src[4] = {x, dl, dy, z};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                r0[m] = r1[m] = Raw8<T>{};
-                if (!src[m]) continue;
-                if (nv > 0 && sa < L) r0[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sa)) * dim + cg, nv, vec);
-                if (nv > 0 && sbb < L) r1[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sbb)) * dim + cg, nv, vec);
-            }
-            uint32_t pbc[2][NW];
-#pragma unroll
-            for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
-            const int64_t s = s0 + sb;
-            if (s < L) {
-                const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
-                if (p.vecbc) {
-#pragma unroll
-                    for (int h = 0; h < NW; h += 4) {
-                        const uint4 qb = *(const uint4 *)((const uint32_t *)(Bg + ro) + h);
-                        const uint4 qc = *(const uint4 *)((const uint32_t *)(Cg + ro) + h);
-                        pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
-                        pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
-                    }
-                } else if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                    for (int h = 0; h < NW; ++h) {
-                        pbc[0][h] = (uint32_t)Bg[ro + 2 * h] | ((uint32_t)Bg[ro + 2 * h + 1] << 16);
-                        pbc[1][h] = (uint32_t)Cg[ro + 2 * h] | ((uint32_t)Cg[ro + 2 * h + 1] << 16);
-                    }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < NW; ++h) {
-                        pbc[0][h] = __float_as_uint(Bg[ro + h]);
-                        pbc[1][h] = __float_as_uint(Cg[ro + h]);
-                    }
-                }
-            }
-            const int si = S::xpos(2 * pp);
-            T *dst[4] = {xt, dtl, dyt, zt};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int ch = 8 * g + e;
-                    if constexpr (sizeof(T) == 2) {
-                        const uint32_t sel = e & 1 ? 0x07060302u : 0x05040100u;
-                        *(uint32_t *)&dst[m][ch * S::kXP + si] = __builtin_amdgcn_perm(r1[m].w[e >> 1], r0[m].w[e >> 1], sel);
-                    } else {
-                        *(uint2 *)&dst[m][ch * S::kXP + si] = make_uint2(r0[m].w[e], r1[m].w[e]);
-                    }
-                }
-            }
-            const int sp = fpos(sb);
-#pragma unroll
-            for (int h = 0; h < kN; ++h) {
-                float bv, cv;
-                if constexpr (sizeof(T) == 2) {
-                    bv = __uint_as_float(h & 1 ? pbc[0][h >> 1] & 0xFFFF0000u : pbc[0][h >> 1] << 16);
-                    cv = __uint_as_float(h & 1 ? pbc[1][h >> 1] & 0xFFFF0000u : pbc[1][h >> 1] << 16);
-                } else {
-                    bv = __uint_as_float(pbc[0][h]);
-                    cv = __uint_as_float(pbc[1][h]);
-                }
-                Bs[h * kFP + sp] = bv;
-                Cs[h * kFP + sp] = cv;
-            }
-            const int ch = tid / kN, n = tid % kN;
-            Hc[tid] = c0 + ch < dim ? p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n]
-                                    : 0.f;
-        }
+        commit();
         lds_barrier();
 
         // ---- this lane's 16 steps of its channel
@@ -432,8 +443,9 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
             lds_barrier();
         }
 
-        // ---- per (step, channel) derivatives: dx, ddelta, dz
-        float o0[kK], o1[kK], o2[kK];
+        // ---- per (step, channel) derivatives: dx, ddelta, and dz (or, with several directions,
+        // this direction's output); they leave through three fp32 tiles: B, C (free after the
+        // state loop) and the x/delta space (free once every wave has read it below)
         float dbl = 0.f;
         {
             float xf[kK], df[kK], yf[kK], zf[kK];
@@ -455,22 +467,32 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                     }
                 }
             }
+            lds_barrier();  // every wave has read x and delta: their space takes the third tile
 #pragma unroll
-            for (int j = 0; j < kK; ++j) {
-                float ddt = fmaf(xf[j], accx[j], accdd[j]);
-                if (p.softplus) ddt *= sigmoidf_(df[j] + bias);
-                ddt = j < lim ? ddt : 0.f;
-                o0[j] = dt[j] * accx[j] + Dd * dyp[j];  // dx
-                o1[j] = ddt;                            // d(delta)
-                if constexpr (multi) {
-                    o2[j] = yv[j];  // this direction's output; dz waits for the sum over directions
-                } else if (z) {
-                    const float sg = sigmoidf_(zf[j]);
-                    o2[j] = yf[j] * yv[j] * sg * (1.f + zf[j] * (1.f - sg));
-                } else {
-                    o2[j] = 0.f;
+            for (int pc = 0; pc < 4; ++pc) {
+                float o0[4], o1[4], o2[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 4 * pc + i;
+                    float ddt = fmaf(xf[j], accx[j], accdd[j]);
+                    if (p.softplus) ddt *= sigmoidf_(df[j] + bias);
+                    ddt = j < lim ? ddt : 0.f;
+                    o0[i] = dt[j] * accx[j] + Dd * dyp[j];  // dx
+                    o1[i] = ddt;                            // d(delta)
+                    if constexpr (multi) {
+                        o2[i] = yv[j];  // this direction's output; dz waits for the sum over directions
+                    } else if (z) {
+                        const float sg = sigmoidf_(zf[j]);
+                        o2[i] = yf[j] * yv[j] * sg * (1.f + zf[j] * (1.f - sg));
+                    } else {
+                        o2[i] = 0.f;
+                    }
+                    dbl += ddt;
                 }
-                dbl += ddt;
+                const int o = cl * kFP + pc * (kLPR * 4) + 4 * l;
+                *(float4 *)&Bs[o] = make_float4(o0[0], o0[1], o0[2], o0[3]);
+                *(float4 *)&Cs[o] = make_float4(o1[0], o1[1], o1[2], o1[3]);
+                *(float4 *)&Os[o] = make_float4(o2[0], o2[1], o2[2], o2[3]);
             }
         }
         dDl = rowsum16(dDl);
@@ -479,32 +501,26 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
             dDs[2 * cl] += dDl;
             dDs[2 * cl + 1] += dbl;
         }
-        // out through the B and C tiles (free after the state loop): dx and ddelta, then dz
+        lds_barrier();
+        const bool want_z = z && p.dz;
 #pragma unroll
-        for (int round = 0; round < 2; ++round) {
-            if (round == 1 && !(z && p.dz)) break;
+        for (int r = 0; r < 2; ++r) {
+            const int sl = so + 128 * r;
+            const int64_t s = s0 + sl;
+            if (nv <= 0 || s >= L) continue;
+            const int64_t off = (rowb + visit<KIND>(p, k, s)) * dim + cg;
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc) {
-                const float *va = round == 0 ? o0 : o2;
-                *(float4 *)&Bs[cl * kFP + pc * (kLPR * 4) + 4 * l] =
-                    make_float4(va[4 * pc], va[4 * pc + 1], va[4 * pc + 2], va[4 * pc + 3]);
-                if (round == 0)
-                    *(float4 *)&Cs[cl * kFP + pc * (kLPR * 4) + 4 * l] =
-                        make_float4(o1[4 * pc], o1[4 * pc + 1], o1[4 * pc + 2], o1[4 * pc + 3]);
-            }
-            lds_barrier();
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int sl = so + 128 * r;
-                const int64_t s = s0 + sl;
-                if (nv <= 0 || s >= L) continue;
-                const int64_t off = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+            for (int round = 0; round < 3; ++round) {
+                if (round == 2 && !want_z) break;
+                const float *tile = round == 0 ? Bs : (round == 1 ? Cs : Os);
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = Bs[(8 * g + e) * kFP + fpos(sl)];
-                if constexpr (multi) {
+                for (int e = 0; e < 8; ++e) v[e] = tile[(8 * g + e) * kFP + fpos(sl)];
+                if (round == 1) {
+                    store8((T *)p.ddelta + k * tok + off, nv, vec, v);
+                } else if constexpr (multi) {
                     // add the earlier directions' sum; keep it, or finish dx / dz
-                    float* acc = round == 0 ? p.wsX : p.wsY;
+                    float *acc = round == 0 ? p.wsX : p.wsY;
                     if (k > 0) {
                         float w8[8];
                         load_f8(acc + off, nv, vec, w8);
@@ -529,13 +545,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                 } else {
                     store8((T *)(round == 0 ? p.dx : p.dz) + off, nv, vec, v);
                 }
-                if (round == 0) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = Cs[(8 * g + e) * kFP + fpos(sl)];
-                    store8((T *)p.ddelta + k * tok + off, nv, vec, v);
-                }
             }
-            lds_barrier();
         }
     }
     lds_barrier();
