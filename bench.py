@@ -34,6 +34,10 @@ FLOP_EQ_PER_ELEMENT = 16
 # e*g) and the step's derivatives (e*h_prev, its product with g, dA, ddelta, sum g*u, sum g*B,
 # g*(delta*x) for dB, dyp*h for dC): 1 exp2 + 15 fp32 ops = 19 FMA slots = 38 flop-equivalents.
 FLOP_EQ_PER_ELEMENT_BWD = 38
+# Zero-order-hold forward: the input factor phi(delta A) = expm1(delta A) / (delta A) adds, per element,
+# y = t ln2, a 4-FMA series, e - 1, one reciprocal (4 FMA slots), a product, the switch (compare +
+# select) and the factor's product: 13 slots over the Euler form's 8 = 21 slots = 42 flop-equivalents.
+FLOP_EQ_PER_ELEMENT_ZOH = 42
 METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
@@ -127,6 +131,8 @@ def main() -> int:
     ap.add_argument("--state", action="store_true",
                     help="single-direction workloads: run selscan_fwd_state with an initial state and the "
                          "final state written (recurrent / chunked inference)")
+    ap.add_argument("--zoh", action="store_true",
+                    help="forward with the zero-order-hold Bbar (SELSCAN_FLAG_ZOH) instead of delta * B")
     ap.add_argument("--cpu-channels", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (a plain copy of known size, for scaling "
@@ -166,6 +172,9 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.zoh and args.pass_ == "bwd":
+        print("--zoh applies to the forward only", file=sys.stderr)
+        return 2
     if args.state and w.kind != "selscan":
         print("--state applies to single-direction workloads only", file=sys.stderr)
         return 2
@@ -190,19 +199,19 @@ def main() -> int:
                                workspace=bws, stream=stream, **geo)
         elif args.state:
             S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, h0=h0,
-                                h_last=hl, workspace=ws, stream=stream)
+                                h_last=hl, workspace=ws, zoh=args.zoh, stream=stream)
         elif w.kind == "selscan":
             S.selscan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, workspace=ws,
-                          stream=stream)
+                          zoh=args.zoh, stream=stream)
         elif w.kind == "bidir":
             S.selscan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
-                                workspace=ws, stream=stream)
+                                workspace=ws, zoh=args.zoh, stream=stream)
         elif w.kind == "local_ss2d":
             S.local_ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, w.window, D=t["D"], z=t["z"], y=y,
-                             workspace=ws, stream=stream)
+                             workspace=ws, zoh=args.zoh, stream=stream)
         else:
             S.ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, D=t["D"], z=t["z"], y=y,
-                       workspace=ws, stream=stream)
+                       workspace=ws, zoh=args.zoh, stream=stream)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -231,9 +240,10 @@ def main() -> int:
     bwd = args.pass_ == "bwd"
     alg = bwd_algorithmic_bytes(w) if bwd else w.algorithmic_bytes()
     hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
-    flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else FLOP_EQ_PER_ELEMENT
+    flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else (FLOP_EQ_PER_ELEMENT_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT)
     alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name, args.pass_)
+    # the counter record is for the plain call of the pass (no state in/out, Euler Bbar)
+    traffic = None if (args.zoh or args.state) else measured_traffic(w.name, args.pass_)
     out = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
@@ -250,10 +260,11 @@ def main() -> int:
         "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate,
                    "window": w.window or None,
-                   "state_io": bool(args.state), "pass": args.pass_},
+                   "state_io": bool(args.state), "pass": args.pass_, "bbar": "zoh" if args.zoh else "delta*B"},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
                      "work_per_element": ("1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
+                                          "1 exp2 + 1 rcp + 13 fp32 ops = 42 fp32 flop-equivalents" if args.zoh else
                                           "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents"),
                      "kernel": "selscan_bwd_chunked + selscan_bwd_reduce" if bwd else "selscan_chunked",
                      "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),

@@ -12,7 +12,10 @@
  * delta = softplus(W x + b), B and C functions of the input, A a fixed diagonal) and
  * section 关键代码 (the selective_scan call with Ds, delta_bias, delta_softplus; the SiLU
  * gate); "从LSTM到Mamba" §2.1 (the D x skip term).  Bbar is taken as delta * B (the
- * first-order form of the page's zero-order-hold Bbar; equal to it as delta*A -> 0).
+ * first-order form of the page's zero-order-hold Bbar; equal to it as delta*A -> 0); with
+ * SELSCAN_FLAG_ZOH the forward uses the zero-order-hold form itself,
+ *     h_t[n] = exp(delta_t A[d,n]) h_{t-1}[n] + (exp(delta_t A[d,n]) - 1) / A[d,n] * B[b,t,n] x[b,t,d]
+ * (delta_t B where A[d,n] = 0), section 选择性 SSM 的数学形式 of the first page.
  *
  * Conventions shared by every entry point
  *  - Layout: row-major, channels fastest.  Per-token tensors x, delta, z, y are
@@ -37,8 +40,8 @@
  *      SELSCAN_E_ALIGN        a pointer is not aligned to its element size (4 B for fp32
  *                             arrays, 2 B for bf16 arrays)
  *      SELSCAN_E_ALIAS        y overlaps an input array
- *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits, or an
- *                             SS2D map with H*W >= 2^31 pixels
+ *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits (ZOH in a
+ *                             backward call), or an SS2D map with H*W >= 2^31 pixels
  *      SELSCAN_E_WORKSPACE    workspace smaller than selscan_workspace_bytes(...)
  *      SELSCAN_E_HIP          the kernel launch was rejected by the HIP runtime
  *    Non-finite inputs are not checked; they propagate.
@@ -70,6 +73,10 @@ typedef enum {
 
 /* flag bits */
 #define SELSCAN_FLAG_DELTA_SOFTPLUS 1u /* delta_t = softplus(delta + delta_bias) */
+/* forward entry points only: zero-order-hold Bbar = (exp(delta A) - 1) / A * B in place of
+ * delta * B (the page's exact discretisation; see the header comment); the backward entry
+ * points return SELSCAN_E_UNSUPPORTED for it */
+#define SELSCAN_FLAG_ZOH 2u
 
 /* operation codes (scan orders) for selscan_workspace_bytes and the selscan_scan_* calls */
 typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2, SELSCAN_OP_LOCAL_SS2D = 3 } selscan_op;
@@ -81,7 +88,7 @@ typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2, SE
  *   A              : [dim][dstate]            fp32 (real, normally negative)
  *   D, delta_bias  : [dim]                    fp32, nullable
  *   z              : nullable (no gate)
- *   flags          : SELSCAN_FLAG_DELTA_SOFTPLUS or 0
+ *   flags          : SELSCAN_FLAG_DELTA_SOFTPLUS, SELSCAN_FLAG_ZOH (any combination) or 0
  * Writes y only.
  */
 int selscan_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C, const float *D,

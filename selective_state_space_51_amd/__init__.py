@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "selscan.h")
 SELSCAN_F32 = 0
 SELSCAN_BF16 = 1
 SELSCAN_FLAG_DELTA_SOFTPLUS = 1
+SELSCAN_FLAG_ZOH = 2
 SELSCAN_OP_FWD, SELSCAN_OP_BIDIR, SELSCAN_OP_SS2D, SELSCAN_OP_LOCAL_SS2D = 0, 1, 2, 3
 STATUS = {
     0: "SELSCAN_OK", 1: "SELSCAN_E_NULL", 2: "SELSCAN_E_SHAPE", 3: "SELSCAN_E_ALIGN", 4: "SELSCAN_E_ALIAS",
@@ -148,6 +149,10 @@ def _workspace(op, x, bt, L, dim, workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
+def _flags(delta_softplus, zoh=False):
+    return (SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0) | (SELSCAN_FLAG_ZOH if zoh else 0)
+
+
 def _check(rc, what):
     if rc != 0:
         raise SelscanError(rc, what)
@@ -159,7 +164,7 @@ def _shape_check(name, t, shape):
 
 
 def selscan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
-                workspace=None, stream=None):
+                zoh=False, workspace=None, stream=None):
     """y = (sum_n C h + D x) * silu(z) for x, delta, z: [batch, L, dim]; B, C: [batch, L, N]; A: [dim, N]."""
     torch = _torch()
     bt, L, dim = x.shape
@@ -175,7 +180,7 @@ def selscan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softpl
     rc = lib.selscan_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
                          _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                          _ptr(delta_bias, "delta_bias", f32=True),
-                         SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                         _flags(delta_softplus, zoh), _ptr(y, "y", io),
                          bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_fwd")
     return y
@@ -191,7 +196,7 @@ def selscan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int =
 
 
 def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
-                      h0=None, h_last=None, chunk_states=None, workspace=None, stream=None):
+                      h0=None, h_last=None, chunk_states=None, zoh=False, workspace=None, stream=None):
     """selscan_fwd with the state carried in (h0) and out (h_last), both fp32 [batch, dim, N],
     and optionally the chunk states selscan_bwd restarts from.
 
@@ -221,7 +226,7 @@ def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     rc = lib.selscan_fwd_state(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
                                _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                                _ptr(delta_bias, "delta_bias", f32=True),
-                               SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                               _flags(delta_softplus, zoh), _ptr(y, "y", io),
                                _ptr(h0, "h0", f32=True), _ptr(h_last, "h_last", f32=True),
                                _ptr(chunk_states, "chunk_states", f32=True),
                                bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
@@ -272,7 +277,7 @@ def selscan_bwd(x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=
 
 
 def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
-                      workspace=None, stream=None):
+                      zoh=False, workspace=None, stream=None):
     """Bidirectional scan; per-direction arrays stacked on a leading axis of 2 (token order)."""
     torch = _torch()
     bt, L, dim = x.shape
@@ -288,14 +293,14 @@ def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     rc = lib.selscan_bidir_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
                                _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                                _ptr(delta_bias, "delta_bias", f32=True),
-                               SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                               _flags(delta_softplus, zoh), _ptr(y, "y", io),
                                bt, L, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_bidir_fwd")
     return y
 
 
 def ss2d_fwd(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
-             workspace=None, stream=None):
+             zoh=False, workspace=None, stream=None):
     """SS2D four-direction scan with merge; per-direction arrays [4, ...] in pixel (row-major) order."""
     torch = _torch()
     bt, L, dim = x.shape
@@ -313,14 +318,14 @@ def ss2d_fwd(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_sof
     rc = lib.ss2d_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
                       _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                       _ptr(delta_bias, "delta_bias", f32=True),
-                      SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                      _flags(delta_softplus, zoh), _ptr(y, "y", io),
                       bt, H, W, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "ss2d_fwd")
     return y
 
 
 def local_ss2d_fwd(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
-                   workspace=None, stream=None):
+                   zoh=False, workspace=None, stream=None):
     """Windowed four-direction cross-scan (square windows of side ``window``); arrays as for ss2d_fwd."""
     torch = _torch()
     bt, L, dim = x.shape
@@ -338,7 +343,7 @@ def local_ss2d_fwd(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=N
     rc = lib.local_ss2d_fwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
                             _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                             _ptr(delta_bias, "delta_bias", f32=True),
-                            SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                            _flags(delta_softplus, zoh), _ptr(y, "y", io),
                             bt, H, W, window, dim, N, _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "local_ss2d_fwd")
     return y
@@ -369,7 +374,7 @@ def _scan_shapes(op, x, A, H, W):
 
 
 def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, H=0, W=0,
-                     window=0, y=None, chunk_states=None, workspace=None, stream=None):
+                     window=0, y=None, chunk_states=None, zoh=False, workspace=None, stream=None):
     """Forward of any scan order (SELSCAN_OP_*), optionally keeping the chunk states the backward
     restarts from (chunk_states=True allocates them).  Per-direction arrays carry a leading
     direction axis for the multi-direction orders.  Returns y, or (y, chunk_states)."""
@@ -391,7 +396,7 @@ def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, del
     rc = lib.selscan_scan_fwd(op, _ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
                               _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                               _ptr(delta_bias, "delta_bias", f32=True),
-                              SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0, _ptr(y, "y", io),
+                              _flags(delta_softplus, zoh), _ptr(y, "y", io),
                               _ptr(chunk_states, "chunk_states", f32=True), bt, L, H, W, window, dim, N,
                               _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_scan_fwd")

@@ -59,7 +59,7 @@ size_t workspace_bytes_for(int op, int64_t batch, int64_t L, int64_t dim) {
 int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
     if (p.batch < 0 || p.L < 0 || p.dim < 0 || p.H < 0 || p.W < 0 || dstate < 0) return SELSCAN_E_SHAPE;
     if (p.dtype != SELSCAN_F32 && p.dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
-    if (p.flags & ~SELSCAN_FLAG_DELTA_SOFTPLUS) return SELSCAN_E_UNSUPPORTED;
+    if (p.flags & ~(SELSCAN_FLAG_DELTA_SOFTPLUS | SELSCAN_FLAG_ZOH)) return SELSCAN_E_UNSUPPORTED;
     if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
     if ((p.kind == SELSCAN_OP_SS2D || p.kind == SELSCAN_OP_LOCAL_SS2D) &&
         (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
@@ -200,7 +200,20 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
 // Priority: the waves of the two workgroups that share a SIMD run their state loops at
 // priorities that alternate with the chunk count, so neither workgroup starves the other,
 // and every phase outside the state loop runs above both.
-template <typename T, int KIND>
+// Zero-order-hold input factor: Bbar x = (e^y - 1) / A * B x = delta phi(y) B x, with y = delta A,
+// e = e^y and phi(y) = (e^y - 1) / y.  e - 1 from the exp carries its absolute rounding error
+// (about 1e-7), which is a large relative error when |y| is small; there phi comes from its
+// series, 1 + y/2 + y^2/6 + y^3/24 + y^4/120 (truncation below 5e-8 for |y| < 1/8), and
+// elsewhere from (e - 1) / y (relative error about 1e-6 for |y| >= 1/8).  t = y log2(e), the
+// exponent the recurrence's exp2 already takes.
+__device__ __forceinline__ float zoh_phi(float e, float t) {
+    const float y = t * kLn2;
+    const float series = fmaf(y, fmaf(y, fmaf(y, fmaf(y, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
+    const float direct = (e - 1.f) * __builtin_amdgcn_rcpf(y);
+    return fabsf(y) < 0.125f ? series : direct;
+}
+
+template <typename T, int KIND, bool ZOH>
 __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     using S = Lds<T>;
     constexpr int CT = kTC;
@@ -452,10 +465,16 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     }
 #pragma unroll
                     for (int j = 0; j < kK; ++j) {
-                        e0[j] = __builtin_amdgcn_exp2f(dt[j] * a2.x);
-                        e1[j] = __builtin_amdgcn_exp2f(dt[j] * a2.y);
-                        u0[j] = dx[j] * B0[j];
-                        u1[j] = dx[j] * B1[j];
+                        const float t0 = dt[j] * a2.x, t1 = dt[j] * a2.y;
+                        e0[j] = __builtin_amdgcn_exp2f(t0);
+                        e1[j] = __builtin_amdgcn_exp2f(t1);
+                        if constexpr (ZOH) {
+                            u0[j] = dx[j] * zoh_phi(e0[j], t0) * B0[j];
+                            u1[j] = dx[j] * zoh_phi(e1[j], t1) * B1[j];
+                        } else {
+                            u0[j] = dx[j] * B0[j];
+                            u1[j] = dx[j] * B1[j];
+                        }
                         b0 = j == 0 ? u0[0] : fmaf(e0[j], b0, u0[j]);  // from a zero state
                         b1 = j == 0 ? u1[0] : fmaf(e1[j], b1, u1[j]);
                     }
@@ -546,14 +565,14 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 }
 
 template <typename T, int KIND>
-int launch_tiles(const Params &a, int64_t batch, void *stream) {
+int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     Params c = a;
     c.ntc = (int)((a.dim + kTC - 1) / kTC);
     const int64_t blocks = batch * (int64_t)c.ntc;
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&c};
-    hipError_t e = hipLaunchKernel((const void *)&selscan_chunked<T, KIND>, dim3((unsigned)blocks), dim3(256),
-                                   args, 0, (hipStream_t)stream);
+    const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true> : (const void *)&selscan_chunked<T, KIND, false>;
+    hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
     if (e != hipSuccess) {
         record_hip_error(e);
         return SELSCAN_E_HIP;
@@ -562,11 +581,11 @@ int launch_tiles(const Params &a, int64_t batch, void *stream) {
 }
 
 template <typename T>
-int launch_kind(const Params &a, int kind, int64_t batch, void *stream) {
-    if (kind == SELSCAN_OP_FWD) return launch_tiles<T, SELSCAN_OP_FWD>(a, batch, stream);
-    if (kind == SELSCAN_OP_BIDIR) return launch_tiles<T, SELSCAN_OP_BIDIR>(a, batch, stream);
-    if (kind == SELSCAN_OP_SS2D) return launch_tiles<T, SELSCAN_OP_SS2D>(a, batch, stream);
-    return launch_tiles<T, SELSCAN_OP_LOCAL_SS2D>(a, batch, stream);
+int launch_kind(const Params &a, int kind, int64_t batch, bool zoh, void *stream) {
+    if (kind == SELSCAN_OP_FWD) return launch_tiles<T, SELSCAN_OP_FWD>(a, batch, zoh, stream);
+    if (kind == SELSCAN_OP_BIDIR) return launch_tiles<T, SELSCAN_OP_BIDIR>(a, batch, zoh, stream);
+    if (kind == SELSCAN_OP_SS2D) return launch_tiles<T, SELSCAN_OP_SS2D>(a, batch, zoh, stream);
+    return launch_tiles<T, SELSCAN_OP_LOCAL_SS2D>(a, batch, zoh, stream);
 }
 
 int launch(const Problem &p, void *stream) {
@@ -587,8 +606,9 @@ int launch(const Problem &p, void *stream) {
     a.vec = vec;
     a.vecbc = aligned(p.B, 16) && aligned(p.C, 16);
     a.ntc = 0;
-    if (p.dtype == SELSCAN_BF16) return launch_kind<uint16_t>(a, p.kind, p.batch, stream);
-    return launch_kind<float>(a, p.kind, p.batch, stream);
+    const bool zoh = (p.flags & SELSCAN_FLAG_ZOH) != 0;
+    if (p.dtype == SELSCAN_BF16) return launch_kind<uint16_t>(a, p.kind, p.batch, zoh, stream);
+    return launch_kind<float>(a, p.kind, p.batch, zoh, stream);
 }
 
 int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {

@@ -49,7 +49,7 @@ def f64(a, dtype):
 
 
 def run_gpu(kind: str, inp: dict, dtype: str, H=0, Wd=0, softplus=False, use_D=True, use_z=True, use_bias=False,
-            stream=None, window=0):
+            stream=None, window=0, zoh=False):
     import selective_state_space_51_amd as S
     x = to_dev(inp["x"], dtype)
     delta = to_dev(inp["w"] if softplus else inp["delta"], dtype)
@@ -60,20 +60,22 @@ def run_gpu(kind: str, inp: dict, dtype: str, H=0, Wd=0, softplus=False, use_D=T
     z = to_dev(inp["z"], dtype) if (use_z and inp.get("z") is not None) else None
     bias = to_dev(inp["delta_bias"], "f32") if use_bias else None
     if kind == "selscan":
-        y = S.selscan_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus, stream=stream)
+        y = S.selscan_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus, zoh=zoh,
+                          stream=stream)
     elif kind == "bidir":
-        y = S.selscan_bidir_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus,
+        y = S.selscan_bidir_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus, zoh=zoh,
                                 stream=stream)
     elif kind == "local_ss2d":
         y = S.local_ss2d_fwd(x, delta, A, B, C, H, Wd, window, D=D, z=z, delta_bias=bias, delta_softplus=softplus,
-                             stream=stream)
+                             zoh=zoh, stream=stream)
     else:
-        y = S.ss2d_fwd(x, delta, A, B, C, H, Wd, D=D, z=z, delta_bias=bias, delta_softplus=softplus, stream=stream)
+        y = S.ss2d_fwd(x, delta, A, B, C, H, Wd, D=D, z=z, delta_bias=bias, delta_softplus=softplus, zoh=zoh,
+                       stream=stream)
     return y
 
 
 def run_oracle(kind: str, inp: dict, dtype: str, H=0, Wd=0, softplus=False, use_D=True, use_z=True,
-               use_bias=False, channels=None, window=0):
+               use_bias=False, channels=None, window=0, zoh=False):
     """Oracle on the same values; ``channels`` restricts it to a subset of channels (the scan
     is independent per channel), returning y[..., channels]."""
     sel = slice(None) if channels is None else np.asarray(channels)
@@ -92,10 +94,10 @@ def run_oracle(kind: str, inp: dict, dtype: str, H=0, Wd=0, softplus=False, use_
     C = f64(inp["C"], dtype)
     del lead
     if kind == "selscan":
-        return oracle.selscan(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus)
+        return oracle.selscan(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus, zoh=zoh)
     if kind == "bidir":
-        return oracle.selscan_bidir(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus)
+        return oracle.selscan_bidir(x, delta, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=softplus, zoh=zoh)
     if kind == "local_ss2d":
         return oracle.local_ss2d(x, delta, A, B, C, H, Wd, window, D=D, z=z, delta_bias=bias,
-                                 delta_softplus=softplus)
-    return oracle.ss2d(x, delta, A, B, C, H, Wd, D=D, z=z, delta_bias=bias, delta_softplus=softplus)
+                                 delta_softplus=softplus, zoh=zoh)
+    return oracle.ss2d(x, delta, A, B, C, H, Wd, D=D, z=z, delta_bias=bias, delta_softplus=softplus, zoh=zoh)

@@ -424,3 +424,43 @@ def test_local_ss2d_shapes(H, Wd, win, dim):
     _say("local", H, Wd, win, dim)
     inp = W.generate(w)
     _check("local_ss2d", w, inp, H=H, Wd=Wd, window=win)
+
+
+# ----------------------------------------------------------------------------- zero-order hold
+@pytest.mark.parametrize("kind,dtype,batch,L,dim,H,Wd,win", [
+    ("selscan", "f32", 2, 700, 40, 0, 0, 0),
+    ("selscan", "bf16", 2, 1100, 64, 0, 0, 0),
+    ("bidir", "f32", 2, 197, 24, 0, 0, 0),
+    ("ss2d", "f32", 2, 90, 16, 9, 10, 0),
+    ("local_ss2d", "bf16", 1, 144, 24, 12, 12, 3),
+], ids=lambda v: str(v))
+def test_zoh_against_oracle(kind, dtype, batch, L, dim, H, Wd, win):
+    """SELSCAN_FLAG_ZOH against the oracle's zero-order-hold mode.  delta*A spans both sides of
+    the kernel's series / direct switch at |delta A| = 1/8 (A = -(n+1), delta in [1e-3, 1e-1]);
+    channel 0 also gets A = 0 (Bbar = delta B), tiny |A| and a positive A."""
+    w = W.Workload("zoh", kind, batch, L, dim, 16, dtype, True, H=H, W=Wd, index=15, window=win)
+    inp = W.generate(w, with_w=True, with_bias=True)
+    A = inp["A"].copy()
+    A[..., 0, :4] = [0.0, -1e-4, -3e-3, 0.2]
+    inp["A"] = A
+    for softplus in (False, True):
+        _say("zoh", kind, dtype, batch, L, dim, (H, Wd, win), "softplus", softplus)
+        _check(kind, w, inp, H=H, Wd=Wd, window=win, zoh=True, softplus=softplus, use_bias=softplus)
+
+
+def test_zoh_changes_only_the_input_factor():
+    """With A = 0 everywhere the zero-order-hold and Euler forms coincide (Bbar = delta B, e = 1):
+    the two kernels give the same y bit for bit."""
+    import torch
+    import selective_state_space_51_amd as S
+    w = W.Workload("zoh0", "selscan", 2, 600, 32, 16, "bf16", True, index=16)
+    inp = W.generate(w)
+    dev = lambda a, dt="bf16": PT.to_dev(a, dt)
+    A = torch.zeros(32, 16, device="cuda")
+    args = (dev(inp["x"]), dev(inp["delta"]), A, dev(inp["B"]), dev(inp["C"]))
+    kw = dict(D=dev(inp["D"], "f32"), z=dev(inp["z"]))
+    y0 = S.selscan_fwd(*args, **kw)
+    y1 = S.selscan_fwd(*args, zoh=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
