@@ -62,6 +62,10 @@ def load(path: Optional[str] = None):
     lib.oracle_selscan_bwd.restype = ci
     lib.oracle_scan_order.argtypes = [ci, ci, i64, i64, i64, i64, dp]
     lib.oracle_scan_order.restype = ci
+    lib.oracle_causal_conv1d.argtypes = [dp, dp, dp, dp, dp, ci, dp, i64, i64, i64, i64]
+    lib.oracle_causal_conv1d.restype = ci
+    lib.oracle_dwconv2d.argtypes = [dp, dp, dp, ci, dp, i64, i64, i64, i64, i64]
+    lib.oracle_dwconv2d.restype = ci
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ci
     if path is None:
@@ -251,5 +255,57 @@ def multi_bwd(kind, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delt
             out["ddelta_bias"][k] = g["ddelta_bias"]
     if z is not None:
         out["dz"] = dy * yp * sg * (1.0 + z * (1.0 - sg))
+    return out
+
+
+def ordered_scan(x, delta, A, B, C, orders, D=None, z=None, delta_bias=None, delta_softplus=False, zoh=False,
+                 nthreads=0, lib=None):
+    """Scans along explicit visiting orders, merged: y = (sum_k scatter_k(scan(gather_k(...)))) * silu(z).
+
+    orders[k][l] is the token direction k visits at step l (each a permutation of range(L));
+    per-direction arrays carry a leading axis of len(orders), in token order.  Each direction is
+    oracle_selscan on its gathered sequence (no gate); the gate multiplies the merged sum.  This
+    is the definition the fixed orders (bidirectional, SS2D, windowed) instantiate."""
+    lib = lib or load()
+    x, delta, A, B, C, D, z, delta_bias = map(_f64, (x, delta, A, B, C, D, z, delta_bias))
+    out = np.zeros_like(x)
+    for k, o in enumerate(orders):
+        o = np.asarray(o, dtype=np.int64)
+        yk = selscan(x[:, o], delta[k][:, o], A[k], B[k][:, o], C[k][:, o], D=None if D is None else D[k],
+                     delta_bias=None if delta_bias is None else delta_bias[k], delta_softplus=delta_softplus,
+                     zoh=zoh, nthreads=nthreads, lib=lib)
+        out[:, o] += yk
+    if z is not None:
+        out *= z / (1.0 + np.exp(-z))
+    return out
+
+
+def causal_conv1d(x, w, bias=None, state=None, silu=True, want_state=False, lib=None):
+    """Causal depthwise 1-D convolution (+ SiLU) over [batch, L, dim]; w [dim, K]; state
+    [batch, K-1, dim] (the K-1 input rows before the sequence).  Returns out, or (out, state_out)."""
+    lib = lib or load()
+    x, w, bias, state = map(_f64, (x, w, bias, state))
+    bt, L, dim = x.shape
+    K = w.shape[1]
+    out = np.empty_like(x)
+    st = np.empty((bt, K - 1, dim)) if want_state else None
+    rc = lib.oracle_causal_conv1d(_ptr(x), _ptr(w), _ptr(bias), _ptr(state), _ptr(st), int(bool(silu)), _ptr(out),
+                                  bt, L, dim, K)
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d: bad arguments")
+    return (out, st) if want_state else out
+
+
+def dwconv2d(x, w, H, W, bias=None, silu=True, lib=None):
+    """Depthwise ks x ks cross-correlation (+ SiLU), zero padding (ks-1)/2, over [batch, H*W, dim]
+    channels-last maps; w [dim, ks, ks]."""
+    lib = lib or load()
+    x, w, bias = map(_f64, (x, w, bias))
+    bt, L, dim = x.shape
+    assert L == H * W
+    out = np.empty_like(x)
+    rc = lib.oracle_dwconv2d(_ptr(x), _ptr(w), _ptr(bias), int(bool(silu)), _ptr(out), bt, H, W, dim, w.shape[-1])
+    if rc != 0:
+        raise ValueError("oracle_dwconv2d: bad arguments")
     return out
 

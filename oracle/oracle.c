@@ -356,6 +356,80 @@ int oracle_scan_order(int kind, int k, int64_t H, int64_t W, int64_t win, int64_
     return 0;
 }
 
+/* ---------------------------------------------------------------------------------
+ * The convolution in front of the scan.
+ *  [MS] "Mamba Series ...", section 方法设计 (architecture diagram): in the Mamba block the
+ *       scan's input branch is Linear -> Conv1D(k=4) -> SiLU -> SSM; in the VSS block it is
+ *       Linear -> DWConv 3x3 -> SiLU -> SS2D (also SS2Dv0.forwardv0 in section 关键代码:
+ *       conv2d, then act).
+ * Readings (the pages give only the kernel sizes): the 1-D convolution is depthwise (one
+ * filter per channel, as the 2-D one is named) and causal, the output at step t seeing
+ * inputs t-(K-1) .. t with zeros (or a carried state) before the sequence; the 2-D one keeps
+ * the map size (zero padding (ks-1)/2, stride 1) and, like the framework layers the code
+ * calls, is a cross-correlation; both add a per-channel bias when one is given.
+ * --------------------------------------------------------------------------------- */
+
+/* out[b,t,d] = act(bias[d] + sum_{i<K} w[d*K+i] * xin(b, t-(K-1)+i, d)), act = silu or identity,
+ * xin(b,s,d) = x[b,s,d] for s >= 0 and, for -(K-1) <= s < 0, state_in[b][K-1+s][d] (zero when
+ * state_in is NULL).  state_out [batch][K-1][dim], if given, receives the last K-1 rows of
+ * (state_in rows ++ x rows).  Layout [batch][L][dim]; w [dim][K]. */
+int oracle_causal_conv1d(const double *x, const double *w, const double *bias, const double *state_in,
+                         double *state_out, int silu_, double *out, int64_t batch, int64_t L, int64_t dim,
+                         int64_t K) {
+    if (batch < 0 || L < 0 || dim < 0 || K < 1 || !w || (L > 0 && (!x || !out))) return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            for (int64_t t = 0; t < L; ++t) {
+                double v = bias ? bias[d] : 0.0;
+                for (int64_t i = 0; i < K; ++i) {
+                    const int64_t s = t - (K - 1) + i;
+                    double xv = 0.0;
+                    if (s >= 0) xv = x[(b * L + s) * dim + d];
+                    else if (state_in) xv = state_in[(b * (K - 1) + (K - 1) + s) * dim + d];
+                    v += w[d * K + i] * xv;
+                }
+                out[(b * L + t) * dim + d] = silu_ ? silu(v) : v;
+            }
+            if (state_out) {
+                for (int64_t r = 0; r < K - 1; ++r) {
+                    const int64_t s = L - (K - 1) + r; /* row of the concatenation, relative to x */
+                    double xv = 0.0;
+                    if (s >= 0) xv = x[(b * L + s) * dim + d];
+                    else if (state_in) xv = state_in[(b * (K - 1) + (K - 1) + s) * dim + d];
+                    state_out[(b * (K - 1) + r) * dim + d] = xv;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* out[b,h,w,d] = act(bias[d] + sum_{i,j<ks} wt[(d*ks+i)*ks+j] * x[b, h+i-p, w+j-p, d]), p = (ks-1)/2,
+ * x read as zero outside the H x W map.  Layout [batch][H][W][dim]; wt [dim][ks][ks]; ks odd. */
+int oracle_dwconv2d(const double *x, const double *wt, const double *bias, int silu_, double *out, int64_t batch,
+                    int64_t H, int64_t W, int64_t dim, int64_t ks) {
+    if (batch < 0 || H < 0 || W < 0 || dim < 0 || ks < 1 || ks % 2 == 0 || !wt) return -1;
+    if (batch * H * W > 0 && (!x || !out)) return -1;
+    const int64_t p = (ks - 1) / 2;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t w = 0; w < W; ++w)
+                for (int64_t d = 0; d < dim; ++d) {
+                    double v = bias ? bias[d] : 0.0;
+                    for (int64_t i = 0; i < ks; ++i) {
+                        const int64_t hh = h + i - p;
+                        if (hh < 0 || hh >= H) continue;
+                        for (int64_t j = 0; j < ks; ++j) {
+                            const int64_t ww = w + j - p;
+                            if (ww < 0 || ww >= W) continue;
+                            v += wt[(d * ks + i) * ks + j] * x[((b * H + hh) * W + ww) * dim + d];
+                        }
+                    }
+                    out[((b * H + h) * W + w) * dim + d] = silu_ ? silu(v) : v;
+                }
+    return 0;
+}
+
 /* number of hardware threads the oracle would use for nthreads <= 0 */
 int oracle_default_threads(void) {
     long c = sysconf(_SC_NPROCESSORS_ONLN);

@@ -474,6 +474,142 @@ def pin_multi_bwd_fd(lib):
             assert abs(fd - an) <= 1e-6 * max(abs(fd), 1.0), (kind, name, fd, an)
 
 
+
+def _video_orders(T, H, W):
+    """Spatial-first (frame by frame, rows, columns) and temporal-first (each pixel through the
+    frames) token orders of a T x H x W clip stored frame-major, forward and reversed."""
+    sf = [t * H * W + h * W + w for t in range(T) for h in range(H) for w in range(W)]
+    tf = [t * H * W + h * W + w for h in range(H) for w in range(W) for t in range(T)]
+    return sf, tf
+
+
+def pin_ordered_scan_maps(lib):
+    """ordered_scan with orders written out from their definitions reproduces the fixed-order
+    oracles: bidirectional = [identity, reversal]; SS2D on an H x W map = [row-major,
+    column-major, both reversed]; and a video clip's spatial-first / temporal-first orders are
+    the bidirectional scan over the clip and SS2D on a T x (H W) grid."""
+    r = _rng(404)
+    T, H, W, dim, N, bt = 3, 2, 4, 5, 3, 2
+    L = T * H * W
+    x = r.standard_normal((bt, L, dim))
+    z = r.standard_normal((bt, L, dim))
+
+    def params(K):
+        return dict(delta=np.exp(r.uniform(-5, -1.5, (K, bt, L, dim))), A=-np.exp(r.uniform(-1, 1.5, (K, dim, N))),
+                    B=r.standard_normal((K, bt, L, N)), C=r.standard_normal((K, bt, L, N)),
+                    D=r.standard_normal((K, dim)))
+
+    sf, tf = _video_orders(T, H, W)
+    p2 = params(2)
+    a = oracle.ordered_scan(x, orders=[sf, sf[::-1]], z=z, lib=lib, **p2)
+    b = oracle.selscan_bidir(x, z=z, lib=lib, **p2)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+    p4 = params(4)
+    a = oracle.ordered_scan(x, orders=[sf, tf, sf[::-1], tf[::-1]], z=z, lib=lib, **p4)
+    b = oracle.ss2d(x, H=T, W=H * W, z=z, lib=lib, **p4)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+    # the same on an ordinary (T H) x W map: column-major written out pixel by pixel
+    H2 = T * H
+    rm = [h * W + w for h in range(H2) for w in range(W)]
+    cm = [h * W + w for w in range(W) for h in range(H2)]
+    b = oracle.ss2d(x, H=H2, W=W, z=z, lib=lib, **p4)
+    a = oracle.ordered_scan(x, orders=[rm, cm, rm[::-1], cm[::-1]], z=z, lib=lib, **p4)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+
+def _silu_np(v):
+    return v * (0.5 * (1.0 + np.tanh(0.5 * v)))  # sigmoid written through tanh: another route than the oracle's
+
+
+def pin_conv1d_impulse(lib):
+    """A unit impulse at step t0 of one channel comes out as that channel's filter reversed in
+    time over steps t0 .. t0+K-1 (causal: nothing before t0), and nowhere else."""
+    r = _rng(501)
+    bt, L, dim, K = 2, 12, 3, 4
+    w = r.standard_normal((dim, K))
+    x = np.zeros((bt, L, dim))
+    x[1, 5, 2] = 1.0
+    out = oracle.causal_conv1d(x, w, silu=False, lib=lib)
+    want = np.zeros_like(x)
+    for k in range(K):
+        want[1, 5 + k, 2] = w[2, K - 1 - k]
+    assert np.array_equal(out, want)
+
+
+def pin_conv1d_numpy(lib):
+    """Against numpy's full linear convolution per channel (first L outputs), with bias and SiLU,
+    for filter widths 1 .. 4."""
+    r = _rng(502)
+    bt, L, dim = 2, 37, 5
+    x = r.standard_normal((bt, L, dim))
+    for K in (1, 2, 3, 4):
+        w = r.standard_normal((dim, K))
+        bias = r.standard_normal(dim)
+        out = oracle.causal_conv1d(x, w, bias=bias, silu=True, lib=lib)
+        want = np.empty_like(x)
+        for b in range(bt):
+            for d in range(dim):
+                want[b, :, d] = np.convolve(x[b, :, d], w[d, ::-1])[:L] + bias[d]
+        assert np.allclose(out, _silu_np(want), rtol=1e-13, atol=1e-13), K
+
+
+def pin_conv1d_state_split(lib):
+    """Streaming: the sequence in two pieces, the first piece's last K-1 input rows carried as the
+    second's state, equals the whole sequence; a state in front equals prepending its rows."""
+    r = _rng(503)
+    bt, L, dim, K = 2, 30, 4, 4
+    x = r.standard_normal((bt, L, dim))
+    w = r.standard_normal((dim, K))
+    st0 = r.standard_normal((bt, K - 1, dim))
+    whole, st_end = oracle.causal_conv1d(x, w, state=st0, want_state=True, lib=lib)
+    for m in (0, 2, 3, 17, 30):
+        a, st = oracle.causal_conv1d(x[:, :m], w, state=st0, want_state=True, lib=lib)
+        b, st2 = oracle.causal_conv1d(x[:, m:], w, state=st, want_state=True, lib=lib)
+        assert np.array_equal(np.concatenate([a, b], axis=1), whole), m
+        assert np.array_equal(st2, st_end), m
+    longer = oracle.causal_conv1d(np.concatenate([st0, x], axis=1), w, lib=lib)
+    assert np.allclose(longer[:, K - 1:], whole, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(st_end, x[:, L - (K - 1):])
+
+
+def pin_dwconv2d_scipy(lib):
+    """Against scipy's 2-D cross-correlation per channel ('same' size, zero fill), with bias and
+    SiLU, for kernel sizes 1, 3 and 5 on a non-square map."""
+    from scipy.signal import correlate2d
+    r = _rng(504)
+    bt, H, W, dim = 2, 7, 9, 3
+    x = r.standard_normal((bt, H * W, dim))
+    for ks in (1, 3, 5):
+        wt = r.standard_normal((dim, ks, ks))
+        bias = r.standard_normal(dim)
+        out = oracle.dwconv2d(x, wt, H, W, bias=bias, silu=True, lib=lib)
+        want = np.empty((bt, H, W, dim))
+        for b in range(bt):
+            for d in range(dim):
+                want[b, :, :, d] = correlate2d(x[b, :, d].reshape(H, W), wt[d], mode="same") + bias[d]
+        assert np.allclose(out, _silu_np(want).reshape(bt, H * W, dim), rtol=1e-13, atol=1e-13), ks
+
+
+def pin_dwconv2d_impulse(lib):
+    """A unit impulse at pixel (h0, w0) of one channel comes out as that channel's kernel turned
+    by 180 degrees, centred on (h0, w0) and cut at the map's edge."""
+    r = _rng(505)
+    H, W, dim, ks = 5, 6, 2, 3
+    wt = r.standard_normal((dim, ks, ks))
+    for (h0, w0) in ((2, 3), (0, 0), (4, 5)):
+        x = np.zeros((1, H * W, dim))
+        x[0, h0 * W + w0, 1] = 1.0
+        out = oracle.dwconv2d(x, wt, H, W, silu=False, lib=lib).reshape(H, W, dim)
+        want = np.zeros((H, W, dim))
+        for i in range(ks):
+            for j in range(ks):
+                h, w = h0 - i + 1, w0 - j + 1
+                if 0 <= h < H and 0 <= w < W:
+                    want[h, w, 1] = wt[1, i, j]
+        assert np.array_equal(out, want), (h0, w0)
+
+
 ALL_PINS = [
     pin_lti_convolution,
     pin_delta_to_zero,
@@ -492,4 +628,10 @@ ALL_PINS = [
     pin_bwd_directional_fd,
     pin_bwd_elementwise_fd,
     pin_multi_bwd_fd,
+    pin_ordered_scan_maps,
+    pin_conv1d_impulse,
+    pin_conv1d_numpy,
+    pin_conv1d_state_split,
+    pin_dwconv2d_scipy,
+    pin_dwconv2d_impulse,
 ]

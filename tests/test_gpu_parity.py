@@ -464,3 +464,28 @@ def test_zoh_changes_only_the_input_factor():
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
 
+
+
+# ----------------------------------------------------------------------------- video clips
+@pytest.mark.parametrize("dtype,batch,T,H,Wd,dim", [("f32", 2, 4, 5, 6, 24), ("bf16", 2, 8, 7, 7, 64)],
+                         ids=lambda v: str(v))
+def test_video_spatiotemporal_orders(dtype, batch, T, H, Wd, dim):
+    """A T x H x W clip stored frame-major: its spatial-first order scanned both ways is
+    selscan_bidir_fwd over the clip, and the spatial-first and temporal-first orders, each both
+    ways, are ss2d_fwd on a T x (H W) grid.  Checked against the oracle run along orders written
+    out from (t, h, w)."""
+    import oracle
+    from tests import oracle_pins as P
+    L = T * H * Wd
+    sf, tf = P._video_orders(T, H, Wd)
+    for kind, orders, grid in (("bidir", [sf, sf[::-1]], (0, 0)), ("ss2d", [sf, tf, sf[::-1], tf[::-1]], (T, H * Wd))):
+        w = W.Workload("video", kind, batch, L, dim, 16, dtype, True, H=grid[0], W=grid[1], index=17)
+        inp = W.generate(w)
+        _say("video", kind, dtype, batch, (T, H, Wd), dim)
+        y = PT.from_dev(PT.run_gpu(kind, inp, dtype, H=grid[0], Wd=grid[1]))
+        f = lambda a: W.to_f64(a, dtype)
+        r = oracle.ordered_scan(f(inp["x"]), f(inp["delta"]), inp["A"].astype(np.float64), f(inp["B"]), f(inp["C"]),
+                                orders, D=inp["D"].astype(np.float64), z=f(inp["z"]))
+        err = PT.rel_err(y, r)
+        _say("video", kind, "max rel err", err)
+        assert err <= PT.TOL[dtype], err

@@ -65,6 +65,17 @@ MUTATIONS = [
     ("bwd_C_after_decay", "            g[n] += Ct[n] * dyp;\n", ""),
     ("bwd_h0_read_transposed", "for (int64_t n = 0; n < N; ++n) h[n] = s->h0 ? s->h0[(b * dim + d) * N + n] : 0.0;\n    const double Dd = s->D ? s->D[d] : 0.0;\n    const double *Arow = s->A + d * N;\n    for (int64_t t = 0; t < L; ++t) {\n        const int64_t i = (b * L + t) * dim + d;\n        double w",
      "for (int64_t n = 0; n < N; ++n) h[n] = s->h0 ? s->h0[(n * dim + d) % (s->batch * dim * N)] : 0.0;\n    const double Dd = s->D ? s->D[d] : 0.0;\n    const double *Arow = s->A + d * N;\n    for (int64_t t = 0; t < L; ++t) {\n        const int64_t i = (b * L + t) * dim + d;\n        double w"),
+    ("conv1d_not_causal", "const int64_t s = t - (K - 1) + i;", "const int64_t s = t - (K - 1) / 2 + i;"),
+    ("conv1d_filter_reversed", "v += w[d * K + i] * xv;", "v += w[d * K + (K - 1 - i)] * xv;"),
+    ("conv1d_state_row_shifted",
+     "else if (state_in) xv = state_in[(b * (K - 1) + (K - 1) + s) * dim + d];\n                    v += w",
+     "else if (state_in) xv = state_in[(b * (K - 1) + (K - 2) + s) * dim + d];\n                    v += w"),
+    ("conv1d_state_out_first_rows", "const int64_t s = L - (K - 1) + r;", "const int64_t s = r - (K - 1);"),
+    ("conv1d_silu_skipped", "out[(b * L + t) * dim + d] = silu_ ? silu(v) : v;", "out[(b * L + t) * dim + d] = v;"),
+    ("dwconv_kernel_transposed", "v += wt[(d * ks + i) * ks + j]", "v += wt[(d * ks + j) * ks + i]"),
+    ("dwconv_no_centring", "const int64_t hh = h + i - p;", "const int64_t hh = h + i - p + (ks > 1);"),
+    ("dwconv_bias_dropped", "double v = bias ? bias[d] : 0.0;\n                    for (int64_t i = 0; i < ks; ++i) {",
+     "double v = 0.0;\n                    for (int64_t i = 0; i < ks; ++i) {"),
 ]
 
 
@@ -90,27 +101,35 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
 
 PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
 
-# (name, text in oracle/__init__.py, replacement): mistakes in the composition of the
-# multi-direction gradients out of the single-direction ones.
+# (name, function, text in oracle/__init__.py, replacement): mistakes in the compositions
+# written in Python (multi-direction gradients out of the single-direction ones; scans along
+# explicit orders).  The mutated function replaces the real one while its pin runs.
 PY_MUTATIONS = [
-    ("multi_dx_not_summed", 'out["dx"][:, o] += g["dx"]', 'out["dx"][:, o] = g["dx"]'),
-    ("multi_dyp_not_gated", "dyp = dy * z * sg", "dyp = dy"),
-    ("multi_dz_missing_silu_derivative", 'out["dz"] = dy * yp * sg * (1.0 + z * (1.0 - sg))', 'out["dz"] = dy * yp * sg'),
-    ("multi_first_direction_params", "A[k], B[k][:, o], C[k][:, o]", "A[0], B[k][:, o], C[k][:, o]"),
-    ("multi_dC_not_scattered", 'out["dC"][k][:, o] = g["dC"]', 'out["dC"][k] = g["dC"]'),
-    ("multi_ddelta_token_order", 'out["ddelta"][k][:, o] = g["ddelta"]', 'out["ddelta"][k] = g["ddelta"]'),
+    ("multi_dx_not_summed", "multi_bwd", 'out["dx"][:, o] += g["dx"]', 'out["dx"][:, o] = g["dx"]'),
+    ("multi_dyp_not_gated", "multi_bwd", "dyp = dy * z * sg", "dyp = dy"),
+    ("multi_dz_missing_silu_derivative", "multi_bwd", 'out["dz"] = dy * yp * sg * (1.0 + z * (1.0 - sg))',
+     'out["dz"] = dy * yp * sg'),
+    ("multi_first_direction_params", "multi_bwd", "A[k], B[k][:, o], C[k][:, o], dyp[:, o]",
+     "A[0], B[k][:, o], C[k][:, o], dyp[:, o]"),
+    ("multi_dC_not_scattered", "multi_bwd", 'out["dC"][k][:, o] = g["dC"]', 'out["dC"][k] = g["dC"]'),
+    ("multi_ddelta_token_order", "multi_bwd", 'out["ddelta"][k][:, o] = g["ddelta"]', 'out["ddelta"][k] = g["ddelta"]'),
+    ("ordered_not_scattered", "ordered_scan", "out[:, o] += yk", "out += yk"),
+    ("ordered_gate_before_merge", "ordered_scan", "out *= z / (1.0 + np.exp(-z))", "out *= z / (1.0 + np.exp(z))"),
+    ("ordered_delta_not_gathered", "ordered_scan", "yk = selscan(x[:, o], delta[k][:, o]",
+     "yk = selscan(x[:, o], delta[k]"),
 ]
+PY_PINS = {"multi_bwd": "pin_multi_bwd_fd", "ordered_scan": "pin_ordered_scan_maps"}
 
 
-@pytest.mark.parametrize("name,old,new", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
-def test_pins_catch_planted_python_mistake(name, old, new, lib, monkeypatch):
+@pytest.mark.parametrize("name,fn,old,new", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_pins_catch_planted_python_mistake(name, fn, old, new, lib, monkeypatch):
     text = open(PY_SRC).read()
-    assert old in text, f"mutation site for {name} not found in oracle/__init__.py"
+    assert text.count(old) == 1, f"mutation site for {name} not found once in oracle/__init__.py"
     ns = {"__name__": "oracle_mutant", "__file__": PY_SRC}
     exec(compile(text.replace(old, new, 1), PY_SRC, "exec"), ns)
-    monkeypatch.setattr(oracle, "multi_bwd", ns["multi_bwd"])
+    monkeypatch.setattr(oracle, fn, ns[fn])
     try:
-        P.pin_multi_bwd_fd(lib)
+        getattr(P, PY_PINS[fn])(lib)
     except AssertionError:
         return
     pytest.fail(f"no pin caught the planted mistake {name}")
