@@ -43,7 +43,8 @@ DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
 CSRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc")
 # the sources each pass's kernels are built from (the hash ties a traffic record to them)
-KERNEL_SRCS = {"fwd": ("selscan_common.h", "selscan_fwd.hip"), "bwd": ("selscan_common.h", "selscan_bwd.hip")}
+KERNEL_SRCS = {"fwd": ("selscan_common.h", "selscan_fwd.hip"), "bwd": ("selscan_common.h", "selscan_bwd.hip"),
+               "conv": ("selscan_common.h", "selscan_conv.hip")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -74,7 +75,7 @@ def measured_traffic(workload: str, pass_: str = "fwd"):
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get(workload + ("/bwd" if pass_ == "bwd" else ""))
+    e = t.get(workload + ("" if pass_ == "fwd" else "/" + pass_))
     if not e or e.get("kernel_source_sha") != kernel_source_hash(pass_):
         return None
     return e.get("bytes_per_launch")
@@ -118,6 +119,56 @@ def cpu_baseline(w, budget_channels: int):
     }
 
 
+METRIC_CONV = "conv prologue (depthwise conv + SiLU) B·L·D elem/s + achieved HBM GB/s vs peak, 1 GPU"
+
+
+def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
+    """--pass conv: the depthwise convolution + SiLU in front of the scan, on the workload's x shape
+    (k = 4 causal along the sequence for 1-D workloads; 3x3 on the H x W map for 2-D ones)."""
+    two_d = w.kind in ("ss2d", "local_ss2d")
+    width = 3 if two_d else 4
+    g = W.generate_conv(w.batch, w.seqlen, w.dim, width, w.dtype, two_d=two_d)
+    x, wt, bias = up(g["x"]), up(g["weight"]), up(g["bias"])
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    if two_d:
+        step = lambda: S.dwconv2d_fwd(x, wt, w.H, w.W, bias=bias, out=out, stream=stream)
+    else:
+        step = lambda: S.causal_conv1d_fwd(x, wt, bias=bias, out=out, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = float(np.mean(launch_ms))
+    ms_step = wall * 1e3 / args.steps
+    elems = w.batch * w.seqlen * w.dim
+    # algorithmic bytes: x read once, out written once, the filters and biases read once
+    alg = 2 * elems * w.io_bytes + w.dim * (width * (width if two_d else 1) + 1) * 4
+    gbs = alg / (kern_ms * 1e-3) / 1e9
+    kname = "dwconv2d3_kernel" if two_d else "causal_conv1d_kernel"
+    out_line = {
+        "metric": METRIC_CONV, "value": elems / (ms_step * 1e-3), "unit": "elem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded: x ~ N(0,1); filter ~ N(0, 1/taps); bias ~ N(0,1))",
+        "config": {"workload": w.name, "kind": "dwconv2d_3x3" if two_d else "causal_conv1d_k4", "batch": w.batch,
+                   "seqlen": w.seqlen, "dim": w.dim, "io_dtype": w.dtype, "silu": True, "pass": "conv"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, "conv"), "kernel": kname, "kernel_ms": kern_ms,
+                     "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
+    }
+    print(json.dumps(out_line))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,9 +176,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "conv"], default="fwd",
                     help="fwd: the forward scan (default); bwd: selscan_scan_bwd (gradients of every input, "
-                         "states recomputed from the chunk states a forward saved beforehand)")
+                         "states recomputed from the chunk states a forward saved beforehand); conv: the "
+                         "convolution in front of the scan (causal conv1d k=4 + SiLU for the 1-D workloads, "
+                         "DWConv 3x3 + SiLU for the 2-D ones) on the workload's x")
     ap.add_argument("--state", action="store_true",
                     help="single-direction workloads: run selscan_fwd_state with an initial state and the "
                          "final state written (recurrent / chunked inference)")
@@ -172,9 +225,11 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    if args.zoh and args.pass_ == "bwd":
+    if args.zoh and args.pass_ != "fwd":
         print("--zoh applies to the forward only", file=sys.stderr)
         return 2
+    if args.pass_ == "conv":
+        return conv_bench(args, w, S, W, torch, np, up, dev)
     if args.state and w.kind != "selscan":
         print("--state applies to single-direction workloads only", file=sys.stderr)
         return 2

@@ -77,6 +77,8 @@ typedef enum {
  * delta * B (the page's exact discretisation; see the header comment); the backward entry
  * points return SELSCAN_E_UNSUPPORTED for it */
 #define SELSCAN_FLAG_ZOH 2u
+/* convolution entry points only: SiLU on the convolution's output */
+#define SELSCAN_FLAG_SILU 4u
 
 /* operation codes (scan orders) for selscan_workspace_bytes and the selscan_scan_* calls */
 typedef enum { SELSCAN_OP_FWD = 0, SELSCAN_OP_BIDIR = 1, SELSCAN_OP_SS2D = 2, SELSCAN_OP_LOCAL_SS2D = 3 } selscan_op;
@@ -264,6 +266,42 @@ int selscan_scan_bwd(int op, const void *x, const void *delta, const float *A, c
  * is not positive or dstate != 16). */
 size_t selscan_scan_bwd_workspace_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                         int io_dtype);
+
+/*
+ * causal_conv1d_fwd - the depthwise causal convolution in front of the Mamba block's scan,
+ * Conv1D(k=4) -> SiLU ("Mamba Series from Selective State Spaces to Visual State Space Models",
+ * section 方法设计, the Mamba block diagram).  Per batch b, step t, channel d:
+ *     v = bias[d] + sum_{i<width} weight[d][i] * xin[b][t-(width-1)+i][d],   out = silu(v) with
+ *     SELSCAN_FLAG_SILU, else v;
+ * xin is x with the width-1 rows of state_in in front (zero rows when state_in is NULL).
+ *   x, out      : [batch][seqlen][dim] io_dtype (out may not overlap x: SELSCAN_E_ALIAS)
+ *   weight      : [dim][width] fp32, width 1..4 (else SELSCAN_E_UNSUPPORTED); bias [dim] fp32, nullable
+ *   state_in    : [batch][width-1][dim] io_dtype, nullable: the input rows before step 0
+ *   state_out   : [batch][width-1][dim] io_dtype, nullable: written with the last width-1 rows of
+ *                 (state_in rows ++ x rows), the state_in of a call on the following steps.  It may
+ *                 not overlap state_in or any other array (double-buffer for streaming).
+ *   flags       : SELSCAN_FLAG_SILU or 0
+ * seqlen 0 with a state_out only copies the state.  The pages give only k = 4; causality (no
+ * step sees a later one) and one filter per channel are the reading this call implements.
+ */
+int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, const void *state_in, void *state_out,
+                      unsigned flags, void *out, int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                      int io_dtype, void *stream);
+
+/*
+ * dwconv2d_fwd - the depthwise 3x3 convolution in front of the VSS block's SS2D, DWConv 3x3 ->
+ * SiLU (same page, VSS block diagram; section 关键代码, SS2Dv0.forwardv0: conv2d then act), on
+ * channels-last maps.  Per batch b, pixel (h, w), channel d:
+ *     v = bias[d] + sum_{i,j<3} weight[d][i][j] * x[b][h+i-1][w+j-1][d]   (x = 0 outside the map),
+ *     out = silu(v) with SELSCAN_FLAG_SILU, else v
+ * (a cross-correlation keeping the map size, stride 1).
+ *   x, out   : [batch][H][W][dim] io_dtype (pixel p = h*W + w, as ss2d_fwd's x); out may not
+ *              overlap x (SELSCAN_E_ALIAS)
+ *   weight   : [dim][3][3] fp32; bias [dim] fp32, nullable; ksize must be 3 (else
+ *              SELSCAN_E_UNSUPPORTED)
+ */
+int dwconv2d_fwd(const void *x, const float *weight, const float *bias, unsigned flags, void *out, int64_t batch,
+                 int64_t H, int64_t W, int64_t dim, int64_t ksize, int io_dtype, void *stream);
 
 /* Scratch bytes the caller must pass as `workspace` for this problem (0 = none). */
 size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,

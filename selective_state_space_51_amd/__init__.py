@@ -20,6 +20,7 @@ SELSCAN_F32 = 0
 SELSCAN_BF16 = 1
 SELSCAN_FLAG_DELTA_SOFTPLUS = 1
 SELSCAN_FLAG_ZOH = 2
+SELSCAN_FLAG_SILU = 4
 SELSCAN_OP_FWD, SELSCAN_OP_BIDIR, SELSCAN_OP_SS2D, SELSCAN_OP_LOCAL_SS2D = 0, 1, 2, 3
 STATUS = {
     0: "SELSCAN_OK", 1: "SELSCAN_E_NULL", 2: "SELSCAN_E_SHAPE", 3: "SELSCAN_E_ALIGN", 4: "SELSCAN_E_ALIAS",
@@ -57,6 +58,10 @@ def _load():
     lib.ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.local_ss2d_fwd.argtypes = common + [i64, i64, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.local_ss2d_fwd.restype = ci
+    lib.causal_conv1d_fwd.argtypes = [vp, vp, vp, vp, vp, cu, vp, i64, i64, i64, i64, ci, vp]
+    lib.causal_conv1d_fwd.restype = ci
+    lib.dwconv2d_fwd.argtypes = [vp, vp, vp, cu, vp, i64, i64, i64, i64, i64, ci, vp]
+    lib.dwconv2d_fwd.restype = ci
     lib.selscan_scan_fwd.argtypes = [ci] + common + [vp, i64, i64, i64, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.selscan_scan_fwd.restype = ci
     lib.selscan_scan_bwd.argtypes = [ci] + [vp] * 8 + [cu] + [vp] * 10 + [i64] * 7 + [ci, vp, sz, vp]
@@ -442,4 +447,47 @@ def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, de
                               _stream(stream))
     _check(rc, "selscan_scan_bwd")
     return g
+
+
+def causal_conv1d_fwd(x, weight, bias=None, state_in=None, state_out=None, silu=True, out=None, stream=None):
+    """Causal depthwise conv1d (+ SiLU) over x [batch, L, dim]; weight [dim, width] fp32 (width <= 4).
+    state_in / state_out: [batch, width-1, dim] in x's dtype (state_out=True allocates it).
+    Returns out, or (out, state_out)."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    K = weight.shape[-1]
+    io = x.dtype
+    _shape_check("weight", weight, (dim, K))
+    _shape_check("bias", bias, (dim,))
+    _shape_check("state_in", state_in, (bt, K - 1, dim))
+    if state_out is True:
+        state_out = torch.empty(bt, K - 1, dim, dtype=io, device=x.device)
+    _shape_check("state_out", state_out, (bt, K - 1, dim))
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.causal_conv1d_fwd(_ptr(x, "x", io), _ptr(weight, "weight", f32=True), _ptr(bias, "bias", f32=True),
+                               _ptr(state_in, "state_in", io), _ptr(state_out, "state_out", io),
+                               SELSCAN_FLAG_SILU if silu else 0, _ptr(out, "out", io), bt, L, dim, K, _dtype_code(x),
+                               _stream(stream))
+    _check(rc, "causal_conv1d_fwd")
+    return (out, state_out) if state_out is not None else out
+
+
+def dwconv2d_fwd(x, weight, H, W, bias=None, silu=True, out=None, stream=None):
+    """Depthwise 3x3 conv (+ SiLU), 'same' size, over channels-last maps x [batch, H*W, dim];
+    weight [dim, 3, 3] fp32."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    io = x.dtype
+    if L != H * W:
+        raise ValueError(f"x has {L} pixels, expected H*W = {H * W}")
+    _shape_check("weight", weight, (dim, 3, 3))
+    _shape_check("bias", bias, (dim,))
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.dwconv2d_fwd(_ptr(x, "x", io), _ptr(weight, "weight", f32=True), _ptr(bias, "bias", f32=True),
+                          SELSCAN_FLAG_SILU if silu else 0, _ptr(out, "out", io), bt, H, W, dim, 3, _dtype_code(x),
+                          _stream(stream))
+    _check(rc, "dwconv2d_fwd")
+    return out
 

@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SRCS = [os.path.join(CSRC, "selscan_fwd.hip"), os.path.join(CSRC, "selscan_bwd.hip")]
+SRCS = [os.path.join(CSRC, f) for f in ("selscan_fwd.hip", "selscan_bwd.hip", "selscan_conv.hip")]
 OUT = os.path.join(PKG, "libselscan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -19,6 +19,7 @@ def test_exports_every_declared_symbol():
                              "selscan_bwd", "selscan_chunk_states_bytes", "selscan_bwd_workspace_bytes",
                              "local_ss2d_fwd", "selscan_scan_fwd", "selscan_scan_bwd",
                              "selscan_scan_chunk_states_bytes", "selscan_scan_bwd_workspace_bytes",
+                             "causal_conv1d_fwd", "dwconv2d_fwd",
                              "selscan_workspace_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
@@ -247,3 +248,43 @@ def test_fast_division_identity():
         assert m < (1 << 32)
         q = [(int(n) * m) >> 32 >> (s - 1) for n in ns]
         assert q == [int(n) // d for n in ns], d
+
+
+def conv1d(**kw):
+    a = dict(x=P, w=P + MB, bias=None, si=None, so=None, flags=4, out=P + 2 * MB, batch=1, L_=16, dim=8, K=4,
+             dtype=S.SELSCAN_BF16)
+    a.update(kw)
+    return L.causal_conv1d_fwd(a["x"], a["w"], a["bias"], a["si"], a["so"], a["flags"], a["out"], a["batch"],
+                               a["L_"], a["dim"], a["K"], a["dtype"], None)
+
+
+def test_conv1d_arguments():
+    """Every call here fails a host-side check or has nothing to do (none reaches a launch)."""
+    assert conv1d(K=5) == 5 and conv1d(K=0) == 5
+    assert conv1d(flags=2) == 5 and conv1d(dtype=2) == 5
+    assert conv1d(L_=-1) == 2
+    assert conv1d(x=None) == 1 and conv1d(w=None) == 1 and conv1d(out=None) == 1
+    assert conv1d(x=P + 1) == 3 and conv1d(w=P + MB + 2) == 3 and conv1d(so=P + 3 * MB + 1) == 3
+    assert conv1d(out=P + 100) == 4                          # on x (16 x 8 bf16 = 256 bytes)
+    assert conv1d(si=P + 3 * MB, so=P + 3 * MB + 16) == 4    # state_out on state_in (3 x 8 x 2 = 48 bytes)
+    assert conv1d(so=P + 2 * MB + 64) == 4                   # state_out on out
+    assert conv1d(L_=0) == 0 and conv1d(batch=0) == 0 and conv1d(dim=0) == 0
+
+
+def dw(**kw):
+    a = dict(x=P, w=P + MB, bias=None, flags=4, out=P + 2 * MB, batch=1, H=4, W=4, dim=8, ks=3,
+             dtype=S.SELSCAN_BF16)
+    a.update(kw)
+    return L.dwconv2d_fwd(a["x"], a["w"], a["bias"], a["flags"], a["out"], a["batch"], a["H"], a["W"], a["dim"],
+                          a["ks"], a["dtype"], None)
+
+
+def test_dwconv2d_arguments():
+    """Every call here fails a host-side check or has nothing to do (none reaches a launch)."""
+    assert dw(ks=5) == 5 and dw(ks=1) == 5 and dw(flags=1) == 5
+    assert dw(H=-1) == 2
+    assert dw(x=None) == 1 and dw(w=None) == 1
+    assert dw(out=P + 200) == 4 and dw(out=P + MB + 16) == 4
+    assert dw(x=P + 1) == 3
+    assert dw(H=0) == 0 and dw(batch=0) == 0
+

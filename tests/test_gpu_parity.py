@@ -489,3 +489,90 @@ def test_video_spatiotemporal_orders(dtype, batch, T, H, Wd, dim):
         err = PT.rel_err(y, r)
         _say("video", kind, "max rel err", err)
         assert err <= PT.TOL[dtype], err
+
+
+# ----------------------------------------------------------------------------- convolution prologue
+@pytest.mark.parametrize("dtype,batch,L,dim,K,bias,silu,state", [
+    ("f32", 2, 300, 40, 4, True, True, False),
+    ("f32", 1, 2, 8, 4, True, False, True),      # shorter than the filter: state rows on both sides
+    ("f32", 3, 129, 17, 3, False, True, True),   # ragged channel groups, unaligned rows
+    ("bf16", 2, 1000, 64, 4, True, True, True),
+    ("bf16", 2, 64, 24, 2, False, False, False),
+    ("f32", 2, 70, 16, 1, True, True, False),
+], ids=lambda v: str(v))
+def test_causal_conv1d_against_oracle(dtype, batch, L, dim, K, bias, silu, state):
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    g = W.generate_conv(batch, L, dim, K, dtype)
+    dev = lambda a, dt=dtype: PT.to_dev(a, dt)
+    st_in = dev(g["state"]) if state else None
+    out, st_out = S.causal_conv1d_fwd(dev(g["x"]), dev(g["weight"], "f32"), bias=dev(g["bias"], "f32") if bias else None,
+                                      state_in=st_in, state_out=True, silu=silu)
+    torch.cuda.synchronize()
+    f = lambda a: W.to_f64(a, dtype)
+    r, rs = oracle.causal_conv1d(f(g["x"]), g["weight"].astype(np.float64), bias=g["bias"].astype(np.float64) if bias else None,
+                                 state=f(g["state"]) if state else None, silu=silu, want_state=True)
+    err = PT.rel_err(PT.from_dev(out), r)
+    _say("conv1d", dtype, batch, L, dim, K, bias, silu, state, "max rel err", err)
+    assert err <= PT.TOL[dtype], err
+    assert np.array_equal(PT.from_dev(st_out), rs)  # raw copies of input rows: exact
+
+
+def test_causal_conv1d_streaming_equals_whole():
+    """Two calls carrying the state equal one call, bit for bit (the same sums in the same order)."""
+    import torch
+    import selective_state_space_51_amd as S
+    g = W.generate_conv(2, 500, 64, 4, "bf16")
+    x = PT.to_dev(g["x"], "bf16")
+    w = PT.to_dev(g["weight"], "f32")
+    whole = S.causal_conv1d_fwd(x, w)
+    a, st = S.causal_conv1d_fwd(x[:, :193].contiguous(), w, state_out=True)
+    b = S.causal_conv1d_fwd(x[:, 193:].contiguous(), w, state_in=st)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a, b], dim=1), whole)
+
+
+def test_causal_conv1d_full_shape_sampled():
+    """The Mamba-1.4B-layer shape (batch 2 x L 65536 x D 4096, bf16, k = 4 + SiLU): every output of
+    a sample of channels against the oracle (the filter is per channel)."""
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    bt, L, dim = 2, 65536, 4096
+    g = W.generate_conv(bt, L, dim, 4, "bf16")
+    out = S.causal_conv1d_fwd(PT.to_dev(g["x"], "bf16"), PT.to_dev(g["weight"], "f32"), bias=PT.to_dev(g["bias"], "f32"))
+    torch.cuda.synchronize()
+    ch = np.array([0, 1, 7, 8, 2047, 2048, 4095])
+    y = PT.from_dev(out[..., torch.as_tensor(ch, device="cuda")])
+    r = oracle.causal_conv1d(W.to_f64(g["x"], "bf16")[..., ch], g["weight"][ch].astype(np.float64),
+                             bias=g["bias"][ch].astype(np.float64))
+    err = PT.rel_err(y, r)
+    _say("conv1d full", "max rel err", err)
+    assert err <= PT.TOL["bf16"], err
+    del out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,batch,H,Wd,dim,bias,silu", [
+    ("f32", 2, 7, 9, 16, True, True),
+    ("f32", 1, 1, 1, 8, True, True),
+    ("f32", 2, 5, 33, 12, False, False),          # a ragged last row segment, ragged channel group
+    ("bf16", 2, 28, 28, 64, True, True),
+    ("bf16", 32, 56, 56, 192, True, True),         # the VMamba stage-1 map
+    ("bf16", 1, 3, 2, 17, True, True),
+], ids=lambda v: str(v))
+def test_dwconv2d_against_oracle(dtype, batch, H, Wd, dim, bias, silu):
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    g = W.generate_conv(batch, H * Wd, dim, 3, dtype, two_d=True)
+    out = S.dwconv2d_fwd(PT.to_dev(g["x"], dtype), PT.to_dev(g["weight"], "f32"), H, Wd,
+                         bias=PT.to_dev(g["bias"], "f32") if bias else None, silu=silu)
+    torch.cuda.synchronize()
+    r = oracle.dwconv2d(W.to_f64(g["x"], dtype), g["weight"].astype(np.float64), H, Wd,
+                        bias=g["bias"].astype(np.float64) if bias else None, silu=silu)
+    err = PT.rel_err(PT.from_dev(out), r)
+    _say("dwconv2d", dtype, batch, H, Wd, dim, bias, silu, "max rel err", err)
+    assert err <= PT.TOL[dtype], err
+

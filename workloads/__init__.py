@@ -245,3 +245,20 @@ def generate_cotangent(batch: int, seqlen: int, dim: int, dtype: str, seed: int 
     backward pass)."""
     return _normal(seed, 8, (batch, seqlen, dim), dtype)
 
+
+def generate_conv(batch: int, seqlen: int, dim: int, width: int, dtype: str, two_d: bool = False,
+                  seed: int = SEED_BASE + 70) -> Dict[str, np.ndarray]:
+    """Seeded inputs of the convolution in front of the scan: x ~ N(0, 1) [batch, seqlen, dim]
+    in the I/O dtype; weight ~ N(0, 1/taps) fp32 ([dim, width] for the causal 1-D filter,
+    [dim, width, width] for the 2-D one); bias ~ N(0, 1) fp32; state ~ N(0, 1) [batch, width-1,
+    dim] in the I/O dtype (the 1-D filter's carried input rows)."""
+    taps = width * width if two_d else width
+    wshape = (dim, width, width) if two_d else (dim, width)
+    w = (_normal(seed, 9, wshape).astype(np.float64) / np.sqrt(taps)).astype(np.float32)
+    return {
+        "x": _normal(seed, 10, (batch, seqlen, dim), dtype),
+        "weight": w,
+        "bias": _normal(seed, 11, (dim,)),
+        "state": _normal(seed, 12, (batch, max(width - 1, 0), dim), dtype),
+    }
+
