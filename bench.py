@@ -135,6 +135,13 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
         step = lambda: S.dwconv2d_fwd(x, wt, w.H, w.W, bias=bias, out=out, stream=stream)
     else:
         step = lambda: S.causal_conv1d_fwd(x, wt, bias=bias, out=out, stream=stream)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -9,19 +9,23 @@
 // produce it in one pass over the input, at the bandwidth of the input and output streams.
 //
 // Work decomposition (both kernels): a thread owns 8 consecutive channels (one 16-byte vector
-// of bf16, two of fp32) and a run of positions; consecutive threads take consecutive channel
-// groups of the same positions, so a wave's loads and stores are contiguous row segments.
-//  - causal_conv1d: a run of kR1 = 64 steps; the K-1 rows before the run are read once and
-//    the K-row window slides in registers; rows are loaded four at a time ahead of use.
-//  - dwconv2d: a segment of kRW = 16 pixels of one image row; the 3x3 window of the three
-//    rows slides along the segment in registers (three 16-byte loads per output pixel, the two
-//    other rows of each coming from the caches: adjacent rows belong to neighbouring threads).
+// of bf16, two of fp32) and a short run of positions; consecutive threads take consecutive
+// channel groups of the same positions, so a wave's loads and stores are contiguous row
+// segments.  A thread issues every load of its run at once, as raw io bits (converted to fp32
+// where used), so each wave keeps many rows in flight: the kernels are bound by memory
+// latency x parallelism otherwise, not by the stream bandwidth.
+//  - causal_conv1d: a run of kR1 = 16 steps plus the K-1 rows before it (those come from the
+//    caches: the previous run's thread read them).
+//  - dwconv2d: R pixels of one image row (8 for bf16, 2 for fp32) and the 3 x (R + 2)
+//    neighbourhood around them (rows above and below are neighbouring threads' rows: cache hits).
+// The filters of a thread's 8 channels are contiguous ([dim][taps]) and read as 16-byte vectors.
 #include "selscan_common.h"
 
 namespace {
 
-constexpr int kR1 = 64;  // steps per thread (conv1d)
-constexpr int kRW = 16;  // pixels per thread along a row (dwconv2d)
+constexpr int kR1 = 16;  // steps per thread (conv1d)
+template <typename T>
+constexpr int rw_of() { return sizeof(T) == 2 ? 8 : 2; }  // pixels per thread along a row (dwconv2d)
 
 struct Conv1dParams {
     const void *x;
@@ -30,7 +34,7 @@ struct Conv1dParams {
     void *state_out;        // [batch][K-1][dim] io dtype, or NULL
     void *out;
     int64_t L, dim;
-    int batch, silu, vec, ncg, ntb;
+    int batch, silu, vec, wvec, ncg, ntb;
 };
 
 template <typename T>
@@ -41,6 +45,34 @@ __device__ __forceinline__ void row8(const T *p, int nv, bool vec, float v[8]) {
 }
 
 __device__ __forceinline__ float act(float v, int silu_) { return silu_ ? silu(v) : v; }
+
+// This thread's index in the logical order (channel group fastest, then position).  Workgroups
+// are dealt round-robin over the 8 XCDs; the remap gives each XCD a contiguous range of logical
+// workgroups, so the image rows a thread shares with its neighbours above and below are read on
+// the same XCD, from its L2 (measured: 30.0 against 31.6 us on the VMamba stage-1 map).  The
+// 1-D kernel keeps the plain order: the remap made it slower (565 against 539 us on the
+// Mamba-1.4B-layer shape), its shared rows being only 3 in 19.
+__device__ __forceinline__ int64_t logical_tid() {
+    const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
+    const int blk = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
+    return (int64_t)blk * 256 + threadIdx.x;
+}
+
+// the TAPS filter taps of channels c0 .. c0+7 ([dim][TAPS] fp32), f[e * TAPS + i]; zeros past nv
+template <int TAPS>
+__device__ __forceinline__ void filters8(const float *w, int64_t c0, int nv, bool vec, float f[8 * TAPS]) {
+    if (vec && nv == 8 && (8 * TAPS) % 4 == 0) {
+        const float4 *q = (const float4 *)(w + c0 * TAPS);
+#pragma unroll
+        for (int k = 0; k < 2 * TAPS; ++k) {
+            const float4 v = q[k];
+            f[4 * k] = v.x, f[4 * k + 1] = v.y, f[4 * k + 2] = v.z, f[4 * k + 3] = v.w;
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8 * TAPS; ++k) f[k] = k / TAPS < nv ? w[c0 * TAPS + k] : 0.f;
+}
 
 template <typename T, int K>
 __global__ __launch_bounds__(256) void causal_conv1d_kernel(Conv1dParams p) {
@@ -56,62 +88,46 @@ __global__ __launch_bounds__(256) void causal_conv1d_kernel(Conv1dParams p) {
     const T *st = p.state_in ? (const T *)p.state_in + (int64_t)b * (K - 1) * dim + c0 : nullptr;
     T *out = (T *)p.out + (int64_t)b * L * dim + c0;
 
-    float wr[K][8], bs[8];
+    float f[8 * K], bs[8];
+    filters8<K>(p.w, c0, nv, p.wvec != 0, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
-#pragma unroll
-        for (int i = 0; i < K; ++i) wr[i][e] = e < nv ? p.w[(c0 + e) * K + i] : 0.f;
-    }
-    // input row s of the sequence extended by the state rows in front (zeros without a state)
-    auto in_row = [&](int64_t s, float v[8]) {
-        if (s >= 0) {
-            row8(x + s * dim, nv, vec, v);
-        } else if (st) {
-            row8(st + (K - 1 + s) * dim, nv, vec, v);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        }
-    };
+    for (int e = 0; e < 8; ++e) bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
     const int64_t t0 = (int64_t)tb * kR1;
-    const int64_t t1 = t0 + kR1 < L ? t0 + kR1 : L;
-    float win[K][8];  // rows t-K+1 .. t; win[K-1] is row t
+    // rows t0-(K-1) .. t0+kR1-1 of the sequence extended by the state rows in front (zero rows
+    // without a state and past the end), all requested before any is used
+    Raw8<T> raw[kR1 + K - 1];
 #pragma unroll
-    for (int i = 0; i < K - 1; ++i) in_row(t0 - (K - 1) + i, win[i]);
-    for (int64_t t = t0; t < t1; t += 4) {
-        float nx[4][8];
+    for (int i = 0; i < kR1 + K - 1; ++i) {
+        const int64_t s = t0 - (K - 1) + i;
+        raw[i] = Raw8<T>{};
+        if (s >= 0 && s < L) raw[i] = load_raw8(x + s * dim, nv, vec);
+        else if (s < 0 && st) raw[i] = load_raw8(st + (K - 1 + s) * dim, nv, vec);
+    }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t + u < t1) row8(x + (t + u) * dim, nv, vec, nx[u]);
+    for (int u = 0; u < kR1; ++u) {
+        if (t0 + u >= L) break;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = bs[e];
+#pragma unroll
+            for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], raw_f32(raw[u + i], e), a);
+            v[e] = act(a, p.silu);
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t + u >= t1) break;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) win[K - 1][e] = nx[u][e];
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = bs[e];
-#pragma unroll
-                for (int i = 0; i < K; ++i) a = fmaf(wr[i][e], win[i][e], a);
-                v[e] = act(a, p.silu);
-            }
-            store8(out + (t + u) * dim, nv, vec, v);
-#pragma unroll
-            for (int i = 0; i < K - 1; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) win[i][e] = win[i + 1][e];
-        }
+        store8(out + (t0 + u) * dim, nv, vec, v);
     }
     if (p.state_out && tb == p.ntb - 1) {
         // the last K-1 input rows (state rows where the sequence is shorter), raw copies
         T *so = (T *)p.state_out + (int64_t)b * (K - 1) * dim + c0;
 #pragma unroll
         for (int r = 0; r < K - 1; ++r) {
+            const int64_t s = L - (K - 1) + r;
             float v[8];
-            in_row(L - (K - 1) + r, v);
+            if (s >= 0) row8(x + s * dim, nv, vec, v);
+            else if (st) row8(st + (K - 1 + s) * dim, nv, vec, v);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
             store8(so + r * dim, nv, vec, v);
         }
     }
@@ -122,12 +138,12 @@ struct Dw2dParams {
     const float *w, *bias;  // [dim][3][3], [dim]
     void *out;
     int64_t dim;
-    int H, W, batch, silu, vec, ncg, nwb;
+    int H, W, batch, silu, vec, wvec, ncg, nwb;
 };
 
 template <typename T>
 __global__ __launch_bounds__(256) void dwconv2d3_kernel(Dw2dParams p) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t gid = logical_tid();
     if (gid >= (int64_t)p.batch * p.H * p.nwb * p.ncg) return;
     const int cg = (int)(gid % p.ncg);
     int64_t rest = gid / p.ncg;
@@ -141,32 +157,28 @@ __global__ __launch_bounds__(256) void dwconv2d3_kernel(Dw2dParams p) {
     const T *x = (const T *)p.x + (int64_t)b * H * W * dim + c0;
     T *out = (T *)p.out + (int64_t)b * H * W * dim + c0;
 
-    float wr[9][8], bs[8];
+    constexpr int R = rw_of<T>();
+    float f[72], bs[8];
+    filters8<9>(p.w, c0, nv, p.wvec != 0, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
+    for (int e = 0; e < 8; ++e) bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
+    const int w0 = wb * R;
+    // the 3 x (R+2) neighbourhood: rows h-1 .. h+1, columns w0-1 .. w0+R (zeros outside the map),
+    // all requested before any is used
+    Raw8<T> raw[3][R + 2];
 #pragma unroll
-        for (int i = 0; i < 9; ++i) wr[i][e] = e < nv ? p.w[(c0 + e) * 9 + i] : 0.f;
-    }
-    // column c of rows h-1, h, h+1 (zeros outside the map)
-    auto col = [&](int c, float v[3][8]) {
+    for (int i = 0; i < 3; ++i) {
+        const int hh = h - 1 + i;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int hh = h - 1 + i;
-            if (hh >= 0 && hh < H && c >= 0 && c < W) {
-                row8(x + ((int64_t)hh * W + c) * dim, nv, vec, v[i]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-            }
+        for (int j = 0; j < R + 2; ++j) {
+            const int c = w0 - 1 + j;
+            raw[i][j] = Raw8<T>{};
+            if (hh >= 0 && hh < H && c >= 0 && c < W) raw[i][j] = load_raw8(x + ((int64_t)hh * W + c) * dim, nv, vec);
         }
-    };
-    const int w0 = wb * kRW, w1 = w0 + kRW < W ? w0 + kRW : W;
-    float win[3][3][8];  // [column w-1, w, w+1][row][channel]
-    col(w0 - 1, win[0]);
-    col(w0, win[1]);
-    for (int w = w0; w < w1; ++w) {
-        col(w + 1, win[2]);
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        if (w0 + u >= W) break;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -174,17 +186,10 @@ __global__ __launch_bounds__(256) void dwconv2d3_kernel(Dw2dParams p) {
 #pragma unroll
             for (int i = 0; i < 3; ++i)
 #pragma unroll
-                for (int j = 0; j < 3; ++j) a = fmaf(wr[i * 3 + j][e], win[j][i][e], a);
+                for (int j = 0; j < 3; ++j) a = fmaf(f[e * 9 + i * 3 + j], raw_f32(raw[i][u + j], e), a);
             v[e] = act(a, p.silu);
         }
-        store8(out + ((int64_t)h * W + w) * dim, nv, vec, v);
-#pragma unroll
-        for (int i = 0; i < 3; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                win[0][i][e] = win[1][i][e];
-                win[1][i][e] = win[2][i][e];
-            }
+        store8(out + ((int64_t)h * W + w0 + u) * dim, nv, vec, v);
     }
 }
 
@@ -245,6 +250,7 @@ int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, con
     for (const void *q : rows)
         if (q && !aligned(q, 16)) vec = false;
     c.vec = vec;
+    c.wvec = aligned(weight, 16);
     c.ncg = (int)((dim + 7) / 8);
     const int64_t ntb = (seqlen + kR1 - 1) / kR1;
     if (ntb > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
@@ -273,8 +279,10 @@ int dwconv2d_fwd(const void *x, const float *weight, const float *bias, unsigned
     c.x = x, c.w = weight, c.bias = bias, c.out = out, c.dim = dim;
     c.H = (int)H, c.W = (int)W, c.batch = (int)batch, c.silu = (flags & SELSCAN_FLAG_SILU) ? 1 : 0;
     c.vec = dim % 8 == 0 && aligned(x, 16) && aligned(out, 16);
+    c.wvec = aligned(weight, 16);
     c.ncg = (int)((dim + 7) / 8);
-    c.nwb = (int)((W + kRW - 1) / kRW);
+    const int R = io_dtype == SELSCAN_BF16 ? rw_of<uint16_t>() : rw_of<float>();
+    c.nwb = (int)((W + R - 1) / R);
     const int64_t threads = (int64_t)batch * H * c.nwb * c.ncg;
     if (io_dtype == SELSCAN_BF16) return launch_grid((const void *)&dwconv2d3_kernel<uint16_t>, threads, &c, stream);
     return launch_grid((const void *)&dwconv2d3_kernel<float>, threads, &c, stream);
