@@ -297,6 +297,9 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
     };
     for (int q = nchunks - 1; q >= 0; --q) {
         const int64_t s0 = (int64_t)q * kCH;
+        // priority: staging, prologue and output above the state loop, whose priority alternates
+        // with the chunk's parity so the two workgroups sharing a SIMD take turns ahead
+        __builtin_amdgcn_s_setprio(2);
         fetch(q);
         lds_barrier();  // the previous (later) chunk is done with every tile
         commit();
@@ -347,6 +350,8 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
         const float *Cc = Cs + 4 * l;
         float *redB = red + wave * kCH, *redC = red + 4 * kCH + wave * kCH;
 
+        if (q & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
 #pragma unroll 1
         for (int n = 0; n < kN; ++n) {
             const float a2 = As[cl * kN + n];
@@ -442,6 +447,7 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
             }
             lds_barrier();
         }
+        __builtin_amdgcn_s_setprio(2);
 
         // ---- per (step, channel) derivatives: dx, ddelta, and dz (or, with several directions,
         // this direction's output); they leave through three fp32 tiles: B, C (free after the
