@@ -226,16 +226,24 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
         const int64_t s0 = (int64_t)q * kCH;
         const int64_t sa = s0 + 2 * pp, sbb = sa + 1;
         const T *src[4] = {x, dl, dy, z};
+        // The lane's channel offset, made opaque per call: otherwise the compiler hoists one
+        // 64-bit per-lane pointer per tensor out of the chunk loop, spills them across the state
+        // loop, and reloads each right before its row load -- and waiting for a scratch reload
+        // waits for every load issued before it, which serialises the staging loads.
+        int64_t cgl = cg;
+        asm volatile("" : "+v"(cgl));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             r0[m] = r1[m] = Raw8<T>{};
             if (!src[m]) continue;
-            if (nv > 0 && sa < L) r0[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sa)) * dim + cg, nv, vec);
-            if (nv > 0 && sbb < L) r1[m] = load_raw8(src[m] + (rowb + visit<KIND>(p, k, sbb)) * dim + cg, nv, vec);
+            if (nv > 0 && sa < L) r0[m] = load_raw8(src[m] + ((rowb + visit<KIND>(p, k, sa)) * dim + cgl), nv, vec);
+            if (nv > 0 && sbb < L) r1[m] = load_raw8(src[m] + ((rowb + visit<KIND>(p, k, sbb)) * dim + cgl), nv, vec);
         }
 #pragma unroll
         for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
-        const int64_t s = s0 + sb;
+        int sbl = sb;  // opaque per call, as cgl above
+        asm volatile("" : "+v"(sbl));
+        const int64_t s = s0 + sbl;
         if (s < L) {
             const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
             if (p.vecbc) {
@@ -260,8 +268,9 @@ __global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
                 }
             }
         }
-        const int ch = tid / kN, n = tid % kN;
-        hck = c0 + ch < dim ? p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] : 0.f;
+        int64_t own = (c0 + tid / kN) * kN + tid % kN;  // this thread's (channel, state) entry
+        asm volatile("" : "+v"(own));
+        hck = c0 + tid / kN < dim ? p.ckpt[(((int64_t)k * p.batch + b) * nchunks + q) * dim * kN + own] : 0.f;
     };
     auto commit = [&]() {
         const int si = S::xpos(2 * pp);
