@@ -119,6 +119,61 @@ def cpu_baseline(w, budget_channels: int):
     }
 
 
+def cpu_baseline_bwd(w, budget_channels: int):
+    """The fp64 oracle backward (all host cores) on a bounded sample: every batch row and the whole
+    sequence for the first `budget_channels` channels (dB, dC then sum over those channels only;
+    the work per element is the same)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    inp = W.generate(w)
+    ch = min(budget_channels, w.dim)
+    f = lambda a: None if a is None else np.ascontiguousarray(W.to_f64(a, w.dtype)[..., :ch])
+    x, dl, z = f(inp["x"]), f(inp["delta"]), f(inp.get("z"))
+    dy = f(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
+    A = np.ascontiguousarray(inp["A"].astype(np.float64)[..., :ch, :])
+    D = np.ascontiguousarray(inp["D"].astype(np.float64)[..., :ch])
+    B, C = W.to_f64(inp["B"], w.dtype), W.to_f64(inp["C"], w.dtype)
+    del inp
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    if w.kind == "selscan":
+        oracle.selscan_bwd(x, dl, A, B, C, dy, D=D, z=z, nthreads=threads)
+    else:
+        oracle.multi_bwd(w.kind, x, dl, A, B, C, dy, D=D, z=z, H=w.H, W=w.W, window=w.window, nthreads=threads)
+    sec = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * ch * w.dstate * w.ndir
+    return {"value": elems / sec, "unit": "elem/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name} backward: all {w.batch} batch rows x {w.seqlen} steps x first {ch} of {w.dim} "
+                      f"channels x {w.ndir} direction(s) ({elems:.3e} elements, {sec:.1f} s wall, fp64)"}
+
+
+def cpu_baseline_conv(w, g, two_d: bool, budget_channels: int):
+    """The fp64 oracle convolution (one host thread: the oracle's direct sum is not threaded) on
+    every batch row and position of the first `budget_channels` channels."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    ch = min(budget_channels, w.dim)
+    x = np.ascontiguousarray(W.to_f64(g["x"], w.dtype)[..., :ch])
+    wt = np.ascontiguousarray(g["weight"][:ch].astype(np.float64))
+    bias = g["bias"][:ch].astype(np.float64)
+    t0 = time.perf_counter()
+    if two_d:
+        oracle.dwconv2d(x, wt, w.H, w.W, bias=bias, silu=True)
+    else:
+        oracle.causal_conv1d(x, wt, bias=bias, silu=True)
+    sec = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * ch
+    return {"value": elems / sec, "unit": "elem/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name} {'3x3' if two_d else 'k=4'} convolution: all {w.batch} batch rows x {w.seqlen} "
+                      f"positions x first {ch} of {w.dim} channels ({elems:.3e} elements, {sec:.1f} s wall, fp64)"}
+
+
 METRIC_CONV = "conv prologue (depthwise conv + SiLU) B·L·D elem/s + achieved HBM GB/s vs peak, 1 GPU"
 
 
@@ -172,6 +227,10 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
                      "traffic": measured_traffic(w.name, "conv"), "kernel": kname, "kernel_ms": kern_ms,
                      "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
     }
+    if not args.no_cpu_baseline:
+        del x, out
+        torch.cuda.empty_cache()
+        out_line["cpu_baseline"] = cpu_baseline_conv(w, g, two_d, min(args.cpu_channels, 1024))
     print(json.dumps(out_line))
     return 0
 
@@ -335,7 +394,9 @@ def main() -> int:
                      "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline and bwd:
-        out["cpu_baseline"] = None  # the timed oracle baseline is the forward's
+        del t, y, ws, h0, hl, ck, dy, bws
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline_bwd(w, min(args.cpu_channels, 2048))
     elif not args.no_cpu_baseline:
         del t, y, ws, h0, hl
         torch.cuda.empty_cache()
