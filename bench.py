@@ -41,10 +41,68 @@ FLOP_EQ_PER_ELEMENT_ZOH = 42
 METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
-CSRC = os.path.join(ROOT, "selective_state_space_51_amd", "csrc")
-# the sources each pass's kernels are built from (the hash ties a traffic record to them)
-KERNEL_SRCS = {"fwd": ("selscan_common.h", "selscan_fwd.hip"), "bwd": ("selscan_common.h", "selscan_bwd.hip"),
-               "conv": ("selscan_common.h", "selscan_conv.hip")}
+LIB_SO = os.path.join(ROOT, "selective_state_space_51_amd", "libselscan.so")
+# the kernels (mangled names) a counter record covers, per pass and workload kind; the record is
+# valid while their machine code in the built library is unchanged
+_FWD = "_ZN12_GLOBAL__N_115selscan_chunkedItLi{k}ELb0EEEvNS_6ParamsE"
+_BWD = ("_ZN12_GLOBAL__N_119selscan_bwd_chunkedItLi{k}EEEvNS_9BwdParamsE",
+        "_ZN12_GLOBAL__N_118selscan_bwd_reduceItLi{k}EEEvNS_15BwdReduceParamsE")
+_KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
+
+
+def profiled_kernels(pass_: str, kind: str):
+    k = _KIND[kind]
+    if pass_ == "fwd":
+        return [_FWD.format(k=k)]
+    if pass_ == "bwd":
+        return [n.format(k=k) for n in _BWD]
+    if kind in ("ss2d", "local_ss2d"):
+        return ["_ZN12_GLOBAL__N_116dwconv2d3_kernelItEEvNS_10Dw2dParamsE"]
+    return ["_ZN12_GLOBAL__N_120causal_conv1d_kernelItLi4EEEvNS_12Conv1dParamsE"]
+
+
+def kernel_code_hash(names, so_path: str = LIB_SO) -> str:
+    """sha256[:16] over the gfx950 machine code and kernel descriptors of the named kernels, read
+    from the code objects embedded in the built library (clang offload bundles; ELF symbol table)."""
+    import struct
+    data = open(so_path, "rb").read()
+    want = set(names) | {n + ".kd" for n in names}
+    found = {}
+    i = data.find(b"__CLANG_OFFLOAD_BUNDLE__")
+    while i >= 0:
+        n = struct.unpack_from("<Q", data, i + 24)[0]
+        off = i + 32
+        for _ in range(n):
+            eo, esz, tl = struct.unpack_from("<QQQ", data, off)
+            triple = data[off + 24:off + 24 + tl]
+            off += 24 + tl
+            if b"gfx950" not in triple or esz == 0:
+                continue
+            elf = data[i + eo:i + eo + esz]
+            shoff, = struct.unpack_from("<Q", elf, 0x28)
+            shentsize, shnum = struct.unpack_from("<HH", elf, 0x3A)
+            secs = [struct.unpack_from("<IIQQQQIIQQ", elf, shoff + j * shentsize) for j in range(shnum)]
+            for sec in secs:
+                if sec[1] != 2:  # SHT_SYMTAB
+                    continue
+                strtab = secs[sec[6]]
+                for j in range(sec[5] // 24):
+                    st_name, st_info, st_other, st_shndx, st_value, st_size = struct.unpack_from(
+                        "<IBBHQQ", elf, sec[4] + j * 24)
+                    end = elf.index(b"\0", strtab[4] + st_name)
+                    name = elf[strtab[4] + st_name:end].decode()
+                    if name in want and st_shndx < shnum and st_size:
+                        home = secs[st_shndx]
+                        start = home[4] + (st_value - home[3])  # file offset = sh_offset + (vaddr - sh_addr)
+                        found[name] = elf[start:start + st_size]
+        i = data.find(b"__CLANG_OFFLOAD_BUNDLE__", i + 1)
+    if set(found) != want:
+        return "missing:" + ",".join(sorted(want - set(found)))[:60]
+    h = hashlib.sha256()
+    for name in sorted(found):
+        h.update(name.encode())
+        h.update(found[name])
+    return h.hexdigest()[:16]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -61,22 +119,15 @@ def bwd_algorithmic_bytes(w) -> int:
     return tok * s * ((2 + k + g) + (1 + k + g)) + 4 * k * bc + ck + params
 
 
-def kernel_source_hash(pass_: str = "fwd") -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SRCS[pass_]:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(workload: str, pass_: str = "fwd"):
+def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
-    current kernel source; else None."""
+    kernels' current machine code; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     e = t.get(workload + ("" if pass_ == "fwd" else "/" + pass_))
-    if not e or e.get("kernel_source_sha") != kernel_source_hash(pass_):
+    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind)):
         return None
     return e.get("bytes_per_launch")
 
@@ -224,7 +275,7 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
         "config": {"workload": w.name, "kind": "dwconv2d_3x3" if two_d else "causal_conv1d_k4", "batch": w.batch,
                    "seqlen": w.seqlen, "dim": w.dim, "io_dtype": w.dtype, "silu": True, "pass": "conv"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, "conv"), "kernel": kname, "kernel_ms": kern_ms,
+                     "traffic": measured_traffic(w.name, "conv", w.kind), "kernel": kname, "kernel_ms": kern_ms,
                      "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:
@@ -364,7 +415,7 @@ def main() -> int:
     flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else (FLOP_EQ_PER_ELEMENT_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT)
     alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar)
-    traffic = None if (args.zoh or args.state) else measured_traffic(w.name, args.pass_)
+    traffic = None if (args.zoh or args.state) else measured_traffic(w.name, args.pass_, w.kind)
     out = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": value,

@@ -147,7 +147,8 @@ __device__ __forceinline__ void rows4_sum(const float p[kK], float out[4]) {
 __device__ __forceinline__ float sigmoidf_(float w) { return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e)); }
 
 template <typename T, int KIND>
-__global__ __launch_bounds__(256, 2) void selscan_bwd_chunked(BwdParams p) {
+// two workgroups per CU with bf16 io; the fp32 io tiles leave LDS for one
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunked(BwdParams p) {
     constexpr bool multi = KIND != SELSCAN_OP_FWD;
     using S = BwdLds<T>;
     constexpr int CT = kTC;

@@ -120,13 +120,11 @@ template <typename T>
 struct Io;
 template <>
 struct Io<float> {
-    static constexpr int kPadE = 4;  // 16 bytes of padding per lane segment
     __device__ static float f32(float v) { return v; }
     __device__ static float to(float v) { return v; }
 };
 template <>
 struct Io<uint16_t> {
-    static constexpr int kPadE = 8;
     __device__ static float f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
     // round to nearest even (v_cvt_pk_bf16_f32); a NaN stays a NaN
     __device__ static uint16_t to(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
