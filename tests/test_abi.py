@@ -288,3 +288,14 @@ def test_dwconv2d_arguments():
     assert dw(x=P + 1) == 3
     assert dw(H=0) == 0 and dw(batch=0) == 0
 
+
+
+def test_bench_finds_profiled_kernels_in_library():
+    """The counter records are keyed to the machine code of named kernels in the built library:
+    every name bench.py asks for must be there (a rename would silently drop the traffic figure)."""
+    import bench
+    for ps in ("fwd", "bwd", "conv"):
+        for kind in ("selscan", "bidir", "ss2d", "local_ss2d"):
+            h = bench.kernel_code_hash(bench.profiled_kernels(ps, kind))
+            assert not h.startswith("missing"), (ps, kind, h)
+            assert len(h) == 16
