@@ -47,6 +47,7 @@ struct BwdParams {
     int H, Wd, win;  // scan order (as for the forward)
     FastDiv dH, dWin, dWin2, dNx, dNy;
     int batch, ndir, softplus, ntc, vec, vecbc;
+    int split;  // one direction per workgroup; dx and output partial rows per direction
 };
 
 // Shared memory of one backward workgroup (16 channels, one chunk).
@@ -173,7 +174,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
     const int cl = wave * 4 + row;
     const float firstf = l == 0 ? 1.f : 0.f, lastf = l == kLPR - 1 ? 1.f : 0.f;
     const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
-    const int tile = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
+    const int tile_all = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
+    const int ntiles = p.batch * p.ntc;
+    const bool split = multi && p.split;  // grid = directions x tiles
+    const int tile = split ? tile_all % ntiles : tile_all;
     const int b = tile / p.ntc, tc = tile % p.ntc;
     const int64_t c0 = (int64_t)tc * CT;
     const int64_t L = p.L, dim = p.dim;
@@ -194,11 +198,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
     constexpr int NW = kN * (int)sizeof(T) / 4;
 
   const int ndir = multi ? p.ndir : 1;
-  for (int k = 0; k < ndir; ++k) {
+  const int k_begin = split ? tile_all / ntiles : 0, k_end = split ? k_begin + 1 : ndir;
+  for (int k = k_begin; k < k_end; ++k) {
     const T *dl = (const T *)p.delta + k * tok;
     const T *Bg = (const T *)p.B + k * bcn;
     const T *Cg = (const T *)p.C + k * bcn;
-    const bool last = k == ndir - 1;
+    const bool last = k == ndir - 1 && !split;
     // the previous direction is done with every tile, and its stores of the summed rows (read
     // back here by other waves) are complete: a full barrier
     __syncthreads();
@@ -536,8 +541,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                     store8((T *)p.ddelta + k * tok + off, nv, vec, v);
                 } else if constexpr (multi) {
                     // add the earlier directions' sum; keep it, or finish dx / dz
-                    float *acc = round == 0 ? p.wsX : p.wsY;
-                    if (k > 0) {
+                    float *acc = (round == 0 ? p.wsX : p.wsY) + (split ? k * tok : 0);
+                    if (k > 0 && !split) {
                         float w8[8];
                         load_f8(acc + off, nv, vec, w8);
 #pragma unroll
@@ -634,16 +639,64 @@ __global__ __launch_bounds__(256) void selscan_bwd_reduce(BwdReduceParams f) {
 }
 
 // workspace of the backward: dB/dC tile partials, dA and dD/dbias batch-row partials, and
-// with several directions the dx and pre-gate output sums
-size_t bwd_ws_parts(int ndir, int64_t batch, int64_t L, int64_t dim, size_t part[5]) {
+// with several directions the dx and pre-gate output sums (one row set, or one per direction
+// for a split launch)
+size_t bwd_ws_parts(int ndir, int64_t batch, int64_t L, int64_t dim, size_t part[5], bool split = false) {
     const int64_t ntc = (dim + kTC - 1) / kTC;
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t K = (size_t)ndir;
     part[0] = up(K * (size_t)ntc * (size_t)batch * 2 * kN * (size_t)L * 4);
     part[1] = up(K * (size_t)batch * (size_t)dim * kN * 4);
     part[2] = up(K * (size_t)batch * (size_t)dim * 2 * 4);
-    part[3] = part[4] = ndir > 1 ? up((size_t)batch * (size_t)L * (size_t)dim * 4) : 0;
+    part[3] = part[4] = ndir > 1 ? up((split ? K : 1) * (size_t)batch * (size_t)L * (size_t)dim * 4) : 0;
     return part[0] + part[1] + part[2] + part[3] + part[4];
+}
+
+// Split launches: dx = ((dx_0 + dx_1) + ...) and, for the gate's derivative, the pre-gate output
+// (o_0 + o_1) + ..., in direction order -- the sums the sequential walk forms -- then dz with
+// the same expression as there.
+struct BwdMergeParams {
+    const float *wsX, *wsY;  // [ndir][batch * L][dim] partial rows
+    const void *dy, *z;
+    void *dx, *dz;
+    int64_t rows, dim, tok;
+    int ndir, vec, ncg;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void selscan_bwd_merge(BwdMergeParams m) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= m.rows * m.ncg) return;
+    const int64_t row = gid / m.ncg, c0 = (gid % m.ncg) * 8;
+    const int nv = (int)(m.dim - c0 < 8 ? m.dim - c0 : 8);
+    const int64_t off = row * m.dim + c0;
+    const bool vec = m.vec != 0;
+    float s[8];
+    load_f8(m.wsX + off, nv, vec, s);
+    for (int k = 1; k < m.ndir; ++k) {
+        float w[8];
+        load_f8(m.wsX + k * m.tok + off, nv, vec, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = w[e] + s[e];
+    }
+    store8((T *)m.dx + off, nv, vec, s);
+    if (m.dz) {
+        load_f8(m.wsY + off, nv, vec, s);
+        for (int k = 1; k < m.ndir; ++k) {
+            float w[8];
+            load_f8(m.wsY + k * m.tok + off, nv, vec, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = w[e] + s[e];
+        }
+        const Raw8<T> dr = load_raw8((const T *)m.dy + off, nv, vec), zr = load_raw8((const T *)m.z + off, nv, vec);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float dyv = raw_f32(dr, e), zv = raw_f32(zr, e);
+            const float sg = sigmoidf_(zv);
+            s[e] = dyv * s[e] * sg * (1.f + zv * (1.f - sg));
+        }
+        store8((T *)m.dz + off, nv, vec, s);
+    }
 }
 
 struct BwdProblem {
@@ -658,7 +711,15 @@ struct BwdProblem {
     int kind = SELSCAN_OP_FWD;
     int ndir = 1;
     int64_t H = 0, W = 0, win = 0;
+    bool split = false;  // decided from the workspace the caller gave (bwd_run)
 };
+
+// split when the grid would be short of workgroups and the workspace holds the per-direction rows
+bool bwd_use_split(const BwdProblem &p, size_t ws_bytes) {
+    size_t part[5];
+    return p.ndir > 1 && split_wanted(p.kind, p.batch, p.dim) && p.ws &&
+           ws_bytes >= bwd_ws_parts(p.ndir, p.batch, p.L, p.dim, part, true);
+}
 
 int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
     if (p.batch < 0 || p.L < 0 || p.dim < 0 || p.H < 0 || p.W < 0 || dstate < 0) return SELSCAN_E_SHAPE;
@@ -682,7 +743,7 @@ int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
     for (const void *q : f32)
         if (q && !aligned(q, 4)) return SELSCAN_E_ALIGN;
     size_t part[5];
-    const size_t need = bwd_ws_parts(p.ndir, p.batch, p.L, p.dim, part);
+    const size_t need = bwd_ws_parts(p.ndir, p.batch, p.L, p.dim, part, p.split);
     if (!p.ws || ws_bytes < need) return SELSCAN_E_WORKSPACE;
     const size_t K = (size_t)p.ndir;
     const size_t tok = (size_t)p.batch * p.L * p.dim * s, bc = (size_t)p.batch * p.L * kN * s;
@@ -710,7 +771,7 @@ int bwd_launch_kind(const BwdProblem &q, void *stream) {
     a.A = q.A, a.D = q.D, a.bias = q.bias, a.ckpt = q.ckpt;
     a.dx = q.dx, a.ddelta = q.ddelta, a.dz = q.z ? q.dz : nullptr, a.dh0 = q.dh0;
     size_t part[5];
-    bwd_ws_parts(q.ndir, q.batch, q.L, q.dim, part);
+    bwd_ws_parts(q.ndir, q.batch, q.L, q.dim, part, q.split);
     char *w = (char *)q.ws;
     a.wsBC = (float *)w;
     a.wsA = (float *)(w + part[0]);
@@ -720,6 +781,7 @@ int bwd_launch_kind(const BwdProblem &q, void *stream) {
     a.dim = q.dim;
     set_order(a, q.kind, q.L, q.H, q.W, q.win);
     a.batch = (int)q.batch, a.ndir = q.ndir;
+    a.split = q.split ? 1 : 0;
     a.softplus = (q.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
     a.ntc = (int)((q.dim + kTC - 1) / kTC);
     const void *rows[] = {q.x, q.delta, q.dy, q.z, q.dx, q.ddelta, q.dz, a.wsX, a.wsY};
@@ -728,7 +790,7 @@ int bwd_launch_kind(const BwdProblem &q, void *stream) {
         if (r && !aligned(r, 16)) vec = false;
     a.vec = vec;
     a.vecbc = aligned(q.B, 16) && aligned(q.C, 16);
-    const int64_t blocks = q.batch * (int64_t)a.ntc;
+    const int64_t blocks = q.batch * (int64_t)a.ntc * (a.split ? q.ndir : 1);
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&a};
     hipError_t e = hipLaunchKernel((const void *)&selscan_bwd_chunked<T, KIND>, dim3((unsigned)blocks), dim3(256),
@@ -747,6 +809,17 @@ int bwd_launch_kind(const BwdProblem &q, void *stream) {
         e = hipLaunchKernel((const void *)&selscan_bwd_reduce<T, KIND>, dim3((unsigned)rb), dim3(256), fargs, 0,
                             (hipStream_t)stream);
     }
+    if (e == hipSuccess && a.split && q.L > 0) {
+        BwdMergeParams m;
+        m.wsX = a.wsX, m.wsY = a.wsY, m.dy = q.dy, m.z = q.z, m.dx = q.dx, m.dz = a.dz;
+        m.rows = q.batch * q.L, m.dim = q.dim, m.tok = m.rows * q.dim;
+        m.ndir = q.ndir, m.vec = a.vec, m.ncg = (int)((q.dim + 7) / 8);
+        const int64_t mb = (m.rows * m.ncg + 255) / 256;
+        if (mb > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+        void *margs[] = {&m};
+        e = hipLaunchKernel((const void *)&selscan_bwd_merge<T>, dim3((unsigned)mb), dim3(256), margs, 0,
+                            (hipStream_t)stream);
+    }
     if (e != hipSuccess) {
         record_hip_error(e);
         return SELSCAN_E_HIP;
@@ -763,6 +836,7 @@ int bwd_launch(const BwdProblem &q, void *stream) {
 }
 
 int bwd_run(BwdProblem &p, int64_t dstate, size_t ws_bytes, void *stream) {
+    p.split = bwd_use_split(p, ws_bytes);
     const int rc = bwd_validate(p, dstate, ws_bytes);
     if (rc != SELSCAN_OK) return rc;
     if (p.batch == 0 || p.dim == 0) return SELSCAN_OK;
@@ -819,7 +893,7 @@ size_t selscan_scan_bwd_workspace_bytes(int op, int64_t batch, int64_t seqlen, i
     const int ndir = ndir_of(op);
     if (ndir == 0 || batch <= 0 || seqlen < 0 || dim <= 0 || dstate != kN) return 0;
     size_t part[5];
-    return bwd_ws_parts(ndir, batch, seqlen, dim, part);
+    return bwd_ws_parts(ndir, batch, seqlen, dim, part, ndir > 1 && split_wanted(op, batch, dim));
 }
 
 }  // extern "C"

@@ -65,6 +65,19 @@ int ndir_of(int op) {
     }
 }
 
+// Several directions run one after another in each workgroup, with the running sums in one
+// fp32 workspace row set -- unless that leaves the chip short of workgroups (fewer than
+// kSplitBelow channel tiles x batch rows, under two rounds of two per compute unit), in which
+// case each workgroup takes one direction and writes its own partial rows, and a merge kernel
+// adds them in direction order (the sums the sequential walk forms, in its order: fp32 addition
+// is commutative, so the results are bit-identical).  Used when the caller's workspace holds
+// the per-direction rows (the size queries ask for them in that case).
+constexpr int64_t kSplitBelow = 1024;
+
+inline bool split_wanted(int op, int64_t batch, int64_t dim) {
+    return op != SELSCAN_OP_FWD && batch * ((dim + kTC - 1) / kTC) < kSplitBelow;
+}
+
 // sequence length and direction count of an op; H and W apply to the two-dimensional orders,
 // whose seqlen must be H * W
 int resolve_op(int op, int64_t seqlen, int64_t H, int64_t W, int64_t *L, int *ndir) {

@@ -51,9 +51,21 @@ struct Problem {
     int64_t win = 0;            // window side of the windowed cross-scan
 };
 
+// the workspace a call would use: split when wanted and the caller's workspace holds it
 size_t workspace_bytes_for(int op, int64_t batch, int64_t L, int64_t dim) {
     if (op == SELSCAN_OP_FWD) return 0;
+    const size_t tok = (size_t)batch * (size_t)L * (size_t)dim * sizeof(float);
+    return split_wanted(op, batch, dim) ? (size_t)ndir_of(op) * tok : tok;
+}
+
+size_t workspace_min_bytes(int op, int64_t batch, int64_t L, int64_t dim) {
+    if (op == SELSCAN_OP_FWD) return 0;
     return (size_t)batch * (size_t)L * (size_t)dim * sizeof(float);
+}
+
+bool use_split(const Problem &p, size_t ws_bytes) {
+    return p.ndir > 1 && split_wanted(p.kind, p.batch, p.dim) && p.ws &&
+           ws_bytes >= workspace_bytes_for(p.kind, p.batch, p.L, p.dim);
 }
 
 int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
@@ -75,7 +87,7 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
     const void *f32[] = {p.A, p.D, p.bias};
     for (const void *q : f32)
         if (q && !aligned(q, 4)) return SELSCAN_E_ALIGN;
-    const size_t need = workspace_bytes_for(p.kind, p.batch, p.L, p.dim);
+    const size_t need = workspace_min_bytes(p.kind, p.batch, p.L, p.dim);
     if (need && p.ws && !aligned(p.ws, 4)) return SELSCAN_E_ALIGN;
     const size_t tok = (size_t)p.batch * p.L * p.dim, bc = (size_t)p.batch * p.L * kN;
     const size_t K = (size_t)p.ndir;
@@ -93,8 +105,10 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
         if (overlap(y, q)) return SELSCAN_E_ALIAS;
     if (need) {
         if (!p.ws || ws_bytes < need) return SELSCAN_E_WORKSPACE;
+        const size_t used = use_split(p, ws_bytes) ? workspace_bytes_for(p.kind, p.batch, p.L, p.dim) : need;
+        if (overlap(y, {p.ws, used})) return SELSCAN_E_ALIAS;
         for (int i = 0; i < 8; ++i)
-            if (overlap({p.ws, need}, in[i])) return SELSCAN_E_ALIAS;
+            if (overlap({p.ws, used}, in[i])) return SELSCAN_E_ALIAS;
     }
     // state in/out: h_last may be h0 itself (in-place update) but must not overlap anything else
     const size_t st = (size_t)p.batch * (size_t)p.dim * kN * 4;
@@ -128,6 +142,7 @@ struct Params {
     FastDiv dH;       // division by H (SS2D column-major order)
     FastDiv dWin, dWin2, dNx, dNy;  // by w, w*w, W/w, H/w (windowed orders)
     int batch, ndir, softplus;
+    int split;        // one direction per workgroup, partial sums per direction in ws
     int vec;          // rows of 8 channels may be moved as 16-byte vectors
     int vecbc;        // a 16-value B/C row may be moved as 16-byte vectors
     int ntc;          // channel tiles per batch row
@@ -234,7 +249,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     const float firstf = l == 0 ? 1.f : 0.f;  // 1 on the first lane of each channel
     // consecutive channel tiles on one XCD: workgroups are dealt round-robin over 8 XCDs
     const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
-    const int tile = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
+    const int tile_all = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
+    // split launches: the grid is directions x tiles, each workgroup one direction of one tile
+    constexpr bool multi = KIND != SELSCAN_OP_FWD;
+    const int ntiles = p.batch * p.ntc;
+    const bool split = multi && p.split;
+    const int tile = split ? tile_all % ntiles : tile_all;
     const int b = tile / p.ntc;
     const int64_t c0 = (int64_t)(tile % p.ntc) * CT;
     const int64_t L = p.L, dim = p.dim;
@@ -256,7 +276,8 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     const int so = 16 * ((lane >> 2) & 7) + 4 * wave + (lane & 3);
 
     int qq = 0;  // chunks done over all directions (priority parity)
-    for (int k = 0; k < p.ndir; ++k) {
+    const int k_begin = split ? tile_all / ntiles : 0, k_end = split ? k_begin + 1 : p.ndir;
+    for (int k = k_begin; k < k_end; ++k) {
         const T *dl = (const T *)p.delta + k * tok;
         const T *Bk = (const T *)p.B + k * bcn;
         const T *Ck = (const T *)p.C + k * bcn;
@@ -385,7 +406,8 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             }
             // gate input for this chunk's output items, then the next chunk's inputs: in flight
             // while this chunk computes
-            const bool last = k == p.ndir - 1;
+            const bool last = k == p.ndir - 1 && !split;
+            float *wsk = split ? p.ws + k * tok : p.ws;  // this direction's partial rows (split) or the running sum
             Raw8<T> zr[2] = {};
             int64_t ooff[2] = {0, 0};
 #pragma unroll
@@ -518,7 +540,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 if constexpr (fast) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
-                    if (k > 0) load_f8(p.ws + ooff[r], 8, true, wv);
+                    if (k > 0 && !split) load_f8(p.ws + ooff[r], 8, true, wv);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] += wv[e];
                     if (last) {
@@ -528,12 +550,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                         }
                         store8(y + ooff[r], 8, true, v);
                     } else {
-                        store8(p.ws + ooff[r], 8, true, v);
+                        store8(wsk + ooff[r], 8, true, v);
                     }
                 } else if (nv > 0 && s0 + sl < L) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
-                    if (k > 0) load_f8(p.ws + ooff[r], nv, vec, wv);
+                    if (k > 0 && !split) load_f8(p.ws + ooff[r], nv, vec, wv);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] += wv[e];
                     if (last) {
@@ -543,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                         }
                         store8(y + ooff[r], nv, vec, v);
                     } else {
-                        store8(p.ws + ooff[r], nv, vec, v);
+                        store8(wsk + ooff[r], nv, vec, v);
                     }
                 }
             }
@@ -564,15 +586,59 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     }
 }
 
+// Split launches: y = (((o_0 + o_1) + o_2) + o_3) * silu(z) from the per-direction partial rows
+// -- the sums the sequential walk forms, in its order (fp32 addition is commutative).
+struct MergeParams {
+    const float *ws;  // [ndir][batch * L][dim] partial outputs
+    const void *z;
+    void *y;
+    int64_t rows, dim, tok;  // rows = batch * L; tok = rows * dim
+    int ndir, vec, ncg;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void selscan_merge(MergeParams m) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= m.rows * m.ncg) return;
+    const int64_t row = gid / m.ncg, c0 = (gid % m.ncg) * 8;
+    const int nv = (int)(m.dim - c0 < 8 ? m.dim - c0 : 8);
+    const int64_t off = row * m.dim + c0;
+    const bool vec = m.vec != 0;
+    float s[8];
+    load_f8(m.ws + off, nv, vec, s);
+    for (int k = 1; k < m.ndir; ++k) {
+        float w[8];
+        load_f8(m.ws + k * m.tok + off, nv, vec, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = w[e] + s[e];
+    }
+    if (m.z) {
+        const Raw8<T> zr = load_raw8((const T *)m.z + off, nv, vec);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] *= silu(raw_f32(zr, e));
+    }
+    store8((T *)m.y + off, nv, vec, s);
+}
+
 template <typename T, int KIND>
 int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     Params c = a;
     c.ntc = (int)((a.dim + kTC - 1) / kTC);
-    const int64_t blocks = batch * (int64_t)c.ntc;
+    const int64_t blocks = batch * (int64_t)c.ntc * (c.split ? c.ndir : 1);
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&c};
     const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true> : (const void *)&selscan_chunked<T, KIND, false>;
     hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+    if (e == hipSuccess && c.split && c.L > 0) {
+        MergeParams m;
+        m.ws = c.ws, m.z = c.z, m.y = c.y;
+        m.rows = (int64_t)batch * c.L, m.dim = c.dim, m.tok = m.rows * c.dim;
+        m.ndir = c.ndir, m.vec = c.vec, m.ncg = (int)((c.dim + 7) / 8);
+        const int64_t mb = (m.rows * m.ncg + 255) / 256;
+        if (mb > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+        void *margs[] = {&m};
+        e = hipLaunchKernel((const void *)&selscan_merge<T>, dim3((unsigned)mb), dim3(256), margs, 0, (hipStream_t)stream);
+    }
     if (e != hipSuccess) {
         record_hip_error(e);
         return SELSCAN_E_HIP;
@@ -588,7 +654,7 @@ int launch_kind(const Params &a, int kind, int64_t batch, bool zoh, void *stream
     return launch_tiles<T, SELSCAN_OP_LOCAL_SS2D>(a, batch, zoh, stream);
 }
 
-int launch(const Problem &p, void *stream) {
+int launch(const Problem &p, size_t ws_bytes, void *stream) {
     Params a;
     a.x = p.x, a.delta = p.delta, a.B = p.B, a.C = p.C, a.z = p.z;
     a.A = p.A, a.D = p.D, a.bias = p.bias, a.y = p.y;
@@ -597,6 +663,7 @@ int launch(const Problem &p, void *stream) {
     a.dim = p.dim;
     set_order(a, p.kind, p.L, p.H, p.W, p.win);
     a.batch = (int)p.batch, a.ndir = p.ndir;
+    a.split = use_split(p, ws_bytes) ? 1 : 0;
     a.softplus = (p.flags & SELSCAN_FLAG_DELTA_SOFTPLUS) ? 1 : 0;
     // rows of 8 channels move as 16-byte vectors when every row start is 16-byte aligned
     const void *rows[] = {p.x, p.delta, p.z, p.y};
@@ -616,7 +683,7 @@ int run(Problem &p, int64_t dstate, size_t ws_bytes, void *stream) {
     if (rc != SELSCAN_OK) return rc;
     if (p.batch == 0 || p.dim == 0 || (p.L == 0 && !p.hlast)) return SELSCAN_OK;
     if (p.batch > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
-    return launch(p, stream);
+    return launch(p, ws_bytes, stream);
 }
 
 }  // namespace

@@ -182,10 +182,14 @@ def scan_bwd(**kw):
 def test_scan_bwd_arguments():
     """Every call here fails a host-side check (none reaches a launch)."""
     ws = S.selscan_scan_bwd_workspace_bytes
-    # per-tile dB/dC partials, dA and dD/dbias partials, and the fp32 dx and output sums
-    assert ws(S.SELSCAN_OP_SS2D, 1, 16, 8) == 8192 + 2048 + 256 + 512 + 512
+    # per-tile dB/dC partials, dA and dD/dbias partials, and the fp32 dx and output rows: one set
+    # per direction here (a grid this small runs one direction per workgroup), one set in all
+    # when batch x channel tiles reaches 1024
+    assert ws(S.SELSCAN_OP_SS2D, 1, 16, 8) == 8192 + 2048 + 256 + 4 * 512 + 4 * 512
     assert ws(S.SELSCAN_OP_FWD, 1, 16, 8) == S.selscan_bwd_workspace_bytes(1, 16, 8)
-    assert ws(S.SELSCAN_OP_BIDIR, 1, 16, 8) == 4096 + 1024 + 256 + 512 + 512
+    assert ws(S.SELSCAN_OP_BIDIR, 1, 16, 8) == 4096 + 1024 + 256 + 2 * 512 + 2 * 512
+    big = ws(S.SELSCAN_OP_BIDIR, 1024, 1, 16)  # 1024 x 1 tiles: the sequential walk, one row set
+    assert big == 1024 * (2 * 2 * 16 * 4 + 2 * 16 * 16 * 4 + 2 * 16 * 2 * 4) + 2 * 1024 * 16 * 4
     assert ws(5, 1, 16, 8) == 0 and ws(S.SELSCAN_OP_SS2D, 0, 16, 8) == 0
     assert scan_bwd(op=5) == 5
     assert scan_bwd(H=2) == 2
@@ -193,7 +197,8 @@ def test_scan_bwd_arguments():
     for k in ("x", "delta", "A", "B", "C", "ck", "dy", "dx", "ddelta", "dA", "dB", "dC"):
         assert scan_bwd(**{k: None}) == 1, k
     assert scan_bwd(ws=None) == 6
-    assert scan_bwd(wsb=ws(S.SELSCAN_OP_SS2D, 1, 16, 8) - 4) == 6
+    # the smallest accepted workspace is the sequential walk's (one row set)
+    assert scan_bwd(wsb=8192 + 2048 + 256 + 512 + 512 - 4) == 6
     # four directions: dB is 4 x 512 bytes, so a dC 1 KiB after it overlaps
     assert scan_bwd(dC=P + 13 * MB + 1024) == 4
     assert scan_bwd(ddelta=P + 10 * MB - 512) == 4    # its third direction lands on dx (256 bytes)
@@ -228,7 +233,9 @@ def test_local_ss2d_window_checks():
     assert loc(6, 4, 3) == 2   # does not divide W
     assert loc(-1, 4, 1) == 2
     assert loc(6, 4, 2) == 6   # valid window: stops at the missing workspace
-    assert S.selscan_workspace_bytes(S.SELSCAN_OP_LOCAL_SS2D, 1, 24, 8) == 24 * 8 * 4
+    # one fp32 row set per direction for a grid this small (split), one set from 1024 tiles up
+    assert S.selscan_workspace_bytes(S.SELSCAN_OP_LOCAL_SS2D, 1, 24, 8) == 4 * 24 * 8 * 4
+    assert S.selscan_workspace_bytes(S.SELSCAN_OP_SS2D, 1024, 4, 16) == 1024 * 4 * 16 * 4
 
 
 def test_fast_division_identity():

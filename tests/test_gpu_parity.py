@@ -576,3 +576,38 @@ def test_dwconv2d_against_oracle(dtype, batch, H, Wd, dim, bias, silu):
     _say("dwconv2d", dtype, batch, H, Wd, dim, bias, silu, "max rel err", err)
     assert err <= PT.TOL[dtype], err
 
+
+
+# ----------------------------------------------------------------------------- split launches
+@pytest.mark.parametrize("kind,H,Wd,win", [("bidir", 0, 0, 0), ("ss2d", 14, 18, 0), ("local_ss2d", 12, 18, 6)])
+def test_split_equals_sequential(kind, H, Wd, win):
+    """A small grid runs one direction per workgroup when the workspace holds per-direction rows
+    (the size the queries return); with only the one-row-set workspace the directions run in
+    sequence.  Both give the same y and the same gradients, bit for bit."""
+    import torch
+    import selective_state_space_51_amd as S
+    op = _OP[kind]
+    L = 300 if kind == "bidir" else H * Wd
+    w = W.Workload("split", kind, 2, L, 40, 16, "bf16", True, H=H, W=Wd, index=18, window=win)
+    inp = W.generate(w, with_bias=True)
+    dev = lambda a, dt="bf16": PT.to_dev(a, dt)
+    args = (dev(inp["x"]), dev(inp["delta"]), dev(inp["A"], "f32"), dev(inp["B"]), dev(inp["C"]))
+    kw = dict(D=dev(inp["D"], "f32"), z=dev(inp["z"]), delta_bias=dev(inp["delta_bias"], "f32"), delta_softplus=True,
+              H=H, W=Wd, window=win)
+    K = 2 if kind == "bidir" else 4
+    rows = 2 * L * 40 * 4
+    full = S.selscan_workspace_bytes(op, 2, L, 40)
+    assert full == K * rows
+    one = torch.empty(rows, dtype=torch.uint8, device="cuda")
+    y_split, ck = S.selscan_scan_fwd(op, *args, chunk_states=True, **kw)
+    y_seq = S.selscan_scan_fwd(op, *args, workspace=one, **kw)
+    dy = dev(W.generate_cotangent(2, L, 40, "bf16"))
+    g_split = S.selscan_scan_bwd(op, *args, dy, ck, **kw)
+    up = lambda v: (v + 255) // 256 * 256
+    bfull = S.selscan_scan_bwd_workspace_bytes(op, 2, L, 40)
+    bone = torch.empty(bfull - 2 * (K - 1) * up(rows), dtype=torch.uint8, device="cuda")
+    g_seq = S.selscan_scan_bwd(op, *args, dy, ck, workspace=bone, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_split, y_seq)
+    for k in g_split:
+        assert torch.equal(g_split[k], g_seq[k]), k
