@@ -263,7 +263,10 @@ int selscan_scan_bwd(int op, const void *x, const void *delta, const float *A, c
                      size_t workspace_bytes, void *stream);
 
 /* Scratch bytes selscan_scan_bwd needs as `workspace` for `op` (0 if op is unknown, batch or dim
- * is not positive or dstate != 16). */
+ * is not positive or dstate != 16).  As for selscan_workspace_bytes, small grids get room for
+ * per-direction dx and output rows (one direction per workgroup); a workspace without it (two
+ * [batch][seqlen][dim] fp32 row sets rather than two per direction) runs the directions in turn,
+ * with the same result bit for bit. */
 size_t selscan_scan_bwd_workspace_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                         int io_dtype);
 
@@ -303,7 +306,12 @@ int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, con
 int dwconv2d_fwd(const void *x, const float *weight, const float *bias, unsigned flags, void *out, int64_t batch,
                  int64_t H, int64_t W, int64_t dim, int64_t ksize, int io_dtype, void *stream);
 
-/* Scratch bytes the caller must pass as `workspace` for this problem (0 = none). */
+/* Scratch bytes to pass as `workspace` for this problem (0 = none).  Several directions keep fp32
+ * partial outputs [batch][seqlen][dim] there.  When batch x ceil(dim/16) is below 1024 (too few
+ * workgroups to fill the GPU when each walks every direction) the returned size holds one such
+ * row set per direction, and the call runs one direction per workgroup plus an in-order merge;
+ * a workspace of a single row set is still accepted and runs the directions one after another.
+ * Both give the same result bit for bit. */
 size_t selscan_workspace_bytes(int op, int64_t batch, int64_t seqlen_or_hw, int64_t dim, int64_t dstate,
                                int io_dtype);
 
