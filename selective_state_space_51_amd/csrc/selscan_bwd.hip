@@ -222,9 +222,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
     }
 
     // global -> registers for chunk q: x, delta, dy, z rows of steps 2p, 2p+1 (8 channels each),
-    // the B and C rows of one step, the chunk's entry state.  (Not issued a chunk ahead: the
-    // state loop holds every register, and a load kept in flight across it would be waited
-    // for by the first spill reload after it.)
+    // the B and C rows of one step, the chunk's entry state.  Issued at the top of the chunk,
+    // not a chunk ahead: the state loop holds every register, and keeping the loads' registers
+    // live from the previous chunk's output phase into this one pushes the spill from 20 to over
+    // 200 bytes per lane (measured slower).
     Raw8<T> r0[4], r1[4];
     uint32_t pbc[2][NW];
     float hck;
