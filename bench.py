@@ -303,6 +303,10 @@ def main() -> int:
                          "final state written (recurrent / chunked inference)")
     ap.add_argument("--zoh", action="store_true",
                     help="forward with the zero-order-hold Bbar (SELSCAN_FLAG_ZOH) instead of delta * B")
+    ap.add_argument("--softplus", action="store_true",
+                    help="pass the pre-activation w and a per-channel bias with delta_softplus=1, so the "
+                         "kernels form delta = softplus(w + bias) themselves (w drawn so that delta has the "
+                         "workload's distribution); no CPU baseline is taken with it")
     ap.add_argument("--cpu-channels", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (a plain copy of known size, for scaling "
@@ -322,7 +326,9 @@ def main() -> int:
     w = W.by_name(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = W.generate(w)
+    inp = W.generate(w, with_w=args.softplus, with_bias=args.softplus)
+    if args.softplus:
+        inp["delta"] = inp.pop("w")
 
     def up(a):
         if a is None:
@@ -357,9 +363,10 @@ def main() -> int:
 
     ck = dy = bws = None
     geo = dict(H=w.H, W=w.W, window=w.window)
+    dkw = dict(delta_bias=t.get("delta_bias"), delta_softplus=args.softplus)
     if args.pass_ == "bwd":
         _, ck = S.selscan_scan_fwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
-                                   chunk_states=True, workspace=ws, stream=stream, **geo)
+                                   chunk_states=True, workspace=ws, stream=stream, **geo, **dkw)
         dy = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
         bws = torch.empty(S.selscan_scan_bwd_workspace_bytes(op, w.batch, w.seqlen, w.dim, w.dstate,
                                                              S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32),
@@ -368,22 +375,22 @@ def main() -> int:
     def step():
         if args.pass_ == "bwd":
             S.selscan_scan_bwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], dy, ck, D=t["D"], z=t["z"],
-                               workspace=bws, stream=stream, **geo)
+                               workspace=bws, stream=stream, **geo, **dkw)
         elif args.state:
             S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, h0=h0,
-                                h_last=hl, workspace=ws, zoh=args.zoh, stream=stream)
+                                h_last=hl, workspace=ws, zoh=args.zoh, stream=stream, **dkw)
         elif w.kind == "selscan":
             S.selscan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, workspace=ws,
-                          zoh=args.zoh, stream=stream)
+                          zoh=args.zoh, stream=stream, **dkw)
         elif w.kind == "bidir":
             S.selscan_bidir_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
-                                workspace=ws, zoh=args.zoh, stream=stream)
+                                workspace=ws, zoh=args.zoh, stream=stream, **dkw)
         elif w.kind == "local_ss2d":
             S.local_ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, w.window, D=t["D"], z=t["z"], y=y,
-                             workspace=ws, zoh=args.zoh, stream=stream)
+                             workspace=ws, zoh=args.zoh, stream=stream, **dkw)
         else:
             S.ss2d_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], w.H, w.W, D=t["D"], z=t["z"], y=y,
-                       workspace=ws, zoh=args.zoh, stream=stream)
+                       workspace=ws, zoh=args.zoh, stream=stream, **dkw)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -411,11 +418,13 @@ def main() -> int:
     value = w.elements / (ms_step * 1e-3)
     bwd = args.pass_ == "bwd"
     alg = bwd_algorithmic_bytes(w) if bwd else w.algorithmic_bytes()
+    if args.softplus:
+        alg += (2 if bwd else 1) * w.ndir * w.dim * 4  # the delta bias read (and its gradient written)
     hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
     flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else (FLOP_EQ_PER_ELEMENT_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT)
     alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
-    # the counter record is for the plain call of the pass (no state in/out, Euler Bbar)
-    traffic = None if (args.zoh or args.state) else measured_traffic(w.name, args.pass_, w.kind)
+    # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
+    traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(w.name, args.pass_, w.kind)
     out = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
@@ -432,7 +441,8 @@ def main() -> int:
         "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate,
                    "window": w.window or None,
-                   "state_io": bool(args.state), "pass": args.pass_, "bbar": "zoh" if args.zoh else "delta*B"},
+                   "state_io": bool(args.state), "pass": args.pass_, "bbar": "zoh" if args.zoh else "delta*B",
+                   "delta_softplus": bool(args.softplus)},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
                      "work_per_element": ("1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
@@ -444,11 +454,11 @@ def main() -> int:
                      "hbm_achieved_GBps": hbm_gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
                      "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
     }
-    if not args.no_cpu_baseline and bwd:
+    if not args.no_cpu_baseline and not args.softplus and bwd:
         del t, y, ws, h0, hl, ck, dy, bws
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline_bwd(w, min(args.cpu_channels, 2048))
-    elif not args.no_cpu_baseline:
+    elif not args.no_cpu_baseline and not args.softplus:
         del t, y, ws, h0, hl
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels)

@@ -365,6 +365,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
         const float *Bc = Bs + 4 * l;
         const float *Cc = Cs + 4 * l;
         float *redB = red + wave * kCH, *redC = red + 4 * kCH + wave * kCH;
+        // lane (row, l) holds the channel sums of steps 16 l + 4 row + (0..3); row r's slots are
+        // rotated by 2 r, so that each 8-lane group of the float4 stores here, and each 32-lane
+        // half of the step-ordered reads after the barrier, meets 32 distinct LDS banks
+        const int rslot = 64 * row + 4 * ((l + 2 * row) & 15);
+        const int rtid = 64 * ((tid >> 2) & 3) + 4 * (((tid >> 4) + 2 * ((tid >> 2) & 3)) & 15) + (tid & 3);
 
         if (q & 1) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
             {
                 float r4[4];
                 rows4_sum(pC, r4);
-                *(float4 *)&redC[16 * l + 4 * row] = make_float4(r4[0], r4[1], r4[2], r4[3]);
+                *(float4 *)&redC[rslot] = make_float4(r4[0], r4[1], r4[2], r4[3]);
             }
             // reverse, pass 1: this lane's map of the adjoint, from a zero input
             float rb = 0.f;
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
             {
                 float r4[4];
                 rows4_sum(pB, r4);
-                *(float4 *)&redB[16 * l + 4 * row] = make_float4(r4[0], r4[1], r4[2], r4[3]);
+                *(float4 *)&redB[rslot] = make_float4(r4[0], r4[1], r4[2], r4[3]);
             }
             dAl = rowsum16(dAl);
             if (l == kLPR - 1) dAs[cl * kN + n] += dAl;
@@ -452,8 +457,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                 float sB = 0.f, sC = 0.f;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    sB += red[w * kCH + tid];
-                    sC += red[4 * kCH + w * kCH + tid];
+                    sB += red[w * kCH + rtid];
+                    sC += red[4 * kCH + w * kCH + rtid];
                 }
                 if (s0 + tid < L) {
                     float *dst = p.wsBC + (((((int64_t)k * p.ntc + tc) * p.batch + b) * 2) * kN + n) * L + s0 + tid;
