@@ -197,8 +197,16 @@ __device__ __forceinline__ int64_t visit(const P &p, int k, int64_t l) {
 // barrier between directions (where the partial sums change hands) stays a full one.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// softplus(w) = log(1 + e^w) without overflow
-__device__ __forceinline__ float softplus(float w) { return w > 0.f ? w + log1pf(__expf(-w)) : log1pf(__expf(w)); }
+// softplus(w) = log(1 + e^w) = max(w, 0) + log1p(t), t = e^-|w|, on v_exp_f32 and v_log_f32.
+// log1p(t) is taken as ln(u) t / (u - 1) with u = 1 + t rounded to fp32 (Kahan's form: the
+// rounding error of u cancels between the logarithm and the denominator), and as t itself once
+// u rounds to 1 (t below half an ulp of 1, where log1p(t) = t to fp32 precision).
+__device__ __forceinline__ float softplus(float w) {
+    const float t = __builtin_amdgcn_exp2f(-fabsf(w) * kLog2e);
+    const float u = 1.f + t, d = u - 1.f;
+    const float l = d == 0.f ? t : __builtin_amdgcn_logf(u) * kLn2 * (t * __builtin_amdgcn_rcpf(d));
+    return fmaxf(w, 0.f) + l;
+}
 
 // silu(z) = z * sigmoid(z) on v_exp_f32 and v_rcp_f32 (large |z| saturates to 0 or z)
 __device__ __forceinline__ float silu(float z) {
