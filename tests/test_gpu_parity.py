@@ -88,6 +88,28 @@ def test_softplus_bias_and_optional_args(dtype):
     _check("selscan", base, inp, use_bias=True)
 
 
+def test_softplus_extreme_preactivations():
+    """delta = softplus(w + bias) over pre-activations far outside the workloads' range: |w| up to
+    40 (e^-|w| far below an ulp of 1, where log1p must not come from 1 + e^-|w|), values near
+    0 and exact zeros, for the forward and the backward (whose chain rule multiplies by
+    sigmoid(w + bias))."""
+    base = W.Workload("sp_ext", "selscan", 2, 300, 64, 16, "f32", True, index=12)
+    inp = W.generate(base, with_w=True, with_bias=True)
+    rng = np.random.default_rng(51012)
+    shape = inp["w"].shape
+    pick = rng.integers(0, 4, size=shape)
+    wv = np.where(pick == 0, rng.uniform(-40, 40, shape),
+                  np.where(pick == 1, rng.uniform(-1e-3, 1e-3, shape),
+                           np.where(pick == 2, -rng.uniform(10, 40, shape), rng.normal(0, 3, shape))))
+    wv[0, :5] = 0.0
+    inp["w"] = wv.astype(np.float32)
+    _say("softplus extremes")
+    _check("selscan", base, inp, softplus=True, use_bias=True)
+    errs = _bwd_run("f32", 2, 300, 64, softplus=True, bias=True, inp=inp)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL["f32"], (k, e)
+
+
 @pytest.mark.parametrize("L,dim,batch", [(1, 8, 1), (2, 24, 3), (17, 72, 2), (257, 8, 1), (64, 1, 2), (5, 3, 1)])
 def test_edge_shapes(L, dim, batch):
     w = W.Workload("edge", "selscan", batch, L, dim, 16, "f32", True, index=8)
@@ -269,12 +291,13 @@ def test_state_in_place_and_empty():
 _BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=False, D=True):
+def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=False, D=True, inp=None):
     import torch
     import oracle
     import selective_state_space_51_amd as S
     w = W.Workload("bwd", "selscan", batch, L, dim, 16, dtype, gate, index=12)
-    inp = W.generate(w, with_w=softplus, with_bias=bias)
+    if inp is None:
+        inp = W.generate(w, with_w=softplus, with_bias=bias)
     dy = W.generate_cotangent(batch, L, dim, dtype)
     h0v = W.generate_state(batch, dim) if h0 else None
     dev = lambda a, dt=dtype: None if a is None else PT.to_dev(a, dt)
