@@ -81,6 +81,9 @@ WORKLOADS: List[Workload] = [
     # the windowed cross-scan on the VMamba stage-1 map, windows of 7 x 7 pixels
     Workload("localmamba_local_ss2d_b32_56x56_w7_D192", "local_ss2d", 32, 56 * 56, 192, 16, "bf16", False, H=56, W=56,
              index=5, window=7),
+    # a video clip of 8 frames of 14 x 14 patches scanned spatial-first in both directions (the
+    # bidirectional scan on the frame-major token sequence), at an inner width of 768 channels
+    Workload("videomamba_bidir_b16_T8x14x14_D768", "bidir", 16, 8 * 14 * 14, 768, 16, "bf16", True, index=6),
 ]
 
 
