@@ -237,10 +237,16 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
     x, wt, bias = up(g["x"]), up(g["weight"]), up(g["bias"])
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
+    # rotate over copies of x and out totalling at least 512 MiB when one pair would fit in the
+    # 256 MB Infinity Cache (as the scan passes do)
+    pair = 2 * x.numel() * x.element_size()
+    copies = 1 if args.no_rotate or pair >= (512 << 20) else -(-(512 << 20) // pair)
+    xs = [(x, out)] + [(x.clone(), torch.empty_like(out)) for _ in range(copies - 1)]
     if two_d:
-        step = lambda: S.dwconv2d_fwd(x, wt, w.H, w.W, bias=bias, out=out, stream=stream)
+        step = lambda i: S.dwconv2d_fwd(xs[i % copies][0], wt, w.H, w.W, bias=bias, out=xs[i % copies][1],
+                                        stream=stream)
     else:
-        step = lambda: S.causal_conv1d_fwd(x, wt, bias=bias, out=out, stream=stream)
+        step = lambda i: S.causal_conv1d_fwd(xs[i % copies][0], wt, bias=bias, out=xs[i % copies][1], stream=stream)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -248,14 +254,14 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
         a.record(stream)
-        step()
+        step(args.warmup + i)
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -273,13 +279,14 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded: x ~ N(0,1); filter ~ N(0, 1/taps); bias ~ N(0,1))",
         "config": {"workload": w.name, "kind": "dwconv2d_3x3" if two_d else "causal_conv1d_k4", "batch": w.batch,
-                   "seqlen": w.seqlen, "dim": w.dim, "io_dtype": w.dtype, "silu": True, "pass": "conv"},
+                   "seqlen": w.seqlen, "dim": w.dim, "io_dtype": w.dtype, "silu": True, "pass": "conv",
+                   "input_sets": copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(w.name, "conv", w.kind), "kernel": kname, "kernel_ms": kern_ms,
                      "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:
-        del x, out
+        del x, out, xs
         torch.cuda.empty_cache()
         out_line["cpu_baseline"] = cpu_baseline_conv(w, g, two_d, min(args.cpu_channels, 1024))
     print(json.dumps(out_line))
@@ -307,6 +314,10 @@ def main() -> int:
                     help="pass the pre-activation w and a per-channel bias with delta_softplus=1, so the "
                          "kernels form delta = softplus(w + bias) themselves (w drawn so that delta has the "
                          "workload's distribution); no CPU baseline is taken with it")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="time every step on the same input and output buffers, even when they would fit in "
+                         "the 256 MB Infinity Cache (by default such workloads rotate over copies totalling "
+                         "at least 512 MiB)")
     ap.add_argument("--cpu-channels", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (a plain copy of known size, for scaling "
@@ -361,21 +372,47 @@ def main() -> int:
         h0 = up(W.generate_state(w.batch, w.dim, w.dstate))
         hl = torch.empty_like(h0)
 
-    ck = dy = bws = None
+    bws = None
     geo = dict(H=w.H, W=w.W, window=w.window)
-    dkw = dict(delta_bias=t.get("delta_bias"), delta_softplus=args.softplus)
-    if args.pass_ == "bwd":
-        _, ck = S.selscan_scan_fwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y,
-                                   chunk_states=True, workspace=ws, stream=stream, **geo, **dkw)
-        dy = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
+    bwd = args.pass_ == "bwd"
+    # Input sets: the workload's tensors, and for workloads whose buffers would fit in the 256 MB
+    # Infinity Cache, copies of them (with their own outputs) up to 512 MiB in all, which the
+    # steps rotate over so that every step streams its inputs from HBM.
+    first = dict(t=t, y=y)
+    if bwd:
+        _, first["ck"] = S.selscan_scan_fwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                            y=y, chunk_states=True, workspace=ws, stream=stream, **geo,
+                                            delta_bias=t.get("delta_bias"), delta_softplus=args.softplus)
+        first["dy"] = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
         bws = torch.empty(S.selscan_scan_bwd_workspace_bytes(op, w.batch, w.seqlen, w.dim, w.dstate,
                                                              S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32),
                           dtype=torch.uint8, device=dev)
+    run_bwd = lambda c, g=None: S.selscan_scan_bwd(
+        op, c["t"]["x"], c["t"]["delta"], c["t"]["A"], c["t"]["B"], c["t"]["C"], c["dy"], c["ck"], D=c["t"]["D"],
+        z=c["t"]["z"], workspace=bws, stream=stream, delta_bias=c["t"].get("delta_bias"),
+        delta_softplus=args.softplus, grads=g, **geo)
+    nbytes = lambda d: sum(v.numel() * v.element_size() for v in d.values() if isinstance(v, torch.Tensor))
+    set_bytes = nbytes(t) + y.numel() * y.element_size()
+    if bwd:
+        first["g"] = run_bwd(first)  # the gradient buffers of the first set
+        set_bytes += nbytes({"ck": first["ck"], "dy": first["dy"]}) + nbytes(first["g"])
+    rotate_to = 512 << 20
+    copies = 1 if args.no_rotate or set_bytes >= rotate_to else -(-rotate_to // set_bytes)
+    sets = [first]
+    for _ in range(copies - 1):
+        c = dict(t={k: None if v is None else v.clone() for k, v in t.items()}, y=torch.empty_like(y))
+        if bwd:
+            c["ck"], c["dy"] = first["ck"].clone(), first["dy"].clone()
+            c["g"] = run_bwd(c)  # each set writes its own gradient buffers
+        sets.append(c)
+    torch.cuda.synchronize()
 
-    def step():
-        if args.pass_ == "bwd":
-            S.selscan_scan_bwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], dy, ck, D=t["D"], z=t["z"],
-                               workspace=bws, stream=stream, **geo, **dkw)
+    def step(i):
+        c = sets[i % copies]
+        t, y = c["t"], c["y"]
+        dkw = dict(delta_bias=t.get("delta_bias"), delta_softplus=args.softplus)
+        if bwd:
+            run_bwd(c, c["g"])
         elif args.state:
             S.selscan_fwd_state(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], y=y, h0=h0,
                                 h_last=hl, workspace=ws, zoh=args.zoh, stream=stream, **dkw)
@@ -399,16 +436,16 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     # per-launch events on the stream the kernel runs on
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
         a.record(stream)
-        step()
+        step(args.warmup + i)
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -416,7 +453,6 @@ def main() -> int:
     ms_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(launch_ms))
     value = w.elements / (ms_step * 1e-3)
-    bwd = args.pass_ == "bwd"
     alg = bwd_algorithmic_bytes(w) if bwd else w.algorithmic_bytes()
     if args.softplus:
         alg += (2 if bwd else 1) * w.ndir * w.dim * 4  # the delta bias read (and its gradient written)
@@ -442,7 +478,7 @@ def main() -> int:
                    "dstate": w.dstate, "directions": w.ndir, "io_dtype": w.dtype, "gate": w.gate,
                    "window": w.window or None,
                    "state_io": bool(args.state), "pass": args.pass_, "bbar": "zoh" if args.zoh else "delta*B",
-                   "delta_softplus": bool(args.softplus)},
+                   "delta_softplus": bool(args.softplus), "input_sets": copies},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
                      "work_per_element": ("1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
@@ -455,11 +491,11 @@ def main() -> int:
                      "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline and not args.softplus and bwd:
-        del t, y, ws, h0, hl, ck, dy, bws
+        del t, y, ws, h0, hl, first, sets, bws
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline_bwd(w, min(args.cpu_channels, 2048))
     elif not args.no_cpu_baseline and not args.softplus:
-        del t, y, ws, h0, hl
+        del t, y, ws, h0, hl, first, sets
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels)
     print(json.dumps(out))

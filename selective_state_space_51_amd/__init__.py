@@ -409,10 +409,11 @@ def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, del
 
 
 def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None,
-                     delta_softplus=False, H=0, W=0, window=0, workspace=None, stream=None):
+                     delta_softplus=False, H=0, W=0, window=0, workspace=None, stream=None, grads=None):
     """Gradients of sum(dy * y) for y = selscan_scan_fwd(op, ...) with chunk_states from that call.
     Returns a dict: dx, ddelta, dA, dB, dC, and dD / dz / ddelta_bias for the inputs that were given;
-    per-direction gradients carry the leading direction axis."""
+    per-direction gradients carry the leading direction axis.  ``grads``: a dict of the same
+    keys, shapes and dtypes to write into instead of allocating."""
     torch = _torch()
     bt, L, dim, N, K, lead = _scan_shapes(op, x, A, H, W)
     io = x.dtype
@@ -421,16 +422,23 @@ def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, de
                        ("z", z, (bt, L, dim)), ("delta_bias", delta_bias, lead + (dim,)),
                        ("dy", dy, (bt, L, dim))):
         _shape_check(n_, t_, s_)
-    f32 = dict(dtype=torch.float32, device=x.device)
-    g = {"dx": torch.empty_like(x), "ddelta": torch.empty(lead + (bt, L, dim), dtype=io, device=x.device),
-         "dA": torch.empty(lead + (dim, N), **f32), "dB": torch.empty(lead + (bt, L, N), dtype=io, device=x.device),
-         "dC": torch.empty(lead + (bt, L, N), dtype=io, device=x.device)}
+    f32 = torch.float32
+    spec = {"dx": ((bt, L, dim), io), "ddelta": (lead + (bt, L, dim), io), "dA": (lead + (dim, N), f32),
+            "dB": (lead + (bt, L, N), io), "dC": (lead + (bt, L, N), io)}
     if D is not None:
-        g["dD"] = torch.empty(lead + (dim,), **f32)
+        spec["dD"] = (lead + (dim,), f32)
     if z is not None:
-        g["dz"] = torch.empty_like(x)
+        spec["dz"] = ((bt, L, dim), io)
     if delta_bias is not None:
-        g["ddelta_bias"] = torch.empty(lead + (dim,), **f32)
+        spec["ddelta_bias"] = (lead + (dim,), f32)
+    if grads is None:
+        g = {k: torch.empty(shp, dtype=dt, device=x.device) for k, (shp, dt) in spec.items()}
+    else:
+        if set(grads) != set(spec):
+            raise ValueError(f"grads must hold exactly {sorted(spec)}")
+        for k, (shp, _) in spec.items():
+            _shape_check(k, grads[k], shp)
+        g = grads
     need = selscan_scan_bwd_workspace_bytes(op, bt, L, dim, N, _dtype_code(x))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
