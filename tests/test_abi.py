@@ -225,6 +225,24 @@ def test_python_binding_rejects_host_tensors():
         S.selscan_fwd(x, x, torch.zeros(8, 16), x.new_zeros(1, 4, 16), x.new_zeros(1, 4, 16), y=x.clone())
 
 
+def test_python_scan_bwd_checks_given_grads():
+    """selscan_scan_bwd(grads=...) must hold exactly the gradients of the given inputs, at their
+    shapes; both checks come before any pointer is taken (host tensors suffice here)."""
+    import torch
+    bt, L, dim = 1, 4, 8
+    x = torch.zeros(bt, L, dim, dtype=torch.bfloat16)
+    bc = x.new_zeros(bt, L, 16)
+    A = torch.zeros(dim, 16)
+    good = {"dx": x.clone(), "ddelta": x.clone(), "dA": torch.zeros(dim, 16), "dB": bc.clone(), "dC": bc.clone()}
+    call = lambda g: S.selscan_scan_bwd(0, x, x, A, bc, bc, x, torch.zeros(1), grads=g)
+    with pytest.raises(ValueError, match="grads must hold"):
+        call({k: v for k, v in good.items() if k != "dC"})
+    with pytest.raises(ValueError, match="grads must hold"):
+        call(dict(good, dz=x.clone()))
+    with pytest.raises(ValueError, match="dB has shape"):
+        call(dict(good, dB=x.clone()))
+
+
 def test_local_ss2d_window_checks():
     loc = lambda H, W, w: L.local_ss2d_fwd(P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0,
                                            P + 8 * MB, 1, H, W, w, 8, 16, 1, None, 0, None)

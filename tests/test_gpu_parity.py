@@ -438,6 +438,13 @@ def test_scan_entry_points_match_single_direction():
     assert set(g1) == set(g2)
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
+    # into preallocated gradient buffers (filled with NaN first): the same bits
+    g3 = {k: torch.full_like(v, float("nan")) for k, v in g1.items()}
+    out = S.selscan_scan_bwd(0, x, dl, A, B, C, dy, ck1, grads=g3, **args)
+    torch.cuda.synchronize()
+    assert out is g3
+    for k in g1:
+        assert torch.equal(g1[k], g3[k]), k
 
 
 @pytest.mark.parametrize("H,Wd,win,dim", [(6, 4, 2, 16), (8, 8, 4, 40), (9, 6, 3, 24), (4, 4, 1, 8), (6, 6, 6, 8),
