@@ -39,12 +39,12 @@ def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
 
 
 def load(path: Optional[str] = None):
-    """Load liboracle.so, building it first only if it is not there."""
+    """Load liboracle.so, building it first if it is not there or is older than oracle.c."""
     global _lib
     if path is None and _lib is not None:
         return _lib
     p = path or _LIB_PATH
-    if not os.path.exists(p):
+    if not os.path.exists(p) or (path is None and os.path.getmtime(_SRC) > os.path.getmtime(p)):
         build(out=p)
     lib = ctypes.CDLL(p)
     dp = ctypes.c_void_p
@@ -58,7 +58,7 @@ def load(path: Optional[str] = None):
     lib.oracle_ss2d.restype = ci
     lib.oracle_local_ss2d.argtypes = [dp] * 8 + [ci, ci, dp, i64, i64, i64, i64, i64, i64, ci]
     lib.oracle_local_ss2d.restype = ci
-    lib.oracle_selscan_bwd.argtypes = [dp] * 8 + [ci] + [dp] * 11 + [i64, i64, i64, i64, ci]
+    lib.oracle_selscan_bwd.argtypes = [dp] * 8 + [ci, ci] + [dp] * 11 + [i64, i64, i64, i64, ci]
     lib.oracle_selscan_bwd.restype = ci
     lib.oracle_scan_order.argtypes = [ci, ci, i64, i64, i64, i64, dp]
     lib.oracle_scan_order.restype = ci
@@ -160,8 +160,9 @@ def local_ss2d(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=None,
 
 
 def selscan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
-                nthreads=0, lib=None):
-    """Gradients of sum(dy * selscan(...)) (Euler Bbar) with respect to every input.
+                zoh=False, nthreads=0, lib=None):
+    """Gradients of sum(dy * selscan(...)) with respect to every input (zoh: of the
+    zero-order-hold form).
 
     Returns a dict with dx, ddelta (with respect to the delta argument, before bias and
     softplus), dA, dB, dC, and dD / dz / ddelta_bias / dh0 for the inputs that are given.
@@ -183,7 +184,8 @@ def selscan_bwd(x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_so
         out["dh0"] = np.empty((bt, dim, N))
     g = lambda k: _ptr(out.get(k))
     rc = lib.oracle_selscan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy), g("dx"),
+                                _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh)), _ptr(h0), _ptr(dy),
+                                g("dx"),
                                 g("ddelta"), g("dA"), g("dB"), g("dC"), g("dD"), g("dz"), g("ddelta_bias"),
                                 g("dh0"), bt, L, dim, N, int(nthreads))
     if rc != 0:
@@ -206,7 +208,7 @@ def scan_orders(kind, L, H=0, W=0, window=0, lib=None):
 
 
 def multi_bwd(kind, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, H=0, W=0,
-              window=0, nthreads=0, lib=None):
+              window=0, zoh=False, nthreads=0, lib=None):
     """Gradients of sum(dy * y) for the multi-direction scans (bidirectional, SS2D, windowed):
     y = (sum_k scatter_k(scan_k(gather_k(x), gather_k(params_k)))) * silu(z).
 
@@ -224,13 +226,13 @@ def multi_bwd(kind, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delt
         dyp = dy * z * sg
         if kind == "bidir":
             yp = selscan_bidir(x, delta, A, B, C, D=D, delta_bias=delta_bias, delta_softplus=delta_softplus,
-                               nthreads=nthreads, lib=lib)
+                               zoh=zoh, nthreads=nthreads, lib=lib)
         elif kind == "ss2d":
             yp = ss2d(x, delta, A, B, C, H, W, D=D, delta_bias=delta_bias, delta_softplus=delta_softplus,
-                      nthreads=nthreads, lib=lib)
+                      zoh=zoh, nthreads=nthreads, lib=lib)
         else:
             yp = local_ss2d(x, delta, A, B, C, H, W, window, D=D, delta_bias=delta_bias,
-                            delta_softplus=delta_softplus, nthreads=nthreads, lib=lib)
+                            delta_softplus=delta_softplus, zoh=zoh, nthreads=nthreads, lib=lib)
     else:
         dyp = dy
     out = {"dx": np.zeros_like(x), "ddelta": np.zeros_like(delta), "dA": np.zeros_like(A), "dB": np.zeros_like(B),
@@ -243,7 +245,7 @@ def multi_bwd(kind, x, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delt
         o = orders[k]
         g = selscan_bwd(x[:, o], delta[k][:, o], A[k], B[k][:, o], C[k][:, o], dyp[:, o],
                         D=None if D is None else D[k], delta_bias=None if delta_bias is None else delta_bias[k],
-                        delta_softplus=delta_softplus, nthreads=nthreads, lib=lib)
+                        delta_softplus=delta_softplus, zoh=zoh, nthreads=nthreads, lib=lib)
         out["dx"][:, o] += g["dx"]
         out["ddelta"][k][:, o] = g["ddelta"]
         out["dB"][k][:, o] = g["dB"]

@@ -25,7 +25,8 @@
  *
  * Readings where the pages are silent or disagree (each listed in the design notes):
  *  - Bbar: the default is Bbar = delta * B (Euler; what the workload statement uses);
- *    zoh != 0 selects the [MS] zero-order-hold Bbar = expm1(delta*A)/A * B (delta*B at A = 0).
+ *    zoh != 0 selects the [MS] zero-order-hold Bbar = expm1(delta*A)/A * B (delta*B at A = 0),
+ *    in the forward and in the backward (input_coef).
  *  - initial state is zero unless h0 is given; D, z, delta_bias may be absent.
  *  - bidirectional fusion is the SUM of the forward output and the backward output
  *    re-reversed to token order (the page concatenates); one gate on the sum.
@@ -449,8 +450,40 @@ typedef struct {
     const double *x, *delta, *A, *B, *C, *D, *z, *delta_bias, *h0, *dy;
     double *dx, *ddelta, *dz, *dh0;           /* per stream: written by the stream's thread */
     int64_t batch, L, dim, N;
-    int softplus;
+    int softplus, zoh;
 } bwd_t;
+
+/* The input coefficient of one step and its two partial derivatives.  Euler: beta = delta.
+ * Zero-order hold ([MS] "选择性 SSM 的数学形式"): beta = (exp(delta a) - 1) / a, i.e.
+ * delta * phi(y) with y = delta a and phi(y) = (e^y - 1) / y (beta = delta at a = 0).  Then
+ *   d beta / d delta = e^y
+ *   d beta / d a     = delta^2 phi'(y),  phi'(y) = (e^y (y - 1) + 1) / y^2
+ *                                                = sum_k (k + 1) y^k / (k + 2)!
+ * (the series near y = 0, where the closed form cancels; 1/2 at y = 0).                  */
+static void input_coef(int zoh, double dt, double a, double *beta, double *dbeta_ddt, double *dbeta_da) {
+    if (!zoh) {
+        *beta = dt;
+        *dbeta_ddt = 1.0;
+        *dbeta_da = 0.0;
+        return;
+    }
+    const double y = dt * a;
+    *beta = a != 0.0 ? expm1(y) / a : dt;
+    *dbeta_ddt = exp(y);
+    double dphi;
+    if (fabs(y) < 0.5) {
+        double term = 1.0, fact = 2.0; /* y^k and (k + 2)! */
+        dphi = 0.0;
+        for (int k = 0; k < 30; ++k) {
+            dphi += (k + 1) * term / fact;
+            term *= y;
+            fact *= k + 3;
+        }
+    } else {
+        dphi = (exp(y) * (y - 1.0) + 1.0) / (y * y);
+    }
+    *dbeta_da = dt * dt * dphi;
+}
 
 typedef struct {
     const bwd_t *s;
@@ -463,12 +496,13 @@ typedef struct {
     int failed;
 } bwd_job_t;
 
-/* Reverse-mode derivative of the recurrence of scan_stream (Euler Bbar), for stream (b, d),
- * given dL/dy.  The forward is rerun and every state kept; then, from t = L-1 down to 0, with
- * g[n] the derivative of L with respect to h_t[n]:
+/* Reverse-mode derivative of the recurrence of scan_stream, for stream (b, d), given dL/dy.
+ * The forward is rerun and every state kept; then, from t = L-1 down to 0, with g[n] the
+ * derivative of L with respect to h_t[n]:
  *   y_t = yp_t * silu(z_t), yp_t = sum_n C_t[n] h_t[n] + D x_t
- *   h_t[n] = e_t[n] h_{t-1}[n] + delta_t B_t[n] x_t,   e_t[n] = exp(delta_t A[n])
- * so  g_t += C_t dyp_t;  then the parameters of step t take their share of g_t and
+ *   h_t[n] = e_t[n] h_{t-1}[n] + beta_t[n] B_t[n] x_t,   e_t[n] = exp(delta_t A[n])
+ * (beta = delta for Euler, the zero-order-hold coefficient otherwise; input_coef) so
+ * g_t += C_t dyp_t;  then the parameters of step t take their share of g_t and
  * g_{t-1} = e_t g_t.                                                                       */
 static void bwd_stream(bwd_job_t *j, int64_t b, int64_t d) {
     const bwd_t *s = j->s;
@@ -486,8 +520,11 @@ static void bwd_stream(bwd_job_t *j, int64_t b, int64_t d) {
         j->dt[t] = dt;
         const double xv = s->x[i];
         const double *Bt = s->B + (b * L + t) * N;
-        for (int64_t n = 0; n < N; ++n)
-            h[(t + 1) * N + n] = exp(dt * Arow[n]) * h[t * N + n] + dt * Bt[n] * xv;
+        for (int64_t n = 0; n < N; ++n) {
+            double beta, dbdt, dbda;
+            input_coef(s->zoh, dt, Arow[n], &beta, &dbdt, &dbda);
+            h[(t + 1) * N + n] = exp(dt * Arow[n]) * h[t * N + n] + beta * Bt[n] * xv;
+        }
     }
     double *g = (double *)calloc((size_t)N, sizeof(double));
     if (!g) { j->failed = 1; return; }
@@ -511,10 +548,12 @@ static void bwd_stream(bwd_job_t *j, int64_t b, int64_t d) {
             g[n] += Ct[n] * dyp;
             j->dC[(b * L + t) * N + n] += dyp * ht[n];
             const double e = exp(dt * Arow[n]);
-            ddt += g[n] * (Arow[n] * e * hp[n] + Bt[n] * xv);
-            j->dA[d * N + n] += g[n] * dt * e * hp[n];
-            j->dB[(b * L + t) * N + n] += g[n] * dt * xv;
-            dxv += g[n] * dt * Bt[n];
+            double beta, dbdt, dbda;
+            input_coef(s->zoh, dt, Arow[n], &beta, &dbdt, &dbda);
+            ddt += g[n] * (Arow[n] * e * hp[n] + dbdt * Bt[n] * xv);
+            j->dA[d * N + n] += g[n] * (dt * e * hp[n] + dbda * Bt[n] * xv);
+            j->dB[(b * L + t) * N + n] += g[n] * beta * xv;
+            dxv += g[n] * beta * Bt[n];
             g[n] *= e;
         }
         s->dx[i] = dxv;
@@ -533,14 +572,14 @@ static void *bwd_worker(void *p) {
     return NULL;
 }
 
-/* Backward of oracle_selscan (Euler Bbar; zoh is not supported here).  Inputs as for
- * oracle_selscan plus dy [batch][L][dim].  Outputs: dx, ddelta [batch][L][dim] (derivative
+/* Backward of oracle_selscan (Euler Bbar, or the zero-order hold when zoh != 0).  Inputs as
+ * for oracle_selscan plus dy [batch][L][dim].  Outputs: dx, ddelta [batch][L][dim] (derivative
  * with respect to the delta argument, before bias and softplus); dA [dim][N]; dB, dC
  * [batch][L][N]; dD, ddelta_bias [dim]; dz [batch][L][dim]; dh0 [batch][dim][N].  dx,
  * ddelta, dA, dB, dC are required; dD, dz, ddelta_bias, dh0 may be NULL (not written).    */
 int oracle_selscan_bwd(const double *x, const double *delta, const double *A, const double *B,
                        const double *C, const double *D, const double *z, const double *delta_bias,
-                       int delta_softplus, const double *h0, const double *dy, double *dx, double *ddelta,
+                       int delta_softplus, int zoh, const double *h0, const double *dy, double *dx, double *ddelta,
                        double *dA, double *dB, double *dC, double *dD, double *dz, double *ddelta_bias,
                        double *dh0, int64_t batch, int64_t L, int64_t dim, int64_t N, int nthreads) {
     if (bad_common(x, delta, A, B, C, dy, batch, L, dim, N) || !dx || !ddelta || !dA || !dB || !dC) return -1;
@@ -555,7 +594,7 @@ int oracle_selscan_bwd(const double *x, const double *delta, const double *A, co
     }
     if (streams == 0 || L == 0) return 0;
     bwd_t s = {x, delta, A, B, C, D, z, delta_bias, h0, dy, dx, ddelta, dz, dh0, batch, L, dim, N,
-               delta_softplus};
+               delta_softplus, zoh};
     nthreads = resolve_threads(nthreads, streams);
     bwd_job_t jobs[256];
     pthread_t tid[256];

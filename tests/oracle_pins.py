@@ -380,13 +380,23 @@ def pin_local_ss2d_limits(lib):
 
 
 # --------------------------------------------------------------------------- backward
-def _bwd_case(seed, bt=2, L=9, dim=3, N=4, gate=True, softplus=False, bias=True, h0=True, D=True):
+def _bwd_case(seed, bt=2, L=9, dim=3, N=4, gate=True, softplus=False, bias=True, h0=True, D=True, zoh=False):
     x, z, dt, A, B, C, Dv = _case(seed, bt, L, dim, N)
     r = _rng(seed + 1000)
     delta = np.log(np.expm1(dt)) if softplus else dt
+    if zoh:
+        # |delta A| on both sides of the oracle's series / closed-form switch at 1/2, and the
+        # special values: A = 0 (Bbar = delta B), a tiny A, a positive A
+        A = -np.exp(r.uniform(-1.0, 3.5, (dim, N)))
+        A[0, 0] = 0.0
+        A[-1, -1] = 1e-9
+        A[1 % dim, 1 % N] = 0.7
+    bv = 0.1 * r.standard_normal(dim)
+    if zoh:
+        bv = np.abs(bv)  # delta stays positive: with these |A|, exp(delta A) > 1 would blow up
     args = dict(x=x, delta=delta, A=A, B=B, C=C, D=Dv if D else None, z=z if gate else None,
-                delta_bias=0.1 * r.standard_normal(dim) if bias else None, delta_softplus=softplus,
-                h0=r.standard_normal((bt, dim, N)) if h0 else None)
+                delta_bias=bv if bias else None, delta_softplus=softplus,
+                h0=r.standard_normal((bt, dim, N)) if h0 else None, zoh=zoh)
     dy = r.standard_normal((bt, L, dim))
     return args, dy
 
@@ -406,7 +416,8 @@ def pin_bwd_directional_fd(lib):
     (separately pinned) forward oracle along random directions, for every input, with and
     without gate, skip, bias, softplus and initial state.  fp64: the two agree to ~1e-9."""
     for i, kw in enumerate([dict(), dict(softplus=True), dict(gate=False, bias=False, h0=False),
-                            dict(D=False, softplus=True, L=17, dim=2, N=3)]):
+                            dict(D=False, softplus=True, L=17, dim=2, N=3), dict(zoh=True),
+                            dict(zoh=True, softplus=True, L=13, dim=4, N=5), dict(zoh=True, gate=False, h0=False)]):
         args, dy = _bwd_case(40 + i, **kw)
         g = oracle.selscan_bwd(dy=dy, lib=lib, **args)
         r = _rng(90 + i)
@@ -424,8 +435,29 @@ def pin_bwd_directional_fd(lib):
 
 
 def pin_bwd_elementwise_fd(lib):
-    """Every entry of every gradient of a tiny problem against its own central difference."""
-    args, dy = _bwd_case(77, bt=2, L=4, dim=2, N=3, softplus=True)
+    """Every entry of every gradient of a tiny problem against its own central difference
+    (Euler and zero-order-hold Bbar)."""
+    for zoh in (False, True):
+        _bwd_elementwise(lib, *_bwd_case(77 + zoh, bt=2, L=4, dim=2, N=3, softplus=True, zoh=zoh))
+
+
+def pin_bwd_zoh_at_A_zero(lib):
+    """With A = 0 the zero-order-hold step is the Euler step (Bbar = delta B, exp(0) = 1), so
+    every gradient but dA equals the Euler backward's bit for bit; dA differs (its input term,
+    delta^2 phi'(0) B x = delta^2 B x / 2, is absent from the Euler form) and is pinned by the
+    finite differences."""
+    args, dy = _bwd_case(5, bt=2, L=11, dim=3, N=4, softplus=True)
+    args["A"] = np.zeros_like(args["A"])
+    ge = oracle.selscan_bwd(dy=dy, lib=lib, **args)
+    gz = oracle.selscan_bwd(dy=dy, lib=lib, **dict(args, zoh=True))
+    assert set(ge) == set(gz)
+    for k in ge:
+        if k != "dA":
+            assert np.array_equal(ge[k], gz[k]), k
+    assert not np.array_equal(ge["dA"], gz["dA"])
+
+
+def _bwd_elementwise(lib, args, dy):
     g = oracle.selscan_bwd(dy=dy, lib=lib, **args)
     eps = 1e-6
     for name, gname in _GRAD_OF.items():
@@ -442,15 +474,17 @@ def pin_bwd_elementwise_fd(lib):
 
 def pin_multi_bwd_fd(lib):
     """Gradients of the bidirectional, SS2D and windowed scans against central finite
-    differences of their (separately pinned) forward oracles along random directions."""
+    differences of their (separately pinned) forward oracles along random directions (the SS2D
+    case also with the zero-order-hold Bbar)."""
     r = _rng(321)
-    for kind, H, W, w in [("bidir", 0, 0, 0), ("ss2d", 3, 4, 0), ("local_ss2d", 4, 6, 2)]:
+    for kind, H, W, w, zoh in [("bidir", 0, 0, 0, False), ("ss2d", 3, 4, 0, False), ("local_ss2d", 4, 6, 2, False),
+                               ("ss2d", 4, 3, 0, True)]:
         K = 2 if kind == "bidir" else 4
         bt, L, dim, N = 2, (7 if kind == "bidir" else H * W), 3, 3
         args = dict(x=r.standard_normal((bt, L, dim)), delta=np.exp(r.uniform(-5, -1.5, (K, bt, L, dim))),
                     A=-np.exp(r.uniform(-1.0, 1.5, (K, dim, N))), B=r.standard_normal((K, bt, L, N)),
                     C=r.standard_normal((K, bt, L, N)), D=r.standard_normal((K, dim)), z=r.standard_normal((bt, L, dim)),
-                    delta_bias=0.1 * r.standard_normal((K, dim)))
+                    delta_bias=0.1 * r.standard_normal((K, dim)), zoh=zoh)
         dy = r.standard_normal((bt, L, dim))
 
         def loss(a):

@@ -53,12 +53,20 @@ MUTATIONS = [
     ("local_window_rows_from_width", "*row = (wi / nwx) * w + r / w;", "*row = (wi / nwx) * w + (r / w + 1) % w;"),
     # backward
     ("bwd_adjoint_not_decayed", "            g[n] *= e;\n", ""),
-    ("bwd_dA_missing_decay", "j->dA[d * N + n] += g[n] * dt * e * hp[n];", "j->dA[d * N + n] += g[n] * dt * hp[n];"),
-    ("bwd_dB_missing_delta", "j->dB[(b * L + t) * N + n] += g[n] * dt * xv;", "j->dB[(b * L + t) * N + n] += g[n] * xv;"),
+    ("bwd_dA_missing_decay", "j->dA[d * N + n] += g[n] * (dt * e * hp[n] + dbda * Bt[n] * xv);",
+     "j->dA[d * N + n] += g[n] * (dt * hp[n] + dbda * Bt[n] * xv);"),
+    ("bwd_dB_missing_delta", "j->dB[(b * L + t) * N + n] += g[n] * beta * xv;", "j->dB[(b * L + t) * N + n] += g[n] * xv;"),
     ("bwd_dC_previous_state", "j->dC[(b * L + t) * N + n] += dyp * ht[n];", "j->dC[(b * L + t) * N + n] += dyp * hp[n];"),
     ("bwd_dx_missing_skip", "double dxv = Dd * dyp, ddt = 0.0;", "double dxv = 0.0, ddt = 0.0;"),
-    ("bwd_ddelta_missing_input_term", "ddt += g[n] * (Arow[n] * e * hp[n] + Bt[n] * xv);",
+    ("bwd_ddelta_missing_input_term", "ddt += g[n] * (Arow[n] * e * hp[n] + dbdt * Bt[n] * xv);",
      "ddt += g[n] * (Arow[n] * e * hp[n]);"),
+    # zero-order-hold backward
+    ("bwd_zoh_input_term_not_decayed", "*dbeta_ddt = exp(y);", "*dbeta_ddt = 1.0;"),
+    ("bwd_zoh_dA_input_term_dropped", "*dbeta_da = dt * dt * dphi;", "*dbeta_da = 0.0;"),
+    ("bwd_zoh_dphi_series_weight", "dphi += (k + 1) * term / fact;", "dphi += term / fact;"),
+    ("bwd_zoh_dphi_closed_form_sign", "dphi = (exp(y) * (y - 1.0) + 1.0) / (y * y);",
+     "dphi = (exp(y) * (y + 1.0) - 1.0) / (y * y);"),
+    ("bwd_zoh_euler_coefficient", "*beta = a != 0.0 ? expm1(y) / a : dt;", "*beta = dt;"),
     ("bwd_softplus_derivative_sign", "ddt * sigmoid(j->w[t])", "ddt * sigmoid(-j->w[t])"),
     ("bwd_silu_derivative_sign", "(1.0 + zv * (1.0 - sg))", "(1.0 - zv * (1.0 - sg))"),
     ("bwd_gate_not_applied", "dyp = s->dy[i] * zv * sg;", "dyp = s->dy[i];"),
