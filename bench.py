@@ -38,6 +38,10 @@ FLOP_EQ_PER_ELEMENT_BWD = 38
 # y = t ln2, a 4-FMA series, e - 1, one reciprocal (4 FMA slots), a product, the switch (compare +
 # select) and the factor's product: 13 slots over the Euler form's 8 = 21 slots = 42 flop-equivalents.
 FLOP_EQ_PER_ELEMENT_ZOH = 42
+# Zero-order-hold backward: the Euler backward's 19 slots, plus phi(y) (y = t ln2, one reciprocal,
+# e - 1 and its product: 7 slots), phi'(y) = (e - phi)/y (2), and one more product in each of
+# u, dx, dB and the delta input term and three in the A input term (7): 35 slots = 70 flop-eq.
+FLOP_EQ_PER_ELEMENT_BWD_ZOH = 70
 METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
@@ -45,7 +49,7 @@ LIB_SO = os.path.join(ROOT, "selective_state_space_51_amd", "libselscan.so")
 # the kernels (mangled names) a counter record covers, per pass and workload kind; the record is
 # valid while their machine code in the built library is unchanged
 _FWD = "_ZN12_GLOBAL__N_115selscan_chunkedItLi{k}ELb0EEEvNS_6ParamsE"
-_BWD = ("_ZN12_GLOBAL__N_119selscan_bwd_chunkedItLi{k}EEEvNS_9BwdParamsE",
+_BWD = ("_ZN12_GLOBAL__N_119selscan_bwd_chunkedItLi{k}ELb0EEEvNS_9BwdParamsE",
         "_ZN12_GLOBAL__N_118selscan_bwd_reduceItLi{k}EEEvNS_15BwdReduceParamsE")
 _KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
 
@@ -359,8 +363,8 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    if args.zoh and args.pass_ != "fwd":
-        print("--zoh applies to the forward only", file=sys.stderr)
+    if args.zoh and args.pass_ == "conv":
+        print("--zoh applies to the scan passes only", file=sys.stderr)
         return 2
     if args.pass_ == "conv":
         return conv_bench(args, w, S, W, torch, np, up, dev)
@@ -382,7 +386,8 @@ def main() -> int:
     if bwd:
         _, first["ck"] = S.selscan_scan_fwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                                             y=y, chunk_states=True, workspace=ws, stream=stream, **geo,
-                                            delta_bias=t.get("delta_bias"), delta_softplus=args.softplus)
+                                            delta_bias=t.get("delta_bias"), delta_softplus=args.softplus,
+                                            zoh=args.zoh)
         first["dy"] = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype))
         bws = torch.empty(S.selscan_scan_bwd_workspace_bytes(op, w.batch, w.seqlen, w.dim, w.dstate,
                                                              S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32),
@@ -390,7 +395,7 @@ def main() -> int:
     run_bwd = lambda c, g=None: S.selscan_scan_bwd(
         op, c["t"]["x"], c["t"]["delta"], c["t"]["A"], c["t"]["B"], c["t"]["C"], c["dy"], c["ck"], D=c["t"]["D"],
         z=c["t"]["z"], workspace=bws, stream=stream, delta_bias=c["t"].get("delta_bias"),
-        delta_softplus=args.softplus, grads=g, **geo)
+        delta_softplus=args.softplus, zoh=args.zoh, grads=g, **geo)
     nbytes = lambda d: sum(v.numel() * v.element_size() for v in d.values() if isinstance(v, torch.Tensor))
     set_bytes = nbytes(t) + y.numel() * y.element_size()
     if bwd:
@@ -457,7 +462,10 @@ def main() -> int:
     if args.softplus:
         alg += (2 if bwd else 1) * w.ndir * w.dim * 4  # the delta bias read (and its gradient written)
     hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
-    flop_eq = FLOP_EQ_PER_ELEMENT_BWD if bwd else (FLOP_EQ_PER_ELEMENT_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT)
+    if bwd:
+        flop_eq = FLOP_EQ_PER_ELEMENT_BWD_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT_BWD
+    else:
+        flop_eq = FLOP_EQ_PER_ELEMENT_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT
     alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
     traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(w.name, args.pass_, w.kind)
@@ -481,7 +489,8 @@ def main() -> int:
                    "delta_softplus": bool(args.softplus), "input_sets": copies},
         "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
-                     "work_per_element": ("1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
+                     "work_per_element": ("1 exp2 + 1 rcp + 27 fp32 ops = 70 fp32 flop-equivalents" if bwd and args.zoh
+                                          else "1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
                                           "1 exp2 + 1 rcp + 13 fp32 ops = 42 fp32 flop-equivalents" if args.zoh else
                                           "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents"),
                      "kernel": "selscan_bwd_chunked + selscan_bwd_reduce" if bwd else "selscan_chunked",

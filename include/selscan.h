@@ -40,8 +40,8 @@
  *      SELSCAN_E_ALIGN        a pointer is not aligned to its element size (4 B for fp32
  *                             arrays, 2 B for bf16 arrays)
  *      SELSCAN_E_ALIAS        y overlaps an input array
- *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits (ZOH in a
- *                             backward call), or an SS2D map with H*W >= 2^31 pixels
+ *      SELSCAN_E_UNSUPPORTED  dstate != 16, unknown io_dtype or unknown flag bits, or an SS2D
+ *                             map with H*W >= 2^31 pixels
  *      SELSCAN_E_WORKSPACE    workspace smaller than selscan_workspace_bytes(...)
  *      SELSCAN_E_HIP          the kernel launch was rejected by the HIP runtime
  *    Non-finite inputs are not checked; they propagate.
@@ -73,9 +73,9 @@ typedef enum {
 
 /* flag bits */
 #define SELSCAN_FLAG_DELTA_SOFTPLUS 1u /* delta_t = softplus(delta + delta_bias) */
-/* forward entry points only: zero-order-hold Bbar = (exp(delta A) - 1) / A * B in place of
- * delta * B (the page's exact discretisation; see the header comment); the backward entry
- * points return SELSCAN_E_UNSUPPORTED for it */
+/* scan entry points: zero-order-hold Bbar = (exp(delta A) - 1) / A * B in place of delta * B
+ * (the page's exact discretisation; see the header comment).  A backward call takes the flag
+ * its forward was run with (the chunk states differ between the two forms). */
 #define SELSCAN_FLAG_ZOH 2u
 /* convolution entry points only: SiLU on the convolution's output */
 #define SELSCAN_FLAG_SILU 4u
@@ -126,11 +126,14 @@ int selscan_fwd_state(const void *x, const void *delta, const float *A, const vo
 size_t selscan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
 /*
- * selscan_bwd - gradients of L = sum(dy * y) for y = selscan_fwd(...) (Euler Bbar), with the
- * states recomputed from the chunk states the forward saved instead of stored: "Mamba论文"
+ * selscan_bwd - gradients of L = sum(dy * y) for y = selscan_fwd(...), with the states
+ * recomputed from the chunk states the forward saved instead of stored: "Mamba论文"
  * (backward recomputes the intermediate states) and "Mamba Series from Selective State
- * Spaces to Visual State Space Models", section 核心洞察.  Inputs are exactly those of the
- * forward call (with its h0 folded into chunk_states) plus
+ * Spaces to Visual State Space Models", section 核心洞察.  flags: SELSCAN_FLAG_DELTA_SOFTPLUS
+ * and SELSCAN_FLAG_ZOH as in the forward call (with the zero-order hold, d Bbar / d delta =
+ * exp(delta A) B and d Bbar / dA = delta^2 phi'(delta A) B, phi(y) = (e^y - 1) / y, from
+ * section 选择性 SSM 的数学形式).  Inputs are exactly those of the forward call (with its h0
+ * folded into chunk_states) plus
  *   dy           : [batch][seqlen][dim] io_dtype, dL/dy
  * Outputs (caller-owned, written in full):
  *   dx, ddelta   : [batch][seqlen][dim] io_dtype; ddelta is with respect to the delta

@@ -241,9 +241,9 @@ def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
 
 
 def selscan_bwd(x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None, delta_softplus=False,
-                dh0=False, workspace=None, stream=None):
-    """Gradients of sum(dy * y) for y = selscan_fwd(...); chunk_states from selscan_fwd_state on the
-    same inputs.  Returns a dict: dx, ddelta, dA, dB, dC, and dD / dz / ddelta_bias / dh0 for the
+                dh0=False, zoh=False, workspace=None, stream=None):
+    """Gradients of sum(dy * y) for y = selscan_fwd(...) (zoh: of the zero-order-hold form);
+    chunk_states from selscan_fwd_state on the same inputs (and the same form).  Returns a dict: dx, ddelta, dA, dB, dC, and dD / dz / ddelta_bias / dh0 for the
     inputs that were given (dh0 when asked for)."""
     torch = _torch()
     bt, L, dim = x.shape
@@ -272,7 +272,7 @@ def selscan_bwd(x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=
     rc = lib.selscan_bwd(_ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True), _ptr(B, "B", io),
                          _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                          _ptr(delta_bias, "delta_bias", f32=True),
-                         SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0,
+                         _flags(delta_softplus, zoh),
                          _ptr(chunk_states, "chunk_states", f32=True), _ptr(dy, "dy", io),
                          p("dx", io=io), p("ddelta", io=io), p("dA", f32=True), p("dB", io=io), p("dC", io=io),
                          p("dD", f32=True), p("dz", io=io), p("ddelta_bias", f32=True), p("dh0", f32=True),
@@ -409,8 +409,9 @@ def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, del
 
 
 def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None,
-                     delta_softplus=False, H=0, W=0, window=0, workspace=None, stream=None, grads=None):
-    """Gradients of sum(dy * y) for y = selscan_scan_fwd(op, ...) with chunk_states from that call.
+                     delta_softplus=False, H=0, W=0, window=0, zoh=False, workspace=None, stream=None, grads=None):
+    """Gradients of sum(dy * y) for y = selscan_scan_fwd(op, ...) with chunk_states from that call
+    (zoh: of the zero-order-hold form, as the forward was run).
     Returns a dict: dx, ddelta, dA, dB, dC, and dD / dz / ddelta_bias for the inputs that were given;
     per-direction gradients carry the leading direction axis.  ``grads``: a dict of the same
     keys, shapes and dtypes to write into instead of allocating."""
@@ -447,7 +448,7 @@ def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, de
     rc = lib.selscan_scan_bwd(op, _ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
                               _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
                               _ptr(delta_bias, "delta_bias", f32=True),
-                              SELSCAN_FLAG_DELTA_SOFTPLUS if delta_softplus else 0,
+                              _flags(delta_softplus, zoh),
                               _ptr(chunk_states, "chunk_states", f32=True), _ptr(dy, "dy", io),
                               p("dx", io=io), p("ddelta", io=io), p("dA", f32=True), p("dB", io=io), p("dC", io=io),
                               p("dD", f32=True), p("dz", io=io), p("ddelta_bias", f32=True),

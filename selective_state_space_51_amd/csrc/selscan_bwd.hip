@@ -147,7 +147,7 @@ __device__ __forceinline__ void rows4_sum(const float p[kK], float out[4]) {
 
 __device__ __forceinline__ float sigmoidf_(float w) { return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e)); }
 
-template <typename T, int KIND>
+template <typename T, int KIND, bool ZOH>
 // two workgroups per CU with bf16 io; the fp32 io tiles leave LDS for one
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunked(BwdParams p) {
     constexpr bool multi = KIND != SELSCAN_OP_FWD;
@@ -324,7 +324,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
         // ---- this lane's 16 steps of its channel
         const int64_t rem = L - (s0 + l * kK);
         const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= kK ? kK : (int)rem));
-        float dt[kK], dlx[kK], dyp[kK], yv[kK];
+        // px: the step's input factor, delta x (Euler) or x (zero-order hold, whose input
+        // coefficient differs per state)
+        float dt[kK], px[kK], dyp[kK], yv[kK];
         float sdt = 0.f, dDl = 0.f;
         const float Dd = Db[2 * cl], bias = Db[2 * cl + 1];
         {
@@ -352,14 +354,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
             for (int j = 0; j < kK; ++j) {
                 const float w = df[j] + bias;
                 dt[j] = (p.softplus ? softplus(w) : w) * __saturatef(limf - (float)j);
-                dlx[j] = dt[j] * xf[j];
+                px[j] = ZOH ? xf[j] : dt[j] * xf[j];
                 dyp[j] = z ? yf[j] * silu(zf[j]) : yf[j];
                 yv[j] = Dd * xf[j];
                 dDl = fmaf(dyp[j], xf[j], dDl);
                 sdt += dt[j];
             }
         }
-        float accdd[kK], accx[kK];  // sum_n g A e h_{t-1};  sum_n g B
+        // Euler: sum_n g A e h_{t-1};  sum_n g B  (d delta = accdd + x accx, dx = delta accx)
+        // ZOH:   sum_n g A e h_{t-1} + x sum_n g e B;  sum_n g phi B  (d delta = accdd, dx = delta accx)
+        float accdd[kK], accx[kK];
 #pragma unroll
         for (int j = 0; j < kK; ++j) accdd[j] = accx[j] = 0.f;
         const float *Bc = Bs + 4 * l;
@@ -386,8 +390,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                 for (int pc = 0; pc < 4; ++pc) *(float4 *)&Bv[4 * pc] = *(const float4 *)&Bc[n * kFP + pc * (kLPR * 4)];
 #pragma unroll
                 for (int j = 0; j < kK; ++j) {
-                    e[j] = __builtin_amdgcn_exp2f(dt[j] * a2);
-                    u[j] = dlx[j] * Bv[j];
+                    const float t = dt[j] * a2;
+                    e[j] = __builtin_amdgcn_exp2f(t);
+                    if constexpr (ZOH)
+                        u[j] = dt[j] * px[j] * (zoh_phi(e[j], t) * Bv[j]);
+                    else
+                        u[j] = px[j] * Bv[j];
                     bq = j == 0 ? u[0] : fmaf(e[j], bq, u[j]);
                 }
             }
@@ -439,9 +447,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                     const float gw = gq * eh[j];
                     dAl = fmaf(dt[j], gw, dAl);
                     accdd[j] = fmaf(Araw, gw, accdd[j]);
-                    accx[j] = fmaf(gq, Bv[j], accx[j]);
-                    pB[j] = gq * dlx[j];
-                    gs = e[j] * gq;
+                    if constexpr (ZOH) {
+                        // input coefficient delta phi(y): d/d delta = e, d/dA = delta^2 phi'(y)
+                        const float t = dt[j] * a2;
+                        const float phi = zoh_phi(e[j], t);
+                        const float dphi = zoh_dphi(e[j], t, phi);
+                        const float gB = gq * Bv[j];
+                        const float dlx = dt[j] * px[j];
+                        accx[j] = fmaf(gB, phi, accx[j]);
+                        pB[j] = gq * phi * dlx;
+                        dAl = fmaf(gB, dlx * dt[j] * dphi, dAl);
+                        gs = e[j] * gq;
+                        accdd[j] = fmaf(px[j], gs * Bv[j], accdd[j]);
+                    } else {
+                        accx[j] = fmaf(gq, Bv[j], accx[j]);
+                        pB[j] = gq * px[j];
+                        gs = e[j] * gq;
+                    }
                 }
             }
             {
@@ -501,7 +523,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int j = 4 * pc + i;
-                    float ddt = fmaf(xf[j], accx[j], accdd[j]);
+                    float ddt = ZOH ? accdd[j] : fmaf(xf[j], accx[j], accdd[j]);
                     if (p.softplus) ddt *= sigmoidf_(df[j] + bias);
                     ddt = j < lim ? ddt : 0.f;
                     o0[i] = dt[j] * accx[j] + Dd * dyp[j];  // dx
@@ -730,7 +752,7 @@ bool bwd_use_split(const BwdProblem &p, size_t ws_bytes) {
 int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
     if (p.batch < 0 || p.L < 0 || p.dim < 0 || p.H < 0 || p.W < 0 || dstate < 0) return SELSCAN_E_SHAPE;
     if (p.dtype != SELSCAN_F32 && p.dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
-    if (p.flags & ~SELSCAN_FLAG_DELTA_SOFTPLUS) return SELSCAN_E_UNSUPPORTED;
+    if (p.flags & ~(SELSCAN_FLAG_DELTA_SOFTPLUS | SELSCAN_FLAG_ZOH)) return SELSCAN_E_UNSUPPORTED;
     if (dstate != kN) return SELSCAN_E_UNSUPPORTED;
     if ((p.kind == SELSCAN_OP_SS2D || p.kind == SELSCAN_OP_LOCAL_SS2D) &&
         (p.L > 0x7FFFFFFF || p.H > 0x7FFFFFFF || p.W > 0x7FFFFFFF))
@@ -770,7 +792,7 @@ int bwd_validate(const BwdProblem &p, int64_t dstate, size_t ws_bytes) {
     return SELSCAN_OK;
 }
 
-template <typename T, int KIND>
+template <typename T, int KIND, bool ZOH>
 int bwd_launch_kind(const BwdProblem &q, void *stream) {
     BwdParams a;
     a.x = q.x, a.delta = q.delta, a.B = q.B, a.C = q.C, a.z = q.z, a.dy = q.dy;
@@ -799,7 +821,7 @@ int bwd_launch_kind(const BwdProblem &q, void *stream) {
     const int64_t blocks = q.batch * (int64_t)a.ntc * (a.split ? q.ndir : 1);
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&a};
-    hipError_t e = hipLaunchKernel((const void *)&selscan_bwd_chunked<T, KIND>, dim3((unsigned)blocks), dim3(256),
+    hipError_t e = hipLaunchKernel((const void *)&selscan_bwd_chunked<T, KIND, ZOH>, dim3((unsigned)blocks), dim3(256),
                                    args, 0, (hipStream_t)stream);
     if (e == hipSuccess) {
         BwdReduceParams f;
@@ -833,12 +855,18 @@ int bwd_launch_kind(const BwdProblem &q, void *stream) {
     return SELSCAN_OK;
 }
 
+template <typename T, bool ZOH>
+int bwd_launch_form(const BwdProblem &q, void *stream) {
+    if (q.kind == SELSCAN_OP_FWD) return bwd_launch_kind<T, SELSCAN_OP_FWD, ZOH>(q, stream);
+    if (q.kind == SELSCAN_OP_BIDIR) return bwd_launch_kind<T, SELSCAN_OP_BIDIR, ZOH>(q, stream);
+    if (q.kind == SELSCAN_OP_SS2D) return bwd_launch_kind<T, SELSCAN_OP_SS2D, ZOH>(q, stream);
+    return bwd_launch_kind<T, SELSCAN_OP_LOCAL_SS2D, ZOH>(q, stream);
+}
+
 template <typename T>
 int bwd_launch(const BwdProblem &q, void *stream) {
-    if (q.kind == SELSCAN_OP_FWD) return bwd_launch_kind<T, SELSCAN_OP_FWD>(q, stream);
-    if (q.kind == SELSCAN_OP_BIDIR) return bwd_launch_kind<T, SELSCAN_OP_BIDIR>(q, stream);
-    if (q.kind == SELSCAN_OP_SS2D) return bwd_launch_kind<T, SELSCAN_OP_SS2D>(q, stream);
-    return bwd_launch_kind<T, SELSCAN_OP_LOCAL_SS2D>(q, stream);
+    if (q.flags & SELSCAN_FLAG_ZOH) return bwd_launch_form<T, true>(q, stream);
+    return bwd_launch_form<T, false>(q, stream);
 }
 
 int bwd_run(BwdProblem &p, int64_t dstate, size_t ws_bytes, void *stream) {

@@ -208,6 +208,31 @@ __device__ __forceinline__ float softplus(float w) {
     return fmaxf(w, 0.f) + l;
 }
 
+// Zero-order-hold input factor: Bbar x = (e^y - 1) / A * B x = delta phi(y) B x, with y = delta A,
+// e = e^y and phi(y) = (e^y - 1) / y.  e - 1 from the exp carries its absolute rounding error
+// (about 1e-7), which is a large relative error when |y| is small; there phi comes from its
+// series, 1 + y/2 + y^2/6 + y^3/24 + y^4/120 (truncation below 5e-8 for |y| < 1/8), and
+// elsewhere from (e - 1) / y (relative error about 1e-6 for |y| >= 1/8).  t = y log2(e), the
+// exponent the recurrence's exp2 already takes.
+__device__ __forceinline__ float zoh_phi(float e, float t) {
+    const float y = t * kLn2;
+    const float series = fmaf(y, fmaf(y, fmaf(y, fmaf(y, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
+    const float direct = (e - 1.f) * __builtin_amdgcn_rcpf(y);
+    return fabsf(y) < 0.125f ? series : direct;
+}
+
+// Its derivative, which the zero-order-hold gradient of A needs (d Bbar / dA = delta^2 phi'(y)):
+// phi'(y) = (e^y (y - 1) + 1) / y^2 = (e^y - phi(y)) / y.  From the series 1/2 + y/3 + y^2/8 +
+// y^3/30 + y^4/144 when |y| < 1/8 (truncation below 1e-7), else from (e - phi) / y (relative
+// error below 2e-5 for |y| >= 1/8, falling as |y| grows); phi as zoh_phi gives it.
+__device__ __forceinline__ float zoh_dphi(float e, float t, float phi) {
+    const float y = t * kLn2;
+    const float series =
+        fmaf(y, fmaf(y, fmaf(y, fmaf(y, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
+    const float direct = (e - phi) * __builtin_amdgcn_rcpf(y);
+    return fabsf(y) < 0.125f ? series : direct;
+}
+
 // silu(z) = z * sigmoid(z) on v_exp_f32 and v_rcp_f32 (large |z| saturates to 0 or z)
 __device__ __forceinline__ float silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));

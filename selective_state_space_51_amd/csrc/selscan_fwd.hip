@@ -215,18 +215,7 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
 // Priority: the waves of the two workgroups that share a SIMD run their state loops at
 // priorities that alternate with the chunk count, so neither workgroup starves the other,
 // and every phase outside the state loop runs above both.
-// Zero-order-hold input factor: Bbar x = (e^y - 1) / A * B x = delta phi(y) B x, with y = delta A,
-// e = e^y and phi(y) = (e^y - 1) / y.  e - 1 from the exp carries its absolute rounding error
-// (about 1e-7), which is a large relative error when |y| is small; there phi comes from its
-// series, 1 + y/2 + y^2/6 + y^3/24 + y^4/120 (truncation below 5e-8 for |y| < 1/8), and
-// elsewhere from (e - 1) / y (relative error about 1e-6 for |y| >= 1/8).  t = y log2(e), the
-// exponent the recurrence's exp2 already takes.
-__device__ __forceinline__ float zoh_phi(float e, float t) {
-    const float y = t * kLn2;
-    const float series = fmaf(y, fmaf(y, fmaf(y, fmaf(y, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
-    const float direct = (e - 1.f) * __builtin_amdgcn_rcpf(y);
-    return fabsf(y) < 0.125f ? series : direct;
-}
+// Zero-order-hold input factor: zoh_phi (selscan_common.h).
 
 template <typename T, int KIND, bool ZOH>
 __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {

@@ -127,7 +127,9 @@ def test_bwd_arguments():
     for k in ("x", "delta", "A", "B", "C", "ck", "dy", "dx", "ddelta", "dA", "dB", "dC"):
         assert bwd(**{k: None}) == 1, k
     assert bwd(batch=-1) == 2
-    assert bwd(N=8) == 5 and bwd(flags=2) == 5 and bwd(dtype=3) == 5
+    # SELSCAN_FLAG_ZOH (2) is accepted; SELSCAN_FLAG_SILU (4) and unknown bits are not
+    assert bwd(N=8) == 5 and bwd(flags=4) == 5 and bwd(flags=8) == 5 and bwd(flags=2, N=8) == 5
+    assert bwd(dtype=3) == 5
     assert bwd(dx=P + 10 * MB + 1) == 3
     assert bwd(dA=P + 12 * MB + 2) == 3
     assert bwd(ws=None) == 6 and bwd(wsb=need - 4) == 6

@@ -291,19 +291,29 @@ def test_state_in_place_and_empty():
 _BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=False, D=True, inp=None):
+def _zoh_A(inp):
+    """A for the zero-order-hold cases: -(n+1) (delta A on both sides of the kernels' series /
+    direct switch at 1/8), and on channel 0 also A = 0, tiny |A| and a positive A."""
+    A = inp["A"].copy()
+    A[..., 0, :4] = [0.0, -1e-4, -3e-3, 0.2]
+    return dict(inp, A=A)
+
+
+def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=False, D=True, inp=None, zoh=False):
     import torch
     import oracle
     import selective_state_space_51_amd as S
     w = W.Workload("bwd", "selscan", batch, L, dim, 16, dtype, gate, index=12)
     if inp is None:
         inp = W.generate(w, with_w=softplus, with_bias=bias)
+        if zoh:
+            inp = _zoh_A(inp)
     dy = W.generate_cotangent(batch, L, dim, dtype)
     h0v = W.generate_state(batch, dim) if h0 else None
     dev = lambda a, dt=dtype: None if a is None else PT.to_dev(a, dt)
     delta = inp["w"] if softplus else inp["delta"]
     args = dict(D=dev(inp["D"], "f32") if D else None, z=dev(inp["z"]), delta_bias=dev(inp.get("delta_bias"), "f32"),
-                delta_softplus=softplus)
+                delta_softplus=softplus, zoh=zoh)
     x, dl, A, B, C = dev(inp["x"]), dev(delta), dev(inp["A"], "f32"), dev(inp["B"]), dev(inp["C"])
     y, ck = S.selscan_fwd_state(x, dl, A, B, C, h0=dev(h0v, "f32"), chunk_states=True, **args)
     g = S.selscan_bwd(x, dl, A, B, C, dev(dy), ck, dh0=h0, **args)
@@ -312,9 +322,9 @@ def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=Fal
     r = oracle.selscan_bwd(f(inp["x"]), f(delta), inp["A"].astype(np.float64), f(inp["B"]), f(inp["C"]), f(dy),
                            D=inp["D"].astype(np.float64) if D else None, z=f(inp["z"]),
                            delta_bias=None if inp.get("delta_bias") is None else inp["delta_bias"].astype(np.float64),
-                           delta_softplus=softplus, h0=None if h0v is None else h0v.astype(np.float64))
+                           delta_softplus=softplus, h0=None if h0v is None else h0v.astype(np.float64), zoh=zoh)
     errs = {k: PT.rel_err(PT.from_dev(g[k]), r[k]) for k in r}
-    _say("bwd", dtype, batch, L, dim, dict(gate=gate, softplus=softplus, bias=bias, h0=h0, D=D),
+    _say("bwd", dtype, batch, L, dim, dict(gate=gate, softplus=softplus, bias=bias, h0=h0, D=D, zoh=zoh),
          {k: f"{v:.2e}" for k, v in errs.items()})
     assert set(g) == set(r), (sorted(g), sorted(r))
     return errs
@@ -330,6 +340,21 @@ def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=Fal
 ], ids=lambda v: str(v))
 def test_bwd_against_oracle(dtype, batch, L, dim, kw):
     errs = _bwd_run(dtype, batch, L, dim, **kw)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL[dtype], (k, e)
+
+
+@pytest.mark.parametrize("dtype,batch,L,dim,kw", [
+    ("f32", 2, 700, 40, {}),
+    ("f32", 2, 300, 40, dict(softplus=True, bias=True, h0=True)),
+    ("f32", 1, 600, 24, dict(gate=False, D=False)),
+    ("bf16", 2, 1100, 64, {}),
+    ("bf16", 2, 700, 64, dict(softplus=True, bias=True)),
+], ids=lambda v: str(v))
+def test_bwd_zoh_against_oracle(dtype, batch, L, dim, kw):
+    """The zero-order-hold backward (SELSCAN_FLAG_ZOH on the forward and the backward) against
+    the oracle's zero-order-hold gradients, with A = 0, tiny, positive and -(n+1) entries."""
+    errs = _bwd_run(dtype, batch, L, dim, zoh=True, **kw)
     for k, e in errs.items():
         assert e <= _BWD_TOL[dtype], (k, e)
 
@@ -350,7 +375,8 @@ def test_bwd_full_size_130m():
 _OP = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
 
 
-def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softplus=False, bias=False, D=True):
+def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softplus=False, bias=False, D=True,
+                  zoh=False):
     """selscan_scan_fwd (with chunk states) then selscan_scan_bwd for a multi-direction order,
     every gradient against oracle.multi_bwd on every element; also checks that the forward's y
     equals the plain entry point's bit for bit."""
@@ -359,11 +385,13 @@ def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softp
     import selective_state_space_51_amd as S
     w = W.Workload("bwd_" + kind, kind, batch, L, dim, 16, dtype, gate, H=H, W=Wd, index=13, window=win)
     inp = W.generate(w, with_w=softplus, with_bias=bias)
+    if zoh:
+        inp = _zoh_A(inp)
     dy = W.generate_cotangent(batch, L, dim, dtype)
     dev = lambda a, dt=dtype: None if a is None else PT.to_dev(a, dt)
     delta = inp["w"] if softplus else inp["delta"]
     args = dict(D=dev(inp["D"], "f32") if D else None, z=dev(inp["z"]), delta_bias=dev(inp.get("delta_bias"), "f32"),
-                delta_softplus=softplus)
+                delta_softplus=softplus, zoh=zoh)
     x, dl, A, B, C = dev(inp["x"]), dev(delta), dev(inp["A"], "f32"), dev(inp["B"]), dev(inp["C"])
     op = _OP[kind]
     y, ck = S.selscan_scan_fwd(op, x, dl, A, B, C, H=H, W=Wd, window=win, chunk_states=True, **args)
@@ -380,9 +408,9 @@ def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softp
     r = oracle.multi_bwd(kind, f(inp["x"]), f(delta), inp["A"].astype(np.float64), f(inp["B"]), f(inp["C"]), f(dy),
                          D=inp["D"].astype(np.float64) if D else None, z=f(inp["z"]),
                          delta_bias=None if inp.get("delta_bias") is None else inp["delta_bias"].astype(np.float64),
-                         delta_softplus=softplus, H=H, W=Wd, window=win)
+                         delta_softplus=softplus, H=H, W=Wd, window=win, zoh=zoh)
     errs = {k: PT.rel_err(PT.from_dev(g[k]), r[k]) for k in r}
-    _say("scan_bwd", kind, dtype, batch, L, dim, (H, Wd, win), dict(gate=gate, softplus=softplus, bias=bias, D=D),
+    _say("scan_bwd", kind, dtype, batch, L, dim, (H, Wd, win), dict(gate=gate, softplus=softplus, bias=bias, D=D, zoh=zoh),
          {k: f"{v:.2e}" for k, v in errs.items()})
     assert set(g) == set(r), (sorted(g), sorted(r))
     return errs
@@ -401,6 +429,20 @@ def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softp
 ], ids=lambda v: str(v))
 def test_scan_bwd_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw):
     errs = _scan_bwd_run(kind, dtype, batch, L, dim, H=H, Wd=Wd, win=win, **kw)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL[dtype], (k, e)
+
+
+@pytest.mark.parametrize("kind,dtype,batch,L,dim,H,Wd,win,kw", [
+    ("bidir", "f32", 2, 197, 24, 0, 0, 0, dict(softplus=True, bias=True)),
+    ("bidir", "bf16", 3, 300, 40, 0, 0, 0, {}),
+    ("ss2d", "f32", 2, 90, 16, 9, 10, 0, {}),
+    ("ss2d", "bf16", 2, 784, 40, 28, 28, 0, dict(gate=False)),
+    ("local_ss2d", "bf16", 1, 144, 24, 12, 12, 3, {}),
+], ids=lambda v: str(v))
+def test_scan_bwd_zoh_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw):
+    """The multi-direction zero-order-hold backward against oracle.multi_bwd(zoh=True)."""
+    errs = _scan_bwd_run(kind, dtype, batch, L, dim, H=H, Wd=Wd, win=win, zoh=True, **kw)
     for k, e in errs.items():
         assert e <= _BWD_TOL[dtype], (k, e)
 
