@@ -581,11 +581,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                     } else if (round == 0) {
                         store8((T *)p.dx + off, nv, vec, v);
                     } else {
-                        const int xs = S::xpos(sl);
+                        // opaque per chunk: otherwise the 16 per-lane addresses are hoisted out of
+                        // every loop and spilled; this way the channel offsets are immediates
+                        int xb = 8 * g * S::kXP + S::xpos(sl);
+                        asm volatile("" : "+v"(xb));
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float dyv = Io<T>::f32(dyt[(8 * g + e) * S::kXP + xs]);
-                            const float zv = Io<T>::f32(zt[(8 * g + e) * S::kXP + xs]);
+                            const float dyv = Io<T>::f32(dyt[xb + e * S::kXP]);
+                            const float zv = Io<T>::f32(zt[xb + e * S::kXP]);
                             const float sg = sigmoidf_(zv);
                             v[e] = dyv * v[e] * sg * (1.f + zv * (1.f - sg));
                         }
