@@ -136,9 +136,9 @@ def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan"):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_channels: int):
-    """The fp64 oracle as it stands, on all host cores, on a bounded sample of the workload:
-    every batch row and the whole sequence for the first `budget_channels` channels."""
+def cpu_baseline(w, budget_channels: int, threads: int = 0):
+    """The fp64 oracle as it stands, on all host cores (or `threads`), on a bounded sample of the
+    workload: every batch row and the whole sequence for the first `budget_channels` channels."""
     import numpy as np
 
     import oracle
@@ -152,7 +152,7 @@ def cpu_baseline(w, budget_channels: int):
     D = inp["D"].astype(np.float64)[..., :ch]
     B, C = W.to_f64(inp["B"], w.dtype), W.to_f64(inp["C"], w.dtype)
     del inp
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     t0 = time.perf_counter()
     if w.kind == "selscan":
         oracle.selscan(x, dl, A, B, C, D=D, z=z, nthreads=threads)
@@ -244,7 +244,7 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
     # rotate over copies of x and out totalling at least 512 MiB when one pair would fit in the
     # 256 MB Infinity Cache (as the scan passes do)
     pair = 2 * x.numel() * x.element_size()
-    copies = 1 if args.no_rotate or pair >= (512 << 20) else -(-(512 << 20) // pair)
+    copies = 1 if args.no_rotate or pair >= (512 << 20) else min(64, -(-(512 << 20) // pair))
     xs = [(x, out)] + [(x.clone(), torch.empty_like(out)) for _ in range(copies - 1)]
     if two_d:
         step = lambda i: S.dwconv2d_fwd(xs[i % copies][0], wt, w.H, w.W, bias=bias, out=xs[i % copies][1],
@@ -323,6 +323,8 @@ def main() -> int:
                          "the 256 MB Infinity Cache (by default such workloads rotate over copies totalling "
                          "at least 512 MiB)")
     ap.add_argument("--cpu-channels", type=int, default=4096)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the CPU baseline (default: all cores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (a plain copy of known size, for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 run)")
@@ -380,8 +382,8 @@ def main() -> int:
     geo = dict(H=w.H, W=w.W, window=w.window)
     bwd = args.pass_ == "bwd"
     # Input sets: the workload's tensors, and for workloads whose buffers would fit in the 256 MB
-    # Infinity Cache, copies of them (with their own outputs) up to 512 MiB in all, which the
-    # steps rotate over so that every step streams its inputs from HBM.
+    # Infinity Cache, copies of them (with their own outputs) up to 512 MiB in all (at most 64
+    # sets), which the steps rotate over so that every step streams its inputs from HBM.
     first = dict(t=t, y=y)
     if bwd:
         _, first["ck"] = S.selscan_scan_fwd(op, t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
@@ -402,7 +404,7 @@ def main() -> int:
         first["g"] = run_bwd(first)  # the gradient buffers of the first set
         set_bytes += nbytes({"ck": first["ck"], "dy": first["dy"]}) + nbytes(first["g"])
     rotate_to = 512 << 20
-    copies = 1 if args.no_rotate or set_bytes >= rotate_to else -(-rotate_to // set_bytes)
+    copies = 1 if args.no_rotate or set_bytes >= rotate_to else min(64, -(-rotate_to // set_bytes))
     sets = [first]
     for _ in range(copies - 1):
         c = dict(t={k: None if v is None else v.clone() for k, v in t.items()}, y=torch.empty_like(y))
@@ -494,7 +496,8 @@ def main() -> int:
                                           "1 exp2 + 1 rcp + 13 fp32 ops = 42 fp32 flop-equivalents" if args.zoh else
                                           "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents"),
                      "kernel": "selscan_bwd_chunked + selscan_bwd_reduce" if bwd else "selscan_chunked",
-                     "kernel_ms": kern_ms, "kernel_ms_min": float(np.min(launch_ms)),
+                     "kernel_ms": kern_ms, "kernel_ms_median": float(np.median(launch_ms)),
+                     "kernel_ms_min": float(np.min(launch_ms)),
                      "elements_per_launch": w.elements, "algorithmic_bytes_per_launch": alg,
                      "hbm_achieved_GBps": hbm_gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
                      "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
@@ -506,7 +509,7 @@ def main() -> int:
     elif not args.no_cpu_baseline and not args.softplus:
         del t, y, ws, h0, hl, first, sets
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_channels, args.cpu_threads)
     print(json.dumps(out))
     return 0
 
