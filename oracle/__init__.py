@@ -66,6 +66,10 @@ def load(path: Optional[str] = None):
     lib.oracle_causal_conv1d.restype = ci
     lib.oracle_dwconv2d.argtypes = [dp, dp, dp, ci, dp, i64, i64, i64, i64, i64]
     lib.oracle_dwconv2d.restype = ci
+    lib.oracle_causal_conv1d_bwd.argtypes = [dp, dp, dp, dp, dp, ci, dp, dp, dp, dp, i64, i64, i64, i64]
+    lib.oracle_causal_conv1d_bwd.restype = ci
+    lib.oracle_dwconv2d_bwd.argtypes = [dp, dp, dp, dp, ci, dp, dp, dp, i64, i64, i64, i64, i64]
+    lib.oracle_dwconv2d_bwd.restype = ci
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ci
     if path is None:
@@ -311,3 +315,35 @@ def dwconv2d(x, w, H, W, bias=None, silu=True, lib=None):
         raise ValueError("oracle_dwconv2d: bad arguments")
     return out
 
+
+def causal_conv1d_bwd(x, w, dout, bias=None, state=None, silu=True, lib=None):
+    """Gradients of sum(dout * causal_conv1d(x, w, bias, state, silu)): a dict with dx [batch, L,
+    dim], dweight [dim, K], dbias [dim] and, when a state is given, dstate [batch, K-1, dim]."""
+    lib = lib or load()
+    x, w, dout, bias, state = map(_f64, (x, w, dout, bias, state))
+    bt, L, dim = x.shape
+    K = w.shape[1]
+    g = {"dx": np.empty_like(x), "dweight": np.empty((dim, K)), "dbias": np.empty(dim)}
+    if state is not None:
+        g["dstate"] = np.empty((bt, K - 1, dim))
+    rc = lib.oracle_causal_conv1d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(state), _ptr(dout), int(bool(silu)),
+                                      _ptr(g["dx"]), _ptr(g["dweight"]), _ptr(g["dbias"]), _ptr(g.get("dstate")),
+                                      bt, L, dim, K)
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d_bwd: bad arguments")
+    return g
+
+
+def dwconv2d_bwd(x, w, H, W, dout, bias=None, silu=True, lib=None):
+    """Gradients of sum(dout * dwconv2d(x, w, H, W, bias, silu)): a dict with dx [batch, H*W, dim],
+    dweight [dim, ks, ks] and dbias [dim]."""
+    lib = lib or load()
+    x, w, dout, bias = map(_f64, (x, w, dout, bias))
+    bt, L, dim = x.shape
+    assert L == H * W
+    g = {"dx": np.empty_like(x), "dweight": np.empty_like(w), "dbias": np.empty(dim)}
+    rc = lib.oracle_dwconv2d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(dout), int(bool(silu)), _ptr(g["dx"]),
+                                 _ptr(g["dweight"]), _ptr(g["dbias"]), bt, H, W, dim, w.shape[-1])
+    if rc != 0:
+        raise ValueError("oracle_dwconv2d_bwd: bad arguments")
+    return g

@@ -638,3 +638,98 @@ int oracle_selscan_bwd(const double *x, const double *delta, const double *A, co
     }
     return rc;
 }
+
+/* ---- backward of the convolutions -------------------------------------- */
+
+/* d act / dv at v: silu'(v) = sigmoid(v) (1 + v (1 - sigmoid(v))), or 1 without the SiLU */
+static double act_grad(int silu_, double v) {
+    if (!silu_) return 1.0;
+    const double s = sigmoid(v);
+    return s * (1.0 + v * (1.0 - s));
+}
+
+/* Backward of oracle_causal_conv1d for dL/dout = dout.  Per (b, t, d) the pre-activation v is
+ * recomputed and dv = dout act'(v); tap i read input row t-(K-1)+i of xin = state_in ++ x, so
+ *   d xin[b, t-(K-1)+i, d] += w[d,i] dv,   dw[d,i] += xin[b, t-(K-1)+i, d] dv,   dbias[d] += dv.
+ * The rows of xin before step 0 are state_in's: their derivative is dstate_in.  dx [batch][L][dim]
+ * and dw [dim][K] are required; dbias [dim] and dstate_in [batch][K-1][dim] may be NULL.       */
+int oracle_causal_conv1d_bwd(const double *x, const double *w, const double *bias, const double *state_in,
+                             const double *dout, int silu_, double *dx, double *dw, double *dbias,
+                             double *dstate_in, int64_t batch, int64_t L, int64_t dim, int64_t K) {
+    if (batch < 0 || L < 0 || dim < 0 || K < 1 || !w || !dw || (L > 0 && (!x || !dout || !dx))) return -1;
+    memset(dw, 0, sizeof(double) * (size_t)(dim * K));
+    if (dbias) memset(dbias, 0, sizeof(double) * (size_t)dim);
+    if (L > 0) memset(dx, 0, sizeof(double) * (size_t)(batch * L * dim));
+    if (dstate_in) memset(dstate_in, 0, sizeof(double) * (size_t)(batch * (K - 1) * dim));
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < dim; ++d)
+            for (int64_t t = 0; t < L; ++t) {
+                double v = bias ? bias[d] : 0.0;
+                for (int64_t i = 0; i < K; ++i) {
+                    const int64_t s = t - (K - 1) + i;
+                    double xv = 0.0;
+                    if (s >= 0) xv = x[(b * L + s) * dim + d];
+                    else if (state_in) xv = state_in[(b * (K - 1) + (K - 1) + s) * dim + d];
+                    v += w[d * K + i] * xv;
+                }
+                const double dv = dout[(b * L + t) * dim + d] * act_grad(silu_, v);
+                if (dbias) dbias[d] += dv;
+                for (int64_t i = 0; i < K; ++i) {
+                    const int64_t s = t - (K - 1) + i;
+                    double xv = 0.0;
+                    if (s >= 0) {
+                        xv = x[(b * L + s) * dim + d];
+                        dx[(b * L + s) * dim + d] += w[d * K + i] * dv;
+                    } else {
+                        if (state_in) xv = state_in[(b * (K - 1) + (K - 1) + s) * dim + d];
+                        if (dstate_in) dstate_in[(b * (K - 1) + (K - 1) + s) * dim + d] += w[d * K + i] * dv;
+                    }
+                    dw[d * K + i] += xv * dv;
+                }
+            }
+    return 0;
+}
+
+/* Backward of oracle_dwconv2d for dL/dout = dout: dv = dout act'(v) with v recomputed; tap (i, j)
+ * of output pixel (h, w) read input pixel (h+i-p, w+j-p) when it lies in the map, so
+ *   dx[b, h+i-p, w+j-p, d] += wt[d,i,j] dv,   dwt[d,i,j] += x[b, h+i-p, w+j-p, d] dv,   dbias[d] += dv.
+ * dx and dwt are required, dbias may be NULL.                                                   */
+int oracle_dwconv2d_bwd(const double *x, const double *wt, const double *bias, const double *dout, int silu_,
+                        double *dx, double *dwt, double *dbias, int64_t batch, int64_t H, int64_t W, int64_t dim,
+                        int64_t ks) {
+    if (batch < 0 || H < 0 || W < 0 || dim < 0 || ks < 1 || ks % 2 == 0 || !wt || !dwt) return -1;
+    if (batch * H * W > 0 && (!x || !dout || !dx)) return -1;
+    const int64_t p = (ks - 1) / 2;
+    memset(dwt, 0, sizeof(double) * (size_t)(dim * ks * ks));
+    if (dbias) memset(dbias, 0, sizeof(double) * (size_t)dim);
+    if (batch * H * W > 0) memset(dx, 0, sizeof(double) * (size_t)(batch * H * W * dim));
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t w = 0; w < W; ++w)
+                for (int64_t d = 0; d < dim; ++d) {
+                    double v = bias ? bias[d] : 0.0;
+                    for (int64_t i = 0; i < ks; ++i) {
+                        const int64_t hh = h + i - p;
+                        if (hh < 0 || hh >= H) continue;
+                        for (int64_t j = 0; j < ks; ++j) {
+                            const int64_t ww = w + j - p;
+                            if (ww < 0 || ww >= W) continue;
+                            v += wt[(d * ks + i) * ks + j] * x[((b * H + hh) * W + ww) * dim + d];
+                        }
+                    }
+                    const double dv = dout[((b * H + h) * W + w) * dim + d] * act_grad(silu_, v);
+                    if (dbias) dbias[d] += dv;
+                    for (int64_t i = 0; i < ks; ++i) {
+                        const int64_t hh = h + i - p;
+                        if (hh < 0 || hh >= H) continue;
+                        for (int64_t j = 0; j < ks; ++j) {
+                            const int64_t ww = w + j - p;
+                            if (ww < 0 || ww >= W) continue;
+                            const int64_t q = ((b * H + hh) * W + ww) * dim + d;
+                            dx[q] += wt[(d * ks + i) * ks + j] * dv;
+                            dwt[(d * ks + i) * ks + j] += x[q] * dv;
+                        }
+                    }
+                }
+    return 0;
+}

@@ -644,6 +644,70 @@ def pin_dwconv2d_impulse(lib):
         assert np.array_equal(out, want), (h0, w0)
 
 
+def _fd_all(loss, args, name, eps=1e-6):
+    """central difference of loss for every entry of args[name]"""
+    base = np.asarray(args[name], dtype=np.float64)
+    fd = np.empty_like(base)
+    for idx in np.ndindex(base.shape):
+        up = base.copy(); up[idx] += eps
+        dn = base.copy(); dn[idx] -= eps
+        fd[idx] = (loss(dict(args, **{name: up})) - loss(dict(args, **{name: dn}))) / (2 * eps)
+    return fd
+
+
+def pin_conv1d_bwd_fd(lib):
+    """Every entry of every gradient of sum(dout * causal_conv1d(...)) against its own central
+    difference of the (separately pinned) forward oracle: widths 1-4, with and without SiLU,
+    bias and carried state rows."""
+    r = _rng(610)
+    for K in (1, 2, 3, 4):
+        for silu in (False, True):
+            for with_state in (False, True):
+                if with_state and K == 1:
+                    continue
+                bt, L, dim = 2, 7, 3
+                args = dict(x=r.standard_normal((bt, L, dim)), w=r.standard_normal((dim, K)),
+                            bias=r.standard_normal(dim) if silu else None,
+                            state=r.standard_normal((bt, K - 1, dim)) if with_state else None)
+                dout = r.standard_normal((bt, L, dim))
+
+                def loss(a):
+                    y = oracle.causal_conv1d(a["x"], a["w"], bias=a["bias"], state=a["state"], silu=silu, lib=lib)
+                    return float(np.sum(dout * y))
+
+                g = oracle.causal_conv1d_bwd(dout=dout, silu=silu, lib=lib, **args)
+                for name, gname in (("x", "dx"), ("w", "dweight"), ("bias", "dbias"), ("state", "dstate")):
+                    if args[name] is None:
+                        continue
+                    fd = _fd_all(loss, args, name)
+                    assert np.abs(fd - g[gname]).max() <= 1e-6 * max(np.abs(fd).max(), 1.0), (K, silu, with_state, name)
+                if args["bias"] is None:  # the bias gradient is the sum of dv, given or not
+                    fd = _fd_all(loss, dict(args, bias=np.zeros(dim)), "bias")
+                    assert np.abs(fd - g["dbias"]).max() <= 1e-6 * max(np.abs(fd).max(), 1.0), (K, "dbias")
+
+
+def pin_dwconv2d_bwd_fd(lib):
+    """Every entry of every gradient of sum(dout * dwconv2d(...)) against its own central
+    difference of the (separately pinned) forward oracle: kernel sizes 1, 3, 5 (5 is wider than
+    the 4 x 5 map's rows), with and without SiLU and bias."""
+    r = _rng(620)
+    for ks in (1, 3, 5):
+        for silu in (False, True):
+            bt, H, W, dim = 2, 4, 5, 2
+            args = dict(x=r.standard_normal((bt, H * W, dim)), w=r.standard_normal((dim, ks, ks)),
+                        bias=r.standard_normal(dim) if silu else None)
+            dout = r.standard_normal((bt, H * W, dim))
+
+            def loss(a):
+                return float(np.sum(dout * oracle.dwconv2d(a["x"], a["w"], H, W, bias=a["bias"], silu=silu, lib=lib)))
+
+            g = oracle.dwconv2d_bwd(args["x"], args["w"], H, W, dout, bias=args["bias"], silu=silu, lib=lib)
+            for name, gname in (("x", "dx"), ("w", "dweight"), ("bias", "dbias")):
+                a = args if args[name] is not None else dict(args, bias=np.zeros(dim))
+                fd = _fd_all(loss, a, name)
+                assert np.abs(fd - g[gname]).max() <= 1e-6 * max(np.abs(fd).max(), 1.0), (ks, silu, name)
+
+
 ALL_PINS = [
     pin_lti_convolution,
     pin_delta_to_zero,
@@ -661,6 +725,7 @@ ALL_PINS = [
     pin_local_ss2d_limits,
     pin_bwd_directional_fd,
     pin_bwd_elementwise_fd,
+    pin_bwd_zoh_at_A_zero,
     pin_multi_bwd_fd,
     pin_ordered_scan_maps,
     pin_conv1d_impulse,
@@ -668,4 +733,6 @@ ALL_PINS = [
     pin_conv1d_state_split,
     pin_dwconv2d_scipy,
     pin_dwconv2d_impulse,
+    pin_conv1d_bwd_fd,
+    pin_dwconv2d_bwd_fd,
 ]

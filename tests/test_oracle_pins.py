@@ -84,6 +84,19 @@ MUTATIONS = [
     ("dwconv_no_centring", "const int64_t hh = h + i - p;", "const int64_t hh = h + i - p + (ks > 1);"),
     ("dwconv_bias_dropped", "double v = bias ? bias[d] : 0.0;\n                    for (int64_t i = 0; i < ks; ++i) {",
      "double v = 0.0;\n                    for (int64_t i = 0; i < ks; ++i) {"),
+    # convolution backward
+    ("conv_bwd_silu_derivative_sign", "return s * (1.0 + v * (1.0 - s));", "return s * (1.0 - v * (1.0 - s));"),
+    ("conv1d_bwd_dx_tap_reversed", "dx[(b * L + s) * dim + d] += w[d * K + i] * dv;",
+     "dx[(b * L + s) * dim + d] += w[d * K + (K - 1 - i)] * dv;"),
+    ("conv1d_bwd_dw_missing_input", "dw[d * K + i] += xv * dv;", "dw[d * K + i] += dv;"),
+    ("conv1d_bwd_state_rows_dropped",
+     "if (dstate_in) dstate_in[(b * (K - 1) + (K - 1) + s) * dim + d] += w[d * K + i] * dv;", ""),
+    ("conv1d_bwd_dbias_before_activation", "if (dbias) dbias[d] += dv;",
+     "if (dbias) dbias[d] += dout[(b * L + t) * dim + d];"),
+    ("dwconv_bwd_dx_kernel_transposed", "dx[q] += wt[(d * ks + i) * ks + j] * dv;",
+     "dx[q] += wt[(d * ks + j) * ks + i] * dv;"),
+    ("dwconv_bwd_dw_from_output_pixel", "dwt[(d * ks + i) * ks + j] += x[q] * dv;",
+     "dwt[(d * ks + i) * ks + j] += x[((b * H + h) * W + w) * dim + d] * dv;"),
 ]
 
 
