@@ -309,6 +309,50 @@ int causal_conv1d_fwd(const void *x, const float *weight, const float *bias, con
 int dwconv2d_fwd(const void *x, const float *weight, const float *bias, unsigned flags, void *out, int64_t batch,
                  int64_t H, int64_t W, int64_t dim, int64_t ksize, int io_dtype, void *stream);
 
+/*
+ * causal_conv1d_bwd - gradients of L = sum(dout * out) for out = causal_conv1d_fwd(x, weight, bias,
+ * state_in, flags) (the chain rule through the convolution of the Mamba block diagram, same page
+ * and section): with v the pre-activation and dv = dout * act'(v) (act' = silu' with
+ * SELSCAN_FLAG_SILU, else 1),
+ *     dxin[b][t-(width-1)+i][d] += weight[d][i] * dv[b][t][d],   dweight[d][i] = sum_{b,t} xin * dv,
+ *     dbias[d] = sum_{b,t} dv[b][t][d]
+ * where xin is state_in's rows followed by x; the rows before step 0 give dstate_in.
+ *   x, dout, dx      : [batch][seqlen][dim] io_dtype
+ *   weight           : [dim][width] fp32, width 1..4; bias [dim] fp32, nullable; state_in nullable
+ *   dweight          : [dim][width] fp32, required; dbias [dim] fp32, nullable (the sum of dv,
+ *                      also when bias is NULL); dstate_in [batch][width-1][dim] io_dtype, nullable
+ *   flags            : SELSCAN_FLAG_SILU or 0, as in the forward call
+ * workspace: at least causal_conv1d_bwd_workspace_bytes(...) bytes, 4-byte aligned (dv in fp32 and
+ * per-thread-group partial sums of dweight and dbias).  No output may overlap an input, another
+ * output or the workspace (SELSCAN_E_ALIAS).  dweight and dbias are sums in a fixed order: the
+ * results are the same from run to run.  seqlen 0 writes zeros to dweight, dbias, dstate_in.
+ */
+int causal_conv1d_bwd(const void *x, const float *weight, const float *bias, const void *state_in, const void *dout,
+                      unsigned flags, void *dx, float *dweight, float *dbias, void *dstate_in, int64_t batch,
+                      int64_t seqlen, int64_t dim, int64_t width, int io_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Scratch bytes causal_conv1d_bwd needs as `workspace` (0 if batch or dim is not positive or the
+ * width is not 1..4). */
+size_t causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int io_dtype);
+
+/*
+ * dwconv2d_bwd - gradients of L = sum(dout * out) for out = dwconv2d_fwd(x, weight, bias, flags)
+ * (the VSS block's DWConv 3x3, same page): dv = dout * act'(v) and
+ *     dx[b][h+i-1][w+j-1][d] += weight[d][i][j] * dv[b][h][w][d]   (pixels inside the map),
+ *     dweight[d][i][j] = sum x[b][h+i-1][w+j-1][d] * dv[b][h][w][d],   dbias[d] = sum dv
+ *   x, dout, dx : [batch][H][W][dim] io_dtype;  weight, dweight [dim][3][3] fp32 (dweight
+ *                 required); bias [dim] fp32, nullable; dbias [dim] fp32, nullable; ksize 3
+ * workspace: at least dwconv2d_bwd_workspace_bytes(...) bytes, 4-byte aligned.  Aliasing,
+ * determinism and errors as for causal_conv1d_bwd; an empty map writes zeros to dweight and dbias.
+ */
+int dwconv2d_bwd(const void *x, const float *weight, const float *bias, const void *dout, unsigned flags, void *dx,
+                 float *dweight, float *dbias, int64_t batch, int64_t H, int64_t W, int64_t dim, int64_t ksize,
+                 int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes dwconv2d_bwd needs as `workspace` (0 if any size is not positive). */
+size_t dwconv2d_bwd_workspace_bytes(int64_t batch, int64_t H, int64_t W, int64_t dim, int io_dtype);
+
 /* Scratch bytes to pass as `workspace` for this problem (0 = none).  Several directions keep fp32
  * partial outputs [batch][seqlen][dim] there.  When batch x ceil(dim/16) is below 1024 (too few
  * workgroups to fill the GPU when each walks every direction) the returned size holds one such

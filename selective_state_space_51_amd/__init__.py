@@ -62,6 +62,14 @@ def _load():
     lib.causal_conv1d_fwd.restype = ci
     lib.dwconv2d_fwd.argtypes = [vp, vp, vp, cu, vp, i64, i64, i64, i64, i64, ci, vp]
     lib.dwconv2d_fwd.restype = ci
+    lib.causal_conv1d_bwd.argtypes = [vp, vp, vp, vp, vp, cu, vp, vp, vp, vp, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.causal_conv1d_bwd.restype = ci
+    lib.causal_conv1d_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    lib.causal_conv1d_bwd_workspace_bytes.restype = sz
+    lib.dwconv2d_bwd.argtypes = [vp, vp, vp, vp, cu, vp, vp, vp, i64, i64, i64, i64, i64, ci, vp, sz, vp]
+    lib.dwconv2d_bwd.restype = ci
+    lib.dwconv2d_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    lib.dwconv2d_bwd_workspace_bytes.restype = sz
     lib.selscan_scan_fwd.argtypes = [ci] + common + [vp, i64, i64, i64, i64, i64, i64, i64, ci, vp, sz, vp]
     lib.selscan_scan_fwd.restype = ci
     lib.selscan_scan_bwd.argtypes = [ci] + [vp] * 8 + [cu] + [vp] * 10 + [i64] * 7 + [ci, vp, sz, vp]
@@ -500,3 +508,64 @@ def dwconv2d_fwd(x, weight, H, W, bias=None, silu=True, out=None, stream=None):
     _check(rc, "dwconv2d_fwd")
     return out
 
+
+def causal_conv1d_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, width: int, io_dtype: int = SELSCAN_BF16) -> int:
+    return int(lib.causal_conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, io_dtype))
+
+
+def dwconv2d_bwd_workspace_bytes(batch: int, H: int, W: int, dim: int, io_dtype: int = SELSCAN_BF16) -> int:
+    return int(lib.dwconv2d_bwd_workspace_bytes(batch, H, W, dim, io_dtype))
+
+
+def causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True, dstate=False, workspace=None,
+                      stream=None):
+    """Gradients of sum(dout * causal_conv1d_fwd(x, weight, bias, state_in, silu)): a dict with dx
+    (x's dtype), dweight, dbias (fp32) and, with dstate=True, dstate [batch, width-1, dim]."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    K = weight.shape[-1]
+    io = x.dtype
+    _shape_check("weight", weight, (dim, K))
+    _shape_check("bias", bias, (dim,))
+    _shape_check("state_in", state_in, (bt, K - 1, dim))
+    _shape_check("dout", dout, (bt, L, dim))
+    g = {"dx": torch.empty_like(x), "dweight": torch.empty(dim, K, dtype=torch.float32, device=x.device),
+         "dbias": torch.empty(dim, dtype=torch.float32, device=x.device)}
+    if dstate:
+        g["dstate"] = torch.empty(bt, K - 1, dim, dtype=io, device=x.device)
+    need = causal_conv1d_bwd_workspace_bytes(bt, L, dim, K, _dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    rc = lib.causal_conv1d_bwd(_ptr(x, "x", io), _ptr(weight, "weight", f32=True), _ptr(bias, "bias", f32=True),
+                               _ptr(state_in, "state_in", io), _ptr(dout, "dout", io), SELSCAN_FLAG_SILU if silu else 0,
+                               _ptr(g["dx"], "dx", io), _ptr(g["dweight"], "dweight", f32=True),
+                               _ptr(g["dbias"], "dbias", f32=True), _ptr(g.get("dstate"), "dstate", io), bt, L, dim, K,
+                               _dtype_code(x), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check(rc, "causal_conv1d_bwd")
+    return g
+
+
+def dwconv2d_bwd(x, weight, H, W, dout, bias=None, silu=True, workspace=None, stream=None):
+    """Gradients of sum(dout * dwconv2d_fwd(x, weight, H, W, bias, silu)): a dict with dx (x's dtype),
+    dweight [dim, 3, 3] and dbias (fp32)."""
+    torch = _torch()
+    bt, L, dim = x.shape
+    io = x.dtype
+    if L != H * W:
+        raise ValueError(f"x has {L} pixels, expected H*W = {H * W}")
+    _shape_check("weight", weight, (dim, 3, 3))
+    _shape_check("bias", bias, (dim,))
+    _shape_check("dout", dout, (bt, L, dim))
+    g = {"dx": torch.empty_like(x), "dweight": torch.empty(dim, 3, 3, dtype=torch.float32, device=x.device),
+         "dbias": torch.empty(dim, dtype=torch.float32, device=x.device)}
+    need = dwconv2d_bwd_workspace_bytes(bt, H, W, dim, _dtype_code(x))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    rc = lib.dwconv2d_bwd(_ptr(x, "x", io), _ptr(weight, "weight", f32=True), _ptr(bias, "bias", f32=True),
+                          _ptr(dout, "dout", io), SELSCAN_FLAG_SILU if silu else 0, _ptr(g["dx"], "dx", io),
+                          _ptr(g["dweight"], "dweight", f32=True), _ptr(g["dbias"], "dbias", f32=True), bt, H, W, dim,
+                          3, _dtype_code(x), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream(stream))
+    _check(rc, "dwconv2d_bwd")
+    return g

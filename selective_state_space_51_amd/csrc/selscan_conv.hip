@@ -216,6 +216,404 @@ int conv1d_launch(Conv1dParams &c, int K, void *stream) {
     }
 }
 
+// ---- backward -------------------------------------------------------------------------------
+// The chain rule through v = bias + sum of taps, out = act(v): dv = dout act'(v) (act' = 1 without
+// the SiLU); every tap spreads dv back to the input it read (dx, and for the 1-D convolution the
+// carried state rows), dw collects input x dv and dbias collects dv.  Three launches:
+//  1. conv_bwd_dv:  v recomputed from the input neighbourhood (as the forward kernels do), dv
+//     written to an fp32 workspace, and each thread's running sums of input x dv and dv over
+//     several runs written as one partial row per thread group (no atomics);
+//  2. conv_bwd_dx:  dx as the transposed convolution of dv (the taps read in mirror order);
+//  3. conv_bwd_reduce: dw and dbias as the sums of the partial rows, in a fixed order, so the
+//     results are the same from run to run.
+
+__device__ __forceinline__ float act_grad(float v, int silu_) {
+    if (!silu_) return 1.f;
+    const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-v * kLog2e));
+    return s * (1.f + v * (1.f - s));
+}
+
+// 8 fp32 values of a row of the dv workspace (zeros past nv)
+__device__ __forceinline__ void load_dv8(const float *p, int nv, bool vec, float v[8]) {
+    if (vec && nv == 8) {
+        const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < nv ? p[e] : 0.f;
+}
+
+__device__ __forceinline__ void store_dv8(float *p, int nv, bool vec, const float v[8]) {
+    if (vec && nv == 8) {
+        *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4 *)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (e < nv) p[e] = v[e];
+}
+
+struct ConvBwdParams {
+    const void *x, *dout, *state_in;
+    const float *w, *bias;  // [dim][taps], [dim]
+    float *dv;              // [batch][positions][dim] fp32
+    float *part;            // [nparts][dim][taps + 1]: sums of input x dv per tap, then of dv
+    void *dx, *dstate;      // dstate: [batch][K-1][dim] (1-D only), nullable
+    float *dw, *dbias;
+    int64_t L, dim;         // positions per batch row (1-D: seqlen; 2-D: H * W)
+    int H, W, batch, silu, vec, wvec, ncg;
+    int nrun;               // runs per batch row (1-D: steps / run; 2-D: row groups)
+    int per;                // runs (1-D) or image rows (2-D) per thread in conv_bwd_dv
+    int ngrp;               // thread groups per batch row in conv_bwd_dv (partial rows per batch row)
+    int nwb;                // 2-D: pixel blocks per image row
+    int nparts, taps;
+};
+
+// 1-D, launch 1: thread (b, group g, channel group); runs g*per .. g*per+per-1 of kRB steps
+template <typename T, int K>
+__global__ __launch_bounds__(256) void conv1d_bwd_dv(ConvBwdParams p) {
+    constexpr int R = sizeof(T) == 2 ? 16 : 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)p.batch * p.ngrp * p.ncg) return;
+    const int cg = (int)(gid % p.ncg);
+    const int64_t rest = gid / p.ncg;
+    const int grp = (int)(rest % p.ngrp), b = (int)(rest / p.ngrp);
+    const int64_t c0 = (int64_t)cg * 8, L = p.L, dim = p.dim;
+    const int nv = (int)(dim - c0 < 8 ? dim - c0 : 8);
+    const bool vec = p.vec != 0;
+    const T *x = (const T *)p.x + (int64_t)b * L * dim + c0;
+    const T *dout = (const T *)p.dout + (int64_t)b * L * dim + c0;
+    const T *st = p.state_in ? (const T *)p.state_in + (int64_t)b * (K - 1) * dim + c0 : nullptr;
+    float *dv = p.dv + (int64_t)b * L * dim + c0;
+    float f[8 * K], bs[8], sw[8 * K], sb[8];
+    filters8<K>(p.w, c0, nv, p.wvec != 0, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
+        sb[e] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8 * K; ++k) sw[k] = 0.f;
+    for (int r = 0; r < p.per; ++r) {
+        const int64_t t0 = ((int64_t)grp * p.per + r) * R;
+        if (t0 >= L) break;
+        Raw8<T> raw[R + K - 1], rd[R];
+#pragma unroll
+        for (int i = 0; i < R + K - 1; ++i) {
+            const int64_t s = t0 - (K - 1) + i;
+            raw[i] = Raw8<T>{};
+            if (s >= 0 && s < L) raw[i] = load_raw8(x + s * dim, nv, vec);
+            else if (s < 0 && st) raw[i] = load_raw8(st + (K - 1 + s) * dim, nv, vec);
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            rd[u] = Raw8<T>{};
+            if (t0 + u < L) rd[u] = load_raw8(dout + (t0 + u) * dim, nv, vec);
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if (t0 + u >= L) break;
+            float g[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = bs[e];
+#pragma unroll
+                for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], raw_f32(raw[u + i], e), a);
+                g[e] = raw_f32(rd[u], e) * act_grad(a, p.silu);
+                sb[e] += g[e];
+#pragma unroll
+                for (int i = 0; i < K; ++i) sw[e * K + i] = fmaf(raw_f32(raw[u + i], e), g[e], sw[e * K + i]);
+            }
+            store_dv8(dv + (t0 + u) * dim, nv, vec, g);
+        }
+    }
+    float *pr = p.part + ((int64_t)b * p.ngrp + grp) * dim * (K + 1) + c0 * (K + 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (e >= nv) break;
+#pragma unroll
+        for (int i = 0; i < K; ++i) pr[e * (K + 1) + i] = sw[e * K + i];
+        pr[e * (K + 1) + K] = sb[e];
+    }
+}
+
+// 1-D, launch 2: thread (b, run, channel group); dx[s] = sum_i w[i] dv[s + K-1-i] for the run's
+// kRB steps, and for the first run also the K-1 state rows (s < 0)
+template <typename T, int K>
+__global__ __launch_bounds__(256) void conv1d_bwd_dx(ConvBwdParams p) {
+    constexpr int R = 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)p.batch * p.nrun * p.ncg) return;
+    const int cg = (int)(gid % p.ncg);
+    const int64_t rest = gid / p.ncg;
+    const int tb = (int)(rest % p.nrun), b = (int)(rest / p.nrun);
+    const int64_t c0 = (int64_t)cg * 8, L = p.L, dim = p.dim;
+    const int nv = (int)(dim - c0 < 8 ? dim - c0 : 8);
+    const bool vec = p.vec != 0;
+    const float *dv = p.dv + (int64_t)b * L * dim + c0;
+    T *dx = (T *)p.dx + (int64_t)b * L * dim + c0;
+    float f[8 * K];
+    filters8<K>(p.w, c0, nv, p.wvec != 0, f);
+    const int64_t t0 = (int64_t)tb * R;
+    float g[R + K - 1][8];  // dv rows t0 .. t0 + R + K - 2 (zeros past the end)
+#pragma unroll
+    for (int i = 0; i < R + K - 1; ++i) {
+        if (t0 + i < L) load_dv8(dv + (t0 + i) * dim, nv, vec, g[i]);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) g[i][e] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        if (t0 + u >= L) break;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], g[u + K - 1 - i][e], a);
+            v[e] = a;
+        }
+        store8(dx + (t0 + u) * dim, nv, vec, v);
+    }
+    if (p.dstate && tb == 0) {
+        // state row r is input position s = r - (K-1): it fed step s + K-1-i through tap i
+        T *ds = (T *)p.dstate + (int64_t)b * (K - 1) * dim + c0;
+#pragma unroll
+        for (int r = 0; r < K - 1; ++r) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = 0.f;
+#pragma unroll
+                for (int i = 0; i <= r; ++i) a = fmaf(f[e * K + i], g[r - i][e], a);
+                v[e] = a;
+            }
+            store8(ds + r * dim, nv, vec, v);
+        }
+    }
+}
+
+// 2-D, launch 1: thread (b, row group, pixel block, channel group); rows grp*per .. +per-1,
+// R pixels of each
+template <typename T>
+__global__ __launch_bounds__(256) void dwconv2d3_bwd_dv(ConvBwdParams p) {
+    constexpr int R = sizeof(T) == 2 ? 4 : 2;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)p.batch * p.ngrp * p.nwb * p.ncg) return;
+    const int cg = (int)(gid % p.ncg);
+    int64_t rest = gid / p.ncg;
+    const int wb = (int)(rest % p.nwb);
+    rest /= p.nwb;
+    const int grp = (int)(rest % p.ngrp), b = (int)(rest / p.ngrp);
+    const int64_t c0 = (int64_t)cg * 8, dim = p.dim;
+    const int H = p.H, W = p.W;
+    const int nv = (int)(dim - c0 < 8 ? dim - c0 : 8);
+    const bool vec = p.vec != 0;
+    const T *x = (const T *)p.x + (int64_t)b * H * W * dim + c0;
+    const T *dout = (const T *)p.dout + (int64_t)b * H * W * dim + c0;
+    float *dv = p.dv + (int64_t)b * H * W * dim + c0;
+    float f[72], bs[8], sw[72], sb[8];
+    filters8<9>(p.w, c0, nv, p.wvec != 0, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
+        sb[e] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 72; ++k) sw[k] = 0.f;
+    const int w0 = wb * R;
+    for (int r = 0; r < p.per; ++r) {
+        const int h = grp * p.per + r;
+        if (h >= H) break;
+        Raw8<T> raw[3][R + 2], rd[R];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int hh = h - 1 + i;
+#pragma unroll
+            for (int j = 0; j < R + 2; ++j) {
+                const int c = w0 - 1 + j;
+                raw[i][j] = Raw8<T>{};
+                if (hh >= 0 && hh < H && c >= 0 && c < W) raw[i][j] = load_raw8(x + ((int64_t)hh * W + c) * dim, nv, vec);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            rd[u] = Raw8<T>{};
+            if (w0 + u < W) rd[u] = load_raw8(dout + ((int64_t)h * W + w0 + u) * dim, nv, vec);
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if (w0 + u >= W) break;
+            float g[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = bs[e];
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) a = fmaf(f[e * 9 + i * 3 + j], raw_f32(raw[i][u + j], e), a);
+                g[e] = raw_f32(rd[u], e) * act_grad(a, p.silu);
+                sb[e] += g[e];
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 3; ++j)
+                        sw[e * 9 + i * 3 + j] = fmaf(raw_f32(raw[i][u + j], e), g[e], sw[e * 9 + i * 3 + j]);
+            }
+            store_dv8(dv + ((int64_t)h * W + w0 + u) * dim, nv, vec, g);
+        }
+    }
+    float *pr = p.part + (((int64_t)b * p.ngrp + grp) * p.nwb + wb) * dim * 10 + c0 * 10;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (e >= nv) break;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) pr[e * 10 + k] = sw[e * 9 + k];
+        pr[e * 10 + 9] = sb[e];
+    }
+}
+
+// 2-D, launch 2: thread (b, image row, pixel block of 2, channel group); dx[h][w] =
+// sum_{i,j} w[i][j] dv[h+1-i][w+1-j] (dv = 0 outside the map)
+template <typename T>
+__global__ __launch_bounds__(256) void dwconv2d3_bwd_dx(ConvBwdParams p) {
+    constexpr int R = 2;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nwb = (p.W + R - 1) / R;
+    if (gid >= (int64_t)p.batch * p.H * nwb * p.ncg) return;
+    const int cg = (int)(gid % p.ncg);
+    int64_t rest = gid / p.ncg;
+    const int wb = (int)(rest % nwb);
+    rest /= nwb;
+    const int h = (int)(rest % p.H), b = (int)(rest / p.H);
+    const int64_t c0 = (int64_t)cg * 8, dim = p.dim;
+    const int H = p.H, W = p.W;
+    const int nv = (int)(dim - c0 < 8 ? dim - c0 : 8);
+    const bool vec = p.vec != 0;
+    const float *dv = p.dv + (int64_t)b * H * W * dim + c0;
+    T *dx = (T *)p.dx + (int64_t)b * H * W * dim + c0;
+    float f[72];
+    filters8<9>(p.w, c0, nv, p.wvec != 0, f);
+    const int w0 = wb * R;
+    float g[3][R + 2][8];  // dv rows h-1 .. h+1, columns w0-1 .. w0+R
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int hh = h - 1 + i;
+#pragma unroll
+        for (int j = 0; j < R + 2; ++j) {
+            const int c = w0 - 1 + j;
+            if (hh >= 0 && hh < H && c >= 0 && c < W) load_dv8(dv + ((int64_t)hh * W + c) * dim, nv, vec, g[i][j]);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[i][j][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        if (w0 + u >= W) break;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int j = 0; j < 3; ++j) a = fmaf(f[e * 9 + i * 3 + j], g[2 - i][u + 2 - j][e], a);
+            v[e] = a;
+        }
+        store8(dx + ((int64_t)h * W + w0 + u) * dim, nv, vec, v);
+    }
+}
+
+// launch 3: one thread per (channel, tap or bias): the sum of the partial rows, in row order
+__global__ __launch_bounds__(256) void conv_bwd_reduce(ConvBwdParams p) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int T1 = p.taps + 1;
+    if (gid >= p.dim * T1) return;
+    const int64_t d = gid / T1;
+    const int k = (int)(gid % T1);
+    float a = 0.f;
+    for (int q = 0; q < p.nparts; ++q) a += p.part[(int64_t)q * p.dim * T1 + gid];
+    if (k < p.taps) p.dw[d * p.taps + k] = a;
+    else if (p.dbias) p.dbias[d] = a;
+}
+
+// the launch geometry of both backward convolutions, and the workspace it needs
+struct ConvBwdPlan {
+    int ngrp, per, nrun, nwb;
+    int64_t parts;
+    size_t dv_bytes, part_bytes;
+};
+
+// 1-D: runs of 16 (bf16) / 8 (fp32) steps for launch 1, 8 steps for launch 2; a launch-1 thread
+// takes enough runs that there are about 2^17 of them (at most 16 runs each)
+ConvBwdPlan plan_conv1d(int64_t batch, int64_t L, int64_t dim, int64_t K, int io_dtype) {
+    ConvBwdPlan q{};
+    const int64_t R1 = io_dtype == SELSCAN_BF16 ? 16 : 8, ncg = (dim + 7) / 8;
+    const int64_t runs = (L + R1 - 1) / R1;
+    int64_t per = (batch * runs * ncg + (1 << 17) - 1) >> 17;
+    per = per < 1 ? 1 : (per > 16 ? 16 : per);
+    q.per = (int)per;
+    q.ngrp = (int)((runs + per - 1) / per);
+    if (q.ngrp < 1) q.ngrp = 1;
+    q.nrun = (int)((L + 7) / 8);
+    if (q.nrun < 1) q.nrun = 1;  // one (empty) run still writes the state rows' gradient
+    q.parts = batch * q.ngrp;
+    q.dv_bytes = (size_t)batch * L * dim * 4;
+    q.part_bytes = (size_t)q.parts * dim * (K + 1) * 4;
+    return q;
+}
+
+// 2-D: launch 1 takes 4 (bf16) / 2 (fp32) pixels of a row and a group of rows (8, or fewer
+// rows per thread when the grid would be small)
+ConvBwdPlan plan_dwconv2d(int64_t batch, int64_t H, int64_t W, int64_t dim, int io_dtype) {
+    ConvBwdPlan q{};
+    const int64_t R = io_dtype == SELSCAN_BF16 ? 4 : 2, ncg = (dim + 7) / 8;
+    q.nwb = (int)((W + R - 1) / R);
+    int64_t per = 8;
+    while (per > 1 && batch * ((H + per - 1) / per) * q.nwb * ncg < (1 << 16)) per /= 2;
+    q.per = (int)per;
+    q.ngrp = (int)((H + per - 1) / per);
+    q.parts = batch * q.ngrp * q.nwb;
+    q.dv_bytes = (size_t)batch * H * W * dim * 4;
+    q.part_bytes = (size_t)q.parts * dim * 10 * 4;
+    return q;
+}
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+template <typename T, int K>
+int conv1d_bwd_launch(ConvBwdParams &c, void *stream) {
+    int rc = launch_grid((const void *)&conv1d_bwd_dv<T, K>, (int64_t)c.batch * c.ngrp * c.ncg, &c, stream);
+    if (rc == SELSCAN_OK)
+        rc = launch_grid((const void *)&conv1d_bwd_dx<T, K>, (int64_t)c.batch * c.nrun * c.ncg, &c, stream);
+    if (rc == SELSCAN_OK) rc = launch_grid((const void *)&conv_bwd_reduce, c.dim * (K + 1), &c, stream);
+    return rc;
+}
+
+template <typename T>
+int conv1d_bwd_width(ConvBwdParams &c, int K, void *stream) {
+    switch (K) {
+        case 1: return conv1d_bwd_launch<T, 1>(c, stream);
+        case 2: return conv1d_bwd_launch<T, 2>(c, stream);
+        case 3: return conv1d_bwd_launch<T, 3>(c, stream);
+        default: return conv1d_bwd_launch<T, 4>(c, stream);
+    }
+}
+
+template <typename T>
+int dwconv2d_bwd_launch(ConvBwdParams &c, void *stream) {
+    int rc = launch_grid((const void *)&dwconv2d3_bwd_dv<T>, (int64_t)c.batch * c.ngrp * c.nwb * c.ncg, &c, stream);
+    if (rc == SELSCAN_OK)
+        rc = launch_grid((const void *)&dwconv2d3_bwd_dx<T>, (int64_t)c.batch * c.H * ((c.W + 1) / 2) * c.ncg, &c,
+                         stream);
+    if (rc == SELSCAN_OK) rc = launch_grid((const void *)&conv_bwd_reduce, c.dim * 10, &c, stream);
+    return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -286,6 +684,122 @@ int dwconv2d_fwd(const void *x, const float *weight, const float *bias, unsigned
     const int64_t threads = (int64_t)batch * H * c.nwb * c.ncg;
     if (io_dtype == SELSCAN_BF16) return launch_grid((const void *)&dwconv2d3_kernel<uint16_t>, threads, &c, stream);
     return launch_grid((const void *)&dwconv2d3_kernel<float>, threads, &c, stream);
+}
+
+size_t causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int io_dtype) {
+    if (batch <= 0 || seqlen < 0 || dim <= 0 || width < 1 || width > 4) return 0;
+    const ConvBwdPlan q = plan_conv1d(batch, seqlen, dim, width, io_dtype);
+    return up256(q.dv_bytes) + up256(q.part_bytes);
+}
+
+int causal_conv1d_bwd(const void *x, const float *weight, const float *bias, const void *state_in, const void *dout,
+                      unsigned flags, void *dx, float *dweight, float *dbias, void *dstate_in, int64_t batch,
+                      int64_t seqlen, int64_t dim, int64_t width, int io_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    if (batch < 0 || seqlen < 0 || dim < 0 || width < 0) return SELSCAN_E_SHAPE;
+    if (io_dtype != SELSCAN_F32 && io_dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
+    if (flags & ~SELSCAN_FLAG_SILU) return SELSCAN_E_UNSUPPORTED;
+    if (width < 1 || width > 4) return SELSCAN_E_UNSUPPORTED;
+    if (batch > 0x7FFFFFFF || seqlen > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    if (batch == 0 || dim == 0) return SELSCAN_OK;
+    if (!weight || !dweight || (seqlen > 0 && (!x || !dout || !dx))) return SELSCAN_E_NULL;
+    const size_t s = io_dtype == SELSCAN_BF16 ? 2 : 4;
+    const void *io[] = {x, state_in, dout, dx, dstate_in};
+    for (const void *q : io)
+        if (q && !aligned(q, s)) return SELSCAN_E_ALIGN;
+    const void *f32[] = {weight, bias, dweight, dbias, workspace};
+    for (const void *q : f32)
+        if (q && !aligned(q, 4)) return SELSCAN_E_ALIGN;
+    const size_t need = causal_conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, io_dtype);
+    if (!workspace || workspace_bytes < need) return SELSCAN_E_WORKSPACE;
+    const size_t tok = (size_t)batch * seqlen * dim * s, sts = (size_t)batch * (width - 1) * dim * s;
+    const size_t wb = (size_t)dim * width * 4, vb = (size_t)dim * 4;
+    const Span in[] = {{x, tok}, {weight, wb}, {bias, vb}, {state_in, sts}, {dout, tok}};
+    const Span out[] = {{dx, tok}, {dweight, wb}, {dbias, vb}, {dstate_in, sts}, {workspace, need}};
+    constexpr int NO = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Span &q : in)
+            if (overlap(out[i], q)) return SELSCAN_E_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(out[i], out[j])) return SELSCAN_E_ALIAS;
+    }
+    const ConvBwdPlan q = plan_conv1d(batch, seqlen, dim, width, io_dtype);
+    ConvBwdParams c{};
+    c.x = x, c.dout = dout, c.state_in = state_in, c.w = weight, c.bias = bias;
+    c.dv = (float *)workspace;
+    c.part = (float *)((char *)workspace + up256(q.dv_bytes));
+    c.dx = dx, c.dstate = width > 1 ? dstate_in : nullptr, c.dw = dweight, c.dbias = dbias;
+    c.L = seqlen, c.dim = dim, c.batch = (int)batch, c.silu = (flags & SELSCAN_FLAG_SILU) ? 1 : 0;
+    const void *rows[] = {x, state_in, dout, dx, dstate_in, workspace};
+    bool vec = dim % 8 == 0;
+    for (const void *r : rows)
+        if (r && !aligned(r, 16)) vec = false;
+    c.vec = vec;
+    c.wvec = aligned(weight, 16);
+    c.ncg = (int)((dim + 7) / 8);
+    c.nrun = q.nrun, c.per = q.per, c.ngrp = q.ngrp;
+    c.nparts = (int)q.parts, c.taps = (int)width;
+    if (q.parts > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    if (io_dtype == SELSCAN_BF16) return conv1d_bwd_width<uint16_t>(c, (int)width, stream);
+    return conv1d_bwd_width<float>(c, (int)width, stream);
+}
+
+size_t dwconv2d_bwd_workspace_bytes(int64_t batch, int64_t H, int64_t W, int64_t dim, int io_dtype) {
+    if (batch <= 0 || H <= 0 || W <= 0 || dim <= 0) return 0;
+    const ConvBwdPlan q = plan_dwconv2d(batch, H, W, dim, io_dtype);
+    return up256(q.dv_bytes) + up256(q.part_bytes);
+}
+
+int dwconv2d_bwd(const void *x, const float *weight, const float *bias, const void *dout, unsigned flags, void *dx,
+                 float *dweight, float *dbias, int64_t batch, int64_t H, int64_t W, int64_t dim, int64_t ksize,
+                 int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 0 || H < 0 || W < 0 || dim < 0 || ksize < 0) return SELSCAN_E_SHAPE;
+    if (io_dtype != SELSCAN_F32 && io_dtype != SELSCAN_BF16) return SELSCAN_E_UNSUPPORTED;
+    if (flags & ~SELSCAN_FLAG_SILU) return SELSCAN_E_UNSUPPORTED;
+    if (ksize != 3) return SELSCAN_E_UNSUPPORTED;
+    if (H > 0x7FFFFFFF || W > 0x7FFFFFFF || batch > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    if (dim == 0) return SELSCAN_OK;
+    if (!weight || !dweight) return SELSCAN_E_NULL;
+    const bool empty = batch == 0 || H == 0 || W == 0;
+    if (!empty && (!x || !dout || !dx)) return SELSCAN_E_NULL;
+    const size_t s = io_dtype == SELSCAN_BF16 ? 2 : 4;
+    const void *io[] = {x, dout, dx};
+    for (const void *q : io)
+        if (q && !aligned(q, s)) return SELSCAN_E_ALIGN;
+    const void *f32[] = {weight, bias, dweight, dbias, workspace};
+    for (const void *q : f32)
+        if (q && !aligned(q, 4)) return SELSCAN_E_ALIGN;
+    const size_t need = empty ? 0 : dwconv2d_bwd_workspace_bytes(batch, H, W, dim, io_dtype);
+    if (!empty && (!workspace || workspace_bytes < need)) return SELSCAN_E_WORKSPACE;
+    const size_t tok = empty ? 0 : (size_t)batch * H * W * dim * s, wb = (size_t)dim * 9 * 4, vb = (size_t)dim * 4;
+    const Span in[] = {{x, tok}, {weight, wb}, {bias, vb}, {dout, tok}};
+    const Span out[] = {{dx, tok}, {dweight, wb}, {dbias, vb}, {workspace, need}};
+    constexpr int NO = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < NO; ++i) {
+        for (const Span &q : in)
+            if (overlap(out[i], q)) return SELSCAN_E_ALIAS;
+        for (int j = i + 1; j < NO; ++j)
+            if (overlap(out[i], out[j])) return SELSCAN_E_ALIAS;
+    }
+    ConvBwdParams c{};
+    c.w = weight, c.bias = bias, c.dw = dweight, c.dbias = dbias, c.dim = dim, c.taps = 9;
+    if (empty) {  // no pixels: dw and dbias are zero sums
+        c.nparts = 0;
+        return launch_grid((const void *)&conv_bwd_reduce, dim * 10, &c, stream);
+    }
+    const ConvBwdPlan q = plan_dwconv2d(batch, H, W, dim, io_dtype);
+    c.x = x, c.dout = dout, c.dx = dx;
+    c.dv = (float *)workspace;
+    c.part = (float *)((char *)workspace + up256(q.dv_bytes));
+    c.H = (int)H, c.W = (int)W, c.batch = (int)batch, c.silu = (flags & SELSCAN_FLAG_SILU) ? 1 : 0;
+    c.vec = dim % 8 == 0 && aligned(x, 16) && aligned(dout, 16) && aligned(dx, 16) && aligned(workspace, 16);
+    c.wvec = aligned(weight, 16);
+    c.ncg = (int)((dim + 7) / 8);
+    c.per = q.per, c.ngrp = q.ngrp, c.nwb = q.nwb;
+    if (q.parts > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
+    c.nparts = (int)q.parts;
+    if (io_dtype == SELSCAN_BF16) return dwconv2d_bwd_launch<uint16_t>(c, stream);
+    return dwconv2d_bwd_launch<float>(c, stream);
 }
 
 }  // extern "C"

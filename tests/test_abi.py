@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol():
                              "selscan_bwd", "selscan_chunk_states_bytes", "selscan_bwd_workspace_bytes",
                              "local_ss2d_fwd", "selscan_scan_fwd", "selscan_scan_bwd",
                              "selscan_scan_chunk_states_bytes", "selscan_scan_bwd_workspace_bytes",
-                             "causal_conv1d_fwd", "dwconv2d_fwd",
+                             "causal_conv1d_fwd", "dwconv2d_fwd", "causal_conv1d_bwd", "dwconv2d_bwd",
+                             "causal_conv1d_bwd_workspace_bytes", "dwconv2d_bwd_workspace_bytes",
                              "selscan_workspace_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
@@ -315,6 +316,53 @@ def test_dwconv2d_arguments():
     assert dw(x=P + 1) == 3
     assert dw(H=0) == 0 and dw(batch=0) == 0
 
+
+
+def c1b(**kw):
+    a = dict(x=P, w=P + MB, bias=None, st=None, dout=P + 2 * MB, flags=0, dx=P + 3 * MB, dw=P + 4 * MB, db=None,
+             dst=None, batch=1, L_=16, dim=8, K=4, dtype=S.SELSCAN_BF16, ws=P + 8 * MB, wsb=1 << 20)
+    a.update(kw)
+    return L.causal_conv1d_bwd(a["x"], a["w"], a["bias"], a["st"], a["dout"], a["flags"], a["dx"], a["dw"], a["db"],
+                               a["dst"], a["batch"], a["L_"], a["dim"], a["K"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_conv1d_bwd_arguments():
+    """Every call here fails a host-side check (none reaches a launch)."""
+    need = S.causal_conv1d_bwd_workspace_bytes(1, 16, 8, 4)
+    assert 16 * 8 * 4 <= need <= 1 << 20
+    assert S.causal_conv1d_bwd_workspace_bytes(0, 16, 8, 4) == 0 and S.causal_conv1d_bwd_workspace_bytes(1, 16, 8, 5) == 0
+    assert c1b(batch=-1) == 2
+    assert c1b(K=5) == 5 and c1b(K=0) == 5 and c1b(flags=1) == 5 and c1b(dtype=3) == 5
+    for k in ("x", "w", "dout", "dx", "dw"):
+        assert c1b(**{k: None}) == 1, k
+    assert c1b(dx=P + 3 * MB + 1) == 3 and c1b(dw=P + 4 * MB + 2) == 3
+    assert c1b(ws=None) == 6 and c1b(wsb=need - 4) == 6
+    assert c1b(dx=P + 16) == 4                    # dx on x
+    assert c1b(dw=P + 3 * MB + 64) == 4           # dweight on dx
+    assert c1b(ws=P + 2 * MB) == 4                # the workspace on dout
+    assert c1b(dst=P + MB + 16, st=P + 5 * MB) == 4  # dstate on the filters
+    assert c1b(batch=0, x=None) == 0
+
+
+def d2b(**kw):
+    a = dict(x=P, w=P + MB, bias=None, dout=P + 2 * MB, flags=0, dx=P + 3 * MB, dw=P + 4 * MB, db=None, batch=1, H=4,
+             W=5, dim=8, ks=3, dtype=S.SELSCAN_BF16, ws=P + 8 * MB, wsb=1 << 20)
+    a.update(kw)
+    return L.dwconv2d_bwd(a["x"], a["w"], a["bias"], a["dout"], a["flags"], a["dx"], a["dw"], a["db"], a["batch"],
+                          a["H"], a["W"], a["dim"], a["ks"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_dwconv2d_bwd_arguments():
+    """Every call here fails a host-side check (none reaches a launch)."""
+    need = S.dwconv2d_bwd_workspace_bytes(1, 4, 5, 8)
+    assert 20 * 8 * 4 <= need <= 1 << 20 and S.dwconv2d_bwd_workspace_bytes(1, 0, 5, 8) == 0
+    assert d2b(H=-1) == 2 and d2b(ks=5) == 5 and d2b(flags=2) == 5
+    for k in ("x", "w", "dout", "dx", "dw"):
+        assert d2b(**{k: None}) == 1, k
+    assert d2b(dx=P + 3 * MB + 1) == 3
+    assert d2b(ws=None) == 6 and d2b(wsb=need - 4) == 6
+    assert d2b(dx=P + 2 * MB + 16) == 4 and d2b(db=P + 3 * MB + 4) == 4
+    assert d2b(dim=0) == 0
 
 
 def test_bench_finds_profiled_kernels_in_library():

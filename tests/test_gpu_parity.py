@@ -650,6 +650,114 @@ def test_dwconv2d_against_oracle(dtype, batch, H, Wd, dim, bias, silu):
 
 
 
+
+# ----------------------------------------------------------------------------- convolution backward
+_CONV_BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}  # dweight, dbias: fp32 sums over batch x positions
+
+
+@pytest.mark.parametrize("dtype,batch,L,dim,K,bias,silu,state", [
+    ("f32", 2, 37, 24, 4, True, True, True),
+    ("f32", 3, 129, 17, 3, False, True, True),   # ragged channel groups, unaligned rows
+    ("f32", 2, 70, 16, 1, True, True, False),
+    ("f32", 1, 1, 8, 4, True, True, True),       # one step: every tap but the last reads the state
+    ("f32", 2, 0, 8, 4, True, True, True),       # no steps: zero gradients
+    ("bf16", 2, 1000, 64, 4, True, True, True),
+    ("bf16", 2, 64, 24, 2, False, False, False),
+    ("bf16", 8, 2048, 1536, 4, True, True, False),  # the Mamba-130M-layer shape
+], ids=lambda v: str(v))
+def test_causal_conv1d_bwd_against_oracle(dtype, batch, L, dim, K, bias, silu, state):
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    g = W.generate_conv(batch, L, dim, K, dtype)
+    dout = W.generate_cotangent(batch, L, dim, dtype)
+    dev = lambda a, dt=dtype: PT.to_dev(a, dt)
+    gg = S.causal_conv1d_bwd(dev(g["x"]), dev(g["weight"], "f32"), dev(dout), bias=dev(g["bias"], "f32") if bias else None,
+                             state_in=dev(g["state"]) if state else None, silu=silu, dstate=True)
+    torch.cuda.synchronize()
+    f = lambda a: W.to_f64(a, dtype)
+    r = oracle.causal_conv1d_bwd(f(g["x"]), g["weight"].astype(np.float64), f(dout),
+                                 bias=g["bias"].astype(np.float64) if bias else None,
+                                 state=f(g["state"]) if state else np.zeros((batch, K - 1, dim)), silu=silu)
+    errs = {k: PT.rel_err(PT.from_dev(gg[k]), r[k]) if r[k].size else 0.0 for k in r}
+    _say("conv1d bwd", dtype, batch, L, dim, K, bias, silu, state, {k: f"{v:.2e}" for k, v in errs.items()})
+    assert set(gg) == set(r)
+    for k, e in errs.items():
+        assert e <= (PT.TOL[dtype] if k in ("dx", "dstate") else _CONV_BWD_TOL[dtype]), (k, e)
+
+
+def test_causal_conv1d_bwd_full_shape_sampled():
+    """The Mamba-1.4B-layer shape (batch 2 x L 65536 x D 4096, bf16, k = 4 + SiLU): every gradient
+    of a sample of channels against the oracle (dx, and the filter and bias sums of those
+    channels over the whole batch and sequence)."""
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    bt, L, dim = 2, 65536, 4096
+    g = W.generate_conv(bt, L, dim, 4, "bf16")
+    dout = W.generate_cotangent(bt, L, dim, "bf16")
+    gg = S.causal_conv1d_bwd(PT.to_dev(g["x"], "bf16"), PT.to_dev(g["weight"], "f32"), PT.to_dev(dout, "bf16"),
+                             bias=PT.to_dev(g["bias"], "f32"))
+    torch.cuda.synchronize()
+    ch = np.array([0, 1, 7, 8, 2047, 2048, 4095])
+    cht = torch.as_tensor(ch, device="cuda")
+    r = oracle.causal_conv1d_bwd(W.to_f64(g["x"], "bf16")[..., ch], g["weight"][ch].astype(np.float64),
+                                 W.to_f64(dout, "bf16")[..., ch], bias=g["bias"][ch].astype(np.float64))
+    errs = {"dx": PT.rel_err(PT.from_dev(gg["dx"][..., cht]), r["dx"]),
+            "dweight": PT.rel_err(PT.from_dev(gg["dweight"][cht]), r["dweight"]),
+            "dbias": PT.rel_err(PT.from_dev(gg["dbias"][cht]), r["dbias"])}
+    _say("conv1d bwd full", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["dx"] <= PT.TOL["bf16"] and errs["dweight"] <= _CONV_BWD_TOL["bf16"] and errs["dbias"] <= _CONV_BWD_TOL["bf16"]
+    del gg
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,batch,H,Wd,dim,bias,silu", [
+    ("f32", 2, 7, 9, 16, True, True),
+    ("f32", 1, 1, 1, 8, True, True),
+    ("f32", 2, 5, 33, 12, False, False),
+    ("f32", 1, 3, 2, 17, True, True),
+    ("bf16", 2, 28, 28, 64, True, True),
+    ("bf16", 32, 56, 56, 192, True, True),        # the VMamba stage-1 map
+], ids=lambda v: str(v))
+def test_dwconv2d_bwd_against_oracle(dtype, batch, H, Wd, dim, bias, silu):
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    g = W.generate_conv(batch, H * Wd, dim, 3, dtype, two_d=True)
+    dout = W.generate_cotangent(batch, H * Wd, dim, dtype)
+    gg = S.dwconv2d_bwd(PT.to_dev(g["x"], dtype), PT.to_dev(g["weight"], "f32"), H, Wd, PT.to_dev(dout, dtype),
+                        bias=PT.to_dev(g["bias"], "f32") if bias else None, silu=silu)
+    torch.cuda.synchronize()
+    r = oracle.dwconv2d_bwd(W.to_f64(g["x"], dtype), g["weight"].astype(np.float64), H, Wd, W.to_f64(dout, dtype),
+                            bias=g["bias"].astype(np.float64) if bias else None, silu=silu)
+    errs = {k: PT.rel_err(PT.from_dev(gg[k]), r[k]) for k in r}
+    _say("dwconv2d bwd", dtype, batch, H, Wd, dim, bias, silu, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e <= (PT.TOL[dtype] if k == "dx" else _CONV_BWD_TOL[dtype]), (k, e)
+
+
+def test_conv_bwd_deterministic():
+    """The filter and bias gradients are sums in a fixed order: two calls give the same bits."""
+    import torch
+    import selective_state_space_51_amd as S
+    g = W.generate_conv(4, 3000, 96, 4, "bf16")
+    dout = PT.to_dev(W.generate_cotangent(4, 3000, 96, "bf16"), "bf16")
+    args = (PT.to_dev(g["x"], "bf16"), PT.to_dev(g["weight"], "f32"), dout)
+    a = S.causal_conv1d_bwd(*args, bias=PT.to_dev(g["bias"], "f32"))
+    b = S.causal_conv1d_bwd(*args, bias=PT.to_dev(g["bias"], "f32"))
+    g2 = W.generate_conv(3, 20 * 30, 40, 3, "bf16", two_d=True)
+    d2 = PT.to_dev(W.generate_cotangent(3, 600, 40, "bf16"), "bf16")
+    c = S.dwconv2d_bwd(PT.to_dev(g2["x"], "bf16"), PT.to_dev(g2["weight"], "f32"), 20, 30, d2)
+    d = S.dwconv2d_bwd(PT.to_dev(g2["x"], "bf16"), PT.to_dev(g2["weight"], "f32"), 20, 30, d2)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    for k in c:
+        assert torch.equal(c[k], d[k]), k
+
+
+
 # ----------------------------------------------------------------------------- split launches
 @pytest.mark.parametrize("kind,H,Wd,win", [("bidir", 0, 0, 0), ("ss2d", 14, 18, 0), ("local_ss2d", 12, 18, 6)])
 def test_split_equals_sequential(kind, H, Wd, win):
