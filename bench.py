@@ -230,23 +230,37 @@ def cpu_baseline_conv(w, g, two_d: bool, budget_channels: int):
 
 
 METRIC_CONV = "conv prologue (depthwise conv + SiLU) B·L·D elem/s + achieved HBM GB/s vs peak, 1 GPU"
+METRIC_CONV_BWD = "conv prologue backward (dx, dweight, dbias) B·L·D elem/s + achieved HBM GB/s vs peak, 1 GPU"
 
 
 def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
     """--pass conv: the depthwise convolution + SiLU in front of the scan, on the workload's x shape
-    (k = 4 causal along the sequence for 1-D workloads; 3x3 on the H x W map for 2-D ones)."""
+    (k = 4 causal along the sequence for 1-D workloads; 3x3 on the H x W map for 2-D ones);
+    --pass conv_bwd: its backward (dx, dweight, dbias from dout)."""
     two_d = w.kind in ("ss2d", "local_ss2d")
     width = 3 if two_d else 4
+    bwd = args.pass_ == "conv_bwd"
     g = W.generate_conv(w.batch, w.seqlen, w.dim, width, w.dtype, two_d=two_d)
     x, wt, bias = up(g["x"]), up(g["weight"]), up(g["bias"])
-    out = torch.empty_like(x)
+    out = up(W.generate_cotangent(w.batch, w.seqlen, w.dim, w.dtype)) if bwd else torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    # rotate over copies of x and out totalling at least 512 MiB when one pair would fit in the
-    # 256 MB Infinity Cache (as the scan passes do)
+    # rotate over copies of x and out (dout for the backward) totalling at least 512 MiB when one
+    # pair would fit in the 256 MB Infinity Cache (as the scan passes do)
     pair = 2 * x.numel() * x.element_size()
     copies = 1 if args.no_rotate or pair >= (512 << 20) else min(64, -(-(512 << 20) // pair))
-    xs = [(x, out)] + [(x.clone(), torch.empty_like(out)) for _ in range(copies - 1)]
-    if two_d:
+    xs = [(x, out)] + [(x.clone(), out.clone() if bwd else torch.empty_like(out)) for _ in range(copies - 1)]
+    if bwd:
+        code = S.SELSCAN_BF16 if w.dtype == "bf16" else S.SELSCAN_F32
+        need = (S.dwconv2d_bwd_workspace_bytes(w.batch, w.H, w.W, w.dim, code) if two_d else
+                S.causal_conv1d_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, width, code))
+        cws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if bwd and two_d:
+        step = lambda i: S.dwconv2d_bwd(xs[i % copies][0], wt, w.H, w.W, xs[i % copies][1], bias=bias, workspace=cws,
+                                        stream=stream)
+    elif bwd:
+        step = lambda i: S.causal_conv1d_bwd(xs[i % copies][0], wt, xs[i % copies][1], bias=bias, workspace=cws,
+                                             stream=stream)
+    elif two_d:
         step = lambda i: S.dwconv2d_fwd(xs[i % copies][0], wt, w.H, w.W, bias=bias, out=xs[i % copies][1],
                                         stream=stream)
     else:
@@ -273,23 +287,31 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
     kern_ms = float(np.mean(launch_ms))
     ms_step = wall * 1e3 / args.steps
     elems = w.batch * w.seqlen * w.dim
-    # algorithmic bytes: x read once, out written once, the filters and biases read once
-    alg = 2 * elems * w.io_bytes + w.dim * (width * (width if two_d else 1) + 1) * 4
+    taps = width * (width if two_d else 1)
+    # algorithmic bytes: x read once, out written once, the filters and biases read once; the
+    # backward reads x and dout, writes dx, reads the filters and writes their gradients
+    alg = (3 if bwd else 2) * elems * w.io_bytes + w.dim * (taps + 1) * 4 * (2 if bwd else 1)
     gbs = alg / (kern_ms * 1e-3) / 1e9
-    kname = "dwconv2d3_kernel" if two_d else "causal_conv1d_kernel"
+    if bwd:
+        kname = ("dwconv2d3_bwd_dv + dwconv2d3_bwd_dx + conv_bwd_reduce" if two_d else
+                 "conv1d_bwd_dv + conv1d_bwd_dx + conv_bwd_reduce")
+    else:
+        kname = "dwconv2d3_kernel" if two_d else "causal_conv1d_kernel"
     out_line = {
-        "metric": METRIC_CONV, "value": elems / (ms_step * 1e-3), "unit": "elem/s", "n_gpus": 1,
+        "metric": METRIC_CONV_BWD if bwd else METRIC_CONV, "value": elems / (ms_step * 1e-3), "unit": "elem/s",
+        "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded: x ~ N(0,1); filter ~ N(0, 1/taps); bias ~ N(0,1))",
         "config": {"workload": w.name, "kind": "dwconv2d_3x3" if two_d else "causal_conv1d_k4", "batch": w.batch,
-                   "seqlen": w.seqlen, "dim": w.dim, "io_dtype": w.dtype, "silu": True, "pass": "conv",
+                   "seqlen": w.seqlen, "dim": w.dim, "io_dtype": w.dtype, "silu": True, "pass": args.pass_,
                    "input_sets": copies},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, "conv", w.kind), "kernel": kname, "kernel_ms": kern_ms,
+                     "traffic": None if bwd else measured_traffic(w.name, "conv", w.kind), "kernel": kname,
+                     "kernel_ms": kern_ms,
                      "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not bwd:
         del x, out, xs
         torch.cuda.empty_cache()
         out_line["cpu_baseline"] = cpu_baseline_conv(w, g, two_d, min(args.cpu_channels, 1024))
@@ -304,11 +326,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "conv"], default="fwd",
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "conv", "conv_bwd"], default="fwd",
                     help="fwd: the forward scan (default); bwd: selscan_scan_bwd (gradients of every input, "
                          "states recomputed from the chunk states a forward saved beforehand); conv: the "
                          "convolution in front of the scan (causal conv1d k=4 + SiLU for the 1-D workloads, "
-                         "DWConv 3x3 + SiLU for the 2-D ones) on the workload's x")
+                         "DWConv 3x3 + SiLU for the 2-D ones) on the workload's x; conv_bwd: its backward")
     ap.add_argument("--state", action="store_true",
                     help="single-direction workloads: run selscan_fwd_state with an initial state and the "
                          "final state written (recurrent / chunked inference)")
@@ -365,10 +387,10 @@ def main() -> int:
     if need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    if args.zoh and args.pass_ == "conv":
+    if args.zoh and args.pass_ in ("conv", "conv_bwd"):
         print("--zoh applies to the scan passes only", file=sys.stderr)
         return 2
-    if args.pass_ == "conv":
+    if args.pass_ in ("conv", "conv_bwd"):
         return conv_bench(args, w, S, W, torch, np, up, dev)
     if args.state and w.kind != "selscan":
         print("--state applies to single-direction workloads only", file=sys.stderr)

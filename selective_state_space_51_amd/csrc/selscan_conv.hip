@@ -220,12 +220,16 @@ int conv1d_launch(Conv1dParams &c, int K, void *stream) {
 // The chain rule through v = bias + sum of taps, out = act(v): dv = dout act'(v) (act' = 1 without
 // the SiLU); every tap spreads dv back to the input it read (dx, and for the 1-D convolution the
 // carried state rows), dw collects input x dv and dbias collects dv.  Three launches:
-//  1. conv_bwd_dv:  v recomputed from the input neighbourhood (as the forward kernels do), dv
-//     written to an fp32 workspace, and each thread's running sums of input x dv and dv over
-//     several runs written as one partial row per thread group (no atomics);
-//  2. conv_bwd_dx:  dx as the transposed convolution of dv (the taps read in mirror order);
-//  3. conv_bwd_reduce: dw and dbias as the sums of the partial rows, in a fixed order, so the
-//     results are the same from run to run.
+//  1. *_bwd_dv:  v recomputed from the input neighbourhood (as the forward kernels do), and each
+//     thread's running sums of input x dv and dv over several runs written as one partial row
+//     per thread group (no atomics); the 2-D kernel also writes dv to an fp32 workspace (dv
+//     rounded to bf16 would add a second rounding to a bf16 dx);
+//  2. *_bwd_dx:  dx as the transposed convolution of dv (the taps read in mirror order) -- the
+//     1-D kernel recomputes the dv it needs from the inputs (a run of 8 steps needs K-1 more),
+//     the 2-D kernel reads it back (a 3 x 3 neighbourhood of dv would need 5 x 5 inputs);
+//  3. conv_bwd_reduce: dw and dbias as the sums of the partial rows, as a tree of fixed shape
+//     (blocks of 64 rows x 64 columns, repeated until one row is left), so the results are the
+//     same from run to run.
 
 __device__ __forceinline__ float act_grad(float v, int silu_) {
     if (!silu_) return 1.f;
@@ -258,7 +262,7 @@ __device__ __forceinline__ void store_dv8(float *p, int nv, bool vec, const floa
 struct ConvBwdParams {
     const void *x, *dout, *state_in;
     const float *w, *bias;  // [dim][taps], [dim]
-    float *dv;              // [batch][positions][dim] fp32
+    float *dv;              // 2-D: [batch][H * W][dim] fp32
     float *part;            // [nparts][dim][taps + 1]: sums of input x dv per tap, then of dv
     void *dx, *dstate;      // dstate: [batch][K-1][dim] (1-D only), nullable
     float *dw, *dbias;
@@ -286,7 +290,6 @@ __global__ __launch_bounds__(256) void conv1d_bwd_dv(ConvBwdParams p) {
     const T *x = (const T *)p.x + (int64_t)b * L * dim + c0;
     const T *dout = (const T *)p.dout + (int64_t)b * L * dim + c0;
     const T *st = p.state_in ? (const T *)p.state_in + (int64_t)b * (K - 1) * dim + c0 : nullptr;
-    float *dv = p.dv + (int64_t)b * L * dim + c0;
     float f[8 * K], bs[8], sw[8 * K], sb[8];
     filters8<K>(p.w, c0, nv, p.wvec != 0, f);
 #pragma unroll
@@ -312,21 +315,22 @@ __global__ __launch_bounds__(256) void conv1d_bwd_dv(ConvBwdParams p) {
             rd[u] = Raw8<T>{};
             if (t0 + u < L) rd[u] = load_raw8(dout + (t0 + u) * dim, nv, vec);
         }
+        // every step is guarded rather than the loop cut short: a constant trip count keeps the
+        // unrolled arrays in registers
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            if (t0 + u >= L) break;
-            float g[8];
+            if (t0 + u < L) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = bs[e];
+                for (int e = 0; e < 8; ++e) {
+                    float a = bs[e];
 #pragma unroll
-                for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], raw_f32(raw[u + i], e), a);
-                g[e] = raw_f32(rd[u], e) * act_grad(a, p.silu);
-                sb[e] += g[e];
+                    for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], raw_f32(raw[u + i], e), a);
+                    const float g = raw_f32(rd[u], e) * act_grad(a, p.silu);
+                    sb[e] += g;
 #pragma unroll
-                for (int i = 0; i < K; ++i) sw[e * K + i] = fmaf(raw_f32(raw[u + i], e), g[e], sw[e * K + i]);
+                    for (int i = 0; i < K; ++i) sw[e * K + i] = fmaf(raw_f32(raw[u + i], e), g, sw[e * K + i]);
+                }
             }
-            store_dv8(dv + (t0 + u) * dim, nv, vec, g);
         }
     }
     float *pr = p.part + ((int64_t)b * p.ngrp + grp) * dim * (K + 1) + c0 * (K + 1);
@@ -340,10 +344,12 @@ __global__ __launch_bounds__(256) void conv1d_bwd_dv(ConvBwdParams p) {
 }
 
 // 1-D, launch 2: thread (b, run, channel group); dx[s] = sum_i w[i] dv[s + K-1-i] for the run's
-// kRB steps, and for the first run also the K-1 state rows (s < 0)
+// 8 steps (and for the first run the K-1 state rows, s < 0), with dv[t] = dout[t] act'(v[t])
+// recomputed for t = t0 .. t0+8+K-2 from the input rows t0-(K-1) .. t0+8+2K-3: the inputs are
+// read again (mostly from the caches) instead of dv round-tripping through memory
 template <typename T, int K>
 __global__ __launch_bounds__(256) void conv1d_bwd_dx(ConvBwdParams p) {
-    constexpr int R = 8;
+    constexpr int R = 8, NT = R + K - 1, NX = R + 2 * K - 2;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gid >= (int64_t)p.batch * p.nrun * p.ncg) return;
     const int cg = (int)(gid % p.ncg);
@@ -352,47 +358,58 @@ __global__ __launch_bounds__(256) void conv1d_bwd_dx(ConvBwdParams p) {
     const int64_t c0 = (int64_t)cg * 8, L = p.L, dim = p.dim;
     const int nv = (int)(dim - c0 < 8 ? dim - c0 : 8);
     const bool vec = p.vec != 0;
-    const float *dv = p.dv + (int64_t)b * L * dim + c0;
+    const T *x = (const T *)p.x + (int64_t)b * L * dim + c0;
+    const T *dout = (const T *)p.dout + (int64_t)b * L * dim + c0;
+    const T *st = p.state_in ? (const T *)p.state_in + (int64_t)b * (K - 1) * dim + c0 : nullptr;
     T *dx = (T *)p.dx + (int64_t)b * L * dim + c0;
-    float f[8 * K];
+    float f[8 * K], bs[8];
     filters8<K>(p.w, c0, nv, p.wvec != 0, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bs[e] = p.bias && e < nv ? p.bias[c0 + e] : 0.f;
     const int64_t t0 = (int64_t)tb * R;
-    float g[R + K - 1][8];  // dv rows t0 .. t0 + R + K - 2 (zeros past the end)
+    Raw8<T> raw[NX], rd[NT];  // input rows t0-(K-1) .. t0+NT-1, dout rows t0 .. t0+NT-1
 #pragma unroll
-    for (int i = 0; i < R + K - 1; ++i) {
-        if (t0 + i < L) load_dv8(dv + (t0 + i) * dim, nv, vec, g[i]);
-        else
-#pragma unroll
-            for (int e = 0; e < 8; ++e) g[i][e] = 0.f;
+    for (int i = 0; i < NX; ++i) {
+        const int64_t s = t0 - (K - 1) + i;
+        raw[i] = Raw8<T>{};
+        if (s >= 0 && s < L) raw[i] = load_raw8(x + s * dim, nv, vec);
+        else if (s < 0 && st) raw[i] = load_raw8(st + (K - 1 + s) * dim, nv, vec);
     }
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-        if (t0 + u >= L) break;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = 0.f;
-#pragma unroll
-            for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], g[u + K - 1 - i][e], a);
-            v[e] = a;
-        }
-        store8(dx + (t0 + u) * dim, nv, vec, v);
+    for (int u = 0; u < NT; ++u) {
+        rd[u] = Raw8<T>{};
+        if (t0 + u < L) rd[u] = load_raw8(dout + (t0 + u) * dim, nv, vec);
     }
-    if (p.dstate && tb == 0) {
-        // state row r is input position s = r - (K-1): it fed step s + K-1-i through tap i
-        T *ds = (T *)p.dstate + (int64_t)b * (K - 1) * dim + c0;
+    // acc[j] collects dx of position t0 - (K-1) + j: the run's steps (j >= K-1) and, for the
+    // first run, the state rows in front (j < K-1)
+    float acc[NX][8];
 #pragma unroll
-        for (int r = 0; r < K - 1; ++r) {
-            float v[8];
+    for (int j = 0; j < NX; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+    // guarded steps, constant trip counts: acc stays in registers
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        if (t0 + u < L) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float a = 0.f;
+                float a = bs[e];
 #pragma unroll
-                for (int i = 0; i <= r; ++i) a = fmaf(f[e * K + i], g[r - i][e], a);
-                v[e] = a;
+                for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], raw_f32(raw[u + i], e), a);
+                const float g = raw_f32(rd[u], e) * act_grad(a, p.silu);
+                // step t0+u read position t0+u-(K-1)+i through tap i
+#pragma unroll
+                for (int i = 0; i < K; ++i) acc[u + i][e] = fmaf(f[e * K + i], g, acc[u + i][e]);
             }
-            store8(ds + r * dim, nv, vec, v);
         }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+        if (t0 + u < L) store8(dx + (t0 + u) * dim, nv, vec, acc[u + K - 1]);
+    if (p.dstate && tb == 0) {
+        T *ds = (T *)p.dstate + (int64_t)b * (K - 1) * dim + c0;
+#pragma unroll
+        for (int r = 0; r < K - 1; ++r) store8(ds + r * dim, nv, vec, acc[r]);
     }
 }
 
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(256) void conv1d_bwd_dx(ConvBwdParams p) {
 // R pixels of each
 template <typename T>
 __global__ __launch_bounds__(256) void dwconv2d3_bwd_dv(ConvBwdParams p) {
-    constexpr int R = sizeof(T) == 2 ? 4 : 2;
+    constexpr int R = 2;  // with the 9-tap filters and sums in registers, 2 pixels keep 2 waves per SIMD
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gid >= (int64_t)p.batch * p.ngrp * p.nwb * p.ncg) return;
     const int cg = (int)(gid % p.ncg);
@@ -476,14 +493,14 @@ __global__ __launch_bounds__(256) void dwconv2d3_bwd_dv(ConvBwdParams p) {
     }
 }
 
-// 2-D, launch 2: thread (b, image row, pixel block of 2, channel group); dx[h][w] =
+// 2-D, launch 2: thread (b, image row, pixel block of 4, channel group); dx[h][w] =
 // sum_{i,j} w[i][j] dv[h+1-i][w+1-j] (dv = 0 outside the map)
 template <typename T>
 __global__ __launch_bounds__(256) void dwconv2d3_bwd_dx(ConvBwdParams p) {
-    constexpr int R = 2;
+    constexpr int R = 4;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int nwb = (p.W + R - 1) / R;
-    if (gid >= (int64_t)p.batch * p.H * nwb * p.ncg) return;
+    if (gid >= (int64_t)p.batch * p.H * nwb * p.ncg) return;  // the launch covers batch x H x ceil(W/4) x ncg
     const int cg = (int)(gid % p.ncg);
     int64_t rest = gid / p.ncg;
     const int wb = (int)(rest % nwb);
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(256) void dwconv2d3_bwd_dx(ConvBwdParams p) {
     float f[72];
     filters8<9>(p.w, c0, nv, p.wvec != 0, f);
     const int w0 = wb * R;
-    float g[3][R + 2][8];  // dv rows h-1 .. h+1, columns w0-1 .. w0+R
+    float g[3][R + 2][8];  // dv rows h-1 .. h+1, columns w0-1 .. w0+R (zeros outside the map)
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const int hh = h - 1 + i;
@@ -528,25 +545,80 @@ __global__ __launch_bounds__(256) void dwconv2d3_bwd_dx(ConvBwdParams p) {
     }
 }
 
-// launch 3: one thread per (channel, tap or bias): the sum of the partial rows, in row order
-__global__ __launch_bounds__(256) void conv_bwd_reduce(ConvBwdParams p) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int T1 = p.taps + 1;
-    if (gid >= p.dim * T1) return;
-    const int64_t d = gid / T1;
-    const int k = (int)(gid % T1);
+struct ReduceParams {
+    const float *src;  // [rows][cols]
+    float *dst;        // [ceil(rows / 64)][cols], or NULL on the last level
+    float *dw, *dbias; // the last level writes column d * (taps + 1) + k to dw[d][k] (k < taps) or dbias[d]
+    int64_t rows, cols;
+    int taps;
+};
+
+// launch 3, one level: block (column tile x, row tile y) adds rows 64 y .. 64 y + 63 of 64
+// columns; thread (column c, slice s) adds rows 16 s .. 16 s + 15 of the tile in order, then the
+// four slices are added in order
+__global__ __launch_bounds__(256) void conv_bwd_reduce(ReduceParams p) {
+    __shared__ float sm[4][64];
+    const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 64 + c, t = blockIdx.y;
     float a = 0.f;
-    for (int q = 0; q < p.nparts; ++q) a += p.part[(int64_t)q * p.dim * T1 + gid];
-    if (k < p.taps) p.dw[d * p.taps + k] = a;
-    else if (p.dbias) p.dbias[d] = a;
+    if (col < p.cols) {
+        const int64_t r0 = t * 64 + sl * 16;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (r0 + k < p.rows) a += p.src[(r0 + k) * p.cols + col];
+    }
+    sm[sl][c] = a;
+    __syncthreads();
+    if (sl != 0 || col >= p.cols) return;
+    const float v = ((sm[0][c] + sm[1][c]) + sm[2][c]) + sm[3][c];
+    if (p.dst) {
+        p.dst[t * p.cols + col] = v;
+    } else {
+        const int64_t d = col / (p.taps + 1);
+        const int k = (int)(col % (p.taps + 1));
+        if (k < p.taps) p.dw[d * p.taps + k] = v;
+        else if (p.dbias) p.dbias[d] = v;
+    }
+}
+
+// the tree: part -> t1 -> t2 -> t1 ... until a level has one row tile, which writes dw and dbias
+int reduce_launch(const ConvBwdParams &c, float *t1, float *t2, void *stream) {
+    ReduceParams r;
+    r.src = c.part, r.dw = c.dw, r.dbias = c.dbias, r.rows = c.nparts, r.cols = c.dim * (c.taps + 1), r.taps = c.taps;
+    float *bufs[2] = {t1, t2};
+    for (int level = 0;; ++level) {
+        const int64_t tiles = r.rows > 64 ? (r.rows + 63) / 64 : 1;
+        r.dst = tiles > 1 ? bufs[level & 1] : nullptr;
+        const int64_t bx = (r.cols + 63) / 64;
+        if (bx > 0x7FFFFFFF || tiles > 65535) return SELSCAN_E_UNSUPPORTED;
+        void *a[] = {&r};
+        hipError_t e = hipLaunchKernel((const void *)&conv_bwd_reduce, dim3((unsigned)bx, (unsigned)tiles), dim3(256), a,
+                                       0, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            record_hip_error(e);
+            return SELSCAN_E_HIP;
+        }
+        if (tiles == 1) return SELSCAN_OK;
+        r.src = r.dst, r.rows = tiles;
+    }
 }
 
 // the launch geometry of both backward convolutions, and the workspace it needs
 struct ConvBwdPlan {
     int ngrp, per, nrun, nwb;
     int64_t parts;
-    size_t dv_bytes, part_bytes;
+    size_t dv_bytes, part_bytes, t1_bytes, t2_bytes;  // dv, partial rows, the reduction's two levels
+    size_t total() const;
 };
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+size_t ConvBwdPlan::total() const { return up256(dv_bytes) + up256(part_bytes) + up256(t1_bytes) + up256(t2_bytes); }
+
+void plan_tree(ConvBwdPlan &q, int64_t cols) {
+    const int64_t r1 = (q.parts + 63) / 64, r2 = (r1 + 63) / 64;
+    q.t1_bytes = (size_t)r1 * cols * 4;
+    q.t2_bytes = (size_t)r2 * cols * 4;
+}
 
 // 1-D: runs of 16 (bf16) / 8 (fp32) steps for launch 1, 8 steps for launch 2; a launch-1 thread
 // takes enough runs that there are about 2^17 of them (at most 16 runs each)
@@ -562,55 +634,55 @@ ConvBwdPlan plan_conv1d(int64_t batch, int64_t L, int64_t dim, int64_t K, int io
     q.nrun = (int)((L + 7) / 8);
     if (q.nrun < 1) q.nrun = 1;  // one (empty) run still writes the state rows' gradient
     q.parts = batch * q.ngrp;
-    q.dv_bytes = (size_t)batch * L * dim * 4;
+    q.dv_bytes = 0;  // launch 2 recomputes dv
     q.part_bytes = (size_t)q.parts * dim * (K + 1) * 4;
+    plan_tree(q, dim * (K + 1));
     return q;
 }
 
-// 2-D: launch 1 takes 4 (bf16) / 2 (fp32) pixels of a row and a group of rows (8, or fewer
-// rows per thread when the grid would be small)
+// 2-D: launch 1 takes 2 pixels of a row and a group of rows (8, or fewer rows per thread until
+// there are 2^18 threads)
 ConvBwdPlan plan_dwconv2d(int64_t batch, int64_t H, int64_t W, int64_t dim, int io_dtype) {
     ConvBwdPlan q{};
-    const int64_t R = io_dtype == SELSCAN_BF16 ? 4 : 2, ncg = (dim + 7) / 8;
+    const int64_t R = 2, ncg = (dim + 7) / 8;
     q.nwb = (int)((W + R - 1) / R);
     int64_t per = 8;
-    while (per > 1 && batch * ((H + per - 1) / per) * q.nwb * ncg < (1 << 16)) per /= 2;
+    while (per > 1 && batch * ((H + per - 1) / per) * q.nwb * ncg < (1 << 18)) per /= 2;
     q.per = (int)per;
     q.ngrp = (int)((H + per - 1) / per);
     q.parts = batch * q.ngrp * q.nwb;
     q.dv_bytes = (size_t)batch * H * W * dim * 4;
     q.part_bytes = (size_t)q.parts * dim * 10 * 4;
+    plan_tree(q, dim * 10);
     return q;
 }
 
-size_t up256(size_t v) { return (v + 255) / 256 * 256; }
-
 template <typename T, int K>
-int conv1d_bwd_launch(ConvBwdParams &c, void *stream) {
+int conv1d_bwd_launch(ConvBwdParams &c, float *t1, float *t2, void *stream) {
     int rc = launch_grid((const void *)&conv1d_bwd_dv<T, K>, (int64_t)c.batch * c.ngrp * c.ncg, &c, stream);
     if (rc == SELSCAN_OK)
         rc = launch_grid((const void *)&conv1d_bwd_dx<T, K>, (int64_t)c.batch * c.nrun * c.ncg, &c, stream);
-    if (rc == SELSCAN_OK) rc = launch_grid((const void *)&conv_bwd_reduce, c.dim * (K + 1), &c, stream);
+    if (rc == SELSCAN_OK) rc = reduce_launch(c, t1, t2, stream);
     return rc;
 }
 
 template <typename T>
-int conv1d_bwd_width(ConvBwdParams &c, int K, void *stream) {
+int conv1d_bwd_width(ConvBwdParams &c, int K, float *t1, float *t2, void *stream) {
     switch (K) {
-        case 1: return conv1d_bwd_launch<T, 1>(c, stream);
-        case 2: return conv1d_bwd_launch<T, 2>(c, stream);
-        case 3: return conv1d_bwd_launch<T, 3>(c, stream);
-        default: return conv1d_bwd_launch<T, 4>(c, stream);
+        case 1: return conv1d_bwd_launch<T, 1>(c, t1, t2, stream);
+        case 2: return conv1d_bwd_launch<T, 2>(c, t1, t2, stream);
+        case 3: return conv1d_bwd_launch<T, 3>(c, t1, t2, stream);
+        default: return conv1d_bwd_launch<T, 4>(c, t1, t2, stream);
     }
 }
 
 template <typename T>
-int dwconv2d_bwd_launch(ConvBwdParams &c, void *stream) {
+int dwconv2d_bwd_launch(ConvBwdParams &c, float *t1, float *t2, void *stream) {
     int rc = launch_grid((const void *)&dwconv2d3_bwd_dv<T>, (int64_t)c.batch * c.ngrp * c.nwb * c.ncg, &c, stream);
     if (rc == SELSCAN_OK)
-        rc = launch_grid((const void *)&dwconv2d3_bwd_dx<T>, (int64_t)c.batch * c.H * ((c.W + 1) / 2) * c.ncg, &c,
+        rc = launch_grid((const void *)&dwconv2d3_bwd_dx<T>, (int64_t)c.batch * c.H * ((c.W + 3) / 4) * c.ncg, &c,
                          stream);
-    if (rc == SELSCAN_OK) rc = launch_grid((const void *)&conv_bwd_reduce, c.dim * 10, &c, stream);
+    if (rc == SELSCAN_OK) rc = reduce_launch(c, t1, t2, stream);
     return rc;
 }
 
@@ -688,8 +760,7 @@ int dwconv2d_fwd(const void *x, const float *weight, const float *bias, unsigned
 
 size_t causal_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int io_dtype) {
     if (batch <= 0 || seqlen < 0 || dim <= 0 || width < 1 || width > 4) return 0;
-    const ConvBwdPlan q = plan_conv1d(batch, seqlen, dim, width, io_dtype);
-    return up256(q.dv_bytes) + up256(q.part_bytes);
+    return plan_conv1d(batch, seqlen, dim, width, io_dtype).total();
 }
 
 int causal_conv1d_bwd(const void *x, const float *weight, const float *bias, const void *state_in, const void *dout,
@@ -726,7 +797,7 @@ int causal_conv1d_bwd(const void *x, const float *weight, const float *bias, con
     const ConvBwdPlan q = plan_conv1d(batch, seqlen, dim, width, io_dtype);
     ConvBwdParams c{};
     c.x = x, c.dout = dout, c.state_in = state_in, c.w = weight, c.bias = bias;
-    c.dv = (float *)workspace;
+    c.dv = nullptr;
     c.part = (float *)((char *)workspace + up256(q.dv_bytes));
     c.dx = dx, c.dstate = width > 1 ? dstate_in : nullptr, c.dw = dweight, c.dbias = dbias;
     c.L = seqlen, c.dim = dim, c.batch = (int)batch, c.silu = (flags & SELSCAN_FLAG_SILU) ? 1 : 0;
@@ -738,16 +809,17 @@ int causal_conv1d_bwd(const void *x, const float *weight, const float *bias, con
     c.wvec = aligned(weight, 16);
     c.ncg = (int)((dim + 7) / 8);
     c.nrun = q.nrun, c.per = q.per, c.ngrp = q.ngrp;
-    c.nparts = (int)q.parts, c.taps = (int)width;
     if (q.parts > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
-    if (io_dtype == SELSCAN_BF16) return conv1d_bwd_width<uint16_t>(c, (int)width, stream);
-    return conv1d_bwd_width<float>(c, (int)width, stream);
+    c.nparts = (int)q.parts, c.taps = (int)width;
+    float *t1 = (float *)((char *)c.part + up256(q.part_bytes));
+    float *t2 = (float *)((char *)t1 + up256(q.t1_bytes));
+    if (io_dtype == SELSCAN_BF16) return conv1d_bwd_width<uint16_t>(c, (int)width, t1, t2, stream);
+    return conv1d_bwd_width<float>(c, (int)width, t1, t2, stream);
 }
 
 size_t dwconv2d_bwd_workspace_bytes(int64_t batch, int64_t H, int64_t W, int64_t dim, int io_dtype) {
     if (batch <= 0 || H <= 0 || W <= 0 || dim <= 0) return 0;
-    const ConvBwdPlan q = plan_dwconv2d(batch, H, W, dim, io_dtype);
-    return up256(q.dv_bytes) + up256(q.part_bytes);
+    return plan_dwconv2d(batch, H, W, dim, io_dtype).total();
 }
 
 int dwconv2d_bwd(const void *x, const float *weight, const float *bias, const void *dout, unsigned flags, void *dx,
@@ -785,7 +857,7 @@ int dwconv2d_bwd(const void *x, const float *weight, const float *bias, const vo
     c.w = weight, c.bias = bias, c.dw = dweight, c.dbias = dbias, c.dim = dim, c.taps = 9;
     if (empty) {  // no pixels: dw and dbias are zero sums
         c.nparts = 0;
-        return launch_grid((const void *)&conv_bwd_reduce, dim * 10, &c, stream);
+        return reduce_launch(c, nullptr, nullptr, stream);
     }
     const ConvBwdPlan q = plan_dwconv2d(batch, H, W, dim, io_dtype);
     c.x = x, c.dout = dout, c.dx = dx;
@@ -798,8 +870,10 @@ int dwconv2d_bwd(const void *x, const float *weight, const float *bias, const vo
     c.per = q.per, c.ngrp = q.ngrp, c.nwb = q.nwb;
     if (q.parts > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     c.nparts = (int)q.parts;
-    if (io_dtype == SELSCAN_BF16) return dwconv2d_bwd_launch<uint16_t>(c, stream);
-    return dwconv2d_bwd_launch<float>(c, stream);
+    float *t1 = (float *)((char *)c.part + up256(q.part_bytes));
+    float *t2 = (float *)((char *)t1 + up256(q.t1_bytes));
+    if (io_dtype == SELSCAN_BF16) return dwconv2d_bwd_launch<uint16_t>(c, t1, t2, stream);
+    return dwconv2d_bwd_launch<float>(c, t1, t2, stream);
 }
 
 }  // extern "C"
