@@ -67,7 +67,9 @@ def profiled_kernels(pass_: str, kind: str):
 
 def kernel_code_hash(names, so_path: str = LIB_SO) -> str:
     """sha256[:16] over the gfx950 machine code and kernel descriptors of the named kernels, read
-    from the code objects embedded in the built library (clang offload bundles; ELF symbol table)."""
+    from the code objects embedded in the built library (clang offload bundles; ELF symbol table).
+    The descriptors' code-entry offsets are left out: they change when other kernels of the same
+    code object move the code, not when the kernel's own code changes."""
     import struct
     data = open(so_path, "rb").read()
     want = set(names) | {n + ".kd" for n in names}
@@ -98,7 +100,12 @@ def kernel_code_hash(names, so_path: str = LIB_SO) -> str:
                     if name in want and st_shndx < shnum and st_size:
                         home = secs[st_shndx]
                         start = home[4] + (st_value - home[3])  # file offset = sh_offset + (vaddr - sh_addr)
-                        found[name] = elf[start:start + st_size]
+                        body = elf[start:start + st_size]
+                        if name.endswith(".kd") and len(body) >= 24:
+                            # the descriptor's code-entry offset (bytes 16..23) moves with the
+                            # layout of the code object, not with the kernel's own code
+                            body = body[:16] + bytes(8) + body[24:]
+                        found[name] = body
         i = data.find(b"__CLANG_OFFLOAD_BUNDLE__", i + 1)
     if set(found) != want:
         return "missing:" + ",".join(sorted(want - set(found)))[:60]
