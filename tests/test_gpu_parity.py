@@ -63,7 +63,7 @@ def test_workload_small(idx, ov):
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6], ids=[W.WORKLOADS[i].name for i in (1, 2, 3, 4, 5, 6)])
 def test_workload_full_size_sampled(idx):
-    """Full BASELINE sizes in the launch configuration the benchmark times; the oracle
+    """The workloads' full sizes in the launch configuration the benchmark times; the oracle
     checks a sample of channels (every batch row, whole sequence)."""
     import torch
     w = W.WORKLOADS[idx]
