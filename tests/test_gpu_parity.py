@@ -75,6 +75,23 @@ def test_workload_full_size_sampled(idx):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("variant", ["zoh", "softplus"])
+def test_benchmark_shape_variants_sampled(variant):
+    """The Mamba-1.4B-layer shape (batch 2 x L 65536 x D 4096, bf16) with the zero-order-hold Bbar,
+    or with delta_bias and the fused softplus (the pre-activation drawn so that delta keeps the
+    workload's distribution), as bench.py --zoh / --softplus time it: a sample of channels
+    against the oracle (every batch row, whole sequence)."""
+    import torch
+    w = W.WORKLOADS[2]
+    sp = variant == "softplus"
+    _say("full variant", w.name, variant)
+    inp = W.generate(w, with_w=sp, with_bias=sp)
+    chans = [0, 1, 15, 16, 2049, 4095]
+    _check(w.kind, w, inp, channels=chans, zoh=variant == "zoh", softplus=sp, use_bias=sp)
+    del inp
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------- options and edges
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_softplus_bias_and_optional_args(dtype):
@@ -445,6 +462,17 @@ def test_scan_bwd_zoh_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw)
     errs = _scan_bwd_run(kind, dtype, batch, L, dim, H=H, Wd=Wd, win=win, zoh=True, **kw)
     for k, e in errs.items():
         assert e <= _BWD_TOL[dtype], (k, e)
+
+
+def test_scan_bwd_zoh_full_vim():
+    """The zero-order-hold backward at the full Vim shape (64 x 197 x 768, two directions, bf16),
+    every gradient against the oracle."""
+    import torch
+    w = W.WORKLOADS[3]
+    errs = _scan_bwd_run(w.kind, w.dtype, w.batch, w.seqlen, w.dim, gate=w.gate, zoh=True)
+    for k, e in errs.items():
+        assert e <= _BWD_TOL[w.dtype], (k, e)
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("idx,batch", [(3, 64), (4, 4), (5, 4)], ids=["vim_bidir_full", "ss2d_56x56_b4",

@@ -62,3 +62,16 @@ def test_algorithmic_bytes_formula():
     tok = 2 * 65536 * 4096
     assert w.algorithmic_bytes() == 4 * tok * 2 + 2 * 2 * 65536 * 16 * 2 + (4096 * 16 + 4096) * 4
     assert w.elements == 2 * 65536 * 4096 * 16
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says why, before it
+    touches a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
