@@ -257,6 +257,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     const T *z = (const T *)p.z;
     T *y = (T *)p.y;
     const int64_t rowb = (int64_t)b * L;
+    // a bidirectional sequence that fits one chunk, bf16 io: direction 0's y tile stays in its
+    // LDS space and direction 1 adds it at its own output stage, so no partial-sum rows pass
+    // through the fp32 workspace (the sum is the same: o_1 + o_0)
+    bool lds_sum = false;
+    if constexpr (KIND == SELSCAN_OP_BIDIR && S::kYOwn) lds_sum = !split && nchunks == 1;
 
     const int g = lane >> 5, nv = ncols - 8 * g;  // 8-channel group of the row items
     const int64_t cg = c0 + 8 * g;
@@ -266,10 +271,13 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 
     int qq = 0;  // chunks done over all directions (priority parity)
     const int k_begin = split ? tile_all / ntiles : 0, k_end = split ? k_begin + 1 : p.ndir;
+    // global -> registers for one chunk, prefetched one chunk ahead (across directions too)
+    Raw8<T> px0, px1, pd0, pd1;
+    uint32_t pbc[2][NW];  // raw B and C values of one chunk step
     for (int k = k_begin; k < k_end; ++k) {
-        const T *dl = (const T *)p.delta + k * tok;
-        const T *Bk = (const T *)p.B + k * bcn;
-        const T *Ck = (const T *)p.C + k * bcn;
+        const T *dlk = (const T *)p.delta + k * tok;
+        const T *Bkk = (const T *)p.B + k * bcn;
+        const T *Ckk = (const T *)p.C + k * bcn;
         // the previous direction is done with the parameter tiles, and its stores of the partial
         // sums (which other waves read back in this direction) are complete: a full barrier
         __syncthreads();
@@ -286,20 +294,21 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             Db[2 * i + 1] = p.bias ? p.bias[k * dim + cc] : 0.f;
         }
 
-        // global -> registers for chunk q (prefetched one chunk ahead)
-        Raw8<T> px0, px1, pd0, pd1;
-        uint32_t pbc[2][NW];  // raw B and C values of one chunk step
-        auto fetch = [&](int q, auto fast_c) {
+        // chunk q of direction kk
+        auto fetch = [&](int kk, int q, auto fast_c) {
+            const T *dl = multi ? (const T *)p.delta + kk * tok : dlk;
+            const T *Bk = multi ? (const T *)p.B + kk * bcn : Bkk;
+            const T *Ck = multi ? (const T *)p.C + kk * bcn : Ckk;
             const int64_t s0 = (int64_t)q * kCH;
             const int64_t sa = s0 + 2 * pp, sbb = sa + 1, s = s0 + sb;
             if constexpr (decltype(fast_c)::value) {
-                const int64_t oa = (rowb + visit<KIND>(p, k, sa)) * dim + cg;
-                const int64_t ob = (rowb + visit<KIND>(p, k, sbb)) * dim + cg;
+                const int64_t oa = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
+                const int64_t ob = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
                 px0 = load_raw8(x + oa, 8, true);
                 pd0 = load_raw8(dl + oa, 8, true);
                 px1 = load_raw8(x + ob, 8, true);
                 pd1 = load_raw8(dl + ob, 8, true);
-                const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
+                const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
 #pragma unroll
                 for (int h = 0; h < NW; h += 4) {
                     const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
@@ -310,19 +319,19 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             } else {
                 px0 = px1 = pd0 = pd1 = Raw8<T>{};
                 if (nv > 0 && sa < L) {
-                    const int64_t off = (rowb + visit<KIND>(p, k, sa)) * dim + cg;
+                    const int64_t off = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
                     px0 = load_raw8(x + off, nv, vec);
                     pd0 = load_raw8(dl + off, nv, vec);
                 }
                 if (nv > 0 && sbb < L) {
-                    const int64_t off = (rowb + visit<KIND>(p, k, sbb)) * dim + cg;
+                    const int64_t off = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
                     px1 = load_raw8(x + off, nv, vec);
                     pd1 = load_raw8(dl + off, nv, vec);
                 }
 #pragma unroll
                 for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
                 if (s < L) {
-                    const int64_t ro = (rowb + visit<KIND>(p, k, s)) * kN;
+                    const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
                     if (p.vecbc) {
 #pragma unroll
                         for (int h = 0; h < NW; h += 4) {
@@ -410,7 +419,13 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                 }
             }
-            if (q + 1 < nchunks) fetch(q + 1, fast_c);
+            if constexpr (fast || !multi) {
+                if (q + 1 < nchunks) fetch(k, q + 1, fast_c);
+            } else {
+                // after a direction's last chunk, the next direction's first
+                const bool next_dir = q + 1 == nchunks;
+                if (!next_dir || k + 1 < k_end) fetch(next_dir ? k + 1 : k, next_dir ? 0 : q + 1, fast_c);
+            }
 
             // ---- this lane's 16 steps of its channel
             const int64_t rem = L - (s0 + l * kK);
@@ -515,12 +530,17 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 }
             }
             __builtin_amdgcn_s_setprio(2);
+            // direction 1 of an LDS-summed pair writes its tile into the x/delta space
+            const bool y_in_xd = lds_sum && k == 1;
             if constexpr (!S::kYOwn) lds_barrier();  // x/delta tiles fully read before y reuses their space
+            else if (y_in_xd) lds_barrier();
+            float *yw = y_in_xd ? (float *)smem : yt;
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc)
-                *(float4 *)&yt[cl * kFP + pc * (kLPR * 4) + 4 * l] =
+                *(float4 *)&yw[cl * kFP + pc * (kLPR * 4) + 4 * l] =
                     make_float4(yv[4 * pc], yv[4 * pc + 1], yv[4 * pc + 2], yv[4 * pc + 3]);
             lds_barrier();
+            if (lds_sum && k == 0) return;  // direction 0's tile waits in LDS for direction 1
             // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -542,9 +562,18 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                         store8(wsk + ooff[r], 8, true, v);
                     }
                 } else if (nv > 0 && s0 + sl < L) {
+                    if (y_in_xd) {
+                        // this direction's step sl is token L-1-sl, direction 0's step L-1-sl
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
-                    if (k > 0 && !split) load_f8(p.ws + ooff[r], nv, vec, wv);
+                        for (int e = 0; e < 8; ++e) {
+                            v[e] = yw[(8 * g + e) * kFP + fpos(sl)];
+                            wv[e] = yt[(8 * g + e) * kFP + fpos((int)L - 1 - sl)];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
+                        if (k > 0 && !split) load_f8(p.ws + ooff[r], nv, vec, wv);
+                    }
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] += wv[e];
                     if (last) {
@@ -559,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 }
             }
         };
-        fetch(0, BoolC<false>{});
+        if (!multi || k == k_begin) fetch(k, 0, BoolC<false>{});
         const int nfast = tile_fast ? (int)(L / kCH) - 1 : 0;
         int q = 0;
         for (; q < nfast; ++q, ++qq) chunk(q, BoolC<true>{});

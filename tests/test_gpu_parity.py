@@ -144,6 +144,19 @@ def test_bidir_edges(L, dim):
     _check("bidir", w, inp, softplus=True, use_bias=True, use_z=False)
 
 
+@pytest.mark.parametrize("L,dim", [(1, 8), (2, 16), (197, 24), (256, 13), (255, 40), (257, 24)])
+def test_bidir_edges_bf16(L, dim):
+    """bf16 bidirectional scans around the one-chunk length (256 steps), where the two
+    directions' outputs are summed in shared memory; partial channel tiles and rows that are not
+    16-byte aligned (dim 13)."""
+    w = W.Workload("bidir_edge_bf16", "bidir", 3, L, dim, 16, "bf16", True, index=9)
+    inp = W.generate(w, with_w=True, with_bias=True)
+    _say("bidir edge bf16", L, dim)
+    _check("bidir", w, inp)
+    _check("bidir", w, inp, softplus=True, use_bias=True, use_z=False)
+    _check("bidir", w, inp, zoh=True)
+
+
 @pytest.mark.parametrize("H,Wd,dim", [(1, 1, 8), (1, 9, 16), (7, 5, 24), (4, 4, 8), (9, 3, 64)])
 def test_ss2d_shapes(H, Wd, dim):
     w = W.Workload("ss2d_edge", "ss2d", 2, H * Wd, dim, 16, "f32", False, H=H, W=Wd, index=10)
