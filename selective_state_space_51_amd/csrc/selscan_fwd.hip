@@ -304,11 +304,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             if constexpr (decltype(fast_c)::value) {
                 const int64_t oa = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
                 const int64_t ob = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
+                const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
                 px0 = load_raw8(x + oa, 8, true);
                 pd0 = load_raw8(dl + oa, 8, true);
                 px1 = load_raw8(x + ob, 8, true);
                 pd1 = load_raw8(dl + ob, 8, true);
-                const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
 #pragma unroll
                 for (int h = 0; h < NW; h += 4) {
                     const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             // while this chunk computes
             const bool last = k == p.ndir - 1 && !split;
             float *wsk = split ? p.ws + k * tok : p.ws;  // this direction's partial rows (split) or the running sum
-            Raw8<T> zr[2] = {};
+            Raw8<T> zr[2];  // read only where it was loaded
             int64_t ooff[2] = {0, 0};
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -414,9 +414,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 if constexpr (fast) {
                     ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
                     if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
-                } else if (nv > 0 && s < L) {
-                    ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
-                    if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                } else {
+                    zr[r] = Raw8<T>{};
+                    if (nv > 0 && s < L) {
+                        ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+                        if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                    }
                 }
             }
             if constexpr (fast || !multi) {
@@ -452,12 +455,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                         }
                     }
                 }
+#pragma unroll
+                for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
                 if (p.softplus) {
+                    // in place: one set of registers for both forms (no copies where they join)
 #pragma unroll
-                    for (int j = 0; j < kK; ++j) dt[j] = softplus(df[j] + bias);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
+                    for (int j = 0; j < kK; ++j) dt[j] = softplus(dt[j]);
                 }
                 if (!fast && !(s0 + kCH <= L && ncols == CT)) {
                     // steps past the sequence end and channels past dim get delta = 0, the
@@ -545,18 +548,22 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int sl = so + 128 * r;
-                float v[8], wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                float v[8], wv[8];
                 if constexpr (fast) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
-                    if (k > 0 && !split) load_f8(p.ws + ooff[r], 8, true, wv);
+                    if (multi && k > 0 && !split) {
+                        load_f8(p.ws + ooff[r], 8, true, wv);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] += wv[e];
-                    if (last) {
-                        if (z) {
+                        for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                    }
+                    if (last && z) {
+                        // the gated and the ungated store are separate calls: no register copies
+                        // where the two forms would join
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
-                        }
+                        for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                        store8(y + ooff[r], 8, true, v);
+                    } else if (last) {
                         store8(y + ooff[r], 8, true, v);
                     } else {
                         store8(wsk + ooff[r], 8, true, v);
@@ -572,10 +579,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
-                        if (k > 0 && !split) load_f8(p.ws + ooff[r], nv, vec, wv);
+                        if (multi && k > 0 && !split) load_f8(p.ws + ooff[r], nv, vec, wv);
                     }
+                    if (multi && (y_in_xd || (k > 0 && !split))) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                        for (int e = 0; e < 8; ++e) v[e] += wv[e];
+                    }
                     if (last) {
                         if (z) {
 #pragma unroll
