@@ -349,11 +349,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                     }
                 }
             }
-            const float limf = (float)lim;
 #pragma unroll
             for (int j = 0; j < kK; ++j) {
                 const float w = df[j] + bias;
-                dt[j] = (p.softplus ? softplus(w) : w) * __saturatef(limf - (float)j);
+                dt[j] = p.softplus ? softplus(w) : w;
+            }
+            if (lim < kK) {
+                // steps past the sequence end and channels past dim: delta = 0, the identity
+                // step (lanes of full chunks skip this)
+                const float limf = (float)lim;
+#pragma unroll
+                for (int j = 0; j < kK; ++j) dt[j] *= __builtin_amdgcn_fmed3f(limf - (float)j, 0.f, 1.f);
+            }
+#pragma unroll
+            for (int j = 0; j < kK; ++j) {
                 px[j] = ZOH ? xf[j] : dt[j] * xf[j];
                 dyp[j] = z ? yf[j] * silu(zf[j]) : yf[j];
                 yv[j] = Dd * xf[j];
