@@ -467,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     // identity step (staged x there is 0 too)
                     const float limf = (float)lim;
 #pragma unroll
-                    for (int j = 0; j < kK; ++j) dt[j] *= __saturatef(limf - (float)j);
+                    for (int j = 0; j < kK; ++j) dt[j] *= __builtin_amdgcn_fmed3f(limf - (float)j, 0.f, 1.f);
                 }
 #pragma unroll
                 for (int j = 0; j < kK; ++j) {
