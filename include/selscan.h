@@ -168,9 +168,10 @@ size_t selscan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, i
  *   delta, B, C : [2][batch][seqlen][...]  direction 0 forward, 1 backward, TOKEN order
  *   A           : [2][dim][dstate];  D, delta_bias : [2][dim] (nullable)
  *   x, z, y     : [batch][seqlen][dim]
- * The workspace holds direction 0's fp32 output rows until direction 1 adds them.  With bf16
- * io and seqlen <= 256 the sum is formed on chip and the workspace is left untouched; it is
- * still required, with the same size.
+ * When the directions run one after another (see selscan_workspace_bytes), the workspace holds
+ * direction 0's fp32 output rows until direction 1 adds them; with bf16 io and seqlen <= 256
+ * that sum is formed on chip instead and the workspace is left untouched.  It is still
+ * required, with the same size.
  */
 int selscan_bidir_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
                       const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,

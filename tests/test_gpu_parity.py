@@ -157,6 +157,28 @@ def test_bidir_edges_bf16(L, dim):
     _check("bidir", w, inp, zoh=True)
 
 
+@pytest.mark.parametrize("L,untouched", [(197, True), (256, True), (257, False)])
+def test_bidir_workspace_use(L, untouched):
+    """With the directions run in turn (a workspace of one row set), a bf16 bidirectional scan of
+    at most 256 steps sums its directions on chip and leaves the workspace as it found it; a
+    longer one passes its running sum through it.  Either way y equals, bit for bit, the
+    direction-split launch's."""
+    import torch
+    import selective_state_space_51_amd as S
+    bt, dim = 2, 40
+    w = W.Workload("bidir_ws", "bidir", bt, L, dim, 16, "bf16", True, index=9)
+    inp = W.generate(w)
+    t = {k: PT.to_dev(inp[k], "bf16") for k in ("x", "delta", "B", "C", "z")}
+    A, D = PT.to_dev(inp["A"], "f32"), PT.to_dev(inp["D"], "f32")
+    _say("bidir workspace", L, dim)
+    ws = torch.full((bt * L * dim * 4,), 0x5A, dtype=torch.uint8, device="cuda")
+    y = S.selscan_bidir_fwd(t["x"], t["delta"], A, t["B"], t["C"], D=D, z=t["z"], workspace=ws)
+    y_split = S.selscan_bidir_fwd(t["x"], t["delta"], A, t["B"], t["C"], D=D, z=t["z"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_split.view(torch.int16))
+    assert bool((ws == 0x5A).all()) == untouched
+
+
 @pytest.mark.parametrize("H,Wd,dim", [(1, 1, 8), (1, 9, 16), (7, 5, 24), (4, 4, 8), (9, 3, 64)])
 def test_ss2d_shapes(H, Wd, dim):
     w = W.Workload("ss2d_edge", "ss2d", 2, H * Wd, dim, 16, "f32", False, H=H, W=Wd, index=10)
