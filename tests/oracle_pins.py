@@ -77,6 +77,48 @@ def pin_lti_convolution(lib):
         assert _rel(y, ref) < 1e-12, ("lti", zoh, _rel(y, ref))
 
 
+# --------------------------------------------------------------------------- P-k
+def pin_zoh_euler_order(lib):
+    """P-k.  The zero-order-hold input matrix ([MS] "选择性 SSM 的数学形式": (delta A)^-1 (exp(delta A) - I)
+    delta B) agrees with the Euler form delta B to first order in delta A.  Checked from the Taylor
+    series of (e^y - 1)/y = 1 + y/2 + y^2/6 + ..., not from the closed form: (1) one step from the
+    zero state (y = C Bbar x) gives the ratio r = y_zoh / y_euler with (r - 1)/(delta A) -> 1/2
+    and the remainder ((r - 1)/(delta A) - 1/2)/(delta A) -> 1/6 (to 1e-3 at |delta A| <= 2e-3);
+    (2) over a 12-step sequence with constant delta the gap between the two forms is second order
+    in delta: halving delta divides it by 4 (to 2 %); (3) the gap changes sign with A."""
+    r_ = _rng(71)
+    for a in (-0.7, -2.0, 1.3):
+        for delta in (2e-3, 1e-3):
+            x = np.array([[[0.8]]])
+            B = np.array([[[1.7]]])
+            C = np.array([[[-0.6]]])
+            dt = np.array([[[delta]]])
+            A = np.array([[a]])
+            ye = oracle.selscan(x, dt, A, B, C, lib=lib)[0, 0, 0]
+            yz = oracle.selscan(x, dt, A, B, C, zoh=True, lib=lib)[0, 0, 0]
+            r = yz / ye
+            y = delta * a
+            assert abs((r - 1.0) / y - 0.5) < abs(y), (a, delta, r)
+            assert abs(((r - 1.0) / y - 0.5) / y - 1.0 / 6.0) < 1e-3, (a, delta, r)
+    x = r_.standard_normal((1, 12, 2))
+    B = r_.standard_normal((1, 12, 3))
+    C = r_.standard_normal((1, 12, 3))
+    A = np.array([[-0.5, -1.5, -3.0], [-1.0, -2.0, -4.0]])
+    gaps = []
+    for delta in (1e-3, 5e-4):
+        dt = np.full_like(x, delta)
+        gaps.append(oracle.selscan(x, dt, A, B, C, zoh=True, lib=lib) - oracle.selscan(x, dt, A, B, C, lib=lib))
+    ratio = np.abs(gaps[0]).max() / np.abs(gaps[1]).max()
+    assert abs(ratio / 4.0 - 1.0) < 0.02, ratio
+    # A -> -A flips the sign of the leading term delta^2 A / 2 C B x of a single step
+    x, B, C, dt = np.array([[[1.0]]]), np.array([[[1.0]]]), np.array([[[1.0]]]), np.array([[[1e-3]]])
+    gp = oracle.selscan(x, dt, np.array([[1.0]]), B, C, zoh=True, lib=lib) - oracle.selscan(
+        x, dt, np.array([[1.0]]), B, C, lib=lib)
+    gm = oracle.selscan(x, dt, np.array([[-1.0]]), B, C, zoh=True, lib=lib) - oracle.selscan(
+        x, dt, np.array([[-1.0]]), B, C, lib=lib)
+    assert gp[0, 0, 0] > 0 > gm[0, 0, 0], (gp, gm)
+
+
 # --------------------------------------------------------------------------- P-b
 def pin_delta_to_zero(lib):
     """P-b.  Abar = exp(delta A) -> 1 and Bbar -> 0 as delta -> 0 ([MS] discretisation), so
@@ -273,46 +315,34 @@ def _ss2d_case(seed, bt=2, H=5, W=7, dim=3, N=3):
     return x, dt, A, B, C, D
 
 
-def _cross_scan_materialised(lib, x, dt, A, B, C, D, H, W):
-    """The four-direction procedure exactly as [MS] "关键代码" spells it in tensor operations,
-    driving the 1-D oracle: channel-first maps, flatten (row-major) and transpose-then-flatten
-    (column-major), flips of both, one scan per direction on its own sequence, then flip the
-    last two back, transpose the column-major ones back, and sum the four."""
-    bt, L, dim = x.shape
-    N = A.shape[-1]
-
-    def seqs(t, ch):  # t: [bt, L(pixel, row-major), ch] -> [bt, 4, ch, L] in scan order
-        m = t.transpose(0, 2, 1).reshape(bt, ch, H, W)
-        hw = np.stack([m.reshape(bt, ch, L), m.transpose(0, 1, 3, 2).reshape(bt, ch, L)], axis=1)
-        return np.concatenate([hw, hw[..., ::-1]], axis=1)
-
-    xs = seqs(x, dim)
-    outs = []
-    for k in range(4):
-        dk = seqs(dt[k], dim)[:, k]
-        bk = seqs(B[k], N)[:, k]
-        ck = seqs(C[k], N)[:, k]
-        o = oracle.selscan(xs[:, k].transpose(0, 2, 1), dk.transpose(0, 2, 1), A[k], bk.transpose(0, 2, 1),
-                           ck.transpose(0, 2, 1), D=D[k], lib=lib)
-        outs.append(o.transpose(0, 2, 1))  # [bt, dim, L] scan order
-    out_y = np.stack(outs, axis=1)
-    inv_y = out_y[:, 2:4, :, ::-1]
-    wh_y = out_y[:, 1].reshape(bt, dim, W, H).transpose(0, 1, 3, 2).reshape(bt, dim, L)
-    invwh_y = inv_y[:, 1].reshape(bt, dim, W, H).transpose(0, 1, 3, 2).reshape(bt, dim, L)
-    y = out_y[:, 0] + inv_y[:, 0] + wh_y + invwh_y
-    return y.transpose(0, 2, 1)
+def _cross_scan_by_coordinates(lib, x, dt, A, B, C, D, H, W):
+    """Reference for the four-direction scan built from pixel coordinates, independently of the
+    oracle's index arithmetic: direction 0 walks the rows top to bottom, each left to right;
+    direction 1 walks the columns left to right, each top to bottom; directions 2 and 3 walk
+    those two paths backwards ([MS] "关键代码": row-major and column-major flattening and their
+    flips).  Each direction's 1-D scan runs on its own parameters gathered along its path, and
+    its outputs are added back at the pixels they were computed for."""
+    rows_first = [h * W + w for h in range(H) for w in range(W)]
+    cols_first = [h * W + w for w in range(W) for h in range(H)]
+    paths = (rows_first, cols_first, rows_first[::-1], cols_first[::-1])
+    total = np.zeros(x.shape, dtype=np.float64)
+    for k, path in enumerate(paths):
+        at = np.asarray(path)
+        out_k = oracle.selscan(x[:, at], dt[k][:, at], A[k], B[k][:, at], C[k][:, at], D=D[k], lib=lib)
+        total[:, at] += out_k  # every path visits each pixel once
+    return total
 
 
 def pin_ss2d(lib):
     """P-j.  SS2D = four independent 1-D scans over permuted sequences, summed at the pixel
     they came from ([MS] cross_scan_fwd / SS2Dv0.forwardv0).  (1) The index-map oracle equals
-    the materialised flip/transpose procedure.  (2) H = 1: column-major equals row-major, so
+    scans along paths built from pixel coordinates.  (2) H = 1: column-major equals row-major, so
     with tied parameter pairs SS2D = 2 x bidirectional.  (3) Transposing the map (H <-> W) and
     swapping directions 0<->1, 2<->3 transposes the output."""
     for (H, W) in ((5, 7), (4, 4), (1, 6), (6, 1)):
         x, dt, A, B, C, D = _ss2d_case(121 + H * 10 + W, H=H, W=W)
         y = oracle.ss2d(x, dt, A, B, C, H, W, D=D, lib=lib)
-        ref = _cross_scan_materialised(lib, x, dt, A, B, C, D, H, W)
+        ref = _cross_scan_by_coordinates(lib, x, dt, A, B, C, D, H, W)
         assert _rel(y, ref) < 1e-13, (H, W, _rel(y, ref))
     # (2)
     H, W = 1, 9
@@ -711,6 +741,7 @@ def pin_dwconv2d_bwd_fd(lib):
 ALL_PINS = [
     pin_lti_convolution,
     pin_delta_to_zero,
+    pin_zoh_euler_order,
     pin_a_zero_prefix_sum,
     pin_first_order_iir,
     pin_brute_force,

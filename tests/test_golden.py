@@ -24,7 +24,7 @@ def test_hand_example(case):
         L = c["L"]
         y = oracle.selscan(f("x").reshape(bt, L, dim), f("delta").reshape(bt, L, dim), f("A"),
                            f("B").reshape(bt, L, N), f("C").reshape(bt, L, N), D=f("D"),
-                           z=None if "z" not in c else f("z").reshape(bt, L, dim))
+                           z=None if "z" not in c else f("z").reshape(bt, L, dim), zoh=c.get("zoh", False))
     elif c["kind"] == "bidir":
         L = c["L"]
         y = oracle.selscan_bidir(f("x").reshape(bt, L, dim), f("delta").reshape(2, bt, L, dim), f("A"),
