@@ -8,12 +8,15 @@ missing the import fails loudly: there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libselscan.so")
+# SELSCAN_LIB names another build of the same library (the host-sanitizer test loads one built
+# with AddressSanitizer and UndefinedBehaviorSanitizer on its host code)
+LIB_PATH = os.environ.get("SELSCAN_LIB") or os.path.join(_PKG, "libselscan.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "selscan.h")
 
 SELSCAN_F32 = 0
@@ -152,6 +155,25 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_launch_stream(fn):
+    """Run `fn` with its `stream` argument (when given) as the current stream, so that every tensor
+    it allocates -- outputs, and workspaces dropped once the launch is enqueued -- belongs to the
+    stream the kernels run on.  The caching allocator then reuses a dropped workspace only for work
+    ordered after those kernels on that stream, never for another stream's allocation while they
+    still write it."""
+
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, stream=None, **kwargs)
+        torch = _torch()
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(s):
+            return fn(*args, stream=s, **kwargs)
+
+    return wrapped
+
+
 def _workspace(op, x, bt, L, dim, workspace):
     torch = _torch()
     need = selscan_workspace_bytes(op, bt, L, dim, 16, _dtype_code(x))
@@ -176,6 +198,7 @@ def _shape_check(name, t, shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+@_on_launch_stream
 def selscan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
                 zoh=False, workspace=None, stream=None):
     """y = (sum_n C h + D x) * silu(z) for x, delta, z: [batch, L, dim]; B, C: [batch, L, N]; A: [dim, N]."""
@@ -208,6 +231,7 @@ def selscan_bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int =
     return int(lib.selscan_bwd_workspace_bytes(batch, seqlen, dim, dstate, io_dtype))
 
 
+@_on_launch_stream
 def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
                       h0=None, h_last=None, chunk_states=None, zoh=False, workspace=None, stream=None):
     """selscan_fwd with the state carried in (h0) and out (h_last), both fp32 [batch, dim, N],
@@ -248,6 +272,7 @@ def selscan_fwd_state(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     return (y, *extra) if extra else y
 
 
+@_on_launch_stream
 def selscan_bwd(x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None, delta_softplus=False,
                 dh0=False, zoh=False, workspace=None, stream=None):
     """Gradients of sum(dy * y) for y = selscan_fwd(...) (zoh: of the zero-order-hold form);
@@ -289,6 +314,7 @@ def selscan_bwd(x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=
     return g
 
 
+@_on_launch_stream
 def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
                       zoh=False, workspace=None, stream=None):
     """Bidirectional scan; per-direction arrays stacked on a leading axis of 2 (token order)."""
@@ -312,6 +338,7 @@ def selscan_bidir_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     return y
 
 
+@_on_launch_stream
 def ss2d_fwd(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
              zoh=False, workspace=None, stream=None):
     """SS2D four-direction scan with merge; per-direction arrays [4, ...] in pixel (row-major) order."""
@@ -337,6 +364,7 @@ def ss2d_fwd(x, delta, A, B, C, H, W, D=None, z=None, delta_bias=None, delta_sof
     return y
 
 
+@_on_launch_stream
 def local_ss2d_fwd(x, delta, A, B, C, H, W, window, D=None, z=None, delta_bias=None, delta_softplus=False, y=None,
                    zoh=False, workspace=None, stream=None):
     """Windowed four-direction cross-scan (square windows of side ``window``); arrays as for ss2d_fwd."""
@@ -386,6 +414,7 @@ def _scan_shapes(op, x, A, H, W):
     return bt, L, dim, N, K, lead
 
 
+@_on_launch_stream
 def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, H=0, W=0,
                      window=0, y=None, chunk_states=None, zoh=False, workspace=None, stream=None):
     """Forward of any scan order (SELSCAN_OP_*), optionally keeping the chunk states the backward
@@ -416,6 +445,7 @@ def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, del
     return (y, chunk_states) if chunk_states is not None else y
 
 
+@_on_launch_stream
 def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, delta_bias=None,
                      delta_softplus=False, H=0, W=0, window=0, zoh=False, workspace=None, stream=None, grads=None):
     """Gradients of sum(dy * y) for y = selscan_scan_fwd(op, ...) with chunk_states from that call
@@ -466,6 +496,7 @@ def selscan_scan_bwd(op, x, delta, A, B, C, dy, chunk_states, D=None, z=None, de
     return g
 
 
+@_on_launch_stream
 def causal_conv1d_fwd(x, weight, bias=None, state_in=None, state_out=None, silu=True, out=None, stream=None):
     """Causal depthwise conv1d (+ SiLU) over x [batch, L, dim]; weight [dim, width] fp32 (width <= 4).
     state_in / state_out: [batch, width-1, dim] in x's dtype (state_out=True allocates it).
@@ -490,6 +521,7 @@ def causal_conv1d_fwd(x, weight, bias=None, state_in=None, state_out=None, silu=
     return (out, state_out) if state_out is not None else out
 
 
+@_on_launch_stream
 def dwconv2d_fwd(x, weight, H, W, bias=None, silu=True, out=None, stream=None):
     """Depthwise 3x3 conv (+ SiLU), 'same' size, over channels-last maps x [batch, H*W, dim];
     weight [dim, 3, 3] fp32."""
@@ -517,6 +549,7 @@ def dwconv2d_bwd_workspace_bytes(batch: int, H: int, W: int, dim: int, io_dtype:
     return int(lib.dwconv2d_bwd_workspace_bytes(batch, H, W, dim, io_dtype))
 
 
+@_on_launch_stream
 def causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True, dstate=False, workspace=None,
                       stream=None):
     """Gradients of sum(dout * causal_conv1d_fwd(x, weight, bias, state_in, silu)): a dict with dx
@@ -546,6 +579,7 @@ def causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True, dsta
     return g
 
 
+@_on_launch_stream
 def dwconv2d_bwd(x, weight, H, W, dout, bias=None, silu=True, workspace=None, stream=None):
     """Gradients of sum(dout * dwconv2d_fwd(x, weight, H, W, bias, silu)): a dict with dx (x's dtype),
     dweight [dim, 3, 3] and dbias (fp32)."""

@@ -103,13 +103,16 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
                  {need ? p.ws : nullptr, need}};
     for (const Span &q : in)
         if (overlap(y, q)) return SELSCAN_E_ALIAS;
+    // the workspace bytes the launch writes: one row set, or one per direction (split launches)
+    size_t used = 0;
     if (need) {
         if (!p.ws || ws_bytes < need) return SELSCAN_E_WORKSPACE;
-        const size_t used = use_split(p, ws_bytes) ? workspace_bytes_for(p.kind, p.batch, p.L, p.dim) : need;
+        used = use_split(p, ws_bytes) ? workspace_bytes_for(p.kind, p.batch, p.L, p.dim) : need;
         if (overlap(y, {p.ws, used})) return SELSCAN_E_ALIAS;
         for (int i = 0; i < 8; ++i)
             if (overlap({p.ws, used}, in[i])) return SELSCAN_E_ALIAS;
     }
+    const Span wsu{used ? p.ws : nullptr, used};
     // state in/out: h_last may be h0 itself (in-place update) but must not overlap anything else
     const size_t st = (size_t)p.batch * (size_t)p.dim * kN * 4;
     if ((p.h0 && !aligned(p.h0, 4)) || (p.hlast && !aligned(p.hlast, 4))) return SELSCAN_E_ALIGN;
@@ -117,11 +120,12 @@ int validate(const Problem &p, int64_t dstate, size_t ws_bytes) {
     if (overlap(y, h0s) || overlap(y, hls)) return SELSCAN_E_ALIAS;
     for (const Span &q : in)
         if (overlap(hls, q)) return SELSCAN_E_ALIAS;
+    if (overlap(hls, wsu)) return SELSCAN_E_ALIAS;
     if (p.h0 != (const float *)p.hlast && overlap(hls, h0s)) return SELSCAN_E_ALIAS;
     if (p.ckpt) {
         const Span cks{p.ckpt, K * ckpt_bytes_for(p.batch, p.L, p.dim)};
         if (!aligned(p.ckpt, 4)) return SELSCAN_E_ALIGN;
-        if (overlap(cks, y) || overlap(cks, h0s) || overlap(cks, hls)) return SELSCAN_E_ALIAS;
+        if (overlap(cks, y) || overlap(cks, h0s) || overlap(cks, hls) || overlap(cks, wsu)) return SELSCAN_E_ALIAS;
         for (const Span &q : in)
             if (overlap(cks, q)) return SELSCAN_E_ALIAS;
     }

@@ -164,6 +164,9 @@ def test_scan_fwd_arguments():
     assert scan_fwd(ck=P + MB - 600) == 4          # the second block reaches into delta
     assert scan_fwd(ck=P + 8 * MB + 100) == 4      # on y
     assert scan_fwd(ck=P + 20 * MB + 2) == 3
+    # a grid this small runs one direction per workgroup and writes a row set per direction (two
+    # of 512 bytes): chunk states in the second one, past the one-set size, still overlap it
+    assert scan_fwd(ck=P + 20 * MB + 600) == 4
     for op, K in ((S.SELSCAN_OP_FWD, 1), (S.SELSCAN_OP_BIDIR, 2), (S.SELSCAN_OP_SS2D, 4), (S.SELSCAN_OP_LOCAL_SS2D, 4)):
         assert S.selscan_scan_chunk_states_bytes(op, 2, 257, 8) == K * 2 * 2 * 8 * 16 * 4
     assert S.selscan_scan_chunk_states_bytes(9, 2, 257, 8) == 0

@@ -253,6 +253,72 @@ def test_side_stream():
     assert PT.rel_err(PT.from_dev(y), r) <= PT.TOL[w.dtype]
 
 
+
+@pytest.mark.parametrize("kind", ["bidir", "ss2d", "scan_bwd"])
+def test_side_stream_internal_workspace(kind, monkeypatch):
+    """A call launched on a stream that is not the current one allocates the workspace it drops on
+    that stream: once it returns, an allocation of the same size on the current stream does not get
+    the workspace's block (which the kernels may still be writing), and the result matches the
+    oracle."""
+    import torch
+
+    import oracle
+    import selective_state_space_51_amd as S
+    seen = {}
+    real = S.lib
+
+    class Spy:
+        def __getattr__(self, name):
+            f = getattr(real, name)
+            if name not in ("selscan_bidir_fwd", "ss2d_fwd", "selscan_scan_bwd"):
+                return f
+
+            def g(*a):
+                seen["ws"], seen["wsb"] = a[-3], a[-2]  # (..., workspace, workspace_bytes, stream)
+                return f(*a)
+            return g
+
+    monkeypatch.setattr(S, "lib", Spy())
+    s = torch.cuda.Stream()
+    if kind == "scan_bwd":
+        w = W.Workload("side", "selscan", 2, 300, 48, 16, "f32", True, index=12)
+    elif kind == "bidir":
+        w = W.Workload("side", "bidir", 2, 300, 64, 16, "f32", True, index=12)
+    else:
+        w = W.Workload("side", "ss2d", 1, 120, 32, 16, "f32", False, H=12, W=10, index=12)
+    _say("side stream, internal workspace", kind)
+    inp = W.generate(w)
+    dev = {k: PT.to_dev(inp[k], "f32") for k in ("x", "delta", "A", "B", "C", "D")}
+    z = PT.to_dev(inp["z"], "f32") if inp.get("z") is not None else None
+    dy = PT.to_dev(W.generate_cotangent(w.batch, w.seqlen, w.dim, "f32"), "f32")
+    torch.cuda.synchronize()
+    args = (dev["x"], dev["delta"], dev["A"], dev["B"], dev["C"])
+    if kind == "scan_bwd":
+        _, ck = S.selscan_scan_fwd(S.SELSCAN_OP_FWD, *args, D=dev["D"], z=z, chunk_states=True, stream=s)
+        out = S.selscan_scan_bwd(S.SELSCAN_OP_FWD, *args, dy, ck, D=dev["D"], z=z, stream=s)
+    elif kind == "bidir":
+        out = S.selscan_bidir_fwd(*args, D=dev["D"], z=z, stream=s)
+    else:
+        out = S.ss2d_fwd(*args, w.H, w.W, D=dev["D"], stream=s)
+    assert seen.get("ws") and seen["wsb"] > 0
+    probe = torch.full((seen["wsb"],), 255, dtype=torch.uint8, device="cuda")  # on the current stream
+    assert probe.data_ptr() != seen["ws"]
+    s.synchronize()
+    torch.cuda.synchronize()
+    f = lambda k: W.to_f64(inp[k], "f32")
+    if kind == "scan_bwd":
+        r = oracle.selscan_bwd(f("x"), f("delta"), inp["A"], f("B"), f("C"), W.generate_cotangent(
+            w.batch, w.seqlen, w.dim, "f32").astype(np.float64), D=inp["D"], z=f("z"))
+        for k in r:
+            assert PT.rel_err(PT.from_dev(out[k]), r[k]) <= 1e-5, k
+    elif kind == "bidir":
+        r = oracle.selscan_bidir(f("x"), f("delta"), inp["A"], f("B"), f("C"), D=inp["D"], z=f("z"))
+        assert PT.rel_err(PT.from_dev(out), r) <= PT.TOL["f32"]
+    else:
+        r = oracle.ss2d(f("x"), f("delta"), inp["A"], f("B"), f("C"), w.H, w.W, D=inp["D"])
+        assert PT.rel_err(PT.from_dev(out), r) <= PT.TOL["f32"]
+
+
 # ----------------------------------------------------------------------------- state in / out
 def _state_case(dtype, batch, L, dim, gate=True):
     w = W.Workload("state", "selscan", batch, L, dim, 16, dtype, gate, index=11)
