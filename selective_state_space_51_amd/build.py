@@ -1,15 +1,21 @@
-"""Build libselscan.so in-tree with hipcc for gfx950 (cross-compiles without a GPU)."""
+"""Build libselscan.so (and the microbenchmark library libselscan_ubench.so) in-tree with hipcc
+for gfx950 (cross-compiles without a GPU).  The sources compile in parallel to objects in a
+temporary directory, then link."""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SRCS = [os.path.join(CSRC, f) for f in ("selscan_fwd.hip", "selscan_bwd.hip", "selscan_conv.hip")]
 OUT = os.path.join(PKG, "libselscan.so")
+UBENCH_SRCS = [os.path.join(CSRC, "ubench.hip")]
+UBENCH_OUT = os.path.join(PKG, "libselscan_ubench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
@@ -18,7 +24,6 @@ HIP_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -26,14 +31,38 @@ HIP_FLAGS = [
 ]
 
 
-def build(extra=None, out=OUT, srcs=None, verbose=False) -> str:
-    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out,
-           *(srcs or SRCS)]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
+
+
+def build(extra=None, out=OUT, srcs=None, verbose=False) -> str:
+    """Compile `srcs` (default: the scan library's sources) and link them into the shared object
+    `out`; `extra` flags go to every hipcc line."""
+    srcs = srcs or SRCS
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="selscan_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
+        with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+            futs = [ex.submit(_run, [HIPCC, *HIP_FLAGS, *(extra or []), *inc, "-c", "-o", o, s], verbose)
+                    for s, o in zip(srcs, objs)]
+            for f in futs:
+                f.result()
+        tmp_out = out + ".tmp"
+        _run([HIPCC, *HIP_FLAGS, *(extra or []), "-shared", "-o", tmp_out, *objs], verbose)
+        os.replace(tmp_out, out)
     return out
 
 
+def build_all(extra=None, verbose=False) -> None:
+    """The scan library and the microbenchmark library, compiled side by side."""
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        a = ex.submit(build, extra, OUT, SRCS, verbose)
+        b = ex.submit(build, extra, UBENCH_OUT, UBENCH_SRCS, verbose)
+        a.result()
+        b.result()
+
+
 if __name__ == "__main__":
-    build(extra=sys.argv[1:], verbose=True)
+    build_all(extra=sys.argv[1:], verbose=True)
