@@ -22,26 +22,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-# ALU roofline.  Per element (b, t, d, n, direction) the method needs one exp2 and four fp32
-# lane operations (delta*A, (delta*x)*B, the state FMA, the output FMA).  MI355X issues
-# transcendentals at a quarter of the fp32 FMA lane rate, so one exp2 occupies the VALU like
-# four FMAs: 8 FMA slots = 16 fp32 flop-equivalents per element, against the published fp32
-# vector peak of 157.3 TFLOP/s (256 CUs x 2.4 GHz x 128 FMA lanes x 2).
-ALU_PEAK_TFLOPS = 157.3
-FLOP_EQ_PER_ELEMENT = 16
-# Backward: per element the recomputed forward (1 exp2, delta*A, u = (delta*x)*B, the state FMA,
-# the output FMA for the gate's derivative) plus the adjoint (C*dyp, g = c + carry, the carry
-# e*g) and the step's derivatives (e*h_prev, its product with g, dA, ddelta, sum g*u, sum g*B,
-# g*(delta*x) for dB, dyp*h for dC): 1 exp2 + 15 fp32 ops = 19 FMA slots = 38 flop-equivalents.
-FLOP_EQ_PER_ELEMENT_BWD = 38
-# Zero-order-hold forward: the input factor phi(delta A) = expm1(delta A) / (delta A) adds, per element,
-# y = t ln2, a 4-FMA series, e - 1, one reciprocal (4 FMA slots), a product, the switch (compare +
-# select) and the factor's product: 13 slots over the Euler form's 8 = 21 slots = 42 flop-equivalents.
-FLOP_EQ_PER_ELEMENT_ZOH = 42
-# Zero-order-hold backward: the Euler backward's 19 slots, plus phi(y) (y = t ln2, one reciprocal,
-# e - 1 and its product: 7 slots), phi'(y) = (e - phi)/y (2), and one more product in each of
-# u, dx, dB and the delta input term and three in the A input term (7): 35 slots = 70 flop-eq.
-FLOP_EQ_PER_ELEMENT_BWD_ZOH = 70
+# The headline roofline is HBM: the metric is achieved algorithmic GB/s (every input read once, y
+# written once) against the published 8 TB/s.  Beside it, the method's arithmetic per element
+# (b, t, d, n, direction): delta*A and (delta*x)*B (2 multiplies), the state update and the output
+# term (2 FMAs) = 6 fp32 flops, and one exp2, against the published fp32 vector peak of
+# 157.3 TFLOP/s (a figure that counts packed fp32 FMAs, which this build does not emit).
+FP32_PEAK_TFLOPS = 157.3
+METHOD_FLOPS_PER_ELEMENT = 6
+# The backward's method arithmetic per element (the recomputed forward's 6 flops, the adjoint
+# g = C*dyp + carry and its decay e*g (4), and the step derivatives e*h_prev, dA, ddelta, dB, dC,
+# the dx sum (12)): 22 flops and one exp2.
+METHOD_FLOPS_PER_ELEMENT_BWD = 22
+# Issue costs on gfx950 in SIMD cycles per wave64 instruction, measured by the committed
+# microbenchmark (selective_state_space_51_amd/ubench.py; summary in profiles/ubench_issue_costs.md):
+# an fp32 FMA/multiply and v_exp_f32.  The method floor below is what the method's own 4 VALU
+# operations + 1 exp2 per element take at the measured shader clock on all 1024 SIMDs.
+ISSUE_CYCLES_FMA = 2.6
+ISSUE_CYCLES_EXP = 8.4
+N_SIMDS = 1024
 METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
 METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GPU"
@@ -115,6 +113,97 @@ def kernel_code_hash(names, so_path: str = LIB_SO) -> str:
         h.update(found[name])
     return h.hexdigest()[:16]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+class ClockSampler:
+    """Shader (gfx) and memory clock of the benchmarked GPU, sampled from a host thread while the
+    timed region runs: amdsmi's current-clock query when the module and the device are available,
+    else the current level of the driver's sysfs DPM tables.  Best effort: with no source the
+    record says so and holds no figures."""
+
+    def __init__(self, torch, dev):
+        import threading
+        self._stop = threading.Event()
+        self._samples = []
+        self._mclk = []
+        self.source = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = handles[0] if handles else None
+            try:  # the handle whose PCI address is the benchmarked device's
+                p = torch.cuda.get_device_properties(dev)
+                want = "%02x:%02x" % (p.pci_bus_id, p.pci_device_id)
+                for c in handles:
+                    if want in amdsmi.amdsmi_get_gpu_device_bdf(c).lower():
+                        h = c
+            except Exception:
+                pass
+            gfx, mem = amdsmi.AmdSmiClkType.GFX, amdsmi.AmdSmiClkType.MEM
+
+            def read_smi():
+                g = amdsmi.amdsmi_get_clock_info(h, gfx)["clk"]
+                m = amdsmi.amdsmi_get_clock_info(h, mem)["clk"]
+                return float(g), float(m)
+
+            read_smi()
+            self._read, self.source = read_smi, "amdsmi clock info"
+        except Exception:
+            self._read = None
+        if self._read is None:
+            import glob
+
+            def cur(path):
+                for line in open(path):
+                    if "*" in line:
+                        return float(line.split(":")[1].lower().replace("mhz", "").replace("*", "").strip())
+                raise ValueError(path)
+
+            for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+                try:
+                    s, m = d + "/pp_dpm_sclk", d + "/pp_dpm_mclk"
+                    cur(s), cur(m)
+                    self._read, self.source = (lambda s=s, m=m: (cur(s), cur(m))), "sysfs " + s
+                    break
+                except Exception:
+                    continue
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import time as _t
+        while not self._stop.is_set():
+            try:
+                g, m = self._read()
+                self._samples.append(g)
+                self._mclk.append(m)
+            except Exception:
+                pass
+            _t.sleep(0.0005)
+
+    def __enter__(self):
+        if self._read is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._read is not None:
+            self._thread.join()
+            try:  # one last sample: a very short timed region may have ended before the first
+                g, m = self._read()
+                self._samples.append(g)
+                self._mclk.append(m)
+            except Exception:
+                pass
+
+    def record(self):
+        if not self._samples:
+            return {"source": self.source, "samples": 0}
+        s, m = self._samples, self._mclk
+        return {"sclk_mhz_mean": sum(s) / len(s), "sclk_mhz_min": min(s), "sclk_mhz_max": max(s),
+                "mclk_mhz_mean": sum(m) / len(m), "samples": len(s), "source": self.source}
 
 
 def bwd_algorithmic_bytes(w) -> int:
@@ -283,13 +372,14 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
         step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        step(args.warmup + i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler(torch, dev) as clk:
+        t0 = time.perf_counter()
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            step(args.warmup + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     kern_ms = float(np.mean(launch_ms))
     ms_step = wall * 1e3 / args.steps
@@ -317,6 +407,7 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
                      "traffic": None if bwd else measured_traffic(w.name, "conv", w.kind), "kernel": kname,
                      "kernel_ms": kern_ms,
                      "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
+        "clock": clk.record(),
     }
     if not args.no_cpu_baseline and not bwd:
         del x, out, xs
@@ -478,13 +569,15 @@ def main() -> int:
     # per-launch events on the stream the kernel runs on
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        step(args.warmup + i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler(torch, dev) as clk:
+        t0 = time.perf_counter()
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            step(args.warmup + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    clock = clk.record()
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(launch_ms))
@@ -493,13 +586,27 @@ def main() -> int:
     if args.softplus:
         alg += (2 if bwd else 1) * w.ndir * w.dim * 4  # the delta bias read (and its gradient written)
     hbm_gbs = alg / (kern_ms * 1e-3) / 1e9
-    if bwd:
-        flop_eq = FLOP_EQ_PER_ELEMENT_BWD_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT_BWD
-    else:
-        flop_eq = FLOP_EQ_PER_ELEMENT_ZOH if args.zoh else FLOP_EQ_PER_ELEMENT
-    alu_tflops = w.elements * flop_eq / (kern_ms * 1e-3) / 1e12
+    flops = w.elements * (METHOD_FLOPS_PER_ELEMENT_BWD if bwd else METHOD_FLOPS_PER_ELEMENT)
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    # the method's own issue floor: 4 VALU operations and 1 exp2 per element on every SIMD at the
+    # measured shader clock (forward, Euler Bbar); this kernel design adds one FMA per element
+    # (its second pass over a lane's steps) to that
+    sclk = clock.get("sclk_mhz_mean")
+    floor = None
+    if sclk and not bwd and not args.zoh:
+        cyc = w.elements / (64 * N_SIMDS) * (4 * ISSUE_CYCLES_FMA + ISSUE_CYCLES_EXP)
+        cyc2 = w.elements / (64 * N_SIMDS) * (5 * ISSUE_CYCLES_FMA + ISSUE_CYCLES_EXP)
+        floor = {"method_ms": cyc / (sclk * 1e3), "two_pass_ms": cyc2 / (sclk * 1e3),
+                 "cycles_per_element": {"fma": ISSUE_CYCLES_FMA, "exp": ISSUE_CYCLES_EXP},
+                 "simds": N_SIMDS, "sclk_mhz": sclk}
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
     traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(w.name, args.pass_, w.kind)
+    split = w.ndir > 1 and w.batch * (-(-w.dim // 16)) < 1024
+    if bwd:
+        kname = "selscan_bwd_chunked + selscan_bwd_merge + selscan_bwd_reduce" if split else \
+            "selscan_bwd_chunked + selscan_bwd_reduce"
+    else:
+        kname = "selscan_chunked + selscan_merge" if split else "selscan_chunked"
     out = {
         "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
@@ -518,18 +625,15 @@ def main() -> int:
                    "window": w.window or None,
                    "state_io": bool(args.state), "pass": args.pass_, "bbar": "zoh" if args.zoh else "delta*B",
                    "delta_softplus": bool(args.softplus), "input_sets": copies},
-        "roofline": {"bound": "alu", "achieved": alu_tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": alu_tflops / ALU_PEAK_TFLOPS, "traffic": traffic,
-                     "work_per_element": ("1 exp2 + 1 rcp + 27 fp32 ops = 70 fp32 flop-equivalents" if bwd and args.zoh
-                                          else "1 exp2 + 15 fp32 ops = 38 fp32 flop-equivalents" if bwd else
-                                          "1 exp2 + 1 rcp + 13 fp32 ops = 42 fp32 flop-equivalents" if args.zoh else
-                                          "1 exp2 + 4 fp32 ops = 16 fp32 flop-equivalents"),
-                     "kernel": "selscan_bwd_chunked + selscan_bwd_reduce" if bwd else "selscan_chunked",
-                     "kernel_ms": kern_ms, "kernel_ms_median": float(np.median(launch_ms)),
+        "roofline": {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kname, "kernel_ms": kern_ms, "kernel_ms_median": float(np.median(launch_ms)),
                      "kernel_ms_min": float(np.min(launch_ms)),
                      "elements_per_launch": w.elements, "algorithmic_bytes_per_launch": alg,
-                     "hbm_achieved_GBps": hbm_gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
-                     "hbm_frac": hbm_gbs / HBM_PEAK_GBS},
+                     "flops_per_element": METHOD_FLOPS_PER_ELEMENT_BWD if bwd else METHOD_FLOPS_PER_ELEMENT,
+                     "flop_achieved_TFLOPs": tflops, "flop_peak_TFLOPs": FP32_PEAK_TFLOPS,
+                     "flop_frac": tflops / FP32_PEAK_TFLOPS, "issue_floor": floor},
+        "clock": clock,
     }
     if not args.no_cpu_baseline and not args.softplus and bwd:
         del t, y, ws, h0, hl, first, sets, bws
