@@ -124,7 +124,7 @@ def test_softplus_extreme_preactivations():
     _check("selscan", base, inp, softplus=True, use_bias=True)
     errs = _bwd_run("f32", 2, 300, 64, softplus=True, bias=True, inp=inp)
     for k, e in errs.items():
-        assert e <= _BWD_TOL["f32"], (k, e)
+        assert e <= _bwd_tol("f32", k), (k, e)
 
 
 @pytest.mark.parametrize("L,dim,batch", [(1, 8, 1), (2, 24, 3), (17, 72, 2), (257, 8, 1), (64, 1, 2), (5, 3, 1)])
@@ -406,7 +406,25 @@ def test_state_in_place_and_empty():
 
 
 # ----------------------------------------------------------------------------- backward
-_BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Backward bars, per gradient.  Gradients returned in fp32 (dA, dD, d(delta_bias), dh0) and every
+# gradient of an fp32-I/O call carry only fp32 accumulation error: sums of at most a few 10^4
+# terms, each recomputed in fp32 from inputs the oracle sees exactly (measured at most 2.5e-6;
+# 5e-6 for the zero-order-hold delta gradient, whose phi' has a relative error near 2e-5 at the
+# series switch, weighted by the share of steps near it).  Gradients returned in bf16 add the
+# output rounding, half an ulp of an 8-bit significand: 2^-8 = 3.9e-3 relative at the RMS-scaled
+# metric (measured 3.89e-3).
+_FP32_GRADS = ("dA", "dD", "ddelta_bias", "dh0")
+
+
+def _bwd_tol(dtype, name, zoh=False):
+    if dtype == "bf16" and name not in _FP32_GRADS:
+        return 5e-3
+    return 2e-5 if (zoh and name == "ddelta") else 1e-5
+
+
+def _check_bwd(errs, dtype, zoh=False):
+    for k, e in errs.items():
+        assert e <= _bwd_tol(dtype, k, zoh), (k, e, _bwd_tol(dtype, k, zoh))
 
 
 def _zoh_A(inp):
@@ -458,8 +476,7 @@ def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=Fal
 ], ids=lambda v: str(v))
 def test_bwd_against_oracle(dtype, batch, L, dim, kw):
     errs = _bwd_run(dtype, batch, L, dim, **kw)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[dtype], (k, e)
+    _check_bwd(errs, dtype, zoh=False)
 
 
 @pytest.mark.parametrize("dtype,batch,L,dim,kw", [
@@ -473,8 +490,7 @@ def test_bwd_zoh_against_oracle(dtype, batch, L, dim, kw):
     """The zero-order-hold backward (SELSCAN_FLAG_ZOH on the forward and the backward) against
     the oracle's zero-order-hold gradients, with A = 0, tiny, positive and -(n+1) entries."""
     errs = _bwd_run(dtype, batch, L, dim, zoh=True, **kw)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[dtype], (k, e)
+    _check_bwd(errs, dtype, zoh=True)
 
 
 def test_bwd_full_size_130m():
@@ -483,8 +499,7 @@ def test_bwd_full_size_130m():
     import torch
     w = W.WORKLOADS[1]
     errs = _bwd_run(w.dtype, w.batch, w.seqlen, w.dim)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[w.dtype], (k, e)
+    _check_bwd(errs, w.dtype, zoh=False)
     torch.cuda.empty_cache()
 
 
@@ -547,8 +562,7 @@ def _scan_bwd_run(kind, dtype, batch, L, dim, H=0, Wd=0, win=0, gate=True, softp
 ], ids=lambda v: str(v))
 def test_scan_bwd_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw):
     errs = _scan_bwd_run(kind, dtype, batch, L, dim, H=H, Wd=Wd, win=win, **kw)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[dtype], (k, e)
+    _check_bwd(errs, dtype, zoh=False)
 
 
 @pytest.mark.parametrize("kind,dtype,batch,L,dim,H,Wd,win,kw", [
@@ -561,8 +575,7 @@ def test_scan_bwd_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw):
 def test_scan_bwd_zoh_against_oracle(kind, dtype, batch, L, dim, H, Wd, win, kw):
     """The multi-direction zero-order-hold backward against oracle.multi_bwd(zoh=True)."""
     errs = _scan_bwd_run(kind, dtype, batch, L, dim, H=H, Wd=Wd, win=win, zoh=True, **kw)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[dtype], (k, e)
+    _check_bwd(errs, dtype, zoh=True)
 
 
 def test_scan_bwd_zoh_full_vim():
@@ -571,8 +584,7 @@ def test_scan_bwd_zoh_full_vim():
     import torch
     w = W.WORKLOADS[3]
     errs = _scan_bwd_run(w.kind, w.dtype, w.batch, w.seqlen, w.dim, gate=w.gate, zoh=True)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[w.dtype], (k, e)
+    _check_bwd(errs, w.dtype, zoh=True)
     torch.cuda.empty_cache()
 
 
@@ -584,8 +596,7 @@ def test_scan_bwd_full_shape(idx, batch):
     import torch
     w = W.WORKLOADS[idx]
     errs = _scan_bwd_run(w.kind, w.dtype, batch, w.seqlen, w.dim, H=w.H, Wd=w.W, win=w.window, gate=w.gate)
-    for k, e in errs.items():
-        assert e <= _BWD_TOL[w.dtype], (k, e)
+    _check_bwd(errs, w.dtype, zoh=False)
     torch.cuda.empty_cache()
 
 
@@ -781,7 +792,10 @@ def test_dwconv2d_against_oracle(dtype, batch, H, Wd, dim, bias, silu):
 
 
 # ----------------------------------------------------------------------------- convolution backward
-_CONV_BWD_TOL = {"f32": 1e-4, "bf16": 2e-2}  # dweight, dbias: fp32 sums over batch x positions
+# Convolution backward: dweight and dbias are fp32 sums over batch x positions (measured at most
+# 1.1e-6 at the full shapes); dx and dstate carry the I/O rounding (bf16: half an ulp, 2^-8).
+_CONV_BWD_TOL = {"f32": 1e-5, "bf16": 1e-5}
+_CONV_DX_TOL = {"f32": 1e-5, "bf16": 5e-3}
 
 
 @pytest.mark.parametrize("dtype,batch,L,dim,K,bias,silu,state", [
@@ -812,7 +826,7 @@ def test_causal_conv1d_bwd_against_oracle(dtype, batch, L, dim, K, bias, silu, s
     _say("conv1d bwd", dtype, batch, L, dim, K, bias, silu, state, {k: f"{v:.2e}" for k, v in errs.items()})
     assert set(gg) == set(r)
     for k, e in errs.items():
-        assert e <= (PT.TOL[dtype] if k in ("dx", "dstate") else _CONV_BWD_TOL[dtype]), (k, e)
+        assert e <= (_CONV_DX_TOL[dtype] if k in ("dx", "dstate") else _CONV_BWD_TOL[dtype]), (k, e)
 
 
 def test_causal_conv1d_bwd_full_shape_sampled():
@@ -836,7 +850,7 @@ def test_causal_conv1d_bwd_full_shape_sampled():
             "dweight": PT.rel_err(PT.from_dev(gg["dweight"][cht]), r["dweight"]),
             "dbias": PT.rel_err(PT.from_dev(gg["dbias"][cht]), r["dbias"])}
     _say("conv1d bwd full", {k: f"{v:.2e}" for k, v in errs.items()})
-    assert errs["dx"] <= PT.TOL["bf16"] and errs["dweight"] <= _CONV_BWD_TOL["bf16"] and errs["dbias"] <= _CONV_BWD_TOL["bf16"]
+    assert errs["dx"] <= _CONV_DX_TOL["bf16"] and errs["dweight"] <= _CONV_BWD_TOL["bf16"] and errs["dbias"] <= _CONV_BWD_TOL["bf16"]
     del gg
     torch.cuda.empty_cache()
 
@@ -863,7 +877,7 @@ def test_dwconv2d_bwd_against_oracle(dtype, batch, H, Wd, dim, bias, silu):
     errs = {k: PT.rel_err(PT.from_dev(gg[k]), r[k]) for k in r}
     _say("dwconv2d bwd", dtype, batch, H, Wd, dim, bias, silu, {k: f"{v:.2e}" for k, v in errs.items()})
     for k, e in errs.items():
-        assert e <= (PT.TOL[dtype] if k == "dx" else _CONV_BWD_TOL[dtype]), (k, e)
+        assert e <= (_CONV_DX_TOL[dtype] if k == "dx" else _CONV_BWD_TOL[dtype]), (k, e)
 
 
 def test_conv_bwd_deterministic():
