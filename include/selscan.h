@@ -235,6 +235,33 @@ int selscan_scan_fwd(int op, const void *x, const void *delta, const float *A, c
                      int64_t dim, int64_t dstate, int io_dtype, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/*
+ * selscan_scan_fwd_noalloc - selscan_scan_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without `workspace` / `workspace_bytes`.  The partial-sum rows of a multi-direction
+ * order live in a static device array of the library, selscan_scan_fwd_noalloc_max_bytes()
+ * (128 MiB) on every GPU the library runs on, held until the process ends.  The call allocates
+ * and frees nothing; its first use on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, with the device current; the caller's current device is restored).
+ *  - A problem whose workspace, selscan_workspace_bytes(op, ...) with one row set per problem
+ *    (batch * seqlen * dim * 4 bytes for BIDIR, SS2D and LOCAL_SS2D), exceeds the array is
+ *    refused with SELSCAN_E_WORKSPACE before anything is enqueued.  The single-direction order
+ *    uses no scratch.
+ *  - The array is shared by every call on a GPU and keeps the last call's contents: calls on one
+ *    GPU whose executions overlap (two streams, or two host threads without ordering) race on it
+ *    and must be serialized by the caller.  No call reads scratch it did not write first.
+ *  - `stream` decides the device: the stream's own device, or the current device for NULL.
+ * Results equal selscan_scan_fwd's with a workspace of the same size.  SELSCAN_E_HIP if the
+ * array's address cannot be obtained.
+ */
+int selscan_scan_fwd_noalloc(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                             float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W,
+                             int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *stream);
+
+/* Bytes of the static device array selscan_scan_fwd_noalloc works in. */
+size_t selscan_scan_fwd_noalloc_max_bytes(void);
+
 /* Bytes of the chunk_states buffer of selscan_scan_fwd / selscan_scan_bwd for `op` (0 if op is
  * unknown, a size is not positive or dstate != 16). */
 size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

@@ -77,6 +77,10 @@ def _load():
     lib.selscan_scan_fwd.restype = ci
     lib.selscan_scan_bwd.argtypes = [ci] + [vp] * 8 + [cu] + [vp] * 10 + [i64] * 7 + [ci, vp, sz, vp]
     lib.selscan_scan_bwd.restype = ci
+    lib.selscan_scan_fwd_noalloc.argtypes = [ci] + common + [vp, i64, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.selscan_scan_fwd_noalloc.restype = ci
+    lib.selscan_scan_fwd_noalloc_max_bytes.argtypes = []
+    lib.selscan_scan_fwd_noalloc_max_bytes.restype = sz
     lib.selscan_scan_chunk_states_bytes.argtypes = [ci, i64, i64, i64, i64]
     lib.selscan_scan_chunk_states_bytes.restype = sz
     lib.selscan_scan_bwd_workspace_bytes.argtypes = [ci, i64, i64, i64, i64, ci]
@@ -443,6 +447,35 @@ def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, del
                               _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_scan_fwd")
     return (y, chunk_states) if chunk_states is not None else y
+
+
+def selscan_scan_fwd_noalloc_max_bytes() -> int:
+    return int(lib.selscan_scan_fwd_noalloc_max_bytes())
+
+
+@_on_launch_stream
+def selscan_scan_fwd_noalloc(op, x, delta, A, B, C, y, D=None, z=None, delta_bias=None, delta_softplus=False, H=0,
+                             W=0, window=0, chunk_states=None, zoh=False, stream=None):
+    """selscan_scan_fwd without a workspace: the library's static device scratch holds the
+    partial-sum rows, and the call allocates nothing (y, and chunk_states if wanted, are the
+    caller's).  Returns y."""
+    bt, L, dim, N, K, lead = _scan_shapes(op, x, A, H, W)
+    io = x.dtype
+    for n_, t_, s_ in (("delta", delta, lead + (bt, L, dim)), ("B", B, lead + (bt, L, N)),
+                       ("C", C, lead + (bt, L, N)), ("A", A, lead + (dim, N)), ("D", D, lead + (dim,)),
+                       ("z", z, (bt, L, dim)), ("delta_bias", delta_bias, lead + (dim,)), ("y", y, (bt, L, dim))):
+        _shape_check(n_, t_, s_)
+    need_cs = selscan_scan_chunk_states_bytes(op, bt, L, dim, N)
+    if chunk_states is not None and chunk_states.numel() * chunk_states.element_size() < need_cs:
+        raise ValueError("chunk_states is smaller than selscan_scan_chunk_states_bytes(...)")
+    rc = lib.selscan_scan_fwd_noalloc(op, _ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
+                                      _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                                      _ptr(delta_bias, "delta_bias", f32=True),
+                                      _flags(delta_softplus, zoh), _ptr(y, "y", io),
+                                      _ptr(chunk_states, "chunk_states", f32=True), bt, L, H, W, window, dim, N,
+                                      _dtype_code(x), _stream(stream))
+    _check(rc, "selscan_scan_fwd_noalloc")
+    return y
 
 
 @_on_launch_stream

@@ -25,9 +25,18 @@
 //    direction adds, gates and writes y once.
 #include "selscan_common.h"
 
+#include <mutex>
+
 namespace selscan_rt {
 thread_local char g_last_hip_error[160] = "no error";
 }  // namespace selscan_rt
+
+// Device scratch of selscan_scan_fwd_noalloc (the partial-sum rows a multi-direction forward
+// otherwise keeps in the caller's workspace).  Every GPU the library runs on holds one copy of
+// this array until the process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -805,6 +814,80 @@ size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, in
     if (ndir == 0 || batch <= 0 || seqlen <= 0 || dim <= 0 || dstate != kN) return 0;
     return (size_t)ndir * ckpt_bytes_for(batch, seqlen, dim);
 }
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// The device a launch on `stream` runs on: the stream's own device, or the current device for the
+// null stream.
+int stream_device(void *stream, int *dev) {
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, dev) : hipGetDevice(dev);
+    if (e != hipSuccess) {
+        record_hip_error(e);
+        return SELSCAN_E_HIP;
+    }
+    return SELSCAN_OK;
+}
+
+// Device address of `scratch` on device `dev`, looked up on the first call for that device with
+// that device current (the caller's current device is restored) and kept for later calls.
+int scratch_on(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return SELSCAN_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void *p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess || !p) {
+            record_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return SELSCAN_E_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SELSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int selscan_scan_fwd_noalloc(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                             float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W,
+                             int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *stream) {
+    int64_t L;
+    int ndir;
+    int rc = resolve_op(op, seqlen, H, W, &L, &ndir);
+    if (rc != SELSCAN_OK) return rc;
+    // the workspace this call needs must fit the static array (one row set at least; the
+    // per-direction rows of a split launch when they fit too)
+    if (batch > 0 && dim > 0 && L > 0 && workspace_min_bytes(op, batch, L, dim) > kScratchBytes)
+        return SELSCAN_E_WORKSPACE;
+    void *ws = nullptr;
+    if (ndir > 1 && batch > 0 && dim > 0 && L > 0) {
+        int dev = 0;
+        rc = stream_device(stream, &dev);
+        if (rc != SELSCAN_OK) return rc;
+        rc = scratch_on(dev, &ws);
+        if (rc != SELSCAN_OK) return rc;
+    }
+    return selscan_scan_fwd(op, x, delta, A, B, C, D, z, delta_bias, flags, y, chunk_states, batch, seqlen, H, W,
+                            window, dim, dstate, io_dtype, ws, ws ? kScratchBytes : 0, stream);
+}
+
+size_t selscan_scan_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
 
 const char *selscan_status_str(int status) {
     switch (status) {

@@ -21,7 +21,7 @@ def test_exports_every_declared_symbol():
                              "selscan_scan_chunk_states_bytes", "selscan_scan_bwd_workspace_bytes",
                              "causal_conv1d_fwd", "dwconv2d_fwd", "causal_conv1d_bwd", "dwconv2d_bwd",
                              "causal_conv1d_bwd_workspace_bytes", "dwconv2d_bwd_workspace_bytes",
-                             "selscan_workspace_bytes",
+                             "selscan_workspace_bytes", "selscan_scan_fwd_noalloc", "selscan_scan_fwd_noalloc_max_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -377,3 +377,19 @@ def test_bench_finds_profiled_kernels_in_library():
             h = bench.kernel_code_hash(bench.profiled_kernels(ps, kind))
             assert not h.startswith("missing"), (ps, kind, h)
             assert len(h) == 16
+
+
+def test_scan_fwd_noalloc_arguments():
+    """Host-side refusals of the no-allocation forward (none reaches a HIP call): an unknown op,
+    a map that is not H x W, and a problem whose partial-sum rows exceed the static array."""
+    cap = S.selscan_scan_fwd_noalloc_max_bytes()
+    assert cap == 128 << 20
+
+    def call(op=S.SELSCAN_OP_SS2D, batch=1, L_=16, H=4, W=4, dim=8):
+        return L.selscan_scan_fwd_noalloc(op, P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0,
+                                          P + 8 * MB, None, batch, L_, H, W, 0, dim, 16, S.SELSCAN_BF16, None)
+    assert call(op=9) == 5
+    assert call(H=3) == 2
+    # one fp32 row set of 64 x 4096 x 256 x 4 bytes = 256 MiB > 128 MiB
+    assert call(batch=64, L_=4096, H=64, W=64, dim=256) == 6
+    assert call(op=S.SELSCAN_OP_BIDIR, batch=64, L_=4096, H=0, W=0, dim=256) == 6
