@@ -33,12 +33,14 @@ METHOD_FLOPS_PER_ELEMENT = 6
 # g = C*dyp + carry and its decay e*g (4), and the step derivatives e*h_prev, dA, ddelta, dB, dC,
 # the dx sum (12)): 22 flops and one exp2.
 METHOD_FLOPS_PER_ELEMENT_BWD = 22
-# Issue costs on gfx950 in SIMD cycles per wave64 instruction, measured by the committed
-# microbenchmark (selective_state_space_51_amd/ubench.py; summary in profiles/ubench_issue_costs.md):
-# an fp32 FMA/multiply and v_exp_f32.  The method floor below is what the method's own 4 VALU
-# operations + 1 exp2 per element take at the measured shader clock on all 1024 SIMDs.
-ISSUE_CYCLES_FMA = 2.6
-ISSUE_CYCLES_EXP = 8.4
+# Issue costs on gfx950 in SIMD cycles per wave64 instruction at two waves per SIMD (the scan
+# kernels' occupancy), in a stream that mixes v_exp_f32 with FMAs, measured by the committed
+# microbenchmark (selective_state_space_51_amd/ubench.py; profiles/ubench_issue_costs_gfx950.md):
+# an fp32 FMA/multiply ~4.2, v_exp_f32 ~8.9.  The method floor below is what the method's own 4
+# FMA-class operations + 1 exp2 per element take at the measured shader clock on all 1024 SIMDs;
+# the two-pass floor adds the one FMA per element this kernel design repeats.
+ISSUE_CYCLES_FMA = 4.2
+ISSUE_CYCLES_EXP = 8.9
 N_SIMDS = 1024
 METRIC_BWD = "selective-scan bwd (gradients of x, delta, A, B, C, D, z) B·L·D·N elem/s, 1 GPU"
 DEFAULT_WORKLOAD = "mamba1p4b_layer_b2_L65536_D4096"
@@ -115,95 +117,32 @@ def kernel_code_hash(names, so_path: str = LIB_SO) -> str:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-class ClockSampler:
-    """Shader (gfx) and memory clock of the benchmarked GPU, sampled from a host thread while the
-    timed region runs: amdsmi's current-clock query when the module and the device are available,
-    else the current level of the driver's sysfs DPM tables.  Best effort: with no source the
-    record says so and holds no figures."""
-
-    def __init__(self, torch, dev):
-        import threading
-        self._stop = threading.Event()
-        self._samples = []
-        self._mclk = []
-        self.source = None
-        self._read = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            h = handles[0] if handles else None
-            try:  # the handle whose PCI address is the benchmarked device's
-                p = torch.cuda.get_device_properties(dev)
-                want = "%02x:%02x" % (p.pci_bus_id, p.pci_device_id)
-                for c in handles:
-                    if want in amdsmi.amdsmi_get_gpu_device_bdf(c).lower():
-                        h = c
-            except Exception:
-                pass
-            gfx, mem = amdsmi.AmdSmiClkType.GFX, amdsmi.AmdSmiClkType.MEM
-
-            def read_smi():
-                g = amdsmi.amdsmi_get_clock_info(h, gfx)["clk"]
-                m = amdsmi.amdsmi_get_clock_info(h, mem)["clk"]
-                return float(g), float(m)
-
-            read_smi()
-            self._read, self.source = read_smi, "amdsmi clock info"
-        except Exception:
-            self._read = None
-        if self._read is None:
-            import glob
-
-            def cur(path):
-                for line in open(path):
-                    if "*" in line:
-                        return float(line.split(":")[1].lower().replace("mhz", "").replace("*", "").strip())
-                raise ValueError(path)
-
-            for d in sorted(glob.glob("/sys/class/drm/card*/device")):
-                try:
-                    s, m = d + "/pp_dpm_sclk", d + "/pp_dpm_mclk"
-                    cur(s), cur(m)
-                    self._read, self.source = (lambda s=s, m=m: (cur(s), cur(m))), "sysfs " + s
-                    break
-                except Exception:
-                    continue
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        import time as _t
-        while not self._stop.is_set():
-            try:
-                g, m = self._read()
-                self._samples.append(g)
-                self._mclk.append(m)
-            except Exception:
-                pass
-            _t.sleep(0.0005)
-
-    def __enter__(self):
-        if self._read is not None:
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._read is not None:
-            self._thread.join()
-            try:  # one last sample: a very short timed region may have ended before the first
-                g, m = self._read()
-                self._samples.append(g)
-                self._mclk.append(m)
-            except Exception:
-                pass
-
-    def record(self):
-        if not self._samples:
-            return {"source": self.source, "samples": 0}
-        s, m = self._samples, self._mclk
-        return {"sclk_mhz_mean": sum(s) / len(s), "sclk_mhz_min": min(s), "sclk_mhz_max": max(s),
-                "mclk_mhz_mean": sum(m) / len(m), "samples": len(s), "source": self.source}
+def kernel_clock(S, torch, run, op, w, dev, launches: int):
+    """Shader clock of the scan kernel itself: `launches` back-to-back calls of the clocked forward
+    (the timed code path plus two counter reads and four stores per workgroup) right after the timed
+    region; per workgroup the s_memtime (shader clock) and s_memrealtime (100 MHz) counters at its
+    start and end.  Returns the clock in MHz weighted by workgroup time, with the kernel time of
+    those launches."""
+    nb = S.selscan_clock_stamps_bytes(op, w.batch, w.dim)
+    bufs = [torch.zeros(nb // 8, dtype=torch.int64, device=dev) for _ in range(launches)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for (a, b), s in zip(ev, bufs):
+        a.record(stream)
+        run(s)
+        b.record(stream)
+    torch.cuda.synchronize()
+    clk = rt = 0.0
+    for s in bufs:
+        v = s.view(-1, 4).double()
+        used = v[:, 3] > 0  # workgroups of the grid (a direction-split grid fills every slot)
+        clk += float((v[used, 1] - v[used, 0]).sum())
+        rt += float((v[used, 3] - v[used, 2]).sum())
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return {"sclk_mhz": clk / (rt / 1e8) / 1e6 if rt > 0 else None, "launches": launches,
+            "kernel_ms": sum(ms) / len(ms),
+            "source": "in-kernel s_memtime / s_memrealtime of selscan_chunked (selscan_scan_fwd_clocked)"}
 
 
 def bwd_algorithmic_bytes(w) -> int:
@@ -372,14 +311,13 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
         step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    with ClockSampler(torch, dev) as clk:
-        t0 = time.perf_counter()
-        for i, (a, b) in enumerate(ev):
-            a.record(stream)
-            step(args.warmup + i)
-            b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(args.warmup + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     kern_ms = float(np.mean(launch_ms))
     ms_step = wall * 1e3 / args.steps
@@ -407,7 +345,6 @@ def conv_bench(args, w, S, W, torch, np, up, dev) -> int:
                      "traffic": None if bwd else measured_traffic(w.name, "conv", w.kind), "kernel": kname,
                      "kernel_ms": kern_ms,
                      "kernel_ms_min": float(np.min(launch_ms)), "algorithmic_bytes_per_launch": alg},
-        "clock": clk.record(),
     }
     if not args.no_cpu_baseline and not bwd:
         del x, out, xs
@@ -569,15 +506,21 @@ def main() -> int:
     # per-launch events on the stream the kernel runs on
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    with ClockSampler(torch, dev) as clk:
-        t0 = time.perf_counter()
-        for i, (a, b) in enumerate(ev):
-            a.record(stream)
-            step(args.warmup + i)
-            b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    clock = clk.record()
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(args.warmup + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the shader clock of the same kernel, over launches right after the timed region
+    clock = None
+    if not bwd and not args.state:
+        c0 = sets[0]["t"]
+        clock = kernel_clock(S, torch, lambda s: S.selscan_scan_fwd_clocked(
+            op, c0["x"], c0["delta"], c0["A"], c0["B"], c0["C"], s, D=c0["D"], z=c0["z"], y=sets[0]["y"],
+            workspace=ws, zoh=args.zoh, delta_bias=c0.get("delta_bias"), delta_softplus=args.softplus, stream=stream,
+            **geo), op, w, dev, min(args.steps, 10))
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(launch_ms))
@@ -591,7 +534,7 @@ def main() -> int:
     # the method's own issue floor: 4 VALU operations and 1 exp2 per element on every SIMD at the
     # measured shader clock (forward, Euler Bbar); this kernel design adds one FMA per element
     # (its second pass over a lane's steps) to that
-    sclk = clock.get("sclk_mhz_mean")
+    sclk = clock.get("sclk_mhz") if clock else None
     floor = None
     if sclk and not bwd and not args.zoh:
         cyc = w.elements / (64 * N_SIMDS) * (4 * ISSUE_CYCLES_FMA + ISSUE_CYCLES_EXP)

@@ -262,6 +262,29 @@ int selscan_scan_fwd_noalloc(int op, const void *x, const void *delta, const flo
 /* Bytes of the static device array selscan_scan_fwd_noalloc works in. */
 size_t selscan_scan_fwd_noalloc_max_bytes(void);
 
+/*
+ * selscan_scan_fwd_clocked - selscan_scan_fwd that also records, for every workgroup of its scan
+ * kernel, the shader-clock counter (s_memtime) and the constant 100 MHz real-time counter
+ * (s_memrealtime) at the workgroup's start and end: stamps[4 w + 0..3] = clock start, clock end,
+ * real time start, real time end, for workgroup w.  sum(clock end - start) * 1e8 /
+ * sum(real end - start) is the shader clock the kernel ran at, in Hz.  The results and the work
+ * are those of selscan_scan_fwd; recording adds two counter reads and four 8-byte stores per
+ * workgroup.  For measuring the library's own kernels under load (the benchmark reports it).
+ *   stamps : device memory of selscan_clock_stamps_bytes(op, batch, dim) bytes, 8-byte aligned,
+ *            caller-owned; SELSCAN_E_NULL if NULL, SELSCAN_E_ALIGN if misaligned.  It is not
+ *            checked for overlap with the other arrays.
+ */
+int selscan_scan_fwd_clocked(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                             float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W,
+                             int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                             size_t workspace_bytes, unsigned long long *stamps, void *stream);
+
+/* Bytes of selscan_scan_fwd_clocked's stamps buffer: 32 per workgroup of the largest grid the call
+ * can launch, batch x ceil(dim / 16) x directions (0 for an unknown op or a size that is not
+ * positive). */
+size_t selscan_clock_stamps_bytes(int op, int64_t batch, int64_t dim);
+
 /* Bytes of the chunk_states buffer of selscan_scan_fwd / selscan_scan_bwd for `op` (0 if op is
  * unknown, a size is not positive or dstate != 16). */
 size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

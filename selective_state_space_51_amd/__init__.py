@@ -77,6 +77,10 @@ def _load():
     lib.selscan_scan_fwd.restype = ci
     lib.selscan_scan_bwd.argtypes = [ci] + [vp] * 8 + [cu] + [vp] * 10 + [i64] * 7 + [ci, vp, sz, vp]
     lib.selscan_scan_bwd.restype = ci
+    lib.selscan_scan_fwd_clocked.argtypes = [ci] + common + [vp, i64, i64, i64, i64, i64, i64, i64, ci, vp, sz, vp, vp]
+    lib.selscan_scan_fwd_clocked.restype = ci
+    lib.selscan_clock_stamps_bytes.argtypes = [ci, i64, i64]
+    lib.selscan_clock_stamps_bytes.restype = sz
     lib.selscan_scan_fwd_noalloc.argtypes = [ci] + common + [vp, i64, i64, i64, i64, i64, i64, i64, ci, vp]
     lib.selscan_scan_fwd_noalloc.restype = ci
     lib.selscan_scan_fwd_noalloc_max_bytes.argtypes = []
@@ -447,6 +451,33 @@ def selscan_scan_fwd(op, x, delta, A, B, C, D=None, z=None, delta_bias=None, del
                               _dtype_code(x), ws, wsb, _stream(stream))
     _check(rc, "selscan_scan_fwd")
     return (y, chunk_states) if chunk_states is not None else y
+
+
+def selscan_clock_stamps_bytes(op: int, batch: int, dim: int) -> int:
+    return int(lib.selscan_clock_stamps_bytes(op, batch, dim))
+
+
+@_on_launch_stream
+def selscan_scan_fwd_clocked(op, x, delta, A, B, C, stamps, D=None, z=None, delta_bias=None, delta_softplus=False,
+                             H=0, W=0, window=0, y=None, zoh=False, workspace=None, stream=None):
+    """selscan_scan_fwd that also writes, per workgroup of its scan kernel, the shader-clock and
+    100 MHz real-time counters at the workgroup's start and end into `stamps` (an int64 device
+    tensor of at least selscan_clock_stamps_bytes(op, batch, dim) bytes).  Returns y."""
+    torch = _torch()
+    bt, L, dim, N, K, lead = _scan_shapes(op, x, A, H, W)
+    io = x.dtype
+    if stamps.dtype != torch.int64 or stamps.numel() * 8 < selscan_clock_stamps_bytes(op, bt, dim):
+        raise ValueError("stamps must be int64 with selscan_clock_stamps_bytes(...) bytes")
+    if y is None:
+        y = torch.empty_like(x)
+    ws, wsb = _workspace(op, x, bt, L, dim, workspace)
+    rc = lib.selscan_scan_fwd_clocked(op, _ptr(x, "x", io), _ptr(delta, "delta", io), _ptr(A, "A", f32=True),
+                                      _ptr(B, "B", io), _ptr(C, "C", io), _ptr(D, "D", f32=True), _ptr(z, "z", io),
+                                      _ptr(delta_bias, "delta_bias", f32=True), _flags(delta_softplus, zoh),
+                                      _ptr(y, "y", io), None, bt, L, H, W, window, dim, N, _dtype_code(x), ws, wsb,
+                                      _ptr(stamps, "stamps"), _stream(stream))
+    _check(rc, "selscan_scan_fwd_clocked")
+    return y
 
 
 def selscan_scan_fwd_noalloc_max_bytes() -> int:

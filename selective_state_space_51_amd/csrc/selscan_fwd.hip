@@ -58,6 +58,7 @@ struct Problem {
     float *hlast = nullptr;     // [batch][dim][N] state after the last step
     float *ckpt = nullptr;      // [ndir][batch][nchunks][dim][N] state entering each chunk
     int64_t win = 0;            // window side of the windowed cross-scan
+    unsigned long long *stamps = nullptr;  // per workgroup: shader clock and real time at start and end
 };
 
 // the workspace a call would use: split when wanted and the caller's workspace holds it
@@ -159,6 +160,7 @@ struct Params {
     int vec;          // rows of 8 channels may be moved as 16-byte vectors
     int vecbc;        // a 16-value B/C row may be moved as 16-byte vectors
     int ntc;          // channel tiles per batch row
+    unsigned long long *stamps;  // NULL, or 4 counters per workgroup (selscan_scan_fwd_clocked)
 };
 
 // Shared-memory layout of a workgroup (16 channels), per chunk of kCH steps.  In every tile
@@ -237,6 +239,13 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     constexpr int NW = kN * (int)sizeof(T) / 4;  // dwords of one 16-value B or C row
     static_assert(CT * kN == 256, "one (channel, state) carry entry per thread");
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
+    // clock stamps (selscan_scan_fwd_clocked): shader-clock and 100 MHz real-time counters at the
+    // workgroup's start (stored at once: nothing stays live across the kernel) and end
+    if (p.stamps && threadIdx.x == 0) {
+        unsigned long long *s = p.stamps + 4 * (int64_t)blockIdx.x;
+        s[0] = __builtin_amdgcn_s_memtime();
+        s[2] = __builtin_amdgcn_s_memrealtime();
+    }
     T *xt = (T *)smem;
     T *dtl = (T *)(smem + S::kIoBytes);
     float *yt = (float *)(smem + S::kY);
@@ -624,6 +633,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             if (c0 + ch < dim) p.hlast[((int64_t)b * dim + c0 + ch) * kN + n] = Cy[i];
         }
     }
+    if (p.stamps && threadIdx.x == 0) {
+        unsigned long long *s = p.stamps + 4 * (int64_t)blockIdx.x;
+        s[1] = __builtin_amdgcn_s_memtime();
+        s[3] = __builtin_amdgcn_s_memrealtime();
+    }
 }
 
 // Split launches: y = (((o_0 + o_1) + o_2) + o_3) * silu(z) from the per-direction partial rows
@@ -713,6 +727,7 @@ int launch(const Problem &p, size_t ws_bytes, void *stream) {
     a.vec = vec;
     a.vecbc = aligned(p.B, 16) && aligned(p.C, 16);
     a.ntc = 0;
+    a.stamps = p.stamps;
     const bool zoh = (p.flags & SELSCAN_FLAG_ZOH) != 0;
     if (p.dtype == SELSCAN_BF16) return launch_kind<uint16_t>(a, p.kind, p.batch, zoh, stream);
     return launch_kind<float>(a, p.kind, p.batch, zoh, stream);
@@ -807,6 +822,32 @@ int selscan_scan_fwd(int op, const void *x, const void *delta, const float *A, c
     p.ckpt = chunk_states;
     p.win = op == SELSCAN_OP_LOCAL_SS2D ? window : 0;
     return run(p, dstate, workspace_bytes, stream);
+}
+
+int selscan_scan_fwd_clocked(int op, const void *x, const void *delta, const float *A, const void *B, const void *C,
+                             const float *D, const void *z, const float *delta_bias, unsigned flags, void *y,
+                             float *chunk_states, int64_t batch, int64_t seqlen, int64_t H, int64_t W,
+                             int64_t window, int64_t dim, int64_t dstate, int io_dtype, void *workspace,
+                             size_t workspace_bytes, unsigned long long *stamps, void *stream) {
+    if (!stamps) return SELSCAN_E_NULL;
+    if (!aligned(stamps, 8)) return SELSCAN_E_ALIGN;
+    int64_t L;
+    int ndir;
+    const int rc = resolve_op(op, seqlen, H, W, &L, &ndir);
+    if (rc != SELSCAN_OK) return rc;
+    const bool two_d = op == SELSCAN_OP_SS2D || op == SELSCAN_OP_LOCAL_SS2D;
+    Problem p{x,     delta, B, C, z, A, D, delta_bias, y, workspace, batch, L, dim, two_d ? H : 0, two_d ? W : 0,
+              ndir,  op,    io_dtype, flags};
+    p.ckpt = chunk_states;
+    p.win = op == SELSCAN_OP_LOCAL_SS2D ? window : 0;
+    p.stamps = stamps;
+    return run(p, dstate, workspace_bytes, stream);
+}
+
+size_t selscan_clock_stamps_bytes(int op, int64_t batch, int64_t dim) {
+    const int ndir = ndir_of(op);
+    if (ndir == 0 || batch <= 0 || dim <= 0) return 0;
+    return (size_t)batch * (size_t)((dim + kTC - 1) / kTC) * (size_t)ndir * 4 * sizeof(unsigned long long);
 }
 
 size_t selscan_scan_chunk_states_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {

@@ -22,6 +22,7 @@ def test_exports_every_declared_symbol():
                              "causal_conv1d_fwd", "dwconv2d_fwd", "causal_conv1d_bwd", "dwconv2d_bwd",
                              "causal_conv1d_bwd_workspace_bytes", "dwconv2d_bwd_workspace_bytes",
                              "selscan_workspace_bytes", "selscan_scan_fwd_noalloc", "selscan_scan_fwd_noalloc_max_bytes",
+                             "selscan_scan_fwd_clocked", "selscan_clock_stamps_bytes",
                              "selscan_status_str", "selscan_abi_version", "selscan_last_hip_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -393,3 +394,18 @@ def test_scan_fwd_noalloc_arguments():
     # one fp32 row set of 64 x 4096 x 256 x 4 bytes = 256 MiB > 128 MiB
     assert call(batch=64, L_=4096, H=64, W=64, dim=256) == 6
     assert call(op=S.SELSCAN_OP_BIDIR, batch=64, L_=4096, H=0, W=0, dim=256) == 6
+
+
+def test_clocked_forward_arguments():
+    """The clocked forward refuses a NULL or misaligned stamps buffer before anything else; its size
+    query counts 32 bytes per workgroup of the largest grid."""
+    ck = lambda stamps, op=S.SELSCAN_OP_SS2D: L.selscan_scan_fwd_clocked(
+        op, P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0, P + 8 * MB, None, 1, 16, 4, 4, 0, 8,
+        16, S.SELSCAN_BF16, None, 0, stamps, None)
+    assert ck(None) == 1
+    assert ck(P + 20 * MB + 4) == 3
+    assert ck(P + 20 * MB, op=9) == 5
+    assert ck(P + 20 * MB) == 6  # the SS2D call itself then stops at the missing workspace
+    assert S.selscan_clock_stamps_bytes(S.SELSCAN_OP_SS2D, 2, 40) == 2 * 3 * 4 * 32
+    assert S.selscan_clock_stamps_bytes(S.SELSCAN_OP_FWD, 2, 40) == 2 * 3 * 32
+    assert S.selscan_clock_stamps_bytes(7, 2, 40) == 0
