@@ -48,16 +48,17 @@ METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GP
 LIB_SO = os.path.join(ROOT, "selective_state_space_51_amd", "libselscan.so")
 # the kernels (mangled names) a counter record covers, per pass and workload kind; the record is
 # valid while their machine code in the built library is unchanged
-_FWD = "_ZN12_GLOBAL__N_115selscan_chunkedItLi{k}ELb0EEEvNS_6ParamsE"
+_FWD = "_ZN12_GLOBAL__N_115selscan_chunkedItLi{k}ELb0ELi{kk}EEEvNS_6ParamsE"
 _BWD = ("_ZN12_GLOBAL__N_119selscan_bwd_chunkedItLi{k}ELb0EEEvNS_9BwdParamsE",
         "_ZN12_GLOBAL__N_118selscan_bwd_reduceItLi{k}EEEvNS_15BwdReduceParamsE")
 _KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
 
 
-def profiled_kernels(pass_: str, kind: str):
+def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30):
     k = _KIND[kind]
     if pass_ == "fwd":
-        return [_FWD.format(k=k)]
+        # sequences of at most 208 steps run the 13-steps-per-lane instance
+        return [_FWD.format(k=k, kk=13 if seqlen <= 208 else 16)]
     if pass_ == "bwd":
         return [n.format(k=k) for n in _BWD]
     if kind in ("ss2d", "local_ss2d"):
@@ -158,7 +159,7 @@ def bwd_algorithmic_bytes(w) -> int:
     return tok * s * ((2 + k + g) + (1 + k + g)) + 4 * k * bc + ck + params
 
 
-def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan"):
+def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan", seqlen: int = 1 << 30):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
     kernels' current machine code; else None."""
     try:
@@ -166,7 +167,7 @@ def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan"):
     except (OSError, ValueError):
         return None
     e = t.get(workload + ("" if pass_ == "fwd" else "/" + pass_))
-    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind)):
+    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind, seqlen)):
         return None
     return e.get("bytes_per_launch")
 
@@ -543,7 +544,7 @@ def main() -> int:
                  "cycles_per_element": {"fma": ISSUE_CYCLES_FMA, "exp": ISSUE_CYCLES_EXP},
                  "simds": N_SIMDS, "sclk_mhz": sclk}
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
-    traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(w.name, args.pass_, w.kind)
+    traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(w.name, args.pass_, w.kind, w.seqlen)
     split = w.ndir > 1 and w.batch * (-(-w.dim // 16)) < 1024
     if bwd:
         kname = "selscan_bwd_chunked + selscan_bwd_merge + selscan_bwd_reduce" if split else \

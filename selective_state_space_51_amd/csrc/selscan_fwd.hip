@@ -232,12 +232,20 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
 // and every phase outside the state loop runs above both.
 // Zero-order-hold input factor: zoh_phi (selscan_common.h).
 
-template <typename T, int KIND, bool ZOH>
+// KK: scan steps per lane, 16 (chunks of 256 steps) or, for sequences of at most 16 KK steps,
+// fewer (the sequence is one chunk): the LDS tiles keep 16 slots per lane, and slot 16 l + j
+// holds chunk step KK l + j for j < KK (the slots past KK are left out everywhere).
+template <typename T, int KIND, bool ZOH, int KK>
 __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     using S = Lds<T>;
     constexpr int CT = kTC;
     constexpr int NW = kN * (int)sizeof(T) / 4;  // dwords of one 16-value B or C row
     static_assert(CT * kN == 256, "one (channel, state) carry entry per thread");
+    static_assert(KK >= 1 && KK <= kK, "steps per lane");
+    constexpr int CHK = kLPR * KK;  // scan steps per chunk
+    // chunk step of LDS slot s (valid when (s & 15) < KK) and slot of chunk step c
+    auto cstep = [](int s) { return KK * (s >> 4) + (s & 15); };
+    auto slot_of = [](int c) { return 16 * (c / KK) + c % KK; };
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::kBytes];
     // clock stamps (selscan_scan_fwd_clocked): shader-clock and 100 MHz real-time counters at the
     // workgroup's start (stored at once: nothing stays live across the kernel) and end
@@ -257,7 +265,6 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l = lane & 15;
     const int cl = wave * 4 + (lane >> 4);     // this lane's channel within the tile
-    const float firstf = l == 0 ? 1.f : 0.f;  // 1 on the first lane of each channel
     // consecutive channel tiles on one XCD: workgroups are dealt round-robin over 8 XCDs
     const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
     const int tile_all = bi < (q8 << 3) ? (bi & 7) * q8 + (bi >> 3) : bi;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     const int64_t tok = (int64_t)p.batch * L * dim, bcn = (int64_t)p.batch * L * kN;
     const int ncols = (int)(dim - c0 < CT ? dim - c0 : CT);
     const bool cvalid = cl < ncols;
-    const int nchunks = (int)((L + kCH - 1) / kCH);
+    const int nchunks = (int)((L + CHK - 1) / CHK);
     const bool tile_fast = ncols == CT && p.vec && p.vecbc;  // full tile, vector rows
     const bool vec = p.vec != 0;
     const T *x = (const T *)p.x;
@@ -289,6 +296,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     const int64_t cg = c0 + 8 * g;
     const int pp = 8 * (((lane >> 2) & 7) + 8 * (wave >> 1)) + 4 * (wave & 1) + (lane & 3);
     const int sb = 16 * (lane >> 2) + 4 * wave + (lane & 3);
+    // zeros read by every lane but the first of a channel in place of the chunk carry
+    __shared__ __attribute__((aligned(16))) float zero_pair[kN];
+    if (tid < kN) zero_pair[tid] = 0.f;
+    const float *carry_src = l == 0 ? Cy + cl * kN : zero_pair;
     const int so = 16 * ((lane >> 2) & 7) + 4 * wave + (lane & 3);
 
     int qq = 0;  // chunks done over all directions (priority parity)
@@ -321,8 +332,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             const T *dl = multi ? (const T *)p.delta + kk * tok : dlk;
             const T *Bk = multi ? (const T *)p.B + kk * bcn : Bkk;
             const T *Ck = multi ? (const T *)p.C + kk * bcn : Ckk;
-            const int64_t s0 = (int64_t)q * kCH;
-            const int64_t sa = s0 + 2 * pp, sbb = sa + 1, s = s0 + sb;
+            const int64_t s0 = (int64_t)q * CHK;
+            const int64_t sa = s0 + cstep(2 * pp), sbb = sa + 1, s = s0 + cstep(sb);
+            // slots past KK in a lane hold no step
+            const bool va = ((2 * pp) & 15) < KK, vb = ((2 * pp) & 15) + 1 < KK, vs = (sb & 15) < KK;
             if constexpr (decltype(fast_c)::value) {
                 const int64_t oa = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
                 const int64_t ob = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
@@ -340,19 +353,19 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 }
             } else {
                 px0 = px1 = pd0 = pd1 = Raw8<T>{};
-                if (nv > 0 && sa < L) {
+                if (nv > 0 && va && sa < L) {
                     const int64_t off = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
                     px0 = load_raw8(x + off, nv, vec);
                     pd0 = load_raw8(dl + off, nv, vec);
                 }
-                if (nv > 0 && sbb < L) {
+                if (nv > 0 && vb && sbb < L) {
                     const int64_t off = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
                     px1 = load_raw8(x + off, nv, vec);
                     pd1 = load_raw8(dl + off, nv, vec);
                 }
 #pragma unroll
                 for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
-                if (s < L) {
+                if (vs && s < L) {
                     const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
                     if (p.vecbc) {
 #pragma unroll
@@ -413,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         // one chunk; FAST: a full chunk of a full tile whose successor is full too
         auto chunk = [&](int q, auto fast_c) {
             constexpr bool fast = decltype(fast_c)::value;
-            const int64_t s0 = (int64_t)q * kCH;
+            const int64_t s0 = (int64_t)q * CHK;
             __builtin_amdgcn_s_setprio(2);
             lds_barrier();  // the previous chunk is done with every tile
             commit();
@@ -432,13 +445,13 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             int64_t ooff[2] = {0, 0};
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int64_t s = s0 + so + 128 * r;
+                const int64_t s = s0 + cstep(so + 128 * r);
                 if constexpr (fast) {
                     ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
                     if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
                 } else {
                     zr[r] = Raw8<T>{};
-                    if (nv > 0 && s < L) {
+                    if (nv > 0 && ((so + 128 * r) & 15) < KK && s < L) {
                         ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
                         if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                     }
@@ -452,47 +465,51 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 if (!next_dir || k + 1 < k_end) fetch(next_dir ? k + 1 : k, next_dir ? 0 : q + 1, fast_c);
             }
 
-            // ---- this lane's 16 steps of its channel
-            const int64_t rem = L - (s0 + l * kK);
-            const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= kK ? kK : (int)rem));
-            float dt[kK], dx[kK], yv[kK];
+            // ---- this lane's KK steps of its channel
+            const int64_t rem = L - (s0 + l * KK);
+            const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= KK ? KK : (int)rem));
+            float dt[KK], dx[KK], yv[KK];
             float sdt = 0.f;
             {
-                const float Dd = Db[2 * cl], bias = Db[2 * cl + 1];
-                float xf[kK], df[kK];
+                const float Dd = Db[2 * cl];
+                float xf[KK];
                 constexpr int V = S::kV;
 #pragma unroll
-                for (int pc = 0; pc < kK / V; ++pc) {
+                for (int pc = 0; pc < (KK + V - 1) / V; ++pc) {
                     const uint4 xq = *(const uint4 *)&xt[cl * S::kXP + pc * (kLPR * V) + l * V];
                     const uint4 dq = *(const uint4 *)&dtl[cl * S::kXP + pc * (kLPR * V) + l * V];
                     const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w}, dw[4] = {dq.x, dq.y, dq.z, dq.w};
 #pragma unroll
                     for (int i = 0; i < V; ++i) {
+                        if (pc * V + i >= KK) continue;
                         if constexpr (sizeof(T) == 2) {
                             xf[pc * V + i] = __uint_as_float(i & 1 ? xw[i >> 1] & 0xFFFF0000u : xw[i >> 1] << 16);
-                            df[pc * V + i] = __uint_as_float(i & 1 ? dw[i >> 1] & 0xFFFF0000u : dw[i >> 1] << 16);
+                            dt[pc * V + i] = __uint_as_float(i & 1 ? dw[i >> 1] & 0xFFFF0000u : dw[i >> 1] << 16);
                         } else {
                             xf[pc * V + i] = __uint_as_float(xw[i]);
-                            df[pc * V + i] = __uint_as_float(dw[i]);
+                            dt[pc * V + i] = __uint_as_float(dw[i]);
                         }
                     }
                 }
+                // bias, then softplus, in place (one set of registers for every form)
+                if (p.bias) {
+                    const float bias = Db[2 * cl + 1];
 #pragma unroll
-                for (int j = 0; j < kK; ++j) dt[j] = df[j] + bias;
-                if (p.softplus) {
-                    // in place: one set of registers for both forms (no copies where they join)
-#pragma unroll
-                    for (int j = 0; j < kK; ++j) dt[j] = softplus(dt[j]);
+                    for (int j = 0; j < KK; ++j) dt[j] += bias;
                 }
-                if (!fast && !(s0 + kCH <= L && ncols == CT)) {
+                if (p.softplus) {
+#pragma unroll
+                    for (int j = 0; j < KK; ++j) dt[j] = softplus(dt[j]);
+                }
+                if (!fast && !(s0 + CHK <= L && ncols == CT)) {
                     // steps past the sequence end and channels past dim get delta = 0, the
                     // identity step (staged x there is 0 too)
                     const float limf = (float)lim;
 #pragma unroll
-                    for (int j = 0; j < kK; ++j) dt[j] *= __builtin_amdgcn_fmed3f(limf - (float)j, 0.f, 1.f);
+                    for (int j = 0; j < KK; ++j) dt[j] *= __builtin_amdgcn_fmed3f(limf - (float)j, 0.f, 1.f);
                 }
 #pragma unroll
-                for (int j = 0; j < kK; ++j) {
+                for (int j = 0; j < KK; ++j) {
                     dx[j] = dt[j] * xf[j];
                     yv[j] = Dd * xf[j];
                     sdt += dt[j];
@@ -505,17 +522,18 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 #pragma unroll 1
             for (int n = 0; n < kN; n += 2) {
                 const float2 a2 = *(const float2 *)&As[cl * kN + n];
-                float e0[kK], u0[kK], e1[kK], u1[kK];
+                constexpr int NP = (KK + 3) / 4;  // 4-step pieces of a lane's slots that hold steps
+                float e0[KK], u0[KK], e1[KK], u1[KK];
                 float b0, b1;
                 {
-                    float B0[kK], B1[kK];
+                    float B0[4 * NP], B1[4 * NP];
 #pragma unroll
-                    for (int pc = 0; pc < 4; ++pc) {
+                    for (int pc = 0; pc < NP; ++pc) {
                         *(float4 *)&B0[4 * pc] = *(const float4 *)&Bc[n * kFP + pc * (kLPR * 4)];
                         *(float4 *)&B1[4 * pc] = *(const float4 *)&Bc[(n + 1) * kFP + pc * (kLPR * 4)];
                     }
 #pragma unroll
-                    for (int j = 0; j < kK; ++j) {
+                    for (int j = 0; j < KK; ++j) {
                         const float t0 = dt[j] * a2.x, t1 = dt[j] * a2.y;
                         e0[j] = __builtin_amdgcn_exp2f(t0);
                         e1[j] = __builtin_amdgcn_exp2f(t1);
@@ -533,21 +551,22 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 float a0 = __builtin_amdgcn_exp2f(a2.x * sdt);
                 float a1 = __builtin_amdgcn_exp2f(a2.y * sdt);
                 // the previous chunk's end state of this channel enters through its first lane
-                const float2 cy = *(const float2 *)&Cy[cl * kN + n];
+                // (the other lanes read zeros)
+                const float2 cy = *(const float2 *)&carry_src[n];
                 float h0 = cy.x, h1 = cy.y;
-                b0 = fmaf(a0, h0 * firstf, b0);
-                b1 = fmaf(a1, h1 * firstf, b1);
+                b0 = fmaf(a0, h0, b0);
+                b1 = fmaf(a1, h1, b1);
                 scan16x2(b0, b1, a0, a1, h0, h1);
                 // the last lane of a channel holds the chunk's end state: the next chunk's carry
                 if (l == kLPR - 1) *(float2 *)&Cy[cl * kN + n] = make_float2(b0, b1);
-                float C0[kK], C1[kK];
+                float C0[4 * NP], C1[4 * NP];
 #pragma unroll
-                for (int pc = 0; pc < 4; ++pc) {
+                for (int pc = 0; pc < NP; ++pc) {
                     *(float4 *)&C0[4 * pc] = *(const float4 *)&Cc[n * kFP + pc * (kLPR * 4)];
                     *(float4 *)&C1[4 * pc] = *(const float4 *)&Cc[(n + 1) * kFP + pc * (kLPR * 4)];
                 }
 #pragma unroll
-                for (int j = 0; j < kK; ++j) {
+                for (int j = 0; j < KK; ++j) {
                     h0 = fmaf(e0[j], h0, u0[j]);
                     h1 = fmaf(e1[j], h1, u1[j]);
                     yv[j] = fmaf(C0[j], h0, yv[j]);
@@ -561,9 +580,13 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             else if (y_in_xd) lds_barrier();
             float *yw = y_in_xd ? (float *)smem : yt;
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
-                *(float4 *)&yw[cl * kFP + pc * (kLPR * 4) + 4 * l] =
-                    make_float4(yv[4 * pc], yv[4 * pc + 1], yv[4 * pc + 2], yv[4 * pc + 3]);
+            for (int pc = 0; pc < (KK + 3) / 4; ++pc) {
+                // (slots past KK are written with zeros and never read)
+                float q4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q4[i] = 4 * pc + i < KK ? yv[4 * pc + i] : 0.f;
+                *(float4 *)&yw[cl * kFP + pc * (kLPR * 4) + 4 * l] = make_float4(q4[0], q4[1], q4[2], q4[3]);
+            }
             lds_barrier();
             if (lds_sum && k == 0) return;  // direction 0's tile waits in LDS for direction 1
             // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
@@ -590,13 +613,14 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     } else {
                         store8(wsk + ooff[r], 8, true, v);
                     }
-                } else if (nv > 0 && s0 + sl < L) {
+                } else if (nv > 0 && (sl & 15) < KK && s0 + cstep(sl) < L) {
                     if (y_in_xd) {
-                        // this direction's step sl is token L-1-sl, direction 0's step L-1-sl
+                        // this direction's step c (slot sl) is token L-1-c, direction 0's step L-1-c
+                        const int sl0 = slot_of((int)L - 1 - cstep(sl));
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             v[e] = yw[(8 * g + e) * kFP + fpos(sl)];
-                            wv[e] = yt[(8 * g + e) * kFP + fpos((int)L - 1 - sl)];
+                            wv[e] = yt[(8 * g + e) * kFP + fpos(sl0)];
                         }
                     } else {
 #pragma unroll
@@ -620,7 +644,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             }
         };
         if (!multi || k == k_begin) fetch(k, 0, BoolC<false>{});
-        const int nfast = tile_fast ? (int)(L / kCH) - 1 : 0;
+        const int nfast = tile_fast && KK == kK ? (int)(L / CHK) - 1 : 0;
         int q = 0;
         for (; q < nfast; ++q, ++qq) chunk(q, BoolC<true>{});
         for (; q < nchunks; ++q, ++qq) chunk(q, BoolC<false>{});
@@ -681,7 +705,11 @@ int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     const int64_t blocks = batch * (int64_t)c.ntc * (c.split ? c.ndir : 1);
     if (blocks > 0x7FFFFFFF) return SELSCAN_E_UNSUPPORTED;
     void *args[] = {&c};
-    const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true> : (const void *)&selscan_chunked<T, KIND, false>;
+    // a sequence of at most 208 steps is one chunk of 13 steps per lane (Euler Bbar); else 16
+    const bool short13 = !zoh && c.L <= kLPR * 13;
+    const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true, kK>
+                           : short13 ? (const void *)&selscan_chunked<T, KIND, false, 13>
+                                     : (const void *)&selscan_chunked<T, KIND, false, kK>;
     hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
     if (e == hipSuccess && c.split && c.L > 0) {
         MergeParams m;
