@@ -54,11 +54,15 @@ _BWD = ("_ZN12_GLOBAL__N_119selscan_bwd_chunkedItLi{k}ELb0EEEvNS_9BwdParamsE",
 _KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
 
 
-def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30):
+_MERGE = "_ZN12_GLOBAL__N_113selscan_mergeItEEvNS_11MergeParamsE"
+
+
+def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool = False):
     k = _KIND[kind]
     if pass_ == "fwd":
-        # sequences of at most 208 steps run the 13-steps-per-lane instance
-        return [_FWD.format(k=k, kk=13 if seqlen <= 208 else 16)]
+        # sequences of at most 208 steps run the 13-steps-per-lane instance; a direction-split
+        # grid adds the merge of the directions' rows
+        return [_FWD.format(k=k, kk=13 if seqlen <= 208 else 16)] + ([_MERGE] if split else [])
     if pass_ == "bwd":
         return [n.format(k=k) for n in _BWD]
     if kind in ("ss2d", "local_ss2d"):
@@ -159,7 +163,8 @@ def bwd_algorithmic_bytes(w) -> int:
     return tok * s * ((2 + k + g) + (1 + k + g)) + 4 * k * bc + ck + params
 
 
-def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan", seqlen: int = 1 << 30):
+def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan", seqlen: int = 1 << 30,
+                     split: bool = False):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
     kernels' current machine code; else None."""
     try:
@@ -167,7 +172,7 @@ def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan", s
     except (OSError, ValueError):
         return None
     e = t.get(workload + ("" if pass_ == "fwd" else "/" + pass_))
-    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind, seqlen)):
+    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind, seqlen, split)):
         return None
     return e.get("bytes_per_launch")
 
@@ -544,8 +549,9 @@ def main() -> int:
                  "cycles_per_element": {"fma": ISSUE_CYCLES_FMA, "exp": ISSUE_CYCLES_EXP},
                  "simds": N_SIMDS, "sclk_mhz": sclk}
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
-    traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(w.name, args.pass_, w.kind, w.seqlen)
     split = w.ndir > 1 and w.batch * (-(-w.dim // 16)) < 1024
+    traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(
+        w.name, args.pass_, w.kind, w.seqlen, split and args.pass_ == "fwd")
     if bwd:
         kname = "selscan_bwd_chunked + selscan_bwd_merge + selscan_bwd_reduce" if split else \
             "selscan_bwd_chunked + selscan_bwd_reduce"

@@ -127,8 +127,11 @@ def test_softplus_extreme_preactivations():
         assert e <= _bwd_tol("f32", k), (k, e)
 
 
-@pytest.mark.parametrize("L,dim,batch", [(1, 8, 1), (2, 24, 3), (17, 72, 2), (257, 8, 1), (64, 1, 2), (5, 3, 1)])
+@pytest.mark.parametrize("L,dim,batch", [(1, 8, 1), (2, 24, 3), (17, 72, 2), (257, 8, 1), (64, 1, 2), (5, 3, 1),
+                                         (207, 24, 2), (208, 40, 1), (209, 16, 2)])
 def test_edge_shapes(L, dim, batch):
+    """Ragged shapes; sequences of at most 208 steps run one chunk of 13 steps per lane, longer ones
+    chunks of 16 per lane (207, 208 and 209 sit on that boundary)."""
     w = W.Workload("edge", "selscan", batch, L, dim, 16, "f32", True, index=8)
     inp = W.generate(w)
     _say("edge", L, dim, batch)
@@ -144,7 +147,8 @@ def test_bidir_edges(L, dim):
     _check("bidir", w, inp, softplus=True, use_bias=True, use_z=False)
 
 
-@pytest.mark.parametrize("L,dim", [(1, 8), (2, 16), (197, 24), (256, 13), (255, 40), (257, 24)])
+@pytest.mark.parametrize("L,dim", [(1, 8), (2, 16), (197, 24), (208, 16), (209, 24), (256, 13), (255, 40),
+                                   (257, 24)])
 def test_bidir_edges_bf16(L, dim):
     """bf16 bidirectional scans around the one-chunk length (256 steps), where the two
     directions' outputs are summed in shared memory; partial channel tiles and rows that are not
@@ -157,7 +161,7 @@ def test_bidir_edges_bf16(L, dim):
     _check("bidir", w, inp, zoh=True)
 
 
-@pytest.mark.parametrize("L,untouched", [(197, True), (256, True), (257, False)])
+@pytest.mark.parametrize("L,untouched", [(197, True), (208, True), (209, True), (256, True), (257, False)])
 def test_bidir_workspace_use(L, untouched):
     """With the directions run in turn (a workspace of one row set), a bf16 bidirectional scan of
     at most 256 steps sums its directions on chip and leaves the workspace as it found it; a
@@ -473,6 +477,8 @@ def _bwd_run(dtype, batch, L, dim, gate=True, softplus=False, bias=False, h0=Fal
     ("bf16", 2, 700, 64, dict(softplus=True, bias=True)),
     ("bf16", 3, 513, 24, dict(h0=True)),
     ("f32", 2, 1, 8, {}),
+    ("f32", 2, 208, 24, dict(h0=True)),
+    ("bf16", 2, 209, 40, {}),
 ], ids=lambda v: str(v))
 def test_bwd_against_oracle(dtype, batch, L, dim, kw):
     errs = _bwd_run(dtype, batch, L, dim, **kw)
