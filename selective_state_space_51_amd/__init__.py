@@ -38,15 +38,16 @@ class SelscanError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({status_str(status)}){extra}")
 
 
-def _load():
+def _load(path=None):
     # torch carries its own HIP runtime; load it first so that the library binds to the same
     # runtime (same soname) and torch's streams and device pointers are valid in it
     import torch  # noqa: F401
-    if not os.path.exists(LIB_PATH):
+    path = path or LIB_PATH
+    if not os.path.exists(path):
         raise ImportError(
-            f"libselscan.so not found at {LIB_PATH}; build it with "
+            f"libselscan.so not found at {path}; build it with "
             "`python selective_state_space_51_amd/build.py` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i64, ci, cu, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
     common = [vp] * 8 + [cu, vp]
     lib.selscan_fwd.argtypes = common + [i64, i64, i64, i64, ci, vp, sz, vp]
@@ -103,6 +104,15 @@ def _load():
 
 
 lib = _load()
+
+
+def use_library(path: str):
+    """Bind every function of this module to another build of the same C ABI at ``path`` (the
+    diagnostic libselscan_phases.so, say) from here on; returns its ctypes handle."""
+    global lib, LIB_PATH
+    lib = _load(path)
+    LIB_PATH = path
+    return lib
 
 
 def status_str(status: int) -> str:

@@ -1,6 +1,7 @@
-"""Build libselscan.so (and the microbenchmark library libselscan_ubench.so) in-tree with hipcc
-for gfx950 (cross-compiles without a GPU).  The sources compile in parallel to objects in a
-temporary directory, then link."""
+"""Build libselscan.so in-tree with hipcc for gfx950 (cross-compiles without a GPU), and beside it
+two diagnostic libraries: libselscan_ubench.so (the microbenchmarks) and libselscan_phases.so (the
+scan library with the backward's per-wave phase clocks compiled in).  The sources compile in
+parallel to objects in a temporary directory, then link."""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -16,6 +17,7 @@ SRCS = [os.path.join(CSRC, f) for f in ("selscan_fwd.hip", "selscan_bwd.hip", "s
 OUT = os.path.join(PKG, "libselscan.so")
 UBENCH_SRCS = [os.path.join(CSRC, "ubench.hip")]
 UBENCH_OUT = os.path.join(PKG, "libselscan_ubench.so")
+PHASES_OUT = os.path.join(PKG, "libselscan_phases.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
@@ -56,12 +58,13 @@ def build(extra=None, out=OUT, srcs=None, verbose=False) -> str:
 
 
 def build_all(extra=None, verbose=False) -> None:
-    """The scan library and the microbenchmark library, compiled side by side."""
-    with cf.ThreadPoolExecutor(max_workers=2) as ex:
-        a = ex.submit(build, extra, OUT, SRCS, verbose)
-        b = ex.submit(build, extra, UBENCH_OUT, UBENCH_SRCS, verbose)
-        a.result()
-        b.result()
+    """The scan library and the two diagnostic libraries, compiled side by side."""
+    with cf.ThreadPoolExecutor(max_workers=3) as ex:
+        futs = [ex.submit(build, extra, OUT, SRCS, verbose),
+                ex.submit(build, extra, UBENCH_OUT, UBENCH_SRCS, verbose),
+                ex.submit(build, [*(extra or []), "-DSELSCAN_PHASE_CLOCKS"], PHASES_OUT, SRCS, verbose)]
+        for f in futs:
+            f.result()
 
 
 if __name__ == "__main__":

@@ -145,6 +145,39 @@ __device__ __forceinline__ void rows4_sum(const float p[kK], float out[4]) {
     }
 }
 
+// Per-wave shader-clock cycles in each phase of the backward's chunk loop: 0 staging (loads and
+// their commit to LDS), 1 prologue, 2 state loop outside its barriers, 3 and 4 the waits at its
+// two barriers, 5 output; 6 the whole kernel.  Compiled in only for the diagnostic library
+// (SELSCAN_PHASE_CLOCKS, libselscan_phases.so); otherwise every call is empty.
+#ifdef SELSCAN_PHASE_CLOCKS
+constexpr int kPhaseWaves = 1 << 14;
+__device__ unsigned long long g_bwd_phase[kPhaseWaves * 8];
+struct PhaseClock {
+    unsigned long long acc[6] = {0, 0, 0, 0, 0, 0}, t = 0, t0 = __builtin_amdgcn_s_memtime();
+    __device__ void mark() { t = __builtin_amdgcn_s_memtime(); }
+    __device__ void add(int i) {
+        const unsigned long long n = __builtin_amdgcn_s_memtime();
+        acc[i] += n - t;
+        t = n;
+    }
+    __device__ void finish(int wave_id, int lane) {
+        const unsigned long long end = __builtin_amdgcn_s_memtime();
+        if (lane == 0 && wave_id < kPhaseWaves) {
+#pragma unroll
+            for (int i = 0; i < 6; ++i) g_bwd_phase[wave_id * 8 + i] = acc[i];
+            g_bwd_phase[wave_id * 8 + 6] = end - t0;
+            g_bwd_phase[wave_id * 8 + 7] = 1;
+        }
+    }
+};
+#else
+struct PhaseClock {
+    __device__ void mark() {}
+    __device__ void add(int) {}
+    __device__ void finish(int, int) {}
+};
+#endif
+
 __device__ __forceinline__ float sigmoidf_(float w) { return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e)); }
 
 template <typename T, int KIND, bool ZOH>
@@ -171,6 +204,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
     float *Os = (float *)(smem + S::kX);  // third output tile (x and delta space)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l = lane & 15, row = lane >> 4;
+    PhaseClock clk;
     const int cl = wave * 4 + row;
     const float firstf = l == 0 ? 1.f : 0.f, lastf = l == kLPR - 1 ? 1.f : 0.f;
     const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
@@ -311,6 +345,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
         }
         Hc[tid] = hck;
     };
+    clk.mark();
     for (int q = nchunks - 1; q >= 0; --q) {
         const int64_t s0 = (int64_t)q * kCH;
         // priority: staging, prologue and output above the state loop, whose priority alternates
@@ -320,6 +355,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
         lds_barrier();  // the previous (later) chunk is done with every tile
         commit();
         lds_barrier();
+        clk.add(0);
 
         // ---- this lane's 16 steps of its channel
         const int64_t rem = L - (s0 + l * kK);
@@ -386,6 +422,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
 
         if (q & 1) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
+        clk.add(1);
 #pragma unroll 1
         for (int n = 0; n < kN; ++n) {
             const float a2 = As[cl * kN + n];
@@ -434,25 +471,30 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                 rows4_sum(pC, r4);
                 *(float4 *)&redC[rslot] = make_float4(r4[0], r4[1], r4[2], r4[3]);
             }
-            // reverse, pass 1: this lane's map of the adjoint, from a zero input
-            float rb = 0.f;
+            // reverse, pass 1: this lane's map of the adjoint, from a zero input.  Down the lane
+            // g_j = c_j + e_{j+1} g_{j+1} (one FMA a step); the lane hands e_0 g_0 to its left
+            // neighbour, and its multiplier is the product of its 16 decays, aown.
+            float rg = c[kK - 1];
 #pragma unroll
-            for (int j = kK - 1; j >= 0; --j) rb = e[j] * (c[j] + rb);
+            for (int j = kK - 2; j >= 0; --j) rg = fmaf(e[j + 1], rg, c[j]);
+            float rb = e[0] * rg;
             float ra = aown;
             float gs = Gc[cl * kN + n];  // what the later chunk hands back, entering through lane 15
             rb = fmaf(ra, gs * lastf, rb);
             scan16_down(rb, ra, gs);
             if (l == 0) Gc[cl * kN + n] = rb;  // handed to the earlier chunk
-            // reverse, pass 2: g_t and every derivative of the step
+            // reverse, pass 2: g_t (the same FMA recurrence, now from what the right neighbour
+            // hands this lane's last step) and every derivative of the step
             float pB[kK];
             float dAl = 0.f;
             {
                 float Bv[kK];
 #pragma unroll
                 for (int pc = 0; pc < 4; ++pc) *(float4 *)&Bv[4 * pc] = *(const float4 *)&Bc[n * kFP + pc * (kLPR * 4)];
+                float gq = c[kK - 1] + gs;
 #pragma unroll
                 for (int j = kK - 1; j >= 0; --j) {
-                    const float gq = c[j] + gs;
+                    if (j < kK - 1) gq = fmaf(e[j + 1], gq, c[j]);
                     const float gw = gq * eh[j];
                     dAl = fmaf(dt[j], gw, dAl);
                     accdd[j] = fmaf(Araw, gw, accdd[j]);
@@ -466,12 +508,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                         accx[j] = fmaf(gB, phi, accx[j]);
                         pB[j] = gq * phi * dlx;
                         dAl = fmaf(gB, dlx * dt[j] * dphi, dAl);
-                        gs = e[j] * gq;
-                        accdd[j] = fmaf(px[j], gs * Bv[j], accdd[j]);
+                        accdd[j] = fmaf(px[j], e[j] * gB, accdd[j]);
                     } else {
                         accx[j] = fmaf(gq, Bv[j], accx[j]);
                         pB[j] = gq * px[j];
-                        gs = e[j] * gq;
                     }
                 }
             }
@@ -482,7 +522,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
             }
             dAl = rowsum16(dAl);
             if (l == kLPR - 1) dAs[cl * kN + n] += dAl;
+            clk.add(2);
             lds_barrier();
+            clk.add(3);
             {
                 // channel sums of this state's dB, dC for step tid of the chunk
                 float sB = 0.f, sC = 0.f;
@@ -497,7 +539,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                     dst[(int64_t)kN * L] = sC;
                 }
             }
+            clk.add(2);
             lds_barrier();
+            clk.add(4);
         }
         __builtin_amdgcn_s_setprio(2);
 
@@ -608,6 +652,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
                 }
             }
         }
+        clk.add(5);
     }
     lds_barrier();
     {
@@ -622,6 +667,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
         }
     }
   }
+    clk.finish(blockIdx.x * 4 + wave, lane);
 }
 
 struct BwdReduceParams {
@@ -932,6 +978,26 @@ int selscan_scan_bwd(int op, const void *x, const void *delta, const float *A, c
     p.win = op == SELSCAN_OP_LOCAL_SS2D ? window : 0;
     return bwd_run(p, dstate, workspace_bytes, stream);
 }
+
+#ifdef SELSCAN_PHASE_CLOCKS
+// Diagnostic library only: copy the phase clocks of the last backward launch (8 u64 per wave,
+// wave = 4 x workgroup + wave in workgroup: phases 0-5, whole kernel, 1 if written) to `host`,
+// which holds `count` u64.  Returns 0, 1 if count is larger than the record, 2 on a HIP error.
+int selscan_bwd_phase_read(unsigned long long *host, size_t count) {
+    if (!host || count > (size_t)kPhaseWaves * 8) return 1;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_bwd_phase), count * sizeof(unsigned long long), 0,
+                               hipMemcpyDeviceToHost) == hipSuccess ? 0 : 2;
+}
+// Clear the record (host-synchronous).
+int selscan_bwd_phase_clear(void) {
+    static const unsigned long long zeros[1024] = {};
+    for (int i = 0; i < kPhaseWaves * 8; i += 1024)
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_bwd_phase), zeros, sizeof(zeros), i * sizeof(unsigned long long),
+                              hipMemcpyHostToDevice) != hipSuccess)
+            return 2;
+    return 0;
+}
+#endif
 
 size_t selscan_scan_bwd_workspace_bytes(int op, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                                         int io_dtype) {

@@ -1,6 +1,6 @@
 // ubench.hip - microbenchmarks of the gfx950 resources the scan's roofline argument uses: the
 // issue cost of the VALU instruction forms the scan kernels are built from (fp32 FMA and multiply,
-// v_exp_f32, v_rcp_f32, an FMA with a scalar operand, a DPP add), the shader clock while they run,
+// v_exp_f32, v_rcp_f32, an FMA with a scalar operand, a DPP add, the cross-half-wave swaps), the shader clock while they run,
 // and the HBM read and copy streams.  Not part of the scan library: it is built into its own shared
 // object (libselscan_ubench.so) and driven by selective_state_space_51_amd/ubench.py.
 //
@@ -23,6 +23,9 @@ enum Kind {
     K_MIX_INDEP = 10,   // 8 exps and 40 FMAs on separate registers: no FMA reads an exp result
     K_MIX_NEAR = 11,    // 8 exps and 40 FMAs, each exp result read by the FMA right after it
     K_MIX_INDEP3 = 12,  // 8 exps and 24 FMAs on separate registers (1 : 3)
+    K_MIX_INDEP19 = 13, // 2 exps and 38 FMAs on separate registers (1 : 19, the backward's mix)
+    K_PERMLANE32 = 14,  // 8 v_permlane32_swap on 4 register pairs
+    K_PERMLANE16 = 15,  // 8 v_permlane16_swap on 4 register pairs
     K_NKIND
 };
 
@@ -94,6 +97,41 @@ __global__ __launch_bounds__(256) void ub_valu(float *out, unsigned long long *s
                 "v_exp_f32 %0, %0\n\tv_exp_f32 %0, %0\n\tv_exp_f32 %0, %0\n\tv_exp_f32 %0, %0\n\t"
                 "v_exp_f32 %0, %0\n\tv_exp_f32 %0, %0\n\tv_exp_f32 %0, %0\n\tv_exp_f32 %0, %0"
                 : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
+        } else if constexpr (KIND == K_MIX_INDEP19) {
+            float e0 = a0 * 0.5f, e1 = a1 * 0.5f;
+            asm volatile(
+                "v_exp_f32 %8, %8\n\t"
+                "v_fmac_f32 %0, %10, %11\n\tv_fmac_f32 %1, %10, %11\n\tv_fmac_f32 %2, %10, %11\n\tv_fmac_f32 %3, %10, %11\n\t"
+                "v_fmac_f32 %4, %10, %11\n\tv_fmac_f32 %5, %10, %11\n\tv_fmac_f32 %6, %10, %11\n\tv_fmac_f32 %7, %10, %11\n\t"
+                "v_fmac_f32 %0, %10, %11\n\tv_fmac_f32 %1, %10, %11\n\tv_fmac_f32 %2, %10, %11\n\tv_fmac_f32 %3, %10, %11\n\t"
+                "v_fmac_f32 %4, %10, %11\n\tv_fmac_f32 %5, %10, %11\n\tv_fmac_f32 %6, %10, %11\n\tv_fmac_f32 %7, %10, %11\n\t"
+                "v_fmac_f32 %0, %10, %11\n\tv_fmac_f32 %1, %10, %11\n\tv_fmac_f32 %2, %10, %11\n\t"
+                "v_exp_f32 %9, %9\n\t"
+                "v_fmac_f32 %3, %10, %11\n\tv_fmac_f32 %4, %10, %11\n\tv_fmac_f32 %5, %10, %11\n\tv_fmac_f32 %6, %10, %11\n\t"
+                "v_fmac_f32 %7, %10, %11\n\tv_fmac_f32 %0, %10, %11\n\tv_fmac_f32 %1, %10, %11\n\tv_fmac_f32 %2, %10, %11\n\t"
+                "v_fmac_f32 %3, %10, %11\n\tv_fmac_f32 %4, %10, %11\n\tv_fmac_f32 %5, %10, %11\n\tv_fmac_f32 %6, %10, %11\n\t"
+                "v_fmac_f32 %7, %10, %11\n\tv_fmac_f32 %0, %10, %11\n\tv_fmac_f32 %1, %10, %11\n\tv_fmac_f32 %2, %10, %11\n\t"
+                "v_fmac_f32 %3, %10, %11\n\tv_fmac_f32 %4, %10, %11\n\tv_fmac_f32 %5, %10, %11"
+                : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7), "+v"(e0), "+v"(e1)
+                : "v"(m), "v"(c));
+            a0 += e0 + e1;
+        } else if constexpr (KIND == K_PERMLANE32 || KIND == K_PERMLANE16) {
+            // through the builtins, so the compiler places whatever wait states the swaps need
+            uint32_t u[8] = {__float_as_uint(a0), __float_as_uint(a1), __float_as_uint(a2), __float_as_uint(a3),
+                             __float_as_uint(a4), __float_as_uint(a5), __float_as_uint(a6), __float_as_uint(a7)};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const auto v = KIND == K_PERMLANE32 ? __builtin_amdgcn_permlane32_swap(u[2 * k], u[2 * k + 1], false, false)
+                                                        : __builtin_amdgcn_permlane16_swap(u[2 * k], u[2 * k + 1], false, false);
+                    u[2 * k] = v[0];
+                    u[2 * k + 1] = v[1];
+                }
+            }
+            a0 = __uint_as_float(u[0]), a1 = __uint_as_float(u[1]), a2 = __uint_as_float(u[2]), a3 = __uint_as_float(u[3]);
+            a4 = __uint_as_float(u[4]), a5 = __uint_as_float(u[5]), a6 = __uint_as_float(u[6]), a7 = __uint_as_float(u[7]);
+            asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
         } else if constexpr (KIND == K_MIX_INDEP || KIND == K_MIX_NEAR || KIND == K_MIX_INDEP3) {
             // exps on e0..e3; FMAs on a0..a7 (K_MIX_NEAR: the FMA after each exp reads its result)
             float e0 = a0 * 0.5f, e1 = a1 * 0.5f, e2 = a2 * 0.5f, e3 = a3 * 0.5f;
@@ -204,7 +242,7 @@ extern "C" {
 
 // Launch the VALU kernel of `kind` (enum Kind) on `blocks` workgroups of 256 threads, each lane
 // issuing iters x 8 instructions (kind 6: iters x 54; kinds 10 and 11: iters x 48; kind 12:
-// iters x 32).  out: blocks x 256 floats; stamps: blocks x 4 u64.  Returns
+// iters x 32; kind 13: iters x 40).  out: blocks x 256 floats; stamps: blocks x 4 u64.  Returns
 // 0, 1 for a bad argument, 2 if the launch was rejected.
 int ub_valu_launch(int kind, int blocks, int iters, float *out, unsigned long long *stamps, void *stream) {
     if (kind < 0 || kind >= K_NKIND || blocks <= 0 || iters < 0 || !out || !stamps) return 1;
@@ -214,7 +252,8 @@ int ub_valu_launch(int kind, int blocks, int iters, float *out, unsigned long lo
                        (const void *)&ub_valu<K_MIX>,        (const void *)&ub_valu<K_FMA_CHAIN1>,
                        (const void *)&ub_valu<K_FMA_CHAIN2>, (const void *)&ub_valu<K_EXP_CHAIN1>,
                        (const void *)&ub_valu<K_MIX_INDEP>,  (const void *)&ub_valu<K_MIX_NEAR>,
-                       (const void *)&ub_valu<K_MIX_INDEP3>};
+                       (const void *)&ub_valu<K_MIX_INDEP3>, (const void *)&ub_valu<K_MIX_INDEP19>,
+                       (const void *)&ub_valu<K_PERMLANE32>, (const void *)&ub_valu<K_PERMLANE16>};
     float s = 1e-6f;
     void *args[] = {&out, &stamps, &iters, &s};
     return hipLaunchKernel(k[kind], dim3(blocks), dim3(256), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 2;

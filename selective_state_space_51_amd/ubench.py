@@ -19,10 +19,11 @@ import sys
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libselscan_ubench.so")
 KINDS = ["fma", "mul", "exp", "fma_sgpr", "dpp_add", "rcp", "mix_5fma_1exp", "fma_chain1", "fma_chain2", "exp_chain1",
-         "exp_fma_1to5_independent", "exp_fma_1to5_exp_read_next", "exp_fma_1to3_independent"]
+         "exp_fma_1to5_independent", "exp_fma_1to5_exp_read_next", "exp_fma_1to3_independent",
+         "exp_fma_1to19_independent", "permlane32_swap", "permlane16_swap"]
 # wave-instructions per loop iteration of each form
 PER_ITER = {"mix_5fma_1exp": 54, "exp_fma_1to5_independent": 48, "exp_fma_1to5_exp_read_next": 48,
-            "exp_fma_1to3_independent": 32}
+            "exp_fma_1to3_independent": 32, "exp_fma_1to19_independent": 40}
 N_CU = 256
 REALTIME_HZ = 100e6  # s_memrealtime counts a constant 100 MHz clock
 

@@ -32,6 +32,23 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, name)
 
 
+def test_diagnostic_libraries_export_their_entry_points():
+    # the phase-clock build is the scan library plus two readers of its record; the production
+    # library carries neither the readers nor the record
+    import os
+    pkg = os.path.dirname(os.path.abspath(S.__file__))
+    phases = os.path.join(pkg, "libselscan_phases.so")
+    ubench = os.path.join(pkg, "libselscan_ubench.so")
+    nm = lambda path: {line.split()[-1] for line in subprocess.run(
+        ["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout.splitlines()
+        if " T " in line}
+    got = nm(phases)
+    assert {"selscan_bwd_phase_read", "selscan_bwd_phase_clear"} <= got
+    assert set(S.header_functions()) <= got
+    assert not any("phase" in name for name in nm(S.LIB_PATH))
+    assert {"ub_valu_launch", "ub_read_launch", "ub_copy_launch"} <= nm(ubench)
+
+
 def test_version_and_status_strings():
     assert S.abi_version() == 1
     for code in range(8):
