@@ -75,6 +75,17 @@ def test_workload_full_size_sampled(idx):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("idx,ov", [(3, dict(batch=129, seqlen=100, dim=264)), (1, dict(batch=129, seqlen=150, dim=264))],
+                         ids=["bidir_b129_L100_D264", "selscan_b129_L150_D264"])
+def test_one_chunk_many_ragged_tiles(idx, ov):
+    """One-chunk sequences (13 steps per lane) over 129 x 17 channel tiles, each batch row ending
+    in an 8-channel tile: sampled channels on both sides of tile boundaries, every batch row."""
+    w = W.WORKLOADS[idx]
+    _say("one chunk, ragged tiles", w.name, ov)
+    inp = W.generate(w, **ov)
+    _check(w.kind, w, inp, channels=[0, 1, 15, 16, 17, 31, 32, 255, 256, 263])
+
+
 @pytest.mark.parametrize("variant", ["zoh", "softplus"])
 def test_benchmark_shape_variants_sampled(variant):
     """The Mamba-1.4B-layer shape (batch 2 x L 65536 x D 4096, bf16) with the zero-order-hold Bbar,
