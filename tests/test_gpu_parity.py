@@ -951,3 +951,41 @@ def test_split_equals_sequential(kind, H, Wd, win):
     assert torch.equal(y_split, y_seq)
     for k in g_split:
         assert torch.equal(g_split[k], g_seq[k]), k
+
+
+_OPS = {"selscan": "SELSCAN_OP_FWD", "bidir": "SELSCAN_OP_BIDIR", "ss2d": "SELSCAN_OP_SS2D",
+        "local_ss2d": "SELSCAN_OP_LOCAL_SS2D"}
+
+
+@pytest.mark.parametrize("idx,ov", [(1, dict(batch=2, seqlen=300, dim=1536)), (3, dict(batch=4, seqlen=197, dim=768)),
+                                    (4, dict(batch=2, dim=64))], ids=["selscan", "bidir", "ss2d_split"])
+def test_clocked_forward(idx, ov):
+    """selscan_scan_fwd_clocked returns the forward's y bit for bit, and every workgroup of its
+    grid stamps an end after its start on both counters, at a shader clock between 0.5 and 3 GHz
+    (the 100 MHz real-time counter against s_memtime)."""
+    import torch
+
+    import selective_state_space_51_amd as S
+    w = W.WORKLOADS[idx]
+    _say("clocked", w.name, ov)
+    inp = W.generate(w, **ov)
+    dev = lambda k, dt=w.dtype: PT.to_dev(inp[k], dt)
+    x, delta, A, B, C, D, z = dev("x"), dev("delta"), dev("A", "f32"), dev("B"), dev("C"), dev("D", "f32"), None
+    if inp.get("z") is not None:
+        z = dev("z")
+    op = getattr(S, _OPS[w.kind])
+    geo = dict(H=w.H or 0, W=w.W or 0, window=w.window or 0)
+    y = S.selscan_scan_fwd(op, x, delta, A, B, C, D=D, z=z, **geo)
+    nb = S.selscan_clock_stamps_bytes(op, x.shape[0], x.shape[-1])
+    stamps = torch.zeros(nb // 8, dtype=torch.int64, device="cuda")
+    yc = S.selscan_scan_fwd_clocked(op, x, delta, A, B, C, stamps, D=D, z=z, **geo)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                       yc.view(torch.int16) if yc.dtype == torch.bfloat16 else yc)
+    st = stamps.view(-1, 4).cpu().numpy().astype(np.float64)
+    used = st[:, 3] > 0
+    assert used.sum() >= 1
+    st = st[used]
+    assert np.all(st[:, 1] > st[:, 0]) and np.all(st[:, 3] > st[:, 2])
+    mhz = (st[:, 1] - st[:, 0]).sum() / ((st[:, 3] - st[:, 2]).sum() / 1e8) / 1e6
+    assert 500 < mhz < 3000, mhz
