@@ -145,37 +145,11 @@ __device__ __forceinline__ void rows4_sum(const float p[kK], float out[4]) {
     }
 }
 
-// Per-wave shader-clock cycles in each phase of the backward's chunk loop: 0 staging (loads and
-// their commit to LDS), 1 prologue, 2 state loop outside its barriers, 3 and 4 the waits at its
-// two barriers, 5 output; 6 the whole kernel.  Compiled in only for the diagnostic library
-// (SELSCAN_PHASE_CLOCKS, libselscan_phases.so); otherwise every call is empty.
 #ifdef SELSCAN_PHASE_CLOCKS
-constexpr int kPhaseWaves = 1 << 14;
+// per-wave phase clocks of the backward (diagnostic library only): 0 staging (loads and their
+// commit to LDS), 1 prologue, 2 state loop outside its barriers, 3 and 4 the waits at its two
+// barriers, 5 output
 __device__ unsigned long long g_bwd_phase[kPhaseWaves * 8];
-struct PhaseClock {
-    unsigned long long acc[6] = {0, 0, 0, 0, 0, 0}, t = 0, t0 = __builtin_amdgcn_s_memtime();
-    __device__ void mark() { t = __builtin_amdgcn_s_memtime(); }
-    __device__ void add(int i) {
-        const unsigned long long n = __builtin_amdgcn_s_memtime();
-        acc[i] += n - t;
-        t = n;
-    }
-    __device__ void finish(int wave_id, int lane) {
-        const unsigned long long end = __builtin_amdgcn_s_memtime();
-        if (lane == 0 && wave_id < kPhaseWaves) {
-#pragma unroll
-            for (int i = 0; i < 6; ++i) g_bwd_phase[wave_id * 8 + i] = acc[i];
-            g_bwd_phase[wave_id * 8 + 6] = end - t0;
-            g_bwd_phase[wave_id * 8 + 7] = 1;
-        }
-    }
-};
-#else
-struct PhaseClock {
-    __device__ void mark() {}
-    __device__ void add(int) {}
-    __device__ void finish(int, int) {}
-};
 #endif
 
 __device__ __forceinline__ float sigmoidf_(float w) { return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e)); }
@@ -667,7 +641,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void selscan_bwd_chunk
         }
     }
   }
-    clk.finish(blockIdx.x * 4 + wave, lane);
+#ifdef SELSCAN_PHASE_CLOCKS
+    clk.finish(g_bwd_phase, blockIdx.x * 4 + wave, lane);
+#endif
 }
 
 struct BwdReduceParams {

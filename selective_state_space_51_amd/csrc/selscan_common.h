@@ -197,6 +197,38 @@ __device__ __forceinline__ int64_t visit(const P &p, int k, int64_t l) {
 // barrier between directions (where the partial sums change hands) stays a full one.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Per-wave shader-clock cycles spent in each phase of a kernel's chunk loop, summed over the
+// chunks: phase i's time runs from the previous add() (or mark()) to add(i).  Compiled in only
+// for the diagnostic library (SELSCAN_PHASE_CLOCKS, libselscan_phases.so), which writes them,
+// with the whole kernel's cycles, to a per-kernel record; otherwise every call is empty.
+#ifdef SELSCAN_PHASE_CLOCKS
+constexpr int kPhaseWaves = 1 << 14;  // waves the record holds: 8 u64 each
+struct PhaseClock {
+    unsigned long long acc[6] = {0, 0, 0, 0, 0, 0}, t = 0, t0 = __builtin_amdgcn_s_memtime();
+    __device__ void mark() { t = __builtin_amdgcn_s_memtime(); }
+    __device__ void add(int i) {
+        const unsigned long long n = __builtin_amdgcn_s_memtime();
+        acc[i] += n - t;
+        t = n;
+    }
+    // lane 0 of the wave writes phases 0-5, the whole kernel, and 1 (written)
+    __device__ void finish(unsigned long long *rec, int wave_id, int lane) {
+        const unsigned long long end = __builtin_amdgcn_s_memtime();
+        if (lane == 0 && wave_id < kPhaseWaves) {
+#pragma unroll
+            for (int i = 0; i < 6; ++i) rec[wave_id * 8 + i] = acc[i];
+            rec[wave_id * 8 + 6] = end - t0;
+            rec[wave_id * 8 + 7] = 1;
+        }
+    }
+};
+#else
+struct PhaseClock {
+    __device__ void mark() {}
+    __device__ void add(int) {}
+};
+#endif
+
 // softplus(w) = log(1 + e^w) = max(w, 0) + log1p(t), t = e^-|w|, on v_exp_f32 and v_log_f32.
 // log1p(t) is taken as ln(u) t / (u - 1) with u = 1 + t rounded to fp32 (Kahan's form: the
 // rounding error of u cancels between the logarithm and the denominator), and as t itself once

@@ -232,6 +232,14 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
 // and every phase outside the state loop runs above both.
 // Zero-order-hold input factor: zoh_phi (selscan_common.h).
 
+#ifdef SELSCAN_PHASE_CLOCKS
+// per-wave phase clocks of the forward (diagnostic library only): 0 staging (the barrier before,
+// the wait for the chunk's loads, their commit to LDS, the barrier after), 1 the issue of the
+// gate's and the next chunk's loads, 2 the prologue's arithmetic, 3 state loop, 4 the y tile's
+// LDS writes and the barrier after them, 5 the output stores
+__device__ unsigned long long g_fwd_phase[kPhaseWaves * 8];
+#endif
+
 // KK: scan steps per lane, 16 (chunks of 256 steps) or, for sequences of at most 16 KK steps,
 // fewer (the sequence is one chunk): the LDS tiles keep 16 slots per lane, and slot 16 l + j
 // holds chunk step KK l + j for j < KK (the slots past KK are left out everywhere).
@@ -264,6 +272,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     float *Db = (float *)(smem + S::kDb);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l = lane & 15;
+    PhaseClock clk;
     const int cl = wave * 4 + (lane >> 4);     // this lane's channel within the tile
     // consecutive channel tiles on one XCD: workgroups are dealt round-robin over 8 XCDs
     const int G = gridDim.x, bi = blockIdx.x, q8 = G >> 3;
@@ -431,40 +440,74 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             lds_barrier();  // the previous chunk is done with every tile
             commit();
             lds_barrier();
+            clk.add(0);
             if (p.ckpt) {
                 // the carry entering this chunk, kept for the backward pass
                 const int ch = tid / kN, n = tid % kN;
                 if (c0 + ch < dim)
                     p.ckpt[((((int64_t)k * p.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] = Cy[tid];
             }
-            // gate input for this chunk's output items, then the next chunk's inputs: in flight
-            // while this chunk computes
+            // gate input for this chunk's output items, then the next chunk's inputs, in flight while
+            // this chunk computes.  A single-direction scan with 16 steps per lane issues them after
+            // the state loop's first state pair: issued right after the chunk-start barrier, every
+            // wave of the workgroup queued its loads at once and waited on the memory pipeline for
+            // ~11 % of the kernel; one state pair later the waves have drifted apart.  The other
+            // forms issue them here, as written out below: they measured no gain from the later
+            // issue, and even calling the same code through the lambda here changes their register
+            // allocation (more spills, Vim 2 % slower).
             const bool last = k == p.ndir - 1 && !split;
             float *wsk = split ? p.ws + k * tok : p.ws;  // this direction's partial rows (split) or the running sum
             Raw8<T> zr[2];  // read only where it was loaded
             int64_t ooff[2] = {0, 0};
+            constexpr bool mid_issue = KIND == SELSCAN_OP_FWD && KK == kK && sizeof(T) == 2 && !ZOH;
+            auto issue_loads = [&]() {
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int64_t s = s0 + cstep(so + 128 * r);
-                if constexpr (fast) {
-                    ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
-                    if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
-                } else {
-                    zr[r] = Raw8<T>{};
-                    if (nv > 0 && ((so + 128 * r) & 15) < KK && s < L) {
+                for (int r = 0; r < 2; ++r) {
+                    const int64_t s = s0 + cstep(so + 128 * r);
+                    if constexpr (fast) {
                         ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
-                        if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                        if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
+                    } else {
+                        zr[r] = Raw8<T>{};
+                        if (nv > 0 && ((so + 128 * r) & 15) < KK && s < L) {
+                            ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+                            if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                        }
                     }
                 }
-            }
-            if constexpr (fast || !multi) {
-                if (q + 1 < nchunks) fetch(k, q + 1, fast_c);
-            } else {
-                // after a direction's last chunk, the next direction's first
-                const bool next_dir = q + 1 == nchunks;
-                if (!next_dir || k + 1 < k_end) fetch(next_dir ? k + 1 : k, next_dir ? 0 : q + 1, fast_c);
+                if constexpr (fast || !multi) {
+                    if (q + 1 < nchunks) fetch(k, q + 1, fast_c);
+                } else {
+                    // after a direction's last chunk, the next direction's first
+                    const bool next_dir = q + 1 == nchunks;
+                    if (!next_dir || k + 1 < k_end) fetch(next_dir ? k + 1 : k, next_dir ? 0 : q + 1, fast_c);
+                }
+            };
+            if constexpr (!mid_issue) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int64_t s = s0 + cstep(so + 128 * r);
+                    if constexpr (fast) {
+                        ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+                        if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
+                    } else {
+                        zr[r] = Raw8<T>{};
+                        if (nv > 0 && ((so + 128 * r) & 15) < KK && s < L) {
+                            ooff[r] = (rowb + visit<KIND>(p, k, s)) * dim + cg;
+                            if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
+                        }
+                    }
+                }
+                if constexpr (fast || !multi) {
+                    if (q + 1 < nchunks) fetch(k, q + 1, fast_c);
+                } else {
+                    // after a direction's last chunk, the next direction's first
+                    const bool next_dir = q + 1 == nchunks;
+                    if (!next_dir || k + 1 < k_end) fetch(next_dir ? k + 1 : k, next_dir ? 0 : q + 1, fast_c);
+                }
             }
 
+            clk.add(1);
             // ---- this lane's KK steps of its channel
             const int64_t rem = L - (s0 + l * KK);
             const int lim = !cvalid ? 0 : (rem <= 0 ? 0 : (rem >= KK ? KK : (int)rem));
@@ -517,10 +560,14 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             }
             if (qq & 1) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
+            clk.add(2);
             const float *Bc = Bs + 4 * l;
             const float *Cc = Cs + 4 * l;
 #pragma unroll 1
             for (int n = 0; n < kN; n += 2) {
+                if constexpr (mid_issue) {
+                    if (n == 2) issue_loads();
+                }
                 const float2 a2 = *(const float2 *)&As[cl * kN + n];
                 constexpr int NP = (KK + 3) / 4;  // 4-step pieces of a lane's slots that hold steps
                 float e0[KK], u0[KK], e1[KK], u1[KK];
@@ -574,6 +621,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 }
             }
             __builtin_amdgcn_s_setprio(2);
+            clk.add(3);
             // direction 1 of an LDS-summed pair writes its tile into the x/delta space
             const bool y_in_xd = lds_sum && k == 1;
             if constexpr (!S::kYOwn) lds_barrier();  // x/delta tiles fully read before y reuses their space
@@ -588,6 +636,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 *(float4 *)&yw[cl * kFP + pc * (kLPR * 4) + 4 * l] = make_float4(q4[0], q4[1], q4[2], q4[3]);
             }
             lds_barrier();
+            clk.add(4);
             if (lds_sum && k == 0) return;  // direction 0's tile waits in LDS for direction 1
             // ---- leave: add earlier directions, gate, store y (or keep the partial sum)
 #pragma unroll
@@ -642,8 +691,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     }
                 }
             }
+            clk.add(5);
         };
         if (!multi || k == k_begin) fetch(k, 0, BoolC<false>{});
+        clk.mark();
         const int nfast = tile_fast && KK == kK ? (int)(L / CHK) - 1 : 0;
         int q = 0;
         for (; q < nfast; ++q, ++qq) chunk(q, BoolC<true>{});
@@ -662,6 +713,9 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         s[1] = __builtin_amdgcn_s_memtime();
         s[3] = __builtin_amdgcn_s_memrealtime();
     }
+#ifdef SELSCAN_PHASE_CLOCKS
+    clk.finish(g_fwd_phase, blockIdx.x * 4 + wave, lane);
+#endif
 }
 
 // Split launches: y = (((o_0 + o_1) + o_2) + o_3) * silu(z) from the per-direction partial rows
@@ -871,6 +925,27 @@ int selscan_scan_fwd_clocked(int op, const void *x, const void *delta, const flo
     p.stamps = stamps;
     return run(p, dstate, workspace_bytes, stream);
 }
+
+#ifdef SELSCAN_PHASE_CLOCKS
+// Diagnostic library only: copy the phase clocks of the last forward launch (8 u64 per wave,
+// wave = 4 x workgroup + wave in workgroup: phases 0-5, whole kernel, 1 if written) to
+// `host`, which holds `count` u64.  Returns 0, 1 if count is larger than the record, 2 on a HIP
+// error.
+int selscan_fwd_phase_read(unsigned long long *host, size_t count) {
+    if (!host || count > (size_t)kPhaseWaves * 8) return 1;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_fwd_phase), count * sizeof(unsigned long long), 0,
+                               hipMemcpyDeviceToHost) == hipSuccess ? 0 : 2;
+}
+// Clear the record (host-synchronous).
+int selscan_fwd_phase_clear(void) {
+    static const unsigned long long zeros[1024] = {};
+    for (int i = 0; i < kPhaseWaves * 8; i += 1024)
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_fwd_phase), zeros, sizeof(zeros), i * sizeof(unsigned long long),
+                              hipMemcpyHostToDevice) != hipSuccess)
+            return 2;
+    return 0;
+}
+#endif
 
 size_t selscan_clock_stamps_bytes(int op, int64_t batch, int64_t dim) {
     const int ndir = ndir_of(op);

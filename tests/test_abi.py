@@ -43,7 +43,8 @@ def test_diagnostic_libraries_export_their_entry_points():
         ["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout.splitlines()
         if " T " in line}
     got = nm(phases)
-    assert {"selscan_bwd_phase_read", "selscan_bwd_phase_clear"} <= got
+    assert {"selscan_bwd_phase_read", "selscan_bwd_phase_clear", "selscan_fwd_phase_read",
+            "selscan_fwd_phase_clear"} <= got
     assert set(S.header_functions()) <= got
     assert not any("phase" in name for name in nm(S.LIB_PATH))
     assert {"ub_valu_launch", "ub_read_launch", "ub_copy_launch"} <= nm(ubench)
