@@ -437,7 +437,9 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             constexpr bool fast = decltype(fast_c)::value;
             const int64_t s0 = (int64_t)q * CHK;
             __builtin_amdgcn_s_setprio(2);
-            lds_barrier();  // the previous chunk is done with every tile
+            // the previous chunk is done with every tile (a one-chunk sequence's only chunk of a
+            // direction follows the direction's opening barrier, which covers this)
+            if constexpr (KK == kK) lds_barrier();
             commit();
             lds_barrier();
             clk.add(0);
