@@ -637,6 +637,18 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 for (int i = 0; i < 4; ++i) q4[i] = 4 * pc + i < KK ? yv[4 * pc + i] : 0.f;
                 *(float4 *)&yw[cl * kFP + pc * (kLPR * 4) + 4 * l] = make_float4(q4[0], q4[1], q4[2], q4[3]);
             }
+            // the gate of this chunk's output items, ahead of the barrier, with 16 steps per lane: a
+            // wave that reaches it early computes its gates while the others finish their state
+            // loops (the one-chunk form measured slower with it, and gates after the barrier)
+            constexpr bool early_gate = KK == kK;
+            float gz[2][8];
+            if (early_gate && last && z) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) gz[r][e] = silu(raw_f32(zr[r], e));
+                }
+            }
             lds_barrier();
             clk.add(4);
             if (lds_sum && k == 0) return;  // direction 0's tile waits in LDS for direction 1
@@ -657,7 +669,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                         // the gated and the ungated store are separate calls: no register copies
                         // where the two forms would join
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                        for (int e = 0; e < 8; ++e) v[e] *= early_gate ? gz[r][e] : silu(raw_f32(zr[r], e));
                         store8(y + ooff[r], 8, true, v);
                     } else if (last) {
                         store8(y + ooff[r], 8, true, v);
@@ -685,7 +697,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     if (last) {
                         if (z) {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] *= silu(raw_f32(zr[r], e));
+                            for (int e = 0; e < 8; ++e) v[e] *= early_gate ? gz[r][e] : silu(raw_f32(zr[r], e));
                         }
                         store8(y + ooff[r], nv, vec, v);
                     } else {
