@@ -166,8 +166,10 @@ struct Params {
 // Shared-memory layout of a workgroup (16 channels), per chunk of kCH steps.  In every tile
 // row the 16 steps of a lane are stored as 16-byte pieces: piece q of lane l sits at
 // q * (16 lanes * piece) + l * piece, so that one 16-byte read by each of the 16 lanes of a
-// row covers 256 contiguous bytes (no bank conflicts).
-template <typename T>
+// row covers 256 contiguous bytes (no bank conflicts).  The scan reads A, D and bias of the
+// current direction from one slot; those of a workgroup's later directions (up to KD - 1) wait
+// in slots of their own.
+template <typename T, int KD>
 struct Lds {
     static constexpr int kCT = kTC;                                  // channels per tile
     static constexpr int kV = 16 / (int)sizeof(T);                    // io elements per piece
@@ -185,7 +187,9 @@ struct Lds {
     static constexpr int kA = kC + kN * kFP * 4;                      // A*log2e [ch][state]
     static constexpr int kCarry = kA + kCT * kN * 4;                  // chunk carry [ch][state]
     static constexpr int kDb = kCarry + kCT * kN * 4;                 // D, bias [ch][2]
-    static constexpr int kBytes = kDb + kCT * 8;
+    static constexpr int kAx = kDb + kCT * 8;                         // later directions' A, D, bias
+    static constexpr int kDbx = kAx + (KD - 1) * kCT * kN * 4;
+    static constexpr int kBytes = kDbx + (KD - 1) * kCT * 8;
     // position of chunk step s in an io tile row
     __device__ static int xpos(int s) { return ((s & 15) / kV) * (kLPR * kV) + (s >> 4) * kV + (s % kV); }
 };
@@ -245,7 +249,8 @@ __device__ unsigned long long g_fwd_phase[kPhaseWaves * 8];
 // holds chunk step KK l + j for j < KK (the slots past KK are left out everywhere).
 template <typename T, int KIND, bool ZOH, int KK>
 __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
-    using S = Lds<T>;
+    constexpr int KD = KIND == SELSCAN_OP_FWD ? 1 : KIND == SELSCAN_OP_BIDIR ? 2 : 4;  // directions
+    using S = Lds<T, KD>;
     constexpr int CT = kTC;
     constexpr int NW = kN * (int)sizeof(T) / 4;  // dwords of one 16-value B or C row
     static_assert(CT * kN == 256, "one (channel, state) carry entry per thread");
@@ -312,94 +317,124 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
     const int so = 16 * ((lane >> 2) & 7) + 4 * wave + (lane & 3);
 
     int qq = 0;  // chunks done over all directions (priority parity)
-    const int k_begin = split ? tile_all / ntiles : 0, k_end = split ? k_begin + 1 : p.ndir;
+    const int k_begin = split ? tile_all / ntiles : 0, k_end = split ? k_begin + 1 : multi ? p.ndir : 1;
+    // A, D and bias of every direction of the workgroup, loaded once, in flight together with the
+    // first chunk's loads; a later direction copies its own from LDS to the scan's slot at its
+    // start instead of waiting on memory there.  The first chunk's fetch sits outside the
+    // direction loop too: a single-direction kernel then has a loop of one known iteration,
+    // and the compiler keeps fewer scalars alive (fewer spills into vector lanes).
+    float av[KD], dv[KD], bv[KD];
+    {
+        const int ch = tid / kN, n = tid % kN;
+        const int64_t cc = c0 + ch < dim ? c0 + ch : 0, cd = c0 + tid < dim ? c0 + tid : 0;
+#pragma unroll
+        for (int j = 0; j < KD; ++j) {
+            const int k = k_begin + j;
+            av[j] = dv[j] = bv[j] = 0.f;
+            if (k < k_end && nchunks > 0) {
+                av[j] = p.A[(k * dim + cc) * kN + n];
+                if (tid < CT && p.D) dv[j] = p.D[k * dim + cd];
+                if (tid < CT && p.bias) bv[j] = p.bias[k * dim + cd];
+            }
+        }
+    }
     // global -> registers for one chunk, prefetched one chunk ahead (across directions too)
     Raw8<T> px0, px1, pd0, pd1;
     uint32_t pbc[2][NW];  // raw B and C values of one chunk step
-    for (int k = k_begin; k < k_end; ++k) {
-        const T *dlk = (const T *)p.delta + k * tok;
-        const T *Bkk = (const T *)p.B + k * bcn;
-        const T *Ckk = (const T *)p.C + k * bcn;
-        // the previous direction is done with the parameter tiles, and its stores of the partial
-        // sums (which other waves read back in this direction) are complete: a full barrier
-        __syncthreads();
-        for (int i = tid; i < CT * kN; i += 256) {
-            const int ch = i / kN, n = i % kN;
-            const int64_t cc = c0 + ch < dim ? c0 + ch : 0;
-            if (nchunks > 0) As[i] = p.A[(k * dim + cc) * kN + n] * kLog2e;
-            // the carry into the first chunk: the caller's initial state, else zero
-            Cy[i] = p.h0 && c0 + ch < dim ? p.h0[((int64_t)b * dim + c0 + ch) * kN + n] : 0.f;
-        }
-        for (int i = tid; i < CT && nchunks > 0; i += 256) {
-            const int64_t cc = c0 + i < dim ? c0 + i : 0;
-            Db[2 * i] = p.D ? p.D[k * dim + cc] : 0.f;
-            Db[2 * i + 1] = p.bias ? p.bias[k * dim + cc] : 0.f;
-        }
-
-        // chunk q of direction kk
-        auto fetch = [&](int kk, int q, auto fast_c) {
-            const T *dl = multi ? (const T *)p.delta + kk * tok : dlk;
-            const T *Bk = multi ? (const T *)p.B + kk * bcn : Bkk;
-            const T *Ck = multi ? (const T *)p.C + kk * bcn : Ckk;
-            const int64_t s0 = (int64_t)q * CHK;
-            const int64_t sa = s0 + cstep(2 * pp), sbb = sa + 1, s = s0 + cstep(sb);
-            // slots past KK in a lane hold no step
-            const bool va = ((2 * pp) & 15) < KK, vb = ((2 * pp) & 15) + 1 < KK, vs = (sb & 15) < KK;
-            if constexpr (decltype(fast_c)::value) {
-                const int64_t oa = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
-                const int64_t ob = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
+    // chunk q of direction kk
+    auto fetch = [&](int kk, int q, auto fast_c) {
+        const int64_t kt = multi ? kk : 0;
+        const T *dl = (const T *)p.delta + kt * tok;
+        const T *Bk = (const T *)p.B + kt * bcn;
+        const T *Ck = (const T *)p.C + kt * bcn;
+        const int64_t s0 = (int64_t)q * CHK;
+        const int64_t sa = s0 + cstep(2 * pp), sbb = sa + 1, s = s0 + cstep(sb);
+        // slots past KK in a lane hold no step
+        const bool va = ((2 * pp) & 15) < KK, vb = ((2 * pp) & 15) + 1 < KK, vs = (sb & 15) < KK;
+        if constexpr (decltype(fast_c)::value) {
+            const int64_t oa = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
+            const int64_t ob = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
+            const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
+            px0 = load_raw8(x + oa, 8, true);
+            pd0 = load_raw8(dl + oa, 8, true);
+            px1 = load_raw8(x + ob, 8, true);
+            pd1 = load_raw8(dl + ob, 8, true);
+#pragma unroll
+            for (int h = 0; h < NW; h += 4) {
+                const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
+                pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+            }
+        } else {
+            px0 = px1 = pd0 = pd1 = Raw8<T>{};
+            if (nv > 0 && va && sa < L) {
+                const int64_t off = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
+                px0 = load_raw8(x + off, nv, vec);
+                pd0 = load_raw8(dl + off, nv, vec);
+            }
+            if (nv > 0 && vb && sbb < L) {
+                const int64_t off = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
+                px1 = load_raw8(x + off, nv, vec);
+                pd1 = load_raw8(dl + off, nv, vec);
+            }
+#pragma unroll
+            for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
+            if (vs && s < L) {
                 const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
-                px0 = load_raw8(x + oa, 8, true);
-                pd0 = load_raw8(dl + oa, 8, true);
-                px1 = load_raw8(x + ob, 8, true);
-                pd1 = load_raw8(dl + ob, 8, true);
+                if (p.vecbc) {
 #pragma unroll
-                for (int h = 0; h < NW; h += 4) {
-                    const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
-                    const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
-                    pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
-                    pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
-                }
-            } else {
-                px0 = px1 = pd0 = pd1 = Raw8<T>{};
-                if (nv > 0 && va && sa < L) {
-                    const int64_t off = (rowb + visit<KIND>(p, kk, sa)) * dim + cg;
-                    px0 = load_raw8(x + off, nv, vec);
-                    pd0 = load_raw8(dl + off, nv, vec);
-                }
-                if (nv > 0 && vb && sbb < L) {
-                    const int64_t off = (rowb + visit<KIND>(p, kk, sbb)) * dim + cg;
-                    px1 = load_raw8(x + off, nv, vec);
-                    pd1 = load_raw8(dl + off, nv, vec);
-                }
+                    for (int h = 0; h < NW; h += 4) {
+                        const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
+                        const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
+                        pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
+                        pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
+                    }
+                } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                for (int h = 0; h < NW; ++h) pbc[0][h] = pbc[1][h] = 0u;
-                if (vs && s < L) {
-                    const int64_t ro = (rowb + visit<KIND>(p, kk, s)) * kN;
-                    if (p.vecbc) {
+                    for (int h = 0; h < NW; ++h) {
+                        pbc[0][h] = (uint32_t)Bk[ro + 2 * h] | ((uint32_t)Bk[ro + 2 * h + 1] << 16);
+                        pbc[1][h] = (uint32_t)Ck[ro + 2 * h] | ((uint32_t)Ck[ro + 2 * h + 1] << 16);
+                    }
+                } else {
 #pragma unroll
-                        for (int h = 0; h < NW; h += 4) {
-                            const uint4 qb = *(const uint4 *)((const uint32_t *)(Bk + ro) + h);
-                            const uint4 qc = *(const uint4 *)((const uint32_t *)(Ck + ro) + h);
-                            pbc[0][h] = qb.x, pbc[0][h + 1] = qb.y, pbc[0][h + 2] = qb.z, pbc[0][h + 3] = qb.w;
-                            pbc[1][h] = qc.x, pbc[1][h + 1] = qc.y, pbc[1][h + 2] = qc.z, pbc[1][h + 3] = qc.w;
-                        }
-                    } else if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                        for (int h = 0; h < NW; ++h) {
-                            pbc[0][h] = (uint32_t)Bk[ro + 2 * h] | ((uint32_t)Bk[ro + 2 * h + 1] << 16);
-                            pbc[1][h] = (uint32_t)Ck[ro + 2 * h] | ((uint32_t)Ck[ro + 2 * h + 1] << 16);
-                        }
-                    } else {
-#pragma unroll
-                        for (int h = 0; h < NW; ++h) {
-                            pbc[0][h] = __float_as_uint(Bk[ro + h]);
-                            pbc[1][h] = __float_as_uint(Ck[ro + h]);
-                        }
+                    for (int h = 0; h < NW; ++h) {
+                        pbc[0][h] = __float_as_uint(Bk[ro + h]);
+                        pbc[1][h] = __float_as_uint(Ck[ro + h]);
                     }
                 }
             }
-        };
+        }
+    };
+    fetch(k_begin, 0, BoolC<false>{});
+    // read in the first direction's first chunk, after the barrier that follows its staging
+#pragma unroll
+    for (int j = 0; j < KD; ++j) {
+        if (k_begin + j >= k_end) continue;
+        float *a = j == 0 ? As : (float *)(smem + S::kAx) + (j - 1) * (CT * kN);
+        float *d = j == 0 ? Db : (float *)(smem + S::kDbx) + (j - 1) * (2 * CT);
+        a[tid] = av[j] * kLog2e;
+        if (tid < CT) {
+            d[2 * tid] = dv[j];
+            d[2 * tid + 1] = bv[j];
+        }
+    }
+    for (int k = k_begin; k < k_end; ++k) {
+        // the previous direction is done with the parameter tiles and the carry, and its stores
+        // of the partial sums (which other waves read back in this direction) are complete: a
+        // full barrier
+        __syncthreads();
+        if (k > k_begin) {
+            const int j = k - k_begin - 1;
+            As[tid] = ((const float *)(smem + S::kAx))[j * (CT * kN) + tid];
+            if (tid < 2 * CT) Db[tid] = ((const float *)(smem + S::kDbx))[j * (2 * CT) + tid];
+        }
+        for (int i = tid; i < CT * kN; i += 256) {
+            const int ch = i / kN, n = i % kN;
+            // the carry into the first chunk: the caller's initial state, else zero
+            Cy[i] = p.h0 && c0 + ch < dim ? p.h0[((int64_t)b * dim + c0 + ch) * kN + n] : 0.f;
+        }
+
         // registers -> LDS
         auto commit = [&]() {
             const int si = S::xpos(2 * pp);  // steps 2p and 2p+1 are adjacent in a piece
@@ -707,7 +742,6 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             }
             clk.add(5);
         };
-        if (!multi || k == k_begin) fetch(k, 0, BoolC<false>{});
         clk.mark();
         const int nfast = tile_fast && KK == kK ? (int)(L / CHK) - 1 : 0;
         int q = 0;
