@@ -106,7 +106,9 @@ FastDiv make_div(uint32_t d) {
     f.sh = s - 1;
     return f;
 }
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+// (F: a FastDiv in any address space)
+template <class F>
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, F &f) {
     return f.d <= 1 ? n : __umulhi(n, f.m) >> f.sh;
 }
 
