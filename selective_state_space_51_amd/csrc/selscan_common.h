@@ -191,6 +191,18 @@ __device__ __forceinline__ int64_t visit(const P &p, int k, int64_t l) {
     }
 }
 
+// The kernel's arguments (a P, the kernel's only parameter), read afresh from the argument
+// segment wherever this is called: the compiler keeps loaded arguments alive across the whole
+// kernel and spills them into vector lanes, while a read through an opaque segment pointer is
+// one scalar load at the use.
+template <class P>
+__device__ __forceinline__ const __attribute__((address_space(4))) P &fresh_args() {
+    using CP = const __attribute__((address_space(4))) P;
+    CP *pq = (CP *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pq));
+    return *pq;
+}
+
 // Workgroup barrier for LDS traffic: waits for this wave's LDS operations only.  A
 // __syncthreads would also wait for every global load and store the wave has in flight (its
 // release fence drains vmcnt), which stalls on stores issued just before the barrier and on

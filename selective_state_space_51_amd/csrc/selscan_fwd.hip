@@ -223,16 +223,6 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
         : "+v"(b0), "+v"(b1), "+v"(a0), "+v"(a1), "+v"(h0), "+v"(h1));
 }
 
-typedef const __attribute__((address_space(4))) Params CParams;
-// The kernel's arguments, read afresh from the argument segment wherever this is called: the
-// compiler keeps loaded arguments alive across the whole kernel, spilling them into vector
-// lanes, while a read through an opaque segment pointer is one scalar load at the use.
-__device__ __forceinline__ CParams &fresh_params() {
-    CParams *pq = (CParams *)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(pq));
-    return *pq;
-}
-
 // One workgroup: 4 waves, a tile of 16 channels of one batch row, every direction.
 //
 // Lane maps of the staging and output items (wave w, lane i of the wave) are chosen so that
@@ -481,11 +471,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
         // one chunk; FAST: a full chunk of a full tile whose successor is full too
         auto chunk = [&](int q, auto fast_c) {
             constexpr bool fast = decltype(fast_c)::value;
-            // (the windowed orders' index map reads four divisions: there, reading them afresh
-            // at every use spills more than it saves)
-            auto &pc = [&]() -> auto & {
+            // the arguments, read afresh in every chunk (fresh_args); not for the windowed orders,
+            // whose index map reads four divisions, where that spills more than it saves
+            auto &args = [&]() -> auto & {
                 if constexpr (KIND == SELSCAN_OP_LOCAL_SS2D) return p;
-                else return fresh_params();
+                else return fresh_args<Params>();
             }();
             const int64_t s0 = (int64_t)q * CHK;
             __builtin_amdgcn_s_setprio(2);
@@ -495,11 +485,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             commit();
             lds_barrier();
             clk.add(0);
-            if (pc.ckpt) {
+            if (args.ckpt) {
                 // the carry entering this chunk, kept for the backward pass
                 const int ch = tid / kN, n = tid % kN;
                 if (c0 + ch < dim)
-                    pc.ckpt[((((int64_t)k * pc.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] = Cy[tid];
+                    args.ckpt[((((int64_t)k * args.batch + b) * nchunks + q) * dim + c0 + ch) * kN + n] = Cy[tid];
             }
             // gate input for this chunk's output items, then the next chunk's inputs, in flight while
             // this chunk computes.  A single-direction scan with 16 steps per lane issues them after
@@ -509,8 +499,8 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             // forms issue them here, as written out below: they measured no gain from the later
             // issue, and even calling the same code through the lambda here changes their register
             // allocation (more spills, Vim 2 % slower).
-            const bool last = k == pc.ndir - 1 && !split;
-            float *wsk = split ? pc.ws + k * tok : pc.ws;  // this direction's partial rows (split) or the running sum
+            const bool last = k == args.ndir - 1 && !split;
+            float *wsk = split ? args.ws + k * tok : args.ws;  // this direction's partial rows (split) or the running sum
             Raw8<T> zr[2];  // read only where it was loaded
             int64_t ooff[2] = {0, 0};
             constexpr bool mid_issue = KIND == SELSCAN_OP_FWD && KK == kK && sizeof(T) == 2 && !ZOH;
@@ -519,12 +509,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 for (int r = 0; r < 2; ++r) {
                     const int64_t s = s0 + cstep(so + 128 * r);
                     if constexpr (fast) {
-                        ooff[r] = (rowb + visit<KIND>(pc, k, s)) * dim + cg;
+                        ooff[r] = (rowb + visit<KIND>(args, k, s)) * dim + cg;
                         if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
                     } else {
                         zr[r] = Raw8<T>{};
                         if (nv > 0 && ((so + 128 * r) & 15) < KK && s < L) {
-                            ooff[r] = (rowb + visit<KIND>(pc, k, s)) * dim + cg;
+                            ooff[r] = (rowb + visit<KIND>(args, k, s)) * dim + cg;
                             if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                         }
                     }
@@ -542,12 +532,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                 for (int r = 0; r < 2; ++r) {
                     const int64_t s = s0 + cstep(so + 128 * r);
                     if constexpr (fast) {
-                        ooff[r] = (rowb + visit<KIND>(pc, k, s)) * dim + cg;
+                        ooff[r] = (rowb + visit<KIND>(args, k, s)) * dim + cg;
                         if (last && z) zr[r] = load_raw8(z + ooff[r], 8, true);
                     } else {
                         zr[r] = Raw8<T>{};
                         if (nv > 0 && ((so + 128 * r) & 15) < KK && s < L) {
-                            ooff[r] = (rowb + visit<KIND>(pc, k, s)) * dim + cg;
+                            ooff[r] = (rowb + visit<KIND>(args, k, s)) * dim + cg;
                             if (last && z) zr[r] = load_raw8(z + ooff[r], nv, vec);
                         }
                     }
@@ -589,12 +579,12 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     }
                 }
                 // bias, then softplus, in place (one set of registers for every form)
-                if (pc.bias) {
+                if (args.bias) {
                     const float bias = Db[2 * cl + 1];
 #pragma unroll
                     for (int j = 0; j < KK; ++j) dt[j] += bias;
                 }
-                if (pc.softplus) {
+                if (args.softplus) {
 #pragma unroll
                     for (int j = 0; j < KK; ++j) dt[j] = softplus(dt[j]);
                 }
@@ -713,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
                     if (multi && k > 0 && !split) {
-                        load_f8(pc.ws + ooff[r], 8, true, wv);
+                        load_f8(args.ws + ooff[r], 8, true, wv);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] += wv[e];
                     }
@@ -740,7 +730,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) v[e] = yt[(8 * g + e) * kFP + fpos(sl)];
-                        if (multi && k > 0 && !split) load_f8(pc.ws + ooff[r], nv, vec, wv);
+                        if (multi && k > 0 && !split) load_f8(args.ws + ooff[r], nv, vec, wv);
                     }
                     if (multi && (y_in_xd || (k > 0 && !split))) {
 #pragma unroll
