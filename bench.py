@@ -364,7 +364,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the shader clock ramps up over the first ~10 launches after an idle moment (up to 15 %
+    # slower at first): the default warm-up covers it
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "conv", "conv_bwd"], default="fwd",
