@@ -10,7 +10,9 @@ five channels (both ends of the first tile, the middle, and the ragged last tile
 over the whole sequence; the backward's per-channel gradients (dx, ddelta, dz, dA, dD) on those
 channels; dB on the last 48 steps over all channels (the adjoint starts at the sequence end and
 dB does not involve the state) and dC on the first 48 steps (the state starts at zero there and
-dC does not involve the adjoint)."""
+dC does not involve the adjoint); and the bidirectional forward at the same size, whose second
+direction's delta starts 2.28e9 elements into its tensor and whose two directions' fp32 partial
+rows (a direction-split launch) are added by the merge kernel, on the same five channels."""
 import sys
 
 import numpy as np
@@ -29,12 +31,19 @@ def _say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
 
 
-@pytest.fixture(scope="module")
-def big():
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import selective_state_space_51_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def big():
+    import torch
     assert L * DIM > 1 << 31
     _say("large: drawing the blocks")
     g = W.generate_periodic(L, DIM, P)
@@ -118,3 +127,34 @@ def test_backward_past_2_32_partials(big):
     _say("large backward", {k: f"{v:.2e}" for k, v in errs.items()})
     for k, e in errs.items():
         assert e <= _bwd_tol("bf16", k), (k, e)
+
+
+def test_bidirectional_past_2_32_elements():
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    _say("large bidir: drawing the blocks")
+    g = W.generate_periodic(L, DIM, P, ndir=2, seed=W.SEED_BASE + 71)
+    n = L * DIM
+
+    def tile(block, k=1):  # [k, 1, L, DIM] (or [1, L, DIM]) on the device, flat element i = block[i % P]
+        b = PT.to_dev(block, "bf16")
+        t = b.repeat(-(-k * n // P))[:k * n]
+        return t.view(k, 1, L, DIM) if k > 1 else t.view(1, L, DIM)
+
+    x, z, dl = tile(g["x"]), tile(g["z"]), tile(g["delta"], 2)
+    B, C = PT.to_dev(g["B"], "bf16"), PT.to_dev(g["C"], "bf16")
+    A, D = PT.to_dev(g["A"], "f32"), PT.to_dev(g["D"], "f32")
+    y = S.selscan_bidir_fwd(x, dl, A, B, C, D=D, z=z)
+    ys = PT.from_dev(y[0][:, torch.from_numpy(CH).cuda()])
+    torch.cuda.synchronize()
+    del x, z, dl, y
+    torch.cuda.empty_cache()
+    steps = np.arange(L)
+    idx = lambda k: (k * n + steps[:, None] * DIM + CH[None, :]) % P
+    dh = np.stack([W.to_f64(g["delta"][idx(k)], "bf16")[None] for k in range(2)])
+    r = oracle.selscan_bidir(_host(g, "x", steps, CH), dh, g["A"][:, CH].astype(np.float64), W.to_f64(g["B"], "bf16"),
+                             W.to_f64(g["C"], "bf16"), D=g["D"][:, CH].astype(np.float64), z=_host(g, "z", steps, CH))
+    err = PT.rel_err(ys, r[0])
+    _say("large bidir", dict(L=L, dim=DIM, channels=CH.tolist()), "max rel err", err)
+    assert err <= PT.TOL["bf16"], err

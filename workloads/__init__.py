@@ -237,21 +237,24 @@ def generate(
     return out
 
 
-def generate_periodic(seqlen: int, dim: int, period: int, dtype: str = "bf16", dstate: int = 16,
+def generate_periodic(seqlen: int, dim: int, period: int, dtype: str = "bf16", dstate: int = 16, ndir: int = 1,
                       seed: int = SEED_BASE + 70) -> Dict[str, np.ndarray]:
     """Inputs of one batch row too large to draw whole: the per-token tensors x, z, delta and a
-    cotangent dy are given as seeded blocks of ``period`` values, element i of the full
-    [seqlen, dim] tensor (row-major) being element i mod period of its block; B and C
-    ([1, seqlen, dstate]), A and D are drawn whole, with the distributions of ``generate``."""
+    cotangent dy are given as seeded blocks of ``period`` values, element i of the full tensor
+    (row-major; delta [ndir, 1, seqlen, dim] with ndir > 1, else [1, seqlen, dim]) being element
+    i mod period of its block; B and C ([ndir,] 1, seqlen, dstate), A and D are drawn whole, with
+    the distributions of ``generate``."""
+    lead = (ndir,) if ndir > 1 else ()
     out: Dict[str, np.ndarray] = {}
     out["x"] = _normal(seed, 0, (period,), dtype)
     out["z"] = _normal(seed, 1, (period,), dtype)
     out["delta"] = _log_uniform(seed, 2, (period,), 1e-3, 1e-1, dtype)
     out["dy"] = _normal(seed, 7, (period,), dtype)
-    out["B"] = _normal(seed, 3, (1, seqlen, dstate), dtype)
-    out["C"] = _normal(seed, 4, (1, seqlen, dstate), dtype)
-    out["D"] = _normal(seed, 5, (dim,))
-    out["A"] = np.ascontiguousarray(np.broadcast_to(-np.arange(1, dstate + 1, dtype=np.float32), (dim, dstate)))
+    out["B"] = _normal(seed, 3, lead + (1, seqlen, dstate), dtype)
+    out["C"] = _normal(seed, 4, lead + (1, seqlen, dstate), dtype)
+    out["D"] = _normal(seed, 5, lead + (dim,))
+    A = -np.arange(1, dstate + 1, dtype=np.float32)
+    out["A"] = np.ascontiguousarray(np.broadcast_to(A, lead + (dim, dstate)))
     return out
 
 
