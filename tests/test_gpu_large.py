@@ -12,7 +12,10 @@ channels; dB on the last 48 steps over all channels (the adjoint starts at the s
 dB does not involve the state) and dC on the first 48 steps (the state starts at zero there and
 dC does not involve the adjoint); and the bidirectional forward at the same size, whose second
 direction's delta starts 2.28e9 elements into its tensor and whose two directions' fp32 partial
-rows (a direction-split launch) are added by the merge kernel, on the same five channels."""
+rows (a direction-split launch) are added by the merge kernel, on the same five channels; the
+SS2D forward on two 512 x 512 maps of 4,344 channels (its four directions' fp32 partial rows run
+to 9.1e9 elements, their index maps divide by the map's side); and the causal conv1d (k = 4 +
+SiLU) on the first tensor's shape."""
 import sys
 
 import numpy as np
@@ -157,4 +160,61 @@ def test_bidirectional_past_2_32_elements():
                              W.to_f64(g["C"], "bf16"), D=g["D"][:, CH].astype(np.float64), z=_host(g, "z", steps, CH))
     err = PT.rel_err(ys, r[0])
     _say("large bidir", dict(L=L, dim=DIM, channels=CH.tolist()), "max rel err", err)
+    assert err <= PT.TOL["bf16"], err
+
+
+def test_ss2d_past_2_33_partials():
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    bt, H = 2, 512
+    Lm = H * H
+    n = bt * Lm * DIM
+    assert n > 1 << 31
+    _say("large ss2d: drawing the blocks")
+    g = W.generate_periodic(Lm, DIM, P, ndir=4, batch=bt, seed=W.SEED_BASE + 72)
+
+    def tile(block, lead):
+        b = PT.to_dev(block, "bf16")
+        k = int(np.prod(lead))
+        return b.repeat(-(-k * n // P))[:k * n].view(*lead, bt, Lm, DIM)
+
+    x, z, dl = tile(g["x"], ()), tile(g["z"], ()), tile(g["delta"], (4,))
+    B, C = PT.to_dev(g["B"], "bf16"), PT.to_dev(g["C"], "bf16")
+    A, D = PT.to_dev(g["A"], "f32"), PT.to_dev(g["D"], "f32")
+    y = S.ss2d_fwd(x, dl, A, B, C, H, H, D=D, z=z)
+    ys = PT.from_dev(y[:, :, torch.from_numpy(CH).cuda()])
+    torch.cuda.synchronize()
+    del x, z, dl, y
+    torch.cuda.empty_cache()
+    pos = np.arange(bt * Lm)  # (batch row, pixel) flattened
+
+    def host(block, k=0):
+        idx = (k * n + pos[:, None] * DIM + CH[None, :]) % P
+        return W.to_f64(block[idx], "bf16").reshape(bt, Lm, len(CH))
+
+    dh = np.stack([host(g["delta"], k) for k in range(4)])
+    r = oracle.ss2d(host(g["x"]), dh, g["A"][:, CH].astype(np.float64), W.to_f64(g["B"], "bf16"),
+                    W.to_f64(g["C"], "bf16"), H, H, D=g["D"][:, CH].astype(np.float64), z=host(g["z"]))
+    err = PT.rel_err(ys, r)
+    _say("large ss2d", dict(batch=bt, H=H, W=H, dim=DIM, channels=CH.tolist()), "max rel err", err)
+    assert err <= PT.TOL["bf16"], err
+
+
+def test_causal_conv1d_past_2_31_elements(big):
+    import torch
+    import oracle
+    import selective_state_space_51_amd as S
+    g, d = big
+    c = W.generate_conv(1, 1, DIM, 4, "bf16", seed=W.SEED_BASE + 73)
+    w, bias = PT.to_dev(c["weight"], "f32"), PT.to_dev(c["bias"], "f32")
+    out = S.causal_conv1d_fwd(d["x"], w, bias=bias, silu=True)
+    os_ = PT.from_dev(out[0][:, torch.from_numpy(CH).cuda()])
+    torch.cuda.synchronize()
+    del out
+    torch.cuda.empty_cache()
+    r = oracle.causal_conv1d(_host(g, "x", np.arange(L), CH), c["weight"][CH].astype(np.float64),
+                             bias=c["bias"][CH].astype(np.float64), silu=True)
+    err = PT.rel_err(os_, r[0])
+    _say("large conv1d", dict(L=L, dim=DIM, channels=CH.tolist()), "max rel err", err)
     assert err <= PT.TOL["bf16"], err

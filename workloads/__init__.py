@@ -238,11 +238,11 @@ def generate(
 
 
 def generate_periodic(seqlen: int, dim: int, period: int, dtype: str = "bf16", dstate: int = 16, ndir: int = 1,
-                      seed: int = SEED_BASE + 70) -> Dict[str, np.ndarray]:
-    """Inputs of one batch row too large to draw whole: the per-token tensors x, z, delta and a
-    cotangent dy are given as seeded blocks of ``period`` values, element i of the full tensor
-    (row-major; delta [ndir, 1, seqlen, dim] with ndir > 1, else [1, seqlen, dim]) being element
-    i mod period of its block; B and C ([ndir,] 1, seqlen, dstate), A and D are drawn whole, with
+                      batch: int = 1, seed: int = SEED_BASE + 70) -> Dict[str, np.ndarray]:
+    """Inputs too large to draw whole: the per-token tensors x, z, delta and a cotangent dy are
+    given as seeded blocks of ``period`` values, element i of the full tensor (row-major; delta
+    [ndir, batch, seqlen, dim] with ndir > 1, else [batch, seqlen, dim]) being element i mod
+    period of its block; B and C ([ndir,] batch, seqlen, dstate), A and D are drawn whole, with
     the distributions of ``generate``."""
     lead = (ndir,) if ndir > 1 else ()
     out: Dict[str, np.ndarray] = {}
@@ -250,8 +250,8 @@ def generate_periodic(seqlen: int, dim: int, period: int, dtype: str = "bf16", d
     out["z"] = _normal(seed, 1, (period,), dtype)
     out["delta"] = _log_uniform(seed, 2, (period,), 1e-3, 1e-1, dtype)
     out["dy"] = _normal(seed, 7, (period,), dtype)
-    out["B"] = _normal(seed, 3, lead + (1, seqlen, dstate), dtype)
-    out["C"] = _normal(seed, 4, lead + (1, seqlen, dstate), dtype)
+    out["B"] = _normal(seed, 3, lead + (batch, seqlen, dstate), dtype)
+    out["C"] = _normal(seed, 4, lead + (batch, seqlen, dstate), dtype)
     out["D"] = _normal(seed, 5, lead + (dim,))
     A = -np.arange(1, dstate + 1, dtype=np.float32)
     out["A"] = np.ascontiguousarray(np.broadcast_to(A, lead + (dim, dstate)))
