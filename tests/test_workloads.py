@@ -75,3 +75,23 @@ def test_bench_refuses_several_gpus():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_periodic_blocks_are_deterministic_shaped_and_distributed():
+    """The inputs of the tests past 32-bit offsets: the same values on every call, the shapes the
+    scan entry points take, and the distributions of the ordinary generator."""
+    a = W.generate_periodic(300, 24, 5003, ndir=4, batch=2, seed=123)
+    b = W.generate_periodic(300, 24, 5003, ndir=4, batch=2, seed=123)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    for k in ("x", "z", "delta", "dy"):
+        assert a[k].shape == (5003,) and a[k].dtype == np.uint16, k
+    assert a["B"].shape == a["C"].shape == (4, 2, 300, 16)
+    assert a["A"].shape == (4, 24, 16) and np.array_equal(a["A"][1, 5], -np.arange(1, 17, dtype=np.float32))
+    assert a["D"].shape == (4, 24)
+    one = W.generate_periodic(300, 24, 5003)
+    assert one["B"].shape == (1, 300, 16) and one["A"].shape == (24, 16) and one["D"].shape == (24,)
+    d = W.to_f64(a["delta"], "bf16")
+    assert d.min() >= 1e-3 * (1 - 2 ** -8) and d.max() <= 1e-1 * (1 + 2 ** -8)
+    x = W.to_f64(a["x"], "bf16")
+    assert abs(x.mean()) < 0.1 and abs(x.std() - 1) < 0.1
