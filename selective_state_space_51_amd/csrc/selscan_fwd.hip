@@ -588,9 +588,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
 #pragma unroll
                     for (int j = 0; j < KK; ++j) dt[j] = softplus(dt[j]);
                 }
-                if (!fast && !(s0 + CHK <= L && ncols == CT)) {
+                if (!fast && !(s0 + CHK <= L && ncols == CT) && (args.bias || args.softplus)) {
                     // steps past the sequence end and channels past dim get delta = 0, the
-                    // identity step (staged x there is 0 too)
+                    // identity step (staged x there is 0 too).  Staging leaves zeros there, so
+                    // only a bias or softplus (which move 0) needs the mask.
                     const float limf = (float)lim;
 #pragma unroll
                     for (int j = 0; j < KK; ++j) dt[j] *= __builtin_amdgcn_fmed3f(limf - (float)j, 0.f, 1.f);
