@@ -1,6 +1,7 @@
 """CPU tests of the C ABI: the library loads, exports what include/selscan.h declares,
 and rejects bad arguments on the host before any HIP call (no GPU needed: every call
-here returns from validation; none reaches a launch)."""
+here returns from validation, except one made in a child process that sees no HIP device,
+whose launch the runtime rejects)."""
 import ctypes
 import subprocess
 
@@ -427,3 +428,38 @@ def test_clocked_forward_arguments():
     assert S.selscan_clock_stamps_bytes(S.SELSCAN_OP_SS2D, 2, 40) == 2 * 3 * 4 * 32
     assert S.selscan_clock_stamps_bytes(S.SELSCAN_OP_FWD, 2, 40) == 2 * 3 * 32
     assert S.selscan_clock_stamps_bytes(7, 2, 40) == 0
+
+
+_NO_DEVICE_CALL = r'''
+import ctypes, sys
+hip = ctypes.CDLL("libamdhip64.so")
+n = ctypes.c_int(0)
+if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0:
+    print("SKIP a device is visible")  # never launch with fake pointers where a GPU could run it
+    sys.exit(0)
+import selective_state_space_51_amd as S
+P, MB = 0x10000, 1 << 20
+rc = S.lib.selscan_fwd(P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB, None, None, None, 0, P + 8 * MB,
+                       1, 16, 8, 16, S.SELSCAN_BF16, None, 0, None)
+msg = S.lib.selscan_last_hip_error()
+print("RC", rc, (msg or b"").decode())
+'''
+
+
+def test_hip_error_path_without_a_device():
+    """Arguments that pass every host check, with no HIP device visible: the launch is rejected by
+    the runtime, and the call returns SELSCAN_E_HIP with the runtime's message (the child process
+    hides every device and checks that none is visible before it calls; nothing runs on a GPU)."""
+    import os
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
+    out = subprocess.run([sys.executable, "-c", _NO_DEVICE_CALL], capture_output=True, text=True, env=env,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))), timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    line = out.stdout.strip().splitlines()[-1]
+    if line.startswith("SKIP"):
+        pytest.skip(line)
+    parts = line.split(" ", 2)
+    assert parts[0] == "RC" and int(parts[1]) == 7, line  # SELSCAN_E_HIP
+    assert len(parts) == 3 and parts[2] and parts[2] != "no error", line
+    assert S.status_str(7) == "the HIP runtime rejected the kernel launch"
