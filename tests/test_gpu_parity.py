@@ -61,6 +61,18 @@ def test_workload_small(idx, ov):
     _check(w.kind, w, inp, H=w.H, Wd=w.W, window=w.window)
 
 
+@pytest.mark.parametrize("idx,ov", [(0, {}), (1, dict(batch=2, seqlen=300, dim=1536))],
+                         ids=["s6_fp32_b1_L256_D16", "mamba130m_layer_b2_L300"])
+def test_workload_small_softplus_form(idx, ov):
+    """Delta in the form the single-S6-scan workload states it: softplus(w), w drawn so that delta
+    keeps its log-uniform distribution (and the 130M-layer shape, which shares that workload's
+    distributions), every output against the oracle."""
+    w = W.WORKLOADS[idx]
+    _say("small softplus form", w.name, ov)
+    inp = W.generate(w, with_w=True, **ov)
+    _check(w.kind, w, inp, softplus=True)
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6], ids=[W.WORKLOADS[i].name for i in (1, 2, 3, 4, 5, 6)])
 def test_workload_full_size_sampled(idx):
     """The workloads' full sizes in the launch configuration the benchmark times; the oracle
