@@ -150,6 +150,20 @@ def kernel_clock(S, torch, run, op, w, dev, launches: int):
             "source": "in-kernel s_memtime / s_memrealtime of selscan_chunked (selscan_scan_fwd_clocked)"}
 
 
+def memory_clock_mhz():
+    """The HBM clock the driver reports as current (the level marked '*' in the card's
+    pp_dpm_mclk), read once after the timed region; None where the file is not readable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_mclk")):
+        try:
+            for line in open(path):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
 def bwd_algorithmic_bytes(w) -> int:
     """Bytes a fused backward must move at least once: x, dy, z and each direction's delta and
     chunk states read, dx, dz and each direction's ddelta written (io dtype); each direction's
@@ -529,6 +543,8 @@ def main() -> int:
             op, c0["x"], c0["delta"], c0["A"], c0["B"], c0["C"], s, D=c0["D"], z=c0["z"], y=sets[0]["y"],
             workspace=ws, zoh=args.zoh, delta_bias=c0.get("delta_bias"), delta_softplus=args.softplus, stream=stream,
             **geo), op, w, dev, min(args.steps, 10))
+        clock["mclk_mhz"] = memory_clock_mhz()
+        clock["mclk_source"] = "current level of the card's pp_dpm_mclk (sysfs), after the timed region"
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / args.steps
     kern_ms = float(np.mean(launch_ms))
