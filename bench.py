@@ -122,17 +122,24 @@ def kernel_code_hash(names, so_path: str = LIB_SO) -> str:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_clock(S, torch, run, op, w, dev, launches: int):
-    """Shader clock of the scan kernel itself: `launches` back-to-back calls of the clocked forward
-    (the timed code path plus two counter reads and four stores per workgroup) right after the timed
-    region; per workgroup the s_memtime (shader clock) and s_memrealtime (100 MHz) counters at its
-    start and end.  Returns the clock in MHz weighted by workgroup time, with the kernel time of
-    those launches."""
+def kernel_clock_prepare(S, torch, op, w, dev, launches: int):
+    """Stamp buffers and events for `kernel_clock`, allocated before the timed region so that the
+    clocked launches follow its last launch without an idle gap (after a few milliseconds of idle
+    the shader clock drops and takes about ten launches to climb back)."""
     nb = S.selscan_clock_stamps_bytes(op, w.batch, w.dim)
     bufs = [torch.zeros(nb // 8, dtype=torch.int64, device=dev) for _ in range(launches)]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    return bufs, ev
+
+
+def kernel_clock(torch, run, prepared):
+    """Shader clock of the scan kernel itself: back-to-back calls of the clocked forward (the timed
+    code path plus two counter reads and four stores per workgroup), enqueued right after the timed
+    region's closing synchronize; per workgroup the s_memtime (shader clock) and s_memrealtime
+    (100 MHz) counters at its start and end.  Returns the clock in MHz weighted by workgroup time,
+    with the kernel time of those launches."""
+    bufs, ev = prepared
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
     for (a, b), s in zip(ev, bufs):
         a.record(stream)
         run(s)
@@ -145,9 +152,10 @@ def kernel_clock(S, torch, run, op, w, dev, launches: int):
         clk += float((v[used, 1] - v[used, 0]).sum())
         rt += float((v[used, 3] - v[used, 2]).sum())
     ms = [a.elapsed_time(b) for a, b in ev]
-    return {"sclk_mhz": clk / (rt / 1e8) / 1e6 if rt > 0 else None, "launches": launches,
+    return {"sclk_mhz": clk / (rt / 1e8) / 1e6 if rt > 0 else None, "launches": len(bufs),
             "kernel_ms": sum(ms) / len(ms),
-            "source": "in-kernel s_memtime / s_memrealtime of selscan_chunked (selscan_scan_fwd_clocked)"}
+            "source": "in-kernel s_memtime / s_memrealtime of selscan_chunked (selscan_scan_fwd_clocked), "
+                      "launched right after the timed region"}
 
 
 def memory_clock_mhz():
@@ -522,6 +530,8 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    clocked = not bwd and not args.state
+    prepared = kernel_clock_prepare(S, torch, op, w, dev, min(args.steps, 10)) if clocked else None
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -537,12 +547,12 @@ def main() -> int:
     wall = time.perf_counter() - t0
     # the shader clock of the same kernel, over launches right after the timed region
     clock = None
-    if not bwd and not args.state:
+    if clocked:
         c0 = sets[0]["t"]
-        clock = kernel_clock(S, torch, lambda s: S.selscan_scan_fwd_clocked(
+        clock = kernel_clock(torch, lambda s: S.selscan_scan_fwd_clocked(
             op, c0["x"], c0["delta"], c0["A"], c0["B"], c0["C"], s, D=c0["D"], z=c0["z"], y=sets[0]["y"],
             workspace=ws, zoh=args.zoh, delta_bias=c0.get("delta_bias"), delta_softplus=args.softplus, stream=stream,
-            **geo), op, w, dev, min(args.steps, 10))
+            **geo), prepared)
         clock["mclk_mhz"] = memory_clock_mhz()
         clock["mclk_source"] = "current level of the card's pp_dpm_mclk (sysfs), after the timed region"
     launch_ms = [a.elapsed_time(b) for a, b in ev]

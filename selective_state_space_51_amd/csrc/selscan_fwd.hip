@@ -480,8 +480,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             const int64_t s0 = (int64_t)q * CHK;
             __builtin_amdgcn_s_setprio(2);
             // the previous chunk is done with every tile (a one-chunk sequence's only chunk of a
-            // direction follows the direction's opening barrier, which covers this)
-            if constexpr (KK == kK) lds_barrier();
+            // direction follows the direction's opening barrier, which covers this).  Where the y
+            // tile has LDS space of its own, the previous chunk's y-tile barrier already follows
+            // every wave's last read of the tiles written here (its state loop comes first), so
+            // only the fp32 form, whose y tile sits in the x/delta space, waits here.
+            if constexpr (KK == kK && !S::kYOwn) lds_barrier();
             commit();
             lds_barrier();
             clk.add(0);
