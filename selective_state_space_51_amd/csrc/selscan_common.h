@@ -341,6 +341,29 @@ __device__ __forceinline__ void store8(T *p, int n, bool vec, const float v[8]) 
         if (e < n) p[e] = Io<T>::to(v[e]);
 }
 
+// store8 with the streaming (nontemporal) hint on the vector path, for outputs that consecutive
+// lanes write as whole cache lines and that the kernel does not read back.  (Outputs written as
+// pieces of lines that other lanes or workgroups complete later keep the plain store: those
+// pieces are merged in L2 before they go to memory.)
+template <typename T>
+__device__ __forceinline__ void store8_stream(T *p, int n, bool vec, const float v[8]) {
+    if (vec && n >= 8) {
+        if constexpr (sizeof(T) == 4) {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+            __builtin_nontemporal_store(a, (f32x4 *)p);
+            __builtin_nontemporal_store(b, (f32x4 *)(p + 4));
+        } else {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 q = {Io<T>::to2(v[0], v[1]), Io<T>::to2(v[2], v[3]), Io<T>::to2(v[4], v[5]),
+                             Io<T>::to2(v[6], v[7])};
+            __builtin_nontemporal_store(q, (u32x4 *)p);
+        }
+        return;
+    }
+    store8(p, n, vec, v);
+}
+
 __device__ __forceinline__ void load_f8(const float *p, int n, bool vec, float v[8]) {
     if (vec && n >= 8) {
         const float4 q = *(const float4 *)p, q2 = *(const float4 *)(p + 4);

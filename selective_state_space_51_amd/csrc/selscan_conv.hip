@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void causal_conv1d_kernel(Conv1dParams p) {
             for (int i = 0; i < K; ++i) a = fmaf(f[e * K + i], raw_f32(raw[u + i], e), a);
             v[e] = act(a, p.silu);
         }
-        store8(out + (t0 + u) * dim, nv, vec, v);
+        store8_stream(out + (t0 + u) * dim, nv, vec, v);
     }
     if (p.state_out && tb == p.ntb - 1) {
         // the last K-1 input rows (state rows where the sequence is shorter), raw copies
