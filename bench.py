@@ -48,7 +48,7 @@ METRIC = "selective-scan fwd B·L·D·N elem/s + achieved HBM GB/s vs peak, 1 GP
 LIB_SO = os.path.join(ROOT, "selective_state_space_51_amd", "libselscan.so")
 # the kernels (mangled names) a counter record covers, per pass and workload kind; the record is
 # valid while their machine code in the built library is unchanged
-_FWD = "_ZN12_GLOBAL__N_115selscan_chunkedItLi{k}ELb0ELi{kk}EEEvNS_6ParamsE"
+_FWD = "_ZN12_GLOBAL__N_115selscan_chunkedItLi{k}ELb0ELi{kk}ELi{occ}EEEvNS_6ParamsE"
 _BWD = ("_ZN12_GLOBAL__N_119selscan_bwd_chunkedItLi{k}ELb0EEEvNS_9BwdParamsE",
         "_ZN12_GLOBAL__N_118selscan_bwd_reduceItLi{k}EEEvNS_15BwdReduceParamsE")
 _KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
@@ -57,12 +57,21 @@ _KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
 _MERGE = "_ZN12_GLOBAL__N_113selscan_mergeItEEvNS_11MergeParamsE"
 
 
-def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool = False):
+def fwd_occ3(kind: str, seqlen: int, batch: int, dim: int, cus: int) -> bool:
+    """Whether the library launches its three-workgroup forward (the rule in selscan_fwd.hip,
+    Euler Bbar, bf16 io): the scan order, more than 208 steps, and a grid of between two and three
+    workgroups per compute unit."""
+    g = batch * (-(-dim // 16))
+    return kind == "selscan" and seqlen > 208 and 2 * cus < g <= 3 * cus
+
+
+def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool = False, occ3: bool = False):
     k = _KIND[kind]
     if pass_ == "fwd":
         # sequences of at most 208 steps run the 13-steps-per-lane instance; a direction-split
         # grid adds the merge of the directions' rows
-        return [_FWD.format(k=k, kk=13 if seqlen <= 208 else 16)] + ([_MERGE] if split else [])
+        kk = 13 if seqlen <= 208 else 16
+        return [_FWD.format(k=k, kk=kk, occ=3 if occ3 and kk == 16 and k == 0 else 2)] + ([_MERGE] if split else [])
     if pass_ == "bwd":
         return [n.format(k=k) for n in _BWD]
     if kind in ("ss2d", "local_ss2d"):
@@ -186,7 +195,7 @@ def bwd_algorithmic_bytes(w) -> int:
 
 
 def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan", seqlen: int = 1 << 30,
-                     split: bool = False):
+                     split: bool = False, occ3: bool = False):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
     kernels' current machine code; else None."""
     try:
@@ -194,7 +203,7 @@ def measured_traffic(workload: str, pass_: str = "fwd", kind: str = "selscan", s
     except (OSError, ValueError):
         return None
     e = t.get(workload + ("" if pass_ == "fwd" else "/" + pass_))
-    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind, seqlen, split)):
+    if not e or e.get("kernel_code_sha") != kernel_code_hash(profiled_kernels(pass_, kind, seqlen, split, occ3)):
         return None
     return e.get("bytes_per_launch")
 
@@ -578,8 +587,10 @@ def main() -> int:
                  "simds": N_SIMDS, "sclk_mhz": sclk}
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
     split = w.ndir > 1 and w.batch * (-(-w.dim // 16)) < 1024
+    occ3 = not bwd and w.dtype == "bf16" and fwd_occ3(
+        w.kind, w.seqlen, w.batch, w.dim, torch.cuda.get_device_properties(0).multi_processor_count)
     traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(
-        w.name, args.pass_, w.kind, w.seqlen, split and args.pass_ == "fwd")
+        w.name, args.pass_, w.kind, w.seqlen, split and args.pass_ == "fwd", occ3)
     if bwd:
         kname = "selscan_bwd_chunked + selscan_bwd_merge + selscan_bwd_reduce" if split else \
             "selscan_bwd_chunked + selscan_bwd_reduce"

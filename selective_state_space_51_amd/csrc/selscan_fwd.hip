@@ -25,6 +25,7 @@
 //    direction adds, gates and writes y once.
 #include "selscan_common.h"
 
+#include <atomic>
 #include <mutex>
 
 namespace selscan_rt {
@@ -169,7 +170,7 @@ struct Params {
 // row covers 256 contiguous bytes (no bank conflicts).  The scan reads A, D and bias of the
 // current direction from one slot; those of a workgroup's later directions (up to KD - 1) wait
 // in slots of their own.
-template <typename T, int KD>
+template <typename T, int KD, int OCC = 2>
 struct Lds {
     static constexpr int kCT = kTC;                                  // channels per tile
     static constexpr int kV = 16 / (int)sizeof(T);                    // io elements per piece
@@ -177,9 +178,10 @@ struct Lds {
     static constexpr int kIoBytes = kCT * kXP * (int)sizeof(T);       // x or delta tile
     static constexpr int kYBytes = kCT * kFP * 4;                     // y tile fp32
     // bf16 io: the y tile has space of its own, so a wave writes its outputs without waiting
-    // for the other waves to finish reading x and delta.  fp32 io: y reuses the x/delta space
-    // (space of its own would leave room for only one workgroup per compute unit).
-    static constexpr bool kYOwn = sizeof(T) == 2;
+    // for the other waves to finish reading x and delta.  fp32 io, and the three-workgroup form:
+    // y reuses the x/delta space (space of its own would leave room for one workgroup fewer per
+    // compute unit).
+    static constexpr bool kYOwn = sizeof(T) == 2 && OCC == 2;
     static constexpr int kXD = 2 * kIoBytes;
     static constexpr int kY = kYOwn ? kXD : 0;
     static constexpr int kB = kYOwn ? kXD + kYBytes : (kXD > kYBytes ? kXD : kYBytes);  // B [state][step]
@@ -223,6 +225,26 @@ __device__ __forceinline__ void scan16x2(float &b0, float &b1, float &a0, float 
         : "+v"(b0), "+v"(b1), "+v"(a0), "+v"(a1), "+v"(h0), "+v"(h1));
 }
 
+// The same scan for one state at a time (the three-workgroup form, whose waves have fewer
+// registers): s_nop 1 before each DPP read of a value written by the instruction before it.
+__device__ __forceinline__ void scan16(float &b, float &a, float &h) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_mov_b32_dpp %2, %0 row_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(b), "+v"(a), "+v"(h));
+}
+
 // One workgroup: 4 waves, a tile of 16 channels of one batch row, every direction.
 //
 // Lane maps of the staging and output items (wave w, lane i of the wave) are chosen so that
@@ -247,10 +269,15 @@ __device__ unsigned long long g_fwd_phase[kPhaseWaves * 8];
 // KK: scan steps per lane, 16 (chunks of 256 steps) or, for sequences of at most 16 KK steps,
 // fewer (the sequence is one chunk): the LDS tiles keep 16 slots per lane, and slot 16 l + j
 // holds chunk step KK l + j for j < KK (the slots past KK are left out everywhere).
-template <typename T, int KIND, bool ZOH, int KK>
-__global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
+// OCC: workgroups per compute unit the kernel is built for, 2 (the registers of two states at a
+// time) or 3 (one state at a time, the y tile in the x/delta space; bf16 io, scan order, Euler
+// Bbar and 16 steps per lane only).
+template <typename T, int KIND, bool ZOH, int KK, int OCC = 2>
+__global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
     constexpr int KD = KIND == SELSCAN_OP_FWD ? 1 : KIND == SELSCAN_OP_BIDIR ? 2 : 4;  // directions
-    using S = Lds<T, KD>;
+    static_assert(OCC == 2 || (OCC == 3 && sizeof(T) == 2 && KIND == SELSCAN_OP_FWD && !ZOH && KK == kK),
+                  "the three-workgroup form");
+    using S = Lds<T, KD, OCC>;
     constexpr int CT = kTC;
     constexpr int NW = kN * (int)sizeof(T) / 4;  // dwords of one 16-value B or C row
     static_assert(CT * kN == 256, "one (channel, state) carry entry per thread");
@@ -507,7 +534,11 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             Raw8<T> zr[2];  // read only where it was loaded
             int64_t ooff[2] = {0, 0};
             constexpr bool mid_issue = KIND == SELSCAN_OP_FWD && KK == kK && sizeof(T) == 2 && !ZOH;
-            auto issue_loads = [&]() {
+            // the three-workgroup form issues them after the state loop: its registers do not
+            // hold the loaded rows, or z, across the loop (issued in the loop, z alone spilled 21
+            // more VGPRs; the rows as well, 39)
+            constexpr bool late_issue = mid_issue && OCC == 3;
+            auto issue_z = [&]() {
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const int64_t s = s0 + cstep(so + 128 * r);
@@ -522,6 +553,8 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                         }
                     }
                 }
+            };
+            auto issue_next = [&]() {
                 if constexpr (fast || !multi) {
                     if (q + 1 < nchunks) fetch(k, q + 1, fast_c);
                 } else {
@@ -529,6 +562,10 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     const bool next_dir = q + 1 == nchunks;
                     if (!next_dir || k + 1 < k_end) fetch(next_dir ? k + 1 : k, next_dir ? 0 : q + 1, fast_c);
                 }
+            };
+            auto issue_loads = [&]() {
+                issue_z();
+                issue_next();
             };
             if constexpr (!mid_issue) {
 #pragma unroll
@@ -611,6 +648,41 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
             clk.add(2);
             const float *Bc = Bs + 4 * l;
             const float *Cc = Cs + 4 * l;
+            if constexpr (OCC == 3) {
+                // one state at a time
+#pragma unroll 1
+                for (int n = 0; n < kN; ++n) {
+                    const float an = As[cl * kN + n];
+                    float e[kK], u[kK], bb;
+                    {
+                        float Bv[kK];
+#pragma unroll
+                        for (int pc = 0; pc < kK / 4; ++pc)
+                            *(float4 *)&Bv[4 * pc] = *(const float4 *)&Bc[n * kFP + pc * (kLPR * 4)];
+#pragma unroll
+                        for (int j = 0; j < kK; ++j) {
+                            e[j] = __builtin_amdgcn_exp2f(dt[j] * an);
+                            u[j] = dx[j] * Bv[j];
+                            bb = j == 0 ? u[0] : fmaf(e[j], bb, u[j]);  // from a zero state
+                        }
+                    }
+                    float a = __builtin_amdgcn_exp2f(an * sdt);
+                    float h = carry_src[n];  // the channel's carry in its first lane, else zero
+                    bb = fmaf(a, h, bb);
+                    scan16(bb, a, h);
+                    if (l == kLPR - 1) Cy[cl * kN + n] = bb;
+                    float Cv[kK];
+#pragma unroll
+                    for (int pc = 0; pc < kK / 4; ++pc)
+                        *(float4 *)&Cv[4 * pc] = *(const float4 *)&Cc[n * kFP + pc * (kLPR * 4)];
+#pragma unroll
+                    for (int j = 0; j < kK; ++j) {
+                        h = fmaf(e[j], h, u[j]);
+                        yv[j] = fmaf(Cv[j], h, yv[j]);
+                    }
+                }
+                if constexpr (late_issue) issue_loads();
+            } else {
 #pragma unroll 1
             for (int n = 0; n < kN; n += 2) {
                 if constexpr (mid_issue) {
@@ -667,6 +739,7 @@ __global__ __launch_bounds__(256, 2) void selscan_chunked(Params p) {
                     yv[j] = fmaf(C0[j], h0, yv[j]);
                     yv[j] = fmaf(C1[j], h1, yv[j]);
                 }
+            }
             }
             __builtin_amdgcn_s_setprio(2);
             clk.add(3);
@@ -811,6 +884,39 @@ __global__ __launch_bounds__(256) void selscan_merge(MergeParams m) {
     store8((T *)m.y + off, nv, vec, s);
 }
 
+// The three-workgroup form for a grid of `blocks` workgroups on a device of `cus` compute units:
+// where two workgroups per unit leave a second, partial round (2 cus < blocks <= 3 cus), three per
+// unit run the grid in one.  Each round of that form takes 1.89x as long as one of the
+// two-workgroup form (measured on the Mamba-130M layer shape, 768 workgroups on 256 units:
+// 0.148 against 0.157 ms), so it pays in that band only.
+bool occ3_wanted(int64_t blocks, int cus) {
+#ifdef SELSCAN_OCC3_ALWAYS
+    (void)blocks, (void)cus;
+    return true;
+#else
+    return cus > 0 && blocks > 2 * (int64_t)cus && blocks <= 3 * (int64_t)cus;
+#endif
+}
+
+// compute units of the device that `stream` launches on (0 if unknown), cached per device
+int stream_cus(void *stream) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return 0;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return 0;
+    }
+    constexpr int kDevs = 64;
+    static std::atomic<int> cache[kDevs];  // zero: not yet asked
+    if (dev < 0 || dev >= kDevs) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <typename T, int KIND>
 int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     Params c = a;
@@ -823,6 +929,10 @@ int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true, kK>
                            : short13 ? (const void *)&selscan_chunked<T, KIND, false, 13>
                                      : (const void *)&selscan_chunked<T, KIND, false, kK>;
+    if constexpr (sizeof(T) == 2 && KIND == SELSCAN_OP_FWD) {
+        if (!zoh && !short13 && occ3_wanted(blocks, stream_cus(stream)))
+            kern = (const void *)&selscan_chunked<T, KIND, false, kK, 3>;
+    }
     hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
     if (e == hipSuccess && c.split && c.L > 0) {
         MergeParams m;

@@ -98,6 +98,25 @@ def test_one_chunk_many_ragged_tiles(idx, ov):
     _check(w.kind, w, inp, channels=[0, 1, 15, 16, 17, 31, 32, 255, 256, 263])
 
 
+@pytest.mark.parametrize("L,opts", [(600, {}), (1024, dict(softplus=True, use_bias=True)), (1024, dict(use_z=False))],
+                         ids=["L600", "L1024_softplus_bias", "L1024_no_gate"])
+def test_three_workgroup_form(L, opts):
+    """A single-direction bf16 grid of 2.5 workgroups per compute unit (between two and three per
+    unit, where the library launches its three-workgroup form), each batch row ending in an
+    8-channel tile, full and ragged chunks: every output against the oracle."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    batch = 3
+    tiles = (5 * cus // 2 + batch - 1) // batch  # per batch row
+    dim = 16 * tiles - 8
+    assert 2 * cus < batch * tiles <= 3 * cus
+    sp = bool(opts.get("softplus"))
+    base = W.Workload("occ3", "selscan", batch, L, dim, 16, "bf16", True, index=9)
+    _say("three-workgroup form", cus, batch, L, dim, opts)
+    inp = W.generate(base, with_w=sp, with_bias=sp)
+    _check("selscan", base, inp, **opts)
+
+
 @pytest.mark.parametrize("variant", ["zoh", "softplus"])
 def test_benchmark_shape_variants_sampled(variant):
     """The Mamba-1.4B-layer shape (batch 2 x L 65536 x D 4096, bf16) with the zero-order-hold Bbar,
