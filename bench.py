@@ -59,10 +59,11 @@ _MERGE = "_ZN12_GLOBAL__N_113selscan_mergeItEEvNS_11MergeParamsE"
 
 def fwd_occ3(kind: str, seqlen: int, batch: int, dim: int, cus: int) -> bool:
     """Whether the library launches its three-workgroup forward (the rule in selscan_fwd.hip,
-    Euler Bbar, bf16 io): the scan order, more than 208 steps, and a grid of between two and three
-    workgroups per compute unit."""
+    Euler Bbar, bf16 io): the scan order, more than 208 steps, and 1.25 r3 < r2 for the rounds of
+    workgroups at three (r3) and two (r2) per compute unit."""
     g = batch * (-(-dim // 16))
-    return kind == "selscan" and seqlen > 208 and 2 * cus < g <= 3 * cus
+    r2, r3 = -(-g // (2 * cus)), -(-g // (3 * cus))
+    return kind == "selscan" and seqlen > 208 and 5 * r3 < 4 * r2
 
 
 def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool = False, occ3: bool = False):

@@ -884,17 +884,23 @@ __global__ __launch_bounds__(256) void selscan_merge(MergeParams m) {
     store8((T *)m.y + off, nv, vec, s);
 }
 
-// The three-workgroup form for a grid of `blocks` workgroups on a device of `cus` compute units:
-// where two workgroups per unit leave a second, partial round (2 cus < blocks <= 3 cus), three per
-// unit run the grid in one.  Each round of that form takes 1.89x as long as one of the
-// two-workgroup form (measured on the Mamba-130M layer shape, 768 workgroups on 256 units:
-// 0.148 against 0.157 ms), so it pays in that band only.
+// The three-workgroup form for a grid of `blocks` workgroups on a device of `cus` compute units.
+// Rounds of workgroups: r2 = ceil(blocks / 2 cus) for the two-workgroup form, r3 = ceil(blocks /
+// 3 cus) for this one, whose round takes longer (one state at a time, loads issued after the state
+// loop, a third barrier); it is launched where 1.25 r3 < r2.  A sweep of the scan order (bf16, 2,048
+// steps, 1.5 to 9 workgroups per unit, 200 warm-up launches) put the break-even ratio between 1.0
+// and 1.33 for every grid size measured: e.g. 2.25-3 per unit 0.125 -> 0.105-0.108 ms, 3.4-3.75 per
+// unit 0.145-0.149 (two-workgroup form) against 0.155-0.159, 9 per unit 0.358 -> 0.331 ms; one
+// round of either (the Mamba-1.4B layer's 512 workgroups) keeps the two-workgroup form.
 bool occ3_wanted(int64_t blocks, int cus) {
 #ifdef SELSCAN_OCC3_ALWAYS
     (void)blocks, (void)cus;
     return true;
 #else
-    return cus > 0 && blocks > 2 * (int64_t)cus && blocks <= 3 * (int64_t)cus;
+    if (cus <= 0) return false;
+    const int64_t r2 = (blocks + 2 * (int64_t)cus - 1) / (2 * (int64_t)cus);
+    const int64_t r3 = (blocks + 3 * (int64_t)cus - 1) / (3 * (int64_t)cus);
+    return 5 * r3 < 4 * r2;
 #endif
 }
 
