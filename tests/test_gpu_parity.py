@@ -407,6 +407,29 @@ def test_state_in_out(dtype, batch, L, dim):
     assert ey <= PT.TOL[dtype] and eh <= PT.TOL["f32"] * (1 if dtype == "f32" else 100), (ey, eh)
 
 
+def test_state_in_out_three_workgroup_form():
+    """State in and out in the three-workgroup form (bf16, a grid of 2.5 workgroups per compute
+    unit): y and h_last from a given h0 against the oracle, and a scan split at a chunk boundary
+    (the first part's h_last as the second part's h0) equal to the whole bit for bit."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    batch = 3
+    tiles = (5 * cus // 2 + batch - 1) // batch
+    dim, L = 16 * tiles - 8, 800  # both parts of the split exceed 208 steps (16 steps per lane)
+    _say("state, three-workgroup form", cus, batch, L, dim)
+    w, inp, h0 = _state_case("bf16", batch, L, dim)
+    y, hl = _run_state(inp, "bf16", h0)
+    torch.cuda.synchronize()
+    ry, rh = _oracle_state(inp, "bf16", h0)
+    ey, eh = PT.rel_err(PT.from_dev(y), ry), PT.rel_err(PT.from_dev(hl), rh)
+    _say("state, three-workgroup form: y err", ey, "h_last err", eh)
+    assert ey <= PT.TOL["bf16"] and eh <= PT.TOL["f32"] * 100, (ey, eh)
+    y1, h1 = _run_state(inp, "bf16", h0, hi=512)
+    y2, h2 = _run_state(inp, "bf16", h1, lo=512)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], dim=1), y) and torch.equal(h2, hl)
+
+
 @pytest.mark.parametrize("m", [512, 300])
 def test_state_split_equals_whole(m):
     """Scanning [0, m) and then [m, L) from the first part's h_last equals one scan: bit-for-bit
