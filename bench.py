@@ -57,13 +57,13 @@ _KIND = {"selscan": 0, "bidir": 1, "ss2d": 2, "local_ss2d": 3}
 _MERGE = "_ZN12_GLOBAL__N_113selscan_mergeItEEvNS_11MergeParamsE"
 
 
-def fwd_occ3(kind: str, seqlen: int, batch: int, dim: int, cus: int) -> bool:
+def fwd_occ3(kind: str, seqlen: int, batch: int, dim: int, cus: int, split: bool = False) -> bool:
     """Whether the library launches its three-workgroup forward (the rule in selscan_fwd.hip,
-    Euler Bbar, bf16 io): the scan order, more than 208 steps, and 1.25 r3 < r2 for the rounds of
-    workgroups at three (r3) and two (r2) per compute unit."""
-    g = batch * (-(-dim // 16))
+    Euler Bbar, bf16 io): the scan order or the bidirectional one, more than 208 steps, and
+    1.25 r3 < r2 for the rounds of workgroups at three (r3) and two (r2) per compute unit."""
+    g = batch * (-(-dim // 16)) * (2 if split else 1)
     r2, r3 = -(-g // (2 * cus)), -(-g // (3 * cus))
-    return kind == "selscan" and seqlen > 208 and 5 * r3 < 4 * r2
+    return kind in ("selscan", "bidir") and seqlen > 208 and 5 * r3 < 4 * r2
 
 
 def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool = False, occ3: bool = False):
@@ -72,7 +72,7 @@ def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool =
         # sequences of at most 208 steps run the 13-steps-per-lane instance; a direction-split
         # grid adds the merge of the directions' rows
         kk = 13 if seqlen <= 208 else 16
-        return [_FWD.format(k=k, kk=kk, occ=3 if occ3 and kk == 16 and k == 0 else 2)] + ([_MERGE] if split else [])
+        return [_FWD.format(k=k, kk=kk, occ=3 if occ3 and kk == 16 and k <= 1 else 2)] + ([_MERGE] if split else [])
     if pass_ == "bwd":
         return [n.format(k=k) for n in _BWD]
     if kind in ("ss2d", "local_ss2d"):
@@ -589,7 +589,7 @@ def main() -> int:
     # the counter record is for the plain call of the pass (no state in/out, Euler Bbar, delta as given)
     split = w.ndir > 1 and w.batch * (-(-w.dim // 16)) < 1024
     occ3 = not bwd and w.dtype == "bf16" and fwd_occ3(
-        w.kind, w.seqlen, w.batch, w.dim, torch.cuda.get_device_properties(0).multi_processor_count)
+        w.kind, w.seqlen, w.batch, w.dim, torch.cuda.get_device_properties(0).multi_processor_count, split)
     traffic = None if (args.zoh or args.state or args.softplus) else measured_traffic(
         w.name, args.pass_, w.kind, w.seqlen, split and args.pass_ == "fwd", occ3)
     if bwd:

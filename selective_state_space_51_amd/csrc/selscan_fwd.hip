@@ -270,12 +270,14 @@ __device__ unsigned long long g_fwd_phase[kPhaseWaves * 8];
 // fewer (the sequence is one chunk): the LDS tiles keep 16 slots per lane, and slot 16 l + j
 // holds chunk step KK l + j for j < KK (the slots past KK are left out everywhere).
 // OCC: workgroups per compute unit the kernel is built for, 2 (the registers of two states at a
-// time) or 3 (one state at a time, the y tile in the x/delta space; bf16 io, scan order, Euler
-// Bbar and 16 steps per lane only).
+// time) or 3 (one state at a time, the y tile in the x/delta space; bf16 io, the scan and the
+// bidirectional orders, Euler Bbar and 16 steps per lane only: the four-direction orders' LDS,
+// with their per-direction parameter slots, does not fit three times in a compute unit).
 template <typename T, int KIND, bool ZOH, int KK, int OCC = 2>
 __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
     constexpr int KD = KIND == SELSCAN_OP_FWD ? 1 : KIND == SELSCAN_OP_BIDIR ? 2 : 4;  // directions
-    static_assert(OCC == 2 || (OCC == 3 && sizeof(T) == 2 && KIND == SELSCAN_OP_FWD && !ZOH && KK == kK),
+    static_assert(OCC == 2 || (OCC == 3 && sizeof(T) == 2 && !ZOH && KK == kK &&
+                               (KIND == SELSCAN_OP_FWD || KIND == SELSCAN_OP_BIDIR)),
                   "the three-workgroup form");
     using S = Lds<T, KD, OCC>;
     constexpr int CT = kTC;
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
             // the three-workgroup form issues them after the state loop: its registers do not
             // hold the loaded rows, or z, across the loop (issued in the loop, z alone spilled 21
             // more VGPRs; the rows as well, 39)
-            constexpr bool late_issue = mid_issue && OCC == 3;
+            constexpr bool late_issue = OCC == 3;
             auto issue_z = [&]() {
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
                 issue_z();
                 issue_next();
             };
-            if constexpr (!mid_issue) {
+            if constexpr (!mid_issue && !late_issue) {
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const int64_t s = s0 + cstep(so + 128 * r);
@@ -891,7 +893,9 @@ __global__ __launch_bounds__(256) void selscan_merge(MergeParams m) {
 // steps, 1.5 to 9 workgroups per unit, 200 warm-up launches) put the break-even ratio between 1.0
 // and 1.33 for every grid size measured: e.g. 2.25-3 per unit 0.125 -> 0.105-0.108 ms, 3.4-3.75 per
 // unit 0.145-0.149 (two-workgroup form) against 0.155-0.159, 9 per unit 0.358 -> 0.331 ms; one
-// round of either (the Mamba-1.4B layer's 512 workgroups) keeps the two-workgroup form.
+// round of either (the Mamba-1.4B layer's 512 workgroups) keeps the two-workgroup form.  The
+// bidirectional order takes the same rule (VideoMamba clip, 1,536 direction-split workgroups: 0.264
+// -> 0.252 ms).
 bool occ3_wanted(int64_t blocks, int cus) {
 #ifdef SELSCAN_OCC3_ALWAYS
     (void)blocks, (void)cus;
@@ -935,7 +939,7 @@ int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true, kK>
                            : short13 ? (const void *)&selscan_chunked<T, KIND, false, 13>
                                      : (const void *)&selscan_chunked<T, KIND, false, kK>;
-    if constexpr (sizeof(T) == 2 && KIND == SELSCAN_OP_FWD) {
+    if constexpr (sizeof(T) == 2 && (KIND == SELSCAN_OP_FWD || KIND == SELSCAN_OP_BIDIR)) {
         if (!zoh && !short13 && occ3_wanted(blocks, stream_cus(stream)))
             kern = (const void *)&selscan_chunked<T, KIND, false, kK, 3>;
     }

@@ -407,6 +407,30 @@ def test_state_in_out(dtype, batch, L, dim):
     assert ey <= PT.TOL[dtype] and eh <= PT.TOL["f32"] * (1 if dtype == "f32" else 100), (ey, eh)
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split_grid", "direction_walk"])
+def test_bidir_three_workgroup_form(split):
+    """The bidirectional scan in the three-workgroup form, bf16: a direction-split grid of 5
+    workgroups per compute unit (one direction each, partial rows added by the merge) and a
+    walk over both directions on 4.5 tiles per unit, each batch row ending in an 8-channel tile;
+    every output against the oracle."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if split:
+        batch = 2
+        tiles = (5 * cus // 2 + batch - 1) // batch  # 2 directions x batch x tiles ~ 5 per unit
+        L = 600
+    else:
+        batch = 4
+        tiles = (9 * cus // 2 + batch - 1) // batch  # batch x tiles ~ 4.5 per unit, not split
+        L = 300
+    if not split and batch * tiles < 1024:
+        pytest.skip("this device's grid would be direction-split")
+    dim = 16 * tiles - 8
+    base = W.Workload("occ3_bidir", "bidir", batch, L, dim, 16, "bf16", True, index=10)
+    _say("bidir three-workgroup form", cus, batch, L, dim, split)
+    _check("bidir", base, W.generate(base))
+
+
 def test_state_in_out_three_workgroup_form():
     """State in and out in the three-workgroup form (bf16, a grid of 2.5 workgroups per compute
     unit): y and h_last from a given h0 against the oracle, and a scan split at a chunk boundary
