@@ -59,11 +59,12 @@ _MERGE = "_ZN12_GLOBAL__N_113selscan_mergeItEEvNS_11MergeParamsE"
 
 def fwd_occ3(kind: str, seqlen: int, batch: int, dim: int, cus: int, split: bool = False) -> bool:
     """Whether the library launches its three-workgroup forward (the rule in selscan_fwd.hip,
-    Euler Bbar, bf16 io): the scan order or the bidirectional one, more than 208 steps, and
-    1.25 r3 < r2 for the rounds of workgroups at three (r3) and two (r2) per compute unit."""
-    g = batch * (-(-dim // 16)) * (2 if split else 1)
+    Euler Bbar, bf16 io): more than 208 steps, and 1.25 r3 < r2 for the rounds of workgroups at
+    three (r3) and two (r2) per compute unit (a direction-split grid has a workgroup per direction
+    and tile)."""
+    g = batch * (-(-dim // 16)) * ({"selscan": 1, "bidir": 2}.get(kind, 4) if split else 1)
     r2, r3 = -(-g // (2 * cus)), -(-g // (3 * cus))
-    return kind in ("selscan", "bidir") and seqlen > 208 and 5 * r3 < 4 * r2
+    return seqlen > 208 and 5 * r3 < 4 * r2
 
 
 def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool = False, occ3: bool = False):
@@ -72,7 +73,7 @@ def profiled_kernels(pass_: str, kind: str, seqlen: int = 1 << 30, split: bool =
         # sequences of at most 208 steps run the 13-steps-per-lane instance; a direction-split
         # grid adds the merge of the directions' rows
         kk = 13 if seqlen <= 208 else 16
-        return [_FWD.format(k=k, kk=kk, occ=3 if occ3 and kk == 16 and k <= 1 else 2)] + ([_MERGE] if split else [])
+        return [_FWD.format(k=k, kk=kk, occ=3 if occ3 and kk == 16 else 2)] + ([_MERGE] if split else [])
     if pass_ == "bwd":
         return [n.format(k=k) for n in _BWD]
     if kind in ("ss2d", "local_ss2d"):

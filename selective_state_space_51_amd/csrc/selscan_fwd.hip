@@ -189,9 +189,14 @@ struct Lds {
     static constexpr int kA = kC + kN * kFP * 4;                      // A*log2e [ch][state]
     static constexpr int kCarry = kA + kCT * kN * 4;                  // chunk carry [ch][state]
     static constexpr int kDb = kCarry + kCT * kN * 4;                 // D, bias [ch][2]
-    static constexpr int kAx = kDb + kCT * 8;                         // later directions' A, D, bias
-    static constexpr int kDbx = kAx + (KD - 1) * kCT * kN * 4;
-    static constexpr int kBytes = kDbx + (KD - 1) * kCT * 8;
+    // later directions' A, D, bias (the three-workgroup form of the four-direction orders reads
+    // them from memory at the direction switch instead: with them, three such workgroups would not
+    // fit a CU)
+    static constexpr bool kNoSlots = OCC == 3 && KD > 2;
+    static constexpr int kSlots = kNoSlots ? 0 : KD - 1;
+    static constexpr int kAx = kDb + kCT * 8;
+    static constexpr int kDbx = kAx + kSlots * kCT * kN * 4;
+    static constexpr int kBytes = kDbx + kSlots * kCT * 8;
     // position of chunk step s in an io tile row
     __device__ static int xpos(int s) { return ((s & 15) / kV) * (kLPR * kV) + (s >> 4) * kV + (s % kV); }
 };
@@ -276,8 +281,7 @@ __device__ unsigned long long g_fwd_phase[kPhaseWaves * 8];
 template <typename T, int KIND, bool ZOH, int KK, int OCC = 2>
 __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
     constexpr int KD = KIND == SELSCAN_OP_FWD ? 1 : KIND == SELSCAN_OP_BIDIR ? 2 : 4;  // directions
-    static_assert(OCC == 2 || (OCC == 3 && sizeof(T) == 2 && !ZOH && KK == kK &&
-                               (KIND == SELSCAN_OP_FWD || KIND == SELSCAN_OP_BIDIR)),
+    static_assert(OCC == 2 || (OCC == 3 && sizeof(T) == 2 && !ZOH && KK == kK),
                   "the three-workgroup form");
     using S = Lds<T, KD, OCC>;
     constexpr int CT = kTC;
@@ -352,12 +356,13 @@ __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
     // start instead of waiting on memory there.  The first chunk's fetch sits outside the
     // direction loop too: a single-direction kernel then has a loop of one known iteration,
     // and the compiler keeps fewer scalars alive (fewer spills into vector lanes).
-    float av[KD], dv[KD], bv[KD];
+    constexpr int KP = S::kNoSlots ? 1 : KD;  // directions whose parameters are loaded up front
+    float av[KP], dv[KP], bv[KP];
     {
         const int ch = tid / kN, n = tid % kN;
         const int64_t cc = c0 + ch < dim ? c0 + ch : 0, cd = c0 + tid < dim ? c0 + tid : 0;
 #pragma unroll
-        for (int j = 0; j < KD; ++j) {
+        for (int j = 0; j < KP; ++j) {
             const int k = k_begin + j;
             av[j] = dv[j] = bv[j] = 0.f;
             if (k < k_end && nchunks > 0) {
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
     fetch(k_begin, 0, BoolC<false>{});
     // read in the first direction's first chunk, after the barrier that follows its staging
 #pragma unroll
-    for (int j = 0; j < KD; ++j) {
+    for (int j = 0; j < KP; ++j) {
         if (k_begin + j >= k_end) continue;
         float *a = j == 0 ? As : (float *)(smem + S::kAx) + (j - 1) * (CT * kN);
         float *d = j == 0 ? Db : (float *)(smem + S::kDbx) + (j - 1) * (2 * CT);
@@ -455,9 +460,19 @@ __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
         // full barrier
         __syncthreads();
         if (k > k_begin) {
-            const int j = k - k_begin - 1;
-            As[tid] = ((const float *)(smem + S::kAx))[j * (CT * kN) + tid];
-            if (tid < 2 * CT) Db[tid] = ((const float *)(smem + S::kDbx))[j * (2 * CT) + tid];
+            if constexpr (S::kNoSlots) {
+                const int ch = tid / kN, n = tid % kN;
+                const int64_t cc = c0 + ch < dim ? c0 + ch : 0, cd = c0 + tid < dim ? c0 + tid : 0;
+                As[tid] = p.A[(k * dim + cc) * kN + n] * kLog2e;
+                if (tid < CT) {
+                    Db[2 * tid] = p.D ? p.D[k * dim + cd] : 0.f;
+                    Db[2 * tid + 1] = p.bias ? p.bias[k * dim + cd] : 0.f;
+                }
+            } else {
+                const int j = k - k_begin - 1;
+                As[tid] = ((const float *)(smem + S::kAx))[j * (CT * kN) + tid];
+                if (tid < 2 * CT) Db[tid] = ((const float *)(smem + S::kDbx))[j * (2 * CT) + tid];
+            }
         }
         for (int i = tid; i < CT * kN; i += 256) {
             const int ch = i / kN, n = i % kN;
@@ -939,7 +954,7 @@ int launch_tiles(const Params &a, int64_t batch, bool zoh, void *stream) {
     const void *kern = zoh ? (const void *)&selscan_chunked<T, KIND, true, kK>
                            : short13 ? (const void *)&selscan_chunked<T, KIND, false, 13>
                                      : (const void *)&selscan_chunked<T, KIND, false, kK>;
-    if constexpr (sizeof(T) == 2 && (KIND == SELSCAN_OP_FWD || KIND == SELSCAN_OP_BIDIR)) {
+    if constexpr (sizeof(T) == 2) {
         if (!zoh && !short13 && occ3_wanted(blocks, stream_cus(stream)))
             kern = (const void *)&selscan_chunked<T, KIND, false, kK, 3>;
     }

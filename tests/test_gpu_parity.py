@@ -431,6 +431,21 @@ def test_bidir_three_workgroup_form(split):
     _check("bidir", base, W.generate(base))
 
 
+@pytest.mark.parametrize("kind", ["ss2d", "local_ss2d"])
+def test_cross_scan_three_workgroup_form(kind):
+    """The four-direction orders in the three-workgroup form, bf16 (direction-split grid of about
+    5 workgroups per compute unit on 24 x 24 maps, each batch row ending in an 8-channel tile; the
+    windowed order with 6 x 6 windows): every output against the oracle."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    dim, H = 184, 24
+    batch = (5 * cus + 4 * 12 - 1) // (4 * 12)  # 4 directions x 12 tiles per batch row
+    win = 6 if kind == "local_ss2d" else 0
+    base = W.Workload("occ3_" + kind, kind, batch, H * H, dim, 16, "bf16", False, H=H, W=H, index=12, window=win)
+    _say("cross-scan three-workgroup form", kind, cus, batch, H, dim)
+    _check(kind, base, W.generate(base), H=H, Wd=H, window=win)
+
+
 def test_state_in_out_three_workgroup_form():
     """State in and out in the three-workgroup form (bf16, a grid of 2.5 workgroups per compute
     unit): y and h_last from a given h0 against the oracle, and a scan split at a chunk boundary
