@@ -275,9 +275,9 @@ __device__ unsigned long long g_fwd_phase[kPhaseWaves * 8];
 // fewer (the sequence is one chunk): the LDS tiles keep 16 slots per lane, and slot 16 l + j
 // holds chunk step KK l + j for j < KK (the slots past KK are left out everywhere).
 // OCC: workgroups per compute unit the kernel is built for, 2 (the registers of two states at a
-// time) or 3 (one state at a time, the y tile in the x/delta space; bf16 io, the scan and the
-// bidirectional orders, Euler Bbar and 16 steps per lane only: the four-direction orders' LDS,
-// with their per-direction parameter slots, does not fit three times in a compute unit).
+// time) or 3 (one state at a time, the y tile in the x/delta space, and for the four-direction
+// orders no LDS slots for later directions' parameters; bf16 io, Euler Bbar and 16 steps per lane
+// only).
 template <typename T, int KIND, bool ZOH, int KK, int OCC = 2>
 __global__ __launch_bounds__(256, OCC) void selscan_chunked(Params p) {
     constexpr int KD = KIND == SELSCAN_OP_FWD ? 1 : KIND == SELSCAN_OP_BIDIR ? 2 : 4;  // directions
@@ -909,8 +909,8 @@ __global__ __launch_bounds__(256) void selscan_merge(MergeParams m) {
 // and 1.33 for every grid size measured: e.g. 2.25-3 per unit 0.125 -> 0.105-0.108 ms, 3.4-3.75 per
 // unit 0.145-0.149 (two-workgroup form) against 0.155-0.159, 9 per unit 0.358 -> 0.331 ms; one
 // round of either (the Mamba-1.4B layer's 512 workgroups) keeps the two-workgroup form.  The
-// bidirectional order takes the same rule (VideoMamba clip, 1,536 direction-split workgroups: 0.264
-// -> 0.252 ms).
+// multi-direction orders take the same rule (direction-split grids of 1,536 workgroups: VideoMamba
+// clip 0.264 -> 0.252 ms, SS2D map 0.478 -> 0.453, windowed map 0.482 -> 0.458 ms with the merge).
 bool occ3_wanted(int64_t blocks, int cus) {
 #ifdef SELSCAN_OCC3_ALWAYS
     (void)blocks, (void)cus;
