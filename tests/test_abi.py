@@ -397,6 +397,9 @@ def test_bench_finds_profiled_kernels_in_library():
             h = bench.kernel_code_hash(bench.profiled_kernels(ps, kind))
             assert not h.startswith("missing"), (ps, kind, h)
             assert len(h) == 16
+        # the three-workgroup forward form of every order
+        h = bench.kernel_code_hash(bench.profiled_kernels("fwd", kind, occ3=True))
+        assert not h.startswith("missing"), (kind, h)
 
 
 def test_scan_fwd_noalloc_arguments():
