@@ -397,7 +397,8 @@ def test_bench_finds_profiled_kernels_in_library():
             h = bench.kernel_code_hash(bench.profiled_kernels(ps, kind))
             assert not h.startswith("missing"), (ps, kind, h)
             assert len(h) == 16
-        # the three-workgroup forward form of every order
+    # the three-workgroup forward form of every order
+    for kind in ("selscan", "bidir", "ss2d", "local_ss2d"):
         h = bench.kernel_code_hash(bench.profiled_kernels("fwd", kind, occ3=True))
         assert not h.startswith("missing"), (kind, h)
 
